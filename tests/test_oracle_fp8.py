@@ -1,0 +1,112 @@
+"""Pins of the FP8 E4M3 oracle against things other than itself.
+
+Exhaustive over the 256 codes; checked against the OCP spec's table points,
+against PyTorch's float8_e4m3fn conversion (a library routine; it rounds to
+nearest-even but does not saturate, so it is only used inside +-448) and
+against closed-form error bounds.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import synthetic
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _torch_decode(codes):
+    return torch.tensor(np.asarray(codes, dtype=np.uint8)).view(torch.float8_e4m3fn).double().numpy()
+
+
+def test_decode_spec_points():
+    spec = json.load(open(os.path.join(GOLDEN, "e4m3fn_spec_points.json")))
+    for p in spec["points"]:
+        assert oracle.e4m3_decode(p["code"]) == p["value"], p
+        assert oracle.e4m3_encode(p["value"]) == p["code"], p
+    for c in spec["nan_codes"]:
+        assert np.isnan(oracle.e4m3_decode(c))
+
+
+def test_decode_all_codes_match_library():
+    codes = np.arange(256)
+    mine = oracle.e4m3_decode(codes)
+    ref = _torch_decode(codes)
+    same = (mine == ref) | (np.isnan(mine) & np.isnan(ref))
+    assert same.all()
+
+
+def test_encode_decode_roundtrip_every_finite_code():
+    codes = np.array([c for c in range(256) if c not in (127, 255)])
+    assert (oracle.e4m3_encode(oracle.e4m3_decode(codes)) == codes).all()
+
+
+def test_encode_midpoints_and_neighbours_match_library():
+    vals = np.sort(oracle.e4m3_decode(np.arange(127)))
+    mids = (vals[:-1] + vals[1:]) / 2.0
+    # offsets that float32 holds exactly (the library converts from float32)
+    eps = np.abs(mids) * 2.0 ** -18
+    pts = np.concatenate([vals, mids, mids - eps, mids + eps, [2.0 ** -30, 2.0 ** -11, 3 * 2.0 ** -11]])
+    pts = np.concatenate([pts, -pts])
+    pts = pts[np.abs(pts) <= 448.0]
+    mine = oracle.e4m3_encode(pts)
+    assert (pts.astype(np.float32).astype(np.float64) == pts).all()
+    ref = torch.tensor(pts.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert (mine == ref).all(), pts[mine != ref][:10]
+
+
+def test_encode_rne_at_ties_is_even_code():
+    # 1 + 1/16 is halfway between 1.0 (code 56, even) and 1.125 (code 57)
+    assert oracle.e4m3_encode(1.0 + 1.0 / 16) == 56
+    # 1.125 + 1/16 is halfway between 1.125 (57) and 1.25 (58, even)
+    assert oracle.e4m3_encode(1.125 + 1.0 / 16) == 58
+    # halfway between the largest subnormal and the smallest normal
+    assert oracle.e4m3_encode(7.5 * 2.0 ** -9) == 8
+    # half the smallest subnormal rounds to (even) zero
+    assert oracle.e4m3_encode(2.0 ** -10) == 0
+
+
+def test_encode_saturates():
+    assert oracle.e4m3_encode(449.0) == 0x7E
+    assert oracle.e4m3_encode(1e30) == 0x7E
+    assert oracle.e4m3_encode(-1e30) == 0xFE
+    assert oracle.e4m3_encode(np.nan) == 0x7F
+
+
+def test_roundtrip_error_bound_random():
+    rng = np.random.default_rng(5)
+    v = rng.uniform(-448, 448, size=20000) * np.exp2(rng.integers(-14, 1, size=20000))
+    back = oracle.e4m3_decode(oracle.e4m3_encode(v))
+    normal = np.abs(v) >= 2.0 ** -6
+    # relative error of a nearest rounding with 3 mantissa bits is <= 2^-4
+    assert (np.abs(back - v)[normal] <= 2.0 ** -4 * np.abs(v)[normal]).all()
+    # subnormal spacing is 2^-9, half of it is the bound
+    assert (np.abs(back - v)[~normal] <= 2.0 ** -10).all()
+
+
+def test_quant_rows_closed_form():
+    x = synthetic.gen_activation(64, 512, seed=3)
+    codes, scales = oracle.quant_fp8_per_token(x)
+    xf = oracle.bf16_bits_to_f64(x)
+    amax = np.abs(xf).max(axis=1)
+    # the scale is amax / 448 to float32 precision
+    assert np.allclose(scales, amax / 448.0, rtol=2.0 ** -23, atol=0)
+    deq = oracle.e4m3_decode(codes) * scales[:, None].astype(np.float64)
+    # each row's largest element lands on +-448 (code 0x7E / 0xFE)
+    arg = np.abs(xf).argmax(axis=1)
+    assert (codes[np.arange(64), arg] & 0x7F == 0x7E).all()
+    # dequantised error: half an E4M3 step, relative to the row scale
+    rel = np.abs(deq - xf) / np.maximum(np.abs(xf), 2.0 ** -6 * scales[:, None])
+    assert rel.max() <= 2.0 ** -4 * (1 + 1e-6)
+
+
+def test_quant_zero_row_and_sign():
+    x = np.zeros((2, 16), dtype=np.uint16)
+    x[1, 3] = 0xBF80  # -1.0
+    codes, scales = oracle.quant_fp8_per_token(x)
+    assert (codes[0] == 0).all() and np.isfinite(scales[0]) and scales[0] > 0
+    assert codes[1, 3] == 0xFE
+    assert scales[1] == np.float32(1.0) / np.float32(448.0)

@@ -1,0 +1,150 @@
+"""Seeded synthetic inputs shaped like the Wan video-DiT attention layers.
+
+This module only draws numbers. It holds none of the attention or
+quantisation arithmetic: both the CPU oracle and the HIP path receive the
+arrays it returns and nothing else from it.
+
+Shapes follow the workloads on the pages: Wan2.1 latent grids of
+21 x 30 x 52 (480P) and 21 x 45 x 80 (720P, 81 frames) tokens, 12 heads
+(1.3B) or 40 heads (14B) of width 128, and 5120-wide activations.
+
+Recipe (one numpy PCG64 stream per call, fixed draw order):
+  1. four frequency triples f^m drawn without replacement from
+     {0,1,2}^3 minus the zero triple, shared by Q, K and V;
+  2. per tensor X in (Q, K, V), in that order: phases phi[m, head, chan]
+     ~ U[0, 2 pi), then noise z ~ N(0, 1);
+     X = 0.5 z + sum_m 0.5 sin(2 pi (f_t t/T + f_h h/Hg + f_w w/Wg) + phi),
+     with token i at raster position (t, h, w), i = (t*Hg + h)*Wg + w;
+  3. values rounded to bfloat16 (round to nearest even).
+Low-rank projection matrices are N(0, 1/d) (separate stream). The per-token
+gate is drawn directly from the distribution that a near-zero-initialised
+gate projection gives: g = 0.05 + 0.1 z ("amplified" runs: g = 1 + z).
+Activations for the FP8 quantiser are Student-t (nu = 4) with 1% of the
+channels scaled by 20 (outlier channels).
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+
+@dataclasses.dataclass(frozen=True)
+class AttnConfig:
+    name: str
+    B: int
+    H: int
+    d: int
+    T: int
+    Hg: int
+    Wg: int
+    block_q: int
+    block_k: int
+    sparsity: float
+    rank: int
+
+    @property
+    def L(self) -> int:
+        return self.T * self.Hg * self.Wg
+
+
+# The attention workloads. Block sizes of the two 14B layers are not stated
+# on the pages; they take the 128-query x 64-key blocks of the 1.3B layer.
+TINY = AttnConfig("tiny-1024", 1, 2, 64, 4, 16, 16, 64, 64, 0.75, 16)
+WAN13B_480P = AttnConfig("wan1.3b-480p", 1, 12, 128, 21, 30, 52, 128, 64, 0.90, 32)
+WAN14B_480P = AttnConfig("wan14b-480p", 1, 40, 128, 21, 30, 52, 128, 64, 0.95, 32)
+WAN14B_720P = AttnConfig("wan14b-720p", 1, 40, 128, 21, 45, 80, 128, 64, 0.97, 32)
+WAN14B_720P_S90 = dataclasses.replace(WAN14B_720P, name="wan14b-720p-s0.90", sparsity=0.90)
+
+CONFIGS = {c.name: c for c in (TINY, WAN13B_480P, WAN14B_480P, WAN14B_720P, WAN14B_720P_S90)}
+
+# Activation shapes for the per-token FP8 quantiser: one 480P and one 720P
+# token count, 5120 channels (the 14B model width).
+QUANT_480P = (32760, 5120)
+QUANT_720P = (75600, 5120)
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest, ties to even); uint16 bits."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    out = np.empty(u.shape, dtype=np.uint16)
+    # process in chunks to bound temporaries on very large tensors
+    flat_u = u.reshape(-1)
+    flat_o = out.reshape(-1)
+    step = 1 << 24
+    for s in range(0, flat_u.size, step):
+        v = flat_u[s:s + step].astype(np.uint64)
+        nan = (v & 0x7FFFFFFF) > 0x7F800000
+        r = (v + 0x7FFF + ((v >> 16) & 1)) >> 16
+        r = np.where(nan, (v >> 16) | 0x40, r)
+        flat_o[s:s + step] = r.astype(np.uint16)
+    return out
+
+
+def _positions(cfg: AttnConfig):
+    i = np.arange(cfg.L)
+    t = i // (cfg.Hg * cfg.Wg)
+    h = (i // cfg.Wg) % cfg.Hg
+    w = i % cfg.Wg
+    return t, h, w
+
+
+def gen_qkv(cfg: AttnConfig, seed: int = 0):
+    """Q, K, V as bfloat16 bit patterns (uint16), layout [B, L, H, d]."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    triples = [(a, b, c) for a in range(3) for b in range(3) for c in range(3) if (a, b, c) != (0, 0, 0)]
+    pick = rng.choice(len(triples), size=4, replace=False)
+    freqs = np.array([triples[p] for p in pick], dtype=np.float64)  # [4, 3]
+    t, h, w = _positions(cfg)
+    ang = 2.0 * math.pi * (np.outer(t / cfg.T, freqs[:, 0]) + np.outer(h / cfg.Hg, freqs[:, 1])
+                           + np.outer(w / cfg.Wg, freqs[:, 2]))  # [L, 4]
+    basis = np.concatenate([np.sin(ang), np.cos(ang)], axis=1).astype(np.float32)  # [L, 8]
+    HD = cfg.H * cfg.d
+    out = []
+    for _ in range(3):
+        phase = rng.uniform(0.0, 2.0 * math.pi, size=(4, HD))
+        # sin(a + p) = sin a cos p + cos a sin p
+        coef = 0.5 * np.concatenate([np.cos(phase), np.sin(phase)], axis=0).astype(np.float32)  # [8, HD]
+        x = np.empty((cfg.B, cfg.L, HD), dtype=np.float32)
+        for b in range(cfg.B):
+            x[b] = basis @ coef
+            x[b] += 0.5 * rng.standard_normal(size=(cfg.L, HD), dtype=np.float32)
+        out.append(f32_to_bf16_bits(x).reshape(cfg.B, cfg.L, cfg.H, cfg.d))
+        del x
+    return tuple(out)
+
+
+def gen_lowrank_params(cfg: AttnConfig, seed: int = 0):
+    """P_q, P_k (bf16 bits, [rank, d]) drawn N(0, 1/d), shared by all heads."""
+    rng = np.random.Generator(np.random.PCG64(seed + 1_000_003))
+    std = 1.0 / math.sqrt(cfg.d)
+    pq = rng.standard_normal(size=(cfg.rank, cfg.d)) * std
+    pk = rng.standard_normal(size=(cfg.rank, cfg.d)) * std
+    return f32_to_bf16_bits(pq.astype(np.float32)), f32_to_bf16_bits(pk.astype(np.float32))
+
+
+def gen_gate(cfg: AttnConfig, seed: int = 0, amplified: bool = False) -> np.ndarray:
+    """Per-token gate, float32 [B, L] (one scalar per token, shared by heads)."""
+    rng = np.random.Generator(np.random.PCG64(seed + 2_000_003))
+    z = rng.standard_normal(size=(cfg.B, cfg.L))
+    g = (1.0 + z) if amplified else (0.05 + 0.1 * z)
+    return g.astype(np.float32)
+
+
+def gen_activation(M: int, K: int, seed: int = 0, outlier_frac: float = 0.01,
+                   outlier_gain: float = 20.0) -> np.ndarray:
+    """bf16 bits [M, K]: Student-t (nu=4) values, a fixed 1% of channels x20."""
+    rng = np.random.Generator(np.random.PCG64(seed + 3_000_003))
+    n_out = max(1, int(round(outlier_frac * K)))
+    chans = rng.choice(K, size=n_out, replace=False)
+    gain = np.ones(K, dtype=np.float32)
+    gain[chans] = outlier_gain
+    out = np.empty((M, K), dtype=np.uint16)
+    step = max(1, (1 << 24) // K)
+    for s in range(0, M, step):
+        e = min(M, s + step)
+        x = rng.standard_t(4.0, size=(e - s, K)).astype(np.float32) * gain
+        out[s:e] = f32_to_bf16_bits(x)
+    return out
