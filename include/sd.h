@@ -1,0 +1,195 @@
+/*
+ * sd.h -- C ABI of libsd: RoLA compensated sparse attention and per-token
+ * FP8 E4M3 activation quantisation on AMD Instinct MI355X (gfx950).
+ *
+ * The method (robotworld.top SparkDiffusion write-up, section 2.1,
+ * "compensated sparse attention"): the attention of a video DiT is replaced
+ * by a block-sparse softmax branch A_M that keeps a 1-s fraction of the
+ * query/key blocks plus a low-rank compensation branch, fused per token:
+ *     q~_i = R_r(p_i) phi(P_q qn_i),  k~_j = R_r(p_j) phi(P_k kn_j),
+ *     C = sum_j k~_j v_j^T,           O_lr,i = RMSNorm(q~_i^T C),
+ *     O_i = O_s,i + g_i r_i O_lr,i    (r_i = RMS of the sparse output O_s,i).
+ * The FP8 quantiser is the deployment step of section 2.3 of the same page.
+ *
+ * Conventions shared by every entry point:
+ *  - Device pointers are HIP device memory owned by the caller. The library
+ *    never allocates or frees; scratch space is a caller-provided workspace
+ *    whose size the matching *_workspace_size function returns.
+ *  - Per-token tensors are bf16 (or f32 where stated) in [B, L, H, d]
+ *    layout: the d elements of one (batch, token, head) are contiguous and
+ *    the three outer strides are given in ELEMENTS (int64). Strides and the
+ *    base pointers must keep every 8-element (16-byte) group aligned.
+ *  - Tokens are in raster order of a T x Hg x Wg latent grid:
+ *    token i sits at p_i = (t, h, w) with i = (t*Hg + h)*Wg + w.
+ *  - `stream` is a hipStream_t (NULL = the null stream). Every call is
+ *    asynchronous and stream-ordered; nothing synchronises the host.
+ *  - Return value: SD_OK (0) or an SD_ERR_* code. Arguments are validated
+ *    on the host before anything is launched; on a validation error no
+ *    device memory is touched. sd_last_error() gives a thread-local message.
+ *    SD_ERR_HIP reports a launch failure seen right after launching.
+ *  - Calls are thread-safe: the library keeps no state beyond the
+ *    thread-local error text.
+ */
+#ifndef SD_H_
+#define SD_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum sd_status {
+  SD_OK = 0,
+  SD_ERR_INVALID_ARG = 1, /* null pointer, bad size, inconsistent shape   */
+  SD_ERR_UNSUPPORTED = 2, /* valid request outside what the kernels do   */
+  SD_ERR_ALIGN = 3,       /* pointer or stride breaks 16-byte alignment  */
+  SD_ERR_WORKSPACE = 4,   /* workspace missing or too small              */
+  SD_ERR_HIP = 5          /* the HIP runtime reported an error           */
+};
+
+enum sd_dtype { SD_DTYPE_BF16 = 1, SD_DTYPE_F32 = 2 };
+
+enum sd_phi { SD_PHI_ELU1 = 1 }; /* phi(x) = ELU(x) + 1 */
+
+/* Geometry of one attention layer. Supported: d in {64, 128},
+ * block_q in {64, 128}, block_k == 64, L <= 131072, B, H >= 1.
+ * T, Hg, Wg are needed (T*Hg*Wg == L) only by the low-rank branch and the
+ * fused entry; the block map and the sparse branch ignore them.
+ * s?_b, s?_l, s?_h: element strides of Q, K, V and of every output tensor
+ * (so_*) in [B, L, H, d] layout. */
+typedef struct sd_attn_shape {
+  int32_t B, H, L, d;
+  int32_t T, Hg, Wg;
+  int32_t block_q, block_k;
+  int64_t sq_b, sq_l, sq_h;
+  int64_t sk_b, sk_l, sk_h;
+  int64_t sv_b, sv_l, sv_h;
+  int64_t so_b, so_l, so_h;
+} sd_attn_shape;
+
+/* One rotated pair of the rank-truncated 3D RoPE R_r(p): feature dims
+ * (dim, dim+1) rotate by the angle p_axis * theta, axis 0/1/2 = t/h/w. */
+typedef struct sd_rope_pair {
+  int32_t dim;
+  int32_t axis;
+  float theta;
+} sd_rope_pair;
+
+/* Parameters of the low-rank branch (robotworld.top write-up, section 2.1,
+ * q~/k~ and O_lr equations; kais-engine report, section 2.1: proj_q and
+ * proj_k map head_dim to rank).
+ *  rank        16 or 32.
+ *  phi         SD_PHI_ELU1.
+ *  Pq, Pk      device bf16 [rank, d] row-major projections; head h uses
+ *              P + h * P_head_stride (0 = one matrix shared by all heads).
+ *  rope        HOST array of n_rope pairs (read during the call only); the
+ *              pairs must not overlap; dims not in any pair are not rotated.
+ *  rms_eps     epsilon of the RMSNorm of O_lr.
+ *  rms_weight  device bf16 [d] RMSNorm weight, or NULL for ones. */
+typedef struct sd_lowrank_params {
+  int32_t rank;
+  int32_t phi;
+  const void* Pq;
+  const void* Pk;
+  int64_t P_head_stride;
+  const sd_rope_pair* rope;
+  int32_t n_rope;
+  float rms_eps;
+  const void* rms_weight;
+} sd_lowrank_params;
+
+/* Key blocks kept per query block at sparsity s: ceil((1-s)*n_kblocks)
+ * clamped to [1, n_kblocks] (SparkDiffusion README_zh, single-sample
+ * inference: `topk` is the kept fraction, 0.1/0.05/0.03 = 90/95/97%).
+ * Returns -1 if n_kblocks < 1 or s is outside [0, 1). Host only. */
+int sd_keep_count(double sparsity, int n_kblocks);
+
+/* Fills out[0..max_pairs) with the default rank-truncated 3D RoPE: the
+ * rank dims split over (t, h, w) as (r - 2*floor(r/3), floor(r/3),
+ * floor(r/3)), adjacent pairs inside each axis block, theta_m =
+ * base^(-2m/n_axis), an odd last dim of a block left unrotated. Returns the
+ * number of pairs, or -1 on bad arguments. Host only. */
+int sd_rope_default(int rank, double base, sd_rope_pair* out, int max_pairs);
+
+/* ---- (1) block map --------------------------------------------------------
+ * robotworld.top write-up, section 2.1: the sparse branch keeps the top-k
+ * key blocks per query block by a block-level score. Score of query block b
+ * and key block c = mean(Q over b) . mean(K over c), means over the valid
+ * tokens of (possibly partial) blocks, accumulated and compared in float64.
+ * idx: device int32 [B, H, Nq, k_keep], Nq = ceil(L/block_q); each row lists
+ * the k_keep highest-scoring key blocks (equal scores: lower index first)
+ * in ascending order. 1 <= k_keep <= Nk = ceil(L/block_k). */
+size_t sd_block_select_workspace_size(const sd_attn_shape* shape);
+int sd_block_select(const sd_attn_shape* shape, const void* Q, const void* K, int k_keep,
+                    int32_t* idx, void* ws, size_t ws_bytes, void* stream);
+
+/* ---- (2) sparse softmax branch A_M --------------------------------------
+ * robotworld.top write-up, section 2.1 (A_M over the kept 1-s of the
+ * blocks; the dense-attention equation for the softmax form). Every query
+ * of block b attends with softmax(q.k * sm_scale) to the valid keys of the
+ * blocks idx[b, h, b, :] (bf16 operands, f32 accumulation).
+ * Os: [B, L, H, d] at the so_* strides, bf16 or f32 (os_dtype).
+ * rms: optional device f32 [B, L, H] (contiguous) = RMS over d of each
+ * O_s row (the r_i of the fusion), or NULL. */
+int sd_sparse_attn(const sd_attn_shape* shape, const void* Q, const void* K, const void* V,
+                   const int32_t* idx, int k_keep, float sm_scale, void* Os, int os_dtype,
+                   float* rms, void* stream);
+
+/* ---- (3) low-rank branch ---------------------------------------------------
+ * robotworld.top write-up, section 2.1, the q~/k~ and C/O_lr equations:
+ * C[b,h] = sum over all L tokens of k~_j v_j^T (f32 [rank, d]), then
+ * O_lr,i = w * y / sqrt(mean(y^2) + eps) with y = q~_i^T C.
+ * Qn, Kn: the normalised q/k the branch reads (strides of Q and K).
+ * Olr: [B, L, H, d] at the so_* strides, bf16 or f32 (olr_dtype).
+ * C_out: optional device f32 [B, H, rank, d], or NULL. */
+size_t sd_lowrank_workspace_size(const sd_attn_shape* shape, const sd_lowrank_params* lr);
+int sd_lowrank_attn(const sd_attn_shape* shape, const sd_lowrank_params* lr, const void* Qn,
+                    const void* Kn, const void* V, void* Olr, int olr_dtype, float* C_out,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/* ---- (4) gated fusion ------------------------------------------------------
+ * robotworld.top write-up, section 2.1, the O_i equation:
+ * O = O_s + g * r * O_lr with r the RMS over d of the O_s row (computed
+ * here from Os). Os, Olr: in_dtype at the so_* strides; O: bf16 at the
+ * so_* strides (may alias neither input). g: device f32, the gate of
+ * (b, token, head) at g[b*g_stride_b + i*g_stride_l + h*g_stride_h]
+ * (g_stride_h = 0: one gate per token). */
+int sd_gate_fuse(const sd_attn_shape* shape, const void* Os, const void* Olr, int in_dtype,
+                 const float* g, int64_t g_stride_b, int64_t g_stride_l, int64_t g_stride_h,
+                 void* O, void* stream);
+
+/* ---- (5) per-token FP8 E4M3 quantisation ---------------------------------
+ * robotworld.top write-up, section 2.3: a dynamic scale per token (row),
+ * scale and conversion in one pass over memory. For row m of x (bf16,
+ * M x K, row stride ldx elements):
+ *   amax = max(max_k |x_mk|, 1e-12f),  scales[m] = amax / 448 (f32),
+ *   q_mk = E4M3FN(fl32(x_mk * fl32(448 / amax))), nearest-even, saturating.
+ * scales are the dequantisation multipliers. q: uint8 codes, row stride ldq.
+ * Needs K % 8 == 0, ldx % 8 == 0, ldq % 8 == 0, K <= 16384, x 16-byte and
+ * q 8-byte aligned. Non-finite inputs give unspecified codes. */
+int sd_quant_fp8_per_token(const void* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
+                           int64_t ldq, float* scales, void* stream);
+
+/* ---- fused layer -------------------------------------------------------------
+ * The whole path of section 2.1 in one call: block map, sparse branch,
+ * low-rank branch and gated fusion. O: bf16 [B, L, H, d] at the so_*
+ * strides. Qn/Kn may be NULL to read Q/K. g as in sd_gate_fuse. idx_out:
+ * optional device int32 [B, H, Nq, k_keep] receiving the block map used
+ * (NULL keeps it in the workspace). */
+size_t sd_rola_workspace_size(const sd_attn_shape* shape, const sd_lowrank_params* lr, int k_keep);
+int sd_rola_attention(const sd_attn_shape* shape, const sd_lowrank_params* lr, const void* Q,
+                      const void* K, const void* V, const void* Qn, const void* Kn, const float* g,
+                      int64_t g_stride_b, int64_t g_stride_l, int64_t g_stride_h, int k_keep,
+                      float sm_scale, void* O, int32_t* idx_out, void* ws, size_t ws_bytes,
+                      void* stream);
+
+const char* sd_status_string(int status);
+const char* sd_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SD_H_ */

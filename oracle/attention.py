@@ -98,14 +98,15 @@ def dense_attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, sm_scale: float
 def sparse_attention(Q, K, V, idx, bq: int, bk: int, sm_scale: float):
     """Block-sparse softmax attention for one head.
 
-    Q, K, V [L, d]; idx [Nq, k] kept key blocks per query block. Each query
-    of block b attends, with an ordinary softmax, to exactly the valid keys
-    of the blocks idx[b]. Returns (O_s [L, d], r [L]) where r is the RMS of
-    each output row over d (section 2.1: r_i is the RMS of O_s,i).
+    Q [Lq, d], K, V [L, d]; idx [Nq, k] kept key blocks per query block
+    (Q may be a run of whole query blocks, with idx the matching rows). Each
+    query of block b attends, with an ordinary softmax, to exactly the valid
+    keys of the blocks idx[b]. Returns (O_s [Lq, d], r [Lq]) where r is the
+    RMS of each output row over d (section 2.1: r_i is the RMS of O_s,i).
     Reading: r is per (token, head), over the head dimension.
     """
     L, d = Q.shape
-    kr = block_ranges(L, bk)
+    kr = block_ranges(K.shape[0], bk)
     Os = np.empty((L, d))
     for b, (s, e) in enumerate(block_ranges(L, bq)):
         keys = np.concatenate([np.arange(*kr[c]) for c in idx[b]])

@@ -1,0 +1,283 @@
+"""Python binding of libsd (RoLA compensated sparse attention + per-token
+FP8 quant on MI355X). Argument marshalling only: every step runs in the HIP
+kernels of libsd.so; PyTorch provides device memory and the current stream.
+
+The functions carry the names of the C entry points in include/sd.h and
+take torch tensors in [B, L, H, d] layout (d contiguous, strides multiples
+of 8 elements). If libsd.so is missing or fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsd.so")
+
+SD_OK = 0
+SD_ERR_INVALID_ARG = 1
+SD_ERR_UNSUPPORTED = 2
+SD_ERR_ALIGN = 3
+SD_ERR_WORKSPACE = 4
+SD_ERR_HIP = 5
+SD_DTYPE_BF16 = 1
+SD_DTYPE_F32 = 2
+SD_PHI_ELU1 = 1
+
+EXPORTED = [
+    "sd_keep_count", "sd_rope_default", "sd_block_select_workspace_size", "sd_block_select",
+    "sd_sparse_attn", "sd_lowrank_workspace_size", "sd_lowrank_attn", "sd_gate_fuse",
+    "sd_quant_fp8_per_token", "sd_rola_workspace_size", "sd_rola_attention", "sd_status_string",
+    "sd_last_error",
+]
+
+
+class SdError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"libsd status {status}: {msg}")
+        self.status = status
+
+
+class sd_attn_shape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("B", "H", "L", "d", "T", "Hg", "Wg", "block_q", "block_k")] + \
+               [(n, ctypes.c_int64) for n in ("sq_b", "sq_l", "sq_h", "sk_b", "sk_l", "sk_h",
+                                              "sv_b", "sv_l", "sv_h", "so_b", "so_l", "so_h")]
+
+
+class sd_rope_pair(ctypes.Structure):
+    _fields_ = [("dim", ctypes.c_int32), ("axis", ctypes.c_int32), ("theta", ctypes.c_float)]
+
+
+class sd_lowrank_params(ctypes.Structure):
+    _fields_ = [("rank", ctypes.c_int32), ("phi", ctypes.c_int32), ("Pq", ctypes.c_void_p),
+                ("Pk", ctypes.c_void_p), ("P_head_stride", ctypes.c_int64),
+                ("rope", ctypes.POINTER(sd_rope_pair)), ("n_rope", ctypes.c_int32),
+                ("rms_eps", ctypes.c_float), ("rms_weight", ctypes.c_void_p)]
+
+
+_lib = None
+_load_error = None
+
+
+def _declare(lib):
+    P = ctypes.c_void_p
+    S = ctypes.POINTER(sd_attn_shape)
+    LR = ctypes.POINTER(sd_lowrank_params)
+    i32, i64, f32, sz = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    sig = {
+        "sd_keep_count": (i32, [ctypes.c_double, i32]),
+        "sd_rope_default": (i32, [i32, ctypes.c_double, ctypes.POINTER(sd_rope_pair), i32]),
+        "sd_block_select_workspace_size": (sz, [S]),
+        "sd_block_select": (i32, [S, P, P, i32, P, P, sz, P]),
+        "sd_sparse_attn": (i32, [S, P, P, P, P, i32, f32, P, i32, P, P]),
+        "sd_lowrank_workspace_size": (sz, [S, LR]),
+        "sd_lowrank_attn": (i32, [S, LR, P, P, P, P, i32, P, P, sz, P]),
+        "sd_gate_fuse": (i32, [S, P, P, i32, P, i64, i64, i64, P, P]),
+        "sd_quant_fp8_per_token": (i32, [P, i64, i64, i64, P, i64, P, P]),
+        "sd_rola_workspace_size": (sz, [S, LR, i32]),
+        "sd_rola_attention": (i32, [S, LR, P, P, P, P, P, P, i64, i64, i64, i32, f32, P, P, P, sz, P]),
+        "sd_status_string": (ctypes.c_char_p, [i32]),
+        "sd_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+
+
+def lib():
+    """The loaded libsd.so; raises if it is not built or does not load."""
+    global _lib, _load_error
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built (run __graft_entry__.build())")
+        _lib = ctypes.CDLL(LIB_PATH)
+        _declare(_lib)
+    return _lib
+
+
+def _check(status: int):
+    if status != SD_OK:
+        raise SdError(status, lib().sd_last_error().decode())
+
+
+# --------------------------------------------------------------------------
+# host helpers
+# --------------------------------------------------------------------------
+
+def sd_keep_count(sparsity: float, n_kblocks: int) -> int:
+    return lib().sd_keep_count(float(sparsity), int(n_kblocks))
+
+
+def sd_rope_default(rank: int, base: float = 10000.0):
+    buf = (sd_rope_pair * 32)()
+    n = lib().sd_rope_default(int(rank), float(base), buf, 32)
+    if n < 0:
+        raise SdError(SD_ERR_INVALID_ARG, "bad rope arguments")
+    return [(buf[i].dim, buf[i].axis, buf[i].theta) for i in range(n)]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_ptr(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def make_shape(Q, K, V, out_like=None, *, block_q=128, block_k=64, grid=(0, 0, 0)) -> sd_attn_shape:
+    """sd_attn_shape from [B, L, H, d] tensors (out_like gives the so_* strides)."""
+    B, L, H, d = Q.shape
+    T, Hg, Wg = grid
+    s = sd_attn_shape(B, H, L, d, T, Hg, Wg, block_q, block_k)
+    o_strides = out_like.stride() if out_like is not None else (L * H * d, H * d, d, 1)
+    for pre, st in (("sq", Q.stride()), ("sk", K.stride()), ("sv", V.stride()), ("so", o_strides)):
+        if st[3] != 1:
+            raise ValueError("the head dimension must be contiguous")
+        setattr(s, pre + "_b", st[0])
+        setattr(s, pre + "_l", st[1])
+        setattr(s, pre + "_h", st[2])
+    return s
+
+
+class LowrankParams:
+    """Keeps the ctypes struct and the host RoPE array alive together."""
+
+    def __init__(self, Pq, Pk, rank=None, rope=None, rms_eps=1e-6, rms_weight=None, head_stride=0):
+        rank = int(rank if rank is not None else Pq.shape[-2])
+        pairs = rope if rope is not None else sd_rope_default(rank)
+        self._rope = (sd_rope_pair * max(1, len(pairs)))(*[sd_rope_pair(d, a, t) for d, a, t in pairs])
+        self._keep = (Pq, Pk, rms_weight)
+        self.p = sd_lowrank_params(rank, SD_PHI_ELU1, Pq.data_ptr(), Pk.data_ptr(), head_stride,
+                                   ctypes.cast(self._rope, ctypes.POINTER(sd_rope_pair)), len(pairs),
+                                   float(rms_eps), rms_weight.data_ptr() if rms_weight is not None else None)
+
+
+def _workspace(nbytes: int, device):
+    torch = _torch()
+    # 256-byte aligned: the caching allocator returns 512-byte aligned blocks
+    return torch.empty(max(256, int(nbytes)), dtype=torch.uint8, device=device)
+
+
+# --------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# --------------------------------------------------------------------------
+
+def sd_block_select(Q, K, k_keep, *, block_q=128, block_k=64, idx=None, stream=None):
+    """int32 [B, H, Nq, k_keep] block map (ascending rows)."""
+    torch = _torch()
+    B, L, H, d = Q.shape
+    s = make_shape(Q, K, K, block_q=block_q, block_k=block_k)
+    nq = -(-L // block_q)
+    if idx is None:
+        idx = torch.empty((B, H, nq, k_keep), dtype=torch.int32, device=Q.device)
+    ws_n = lib().sd_block_select_workspace_size(ctypes.byref(s))
+    ws = _workspace(ws_n, Q.device)
+    _check(lib().sd_block_select(ctypes.byref(s), _ptr(Q), _ptr(K), int(k_keep), _ptr(idx), _ptr(ws), ws.numel(),
+                                 _stream_ptr(stream)))
+    return idx
+
+
+def sd_sparse_attn(Q, K, V, idx, *, block_q=128, block_k=64, sm_scale=None, out_dtype=None, want_rms=True,
+                   out=None, stream=None):
+    """(O_s [B, L, H, d], rms [B, L, H] or None)."""
+    torch = _torch()
+    B, L, H, d = Q.shape
+    out_dtype = out_dtype or torch.float32
+    if out is None:
+        out = torch.empty((B, L, H, d), dtype=out_dtype, device=Q.device)
+    s = make_shape(Q, K, V, out, block_q=block_q, block_k=block_k)
+    rms = torch.empty((B, L, H), dtype=torch.float32, device=Q.device) if want_rms else None
+    scale = sm_scale if sm_scale is not None else 1.0 / math.sqrt(d)
+    dt = SD_DTYPE_F32 if out.dtype == torch.float32 else SD_DTYPE_BF16
+    _check(lib().sd_sparse_attn(ctypes.byref(s), _ptr(Q), _ptr(K), _ptr(V), _ptr(idx), int(idx.shape[-1]),
+                                float(scale), _ptr(out), dt, _ptr(rms), _stream_ptr(stream)))
+    return out, rms
+
+
+def sd_lowrank_attn(Qn, Kn, V, lr: LowrankParams, *, grid, block_q=128, out_dtype=None, want_C=True, out=None,
+                    stream=None):
+    """(O_lr [B, L, H, d], C [B, H, rank, d] or None)."""
+    torch = _torch()
+    B, L, H, d = Qn.shape
+    out_dtype = out_dtype or torch.float32
+    if out is None:
+        out = torch.empty((B, L, H, d), dtype=out_dtype, device=Qn.device)
+    s = make_shape(Qn, Kn, V, out, block_q=block_q, grid=grid)
+    C = torch.empty((B, H, lr.p.rank, d), dtype=torch.float32, device=Qn.device) if want_C else None
+    ws = _workspace(lib().sd_lowrank_workspace_size(ctypes.byref(s), ctypes.byref(lr.p)), Qn.device)
+    dt = SD_DTYPE_F32 if out.dtype == torch.float32 else SD_DTYPE_BF16
+    _check(lib().sd_lowrank_attn(ctypes.byref(s), ctypes.byref(lr.p), _ptr(Qn), _ptr(Kn), _ptr(V), _ptr(out), dt,
+                                 _ptr(C), _ptr(ws), ws.numel(), _stream_ptr(stream)))
+    return out, C
+
+
+def _gate_strides(g, B, L, H):
+    if g.dim() == 2:  # [B, L]: one gate per token
+        return g.stride(0), g.stride(1), 0
+    return g.stride(0), g.stride(1), g.stride(2)
+
+
+def sd_gate_fuse(Os, Olr, g, *, out=None, stream=None):
+    """O = O_s + g * rms(O_s) * O_lr as bf16 [B, L, H, d]; g [B, L] or [B, L, H]."""
+    torch = _torch()
+    B, L, H, d = Os.shape
+    if out is None:
+        out = torch.empty((B, L, H, d), dtype=torch.bfloat16, device=Os.device)
+    if Olr.stride() != Os.stride() or out.stride() != Os.stride() or Olr.dtype != Os.dtype:
+        raise ValueError("Os, Olr and out must share strides and Os/Olr a dtype")
+    s = make_shape(Os, Os, Os, Os)
+    dt = SD_DTYPE_F32 if Os.dtype == torch.float32 else SD_DTYPE_BF16
+    gb, gl, gh = _gate_strides(g, B, L, H)
+    _check(lib().sd_gate_fuse(ctypes.byref(s), _ptr(Os), _ptr(Olr), dt, _ptr(g), gb, gl, gh, _ptr(out),
+                              _stream_ptr(stream)))
+    return out
+
+
+def sd_quant_fp8_per_token(x, *, q=None, scales=None, stream=None):
+    """(codes uint8 [M, K], scales f32 [M]) for bf16 x [M, K]."""
+    torch = _torch()
+    M, K = x.shape
+    if x.stride(1) != 1:
+        raise ValueError("rows of x must be contiguous")
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _check(lib().sd_quant_fp8_per_token(_ptr(x), M, K, x.stride(0), _ptr(q), q.stride(0), _ptr(scales),
+                                        _stream_ptr(stream)))
+    return q, scales
+
+
+def rola_workspace(Q, lr: LowrankParams, k_keep, *, grid, block_q=128):
+    s = make_shape(Q, Q, Q, block_q=block_q, grid=grid)
+    return _workspace(lib().sd_rola_workspace_size(ctypes.byref(s), ctypes.byref(lr.p), int(k_keep)), Q.device)
+
+
+def sd_rola_attention(Q, K, V, g, lr: LowrankParams, k_keep, *, grid, block_q=128, Qn=None, Kn=None,
+                      sm_scale=None, out=None, idx_out=None, workspace=None, stream=None):
+    """Fused layer: bf16 O [B, L, H, d]."""
+    torch = _torch()
+    B, L, H, d = Q.shape
+    if out is None:
+        out = torch.empty((B, L, H, d), dtype=torch.bfloat16, device=Q.device)
+    if Qn is not None and Qn.stride() != Q.stride():
+        raise ValueError("Qn must have the strides of Q")
+    if Kn is not None and Kn.stride() != K.stride():
+        raise ValueError("Kn must have the strides of K")
+    s = make_shape(Q, K, V, out, block_q=block_q, grid=grid)
+    ws = workspace if workspace is not None else rola_workspace(Q, lr, k_keep, grid=grid, block_q=block_q)
+    scale = sm_scale if sm_scale is not None else 1.0 / math.sqrt(d)
+    gb, gl, gh = _gate_strides(g, B, L, H)
+    _check(lib().sd_rola_attention(ctypes.byref(s), ctypes.byref(lr.p), _ptr(Q), _ptr(K), _ptr(V), _ptr(Qn), _ptr(Kn),
+                                   _ptr(g), gb, gl, gh, int(k_keep), float(scale), _ptr(out), _ptr(idx_out), _ptr(ws),
+                                   ws.numel(), _stream_ptr(stream)))
+    return out

@@ -1,0 +1,499 @@
+// libsd C ABI: host-side validation, workspace layout and kernel dispatch.
+// Semantics of every entry point are documented in include/sd.h.
+#include "sd.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "sd_launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return SD_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(SD_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int kMaxL = 131072;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Geo {
+  int B, H, L, D, bq, bk, Nq, Nk;
+};
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_shape(const sd_attn_shape* s, Geo* g, bool need_grid) {
+  if (!s) return fail(SD_ERR_INVALID_ARG, "shape is NULL");
+  if (s->B < 1 || s->H < 1 || s->L < 1) return fail(SD_ERR_INVALID_ARG, "B, H, L must be >= 1");
+  if (s->d != 64 && s->d != 128) return fail(SD_ERR_UNSUPPORTED, "d = %d (supported: 64, 128)", s->d);
+  if (s->block_q != 64 && s->block_q != 128)
+    return fail(SD_ERR_UNSUPPORTED, "block_q = %d (supported: 64, 128)", s->block_q);
+  if (s->block_k != 64) return fail(SD_ERR_UNSUPPORTED, "block_k = %d (supported: 64)", s->block_k);
+  if (s->L > kMaxL) return fail(SD_ERR_UNSUPPORTED, "L = %d exceeds %d", s->L, kMaxL);
+  if (need_grid) {
+    if (s->T < 1 || s->Hg < 1 || s->Wg < 1 || (int64_t)s->T * s->Hg * s->Wg != s->L)
+      return fail(SD_ERR_INVALID_ARG, "T*Hg*Wg (%d*%d*%d) must equal L = %d", s->T, s->Hg, s->Wg, s->L);
+  }
+  const int64_t st[12] = {s->sq_b, s->sq_l, s->sq_h, s->sk_b, s->sk_l, s->sk_h,
+                          s->sv_b, s->sv_l, s->sv_h, s->so_b, s->so_l, s->so_h};
+  for (int i = 0; i < 12; ++i) {
+    if (st[i] < 0) return fail(SD_ERR_INVALID_ARG, "negative stride");
+    if (st[i] % 8) return fail(SD_ERR_ALIGN, "strides must be multiples of 8 elements (16 bytes)");
+  }
+  g->B = s->B;
+  g->H = s->H;
+  g->L = s->L;
+  g->D = s->d;
+  g->bq = s->block_q;
+  g->bk = s->block_k;
+  g->Nq = (s->L + s->block_q - 1) / s->block_q;
+  g->Nk = (s->L + s->block_k - 1) / s->block_k;
+  if ((int64_t)g->B * g->H * g->Nq >= (int64_t)1 << 31) return fail(SD_ERR_UNSUPPORTED, "too many query blocks");
+  if ((int64_t)g->B * g->H > 65535) return fail(SD_ERR_UNSUPPORTED, "B*H exceeds 65535");
+  return SD_OK;
+}
+
+int check_dev_ptr(const void* p, const char* name, size_t align = 16) {
+  if (!p) return fail(SD_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned(p, align)) return fail(SD_ERR_ALIGN, "%s is not %zu-byte aligned", name, align);
+  return SD_OK;
+}
+
+int check_lowrank(const sd_lowrank_params* lr, const Geo& g) {
+  if (!lr) return fail(SD_ERR_INVALID_ARG, "low-rank params are NULL");
+  if (lr->rank != 16 && lr->rank != 32) return fail(SD_ERR_UNSUPPORTED, "rank = %d (supported: 16, 32)", lr->rank);
+  if (lr->phi != SD_PHI_ELU1) return fail(SD_ERR_UNSUPPORTED, "phi = %d (supported: SD_PHI_ELU1)", lr->phi);
+  int rc;
+  if ((rc = check_dev_ptr(lr->Pq, "Pq"))) return rc;
+  if ((rc = check_dev_ptr(lr->Pk, "Pk"))) return rc;
+  if (lr->P_head_stride < 0 || lr->P_head_stride % 8)
+    return fail(SD_ERR_ALIGN, "P_head_stride must be a non-negative multiple of 8");
+  if (lr->n_rope < 0 || lr->n_rope > sd::kMaxRopePairs || lr->n_rope > lr->rank / 2)
+    return fail(SD_ERR_INVALID_ARG, "n_rope = %d out of range", lr->n_rope);
+  if (lr->n_rope > 0 && !lr->rope) return fail(SD_ERR_INVALID_ARG, "rope is NULL");
+  uint32_t used = 0;
+  for (int i = 0; i < lr->n_rope; ++i) {
+    const sd_rope_pair& p = lr->rope[i];
+    if (p.dim < 0 || p.dim + 1 >= lr->rank || p.axis < 0 || p.axis > 2 || !std::isfinite(p.theta))
+      return fail(SD_ERR_INVALID_ARG, "rope pair %d invalid", i);
+    const uint32_t bits = 3u << p.dim;
+    if (used & bits) return fail(SD_ERR_INVALID_ARG, "rope pairs overlap at pair %d", i);
+    used |= bits;
+  }
+  if (!(lr->rms_eps >= 0.f) || !std::isfinite(lr->rms_eps)) return fail(SD_ERR_INVALID_ARG, "rms_eps invalid");
+  if (lr->rms_weight && !aligned(lr->rms_weight, 2)) return fail(SD_ERR_ALIGN, "rms_weight misaligned");
+  (void)g;
+  return SD_OK;
+}
+
+// Bump allocator over the caller's workspace (or a size computation when
+// base is NULL).
+struct Carve {
+  char* base;
+  size_t off = 0;
+  explicit Carve(void* b) : base(static_cast<char*>(b)) {}
+  void* take(size_t bytes) {
+    off = align_up(off);
+    void* p = base ? base + off : nullptr;
+    off += bytes;
+    return p;
+  }
+};
+
+struct SelectWs {
+  double* qmean;
+  double* kmean;
+  double* S;
+};
+
+SelectWs carve_select(Carve& c, const Geo& g) {
+  SelectWs w;
+  w.qmean = static_cast<double*>(c.take(sizeof(double) * g.B * g.H * g.Nq * g.D));
+  w.kmean = static_cast<double*>(c.take(sizeof(double) * g.B * g.H * g.Nk * g.D));
+  w.S = static_cast<double*>(c.take(sizeof(double) * g.B * g.H * (size_t)g.Nq * g.Nk));
+  return w;
+}
+
+int lowrank_chunks(const Geo& g, int* chunk_tiles) {
+  const int ntiles = (g.L + 63) / 64;
+  const int64_t bh = (int64_t)g.B * g.H;
+  int n_chunks = (int)std::min<int64_t>(ntiles, std::max<int64_t>(1, (2048 + bh - 1) / bh));
+  const int ct = (ntiles + n_chunks - 1) / n_chunks;
+  *chunk_tiles = ct;
+  return (ntiles + ct - 1) / ct;
+}
+
+int max_extent(const sd_attn_shape* s) { return std::max(s->T, std::max(s->Hg, s->Wg)); }
+
+struct LowrankWs {
+  float2* rope_tab;
+  float* partial;
+  uint16_t* ct_hi;
+  uint16_t* ct_lo;
+  int n_chunks, chunk_tiles;
+};
+
+LowrankWs carve_lowrank(Carve& c, const Geo& g, const sd_attn_shape* s) {
+  LowrankWs w;
+  w.n_chunks = lowrank_chunks(g, &w.chunk_tiles);
+  w.rope_tab = static_cast<float2*>(c.take(sizeof(float2) * sd::kMaxRopePairs * max_extent(s)));
+  w.partial = static_cast<float*>(c.take(sizeof(float) * g.B * g.H * (size_t)w.n_chunks * 32 * g.D));
+  w.ct_hi = static_cast<uint16_t*>(c.take(sizeof(uint16_t) * g.B * g.H * g.D * 32));
+  w.ct_lo = static_cast<uint16_t*>(c.take(sizeof(uint16_t) * g.B * g.H * g.D * 32));
+  return w;
+}
+
+sd::RopeArgs rope_args(const sd_lowrank_params* lr, const sd_attn_shape* s) {
+  sd::RopeArgs r{};
+  r.n = lr->n_rope;
+  r.max_ext = max_extent(s);
+  for (int i = 0; i < lr->n_rope; ++i) {
+    r.dim[i] = lr->rope[i].dim;
+    r.axis[i] = lr->rope[i].axis;
+  }
+  return r;
+}
+
+// Low-rank state: RoPE table, partial C per token chunk, finalisation.
+int run_lowrank_state(const sd_attn_shape* s, const Geo& g, const sd_lowrank_params* lr, const void* Kn,
+                      const void* V, float* C_out, const LowrankWs& w, hipStream_t st) {
+  sd::RopeThetas th{};
+  for (int i = 0; i < lr->n_rope; ++i) th.theta[i] = lr->rope[i].theta;
+  hipError_t e = sd::launch_rope_table(th, lr->n_rope, max_extent(s), w.rope_tab, st);
+  if (e != hipSuccess) return hip_fail(e, "rope table");
+  sd::LowrankKvArgs a{};
+  a.Kn = static_cast<const uint16_t*>(Kn);
+  a.V = static_cast<const uint16_t*>(V);
+  a.sk_b = s->sk_b;
+  a.sk_l = s->sk_l;
+  a.sk_h = s->sk_h;
+  a.sv_b = s->sv_b;
+  a.sv_l = s->sv_l;
+  a.sv_h = s->sv_h;
+  a.B = g.B;
+  a.H = g.H;
+  a.L = g.L;
+  a.Hg = s->Hg;
+  a.Wg = s->Wg;
+  a.chunk_tiles = w.chunk_tiles;
+  a.n_chunks = w.n_chunks;
+  a.Pk = static_cast<const uint16_t*>(lr->Pk);
+  a.P_hs = lr->P_head_stride;
+  a.rank = lr->rank;
+  a.rope_tab = w.rope_tab;
+  a.rope = rope_args(lr, s);
+  a.partial = w.partial;
+  e = sd::launch_lowrank_kv(a, g.D, st);
+  if (e != hipSuccess) return hip_fail(e, "low-rank state");
+  e = sd::launch_lowrank_finalize(w.partial, g.B * g.H, w.n_chunks, lr->rank, g.D, C_out, w.ct_hi, w.ct_lo, st);
+  if (e != hipSuccess) return hip_fail(e, "low-rank finalize");
+  return SD_OK;
+}
+
+int run_block_select(const sd_attn_shape* s, const Geo& g, const void* Q, const void* K, int k_keep, int32_t* idx,
+                     const SelectWs& w, hipStream_t st) {
+  hipError_t e = sd::launch_pool_blocks(static_cast<const uint16_t*>(Q), s->sq_b, s->sq_l, s->sq_h, g.B, g.L, g.H,
+                                        g.D, g.bq, w.qmean, st);
+  if (e != hipSuccess) return hip_fail(e, "pool Q");
+  e = sd::launch_pool_blocks(static_cast<const uint16_t*>(K), s->sk_b, s->sk_l, s->sk_h, g.B, g.L, g.H, g.D, g.bk,
+                             w.kmean, st);
+  if (e != hipSuccess) return hip_fail(e, "pool K");
+  e = sd::launch_block_scores(w.qmean, w.kmean, g.B * g.H, g.Nq, g.Nk, g.D, w.S, st);
+  if (e != hipSuccess) return hip_fail(e, "block scores");
+  e = sd::launch_topk_rows(w.S, (int64_t)g.B * g.H * g.Nq, g.Nk, k_keep, idx, st);
+  if (e != hipSuccess) return hip_fail(e, "top-k");
+  return SD_OK;
+}
+
+void fill_attn_common(sd::AttnArgs& a, const sd_attn_shape* s, const Geo& g) {
+  a.sq_b = s->sq_b;
+  a.sq_l = s->sq_l;
+  a.sq_h = s->sq_h;
+  a.sk_b = s->sk_b;
+  a.sk_l = s->sk_l;
+  a.sk_h = s->sk_h;
+  a.sv_b = s->sv_b;
+  a.sv_l = s->sv_l;
+  a.sv_h = s->sv_h;
+  a.so_b = s->so_b;
+  a.so_l = s->so_l;
+  a.so_h = s->so_h;
+  a.B = g.B;
+  a.H = g.H;
+  a.L = g.L;
+  a.Nq = g.Nq;
+  a.Nk = g.Nk;
+  a.Hg = s->Hg;
+  a.Wg = s->Wg;
+}
+
+void fill_attn_lowrank(sd::AttnArgs& a, const sd_lowrank_params* lr, const sd_attn_shape* s, const LowrankWs& w) {
+  a.Pq = static_cast<const uint16_t*>(lr->Pq);
+  a.P_hs = lr->P_head_stride;
+  a.rank = lr->rank;
+  a.rope_tab = w.rope_tab;
+  a.rope = rope_args(lr, s);
+  a.Ct_hi = w.ct_hi;
+  a.Ct_lo = w.ct_lo;
+  a.eps = lr->rms_eps;
+  a.rmsw = static_cast<const uint16_t*>(lr->rms_weight);
+}
+
+bool valid_dtype(int dt) { return dt == SD_DTYPE_BF16 || dt == SD_DTYPE_F32; }
+
+}  // namespace
+
+extern "C" {
+
+int sd_keep_count(double sparsity, int n_kblocks) {
+  if (n_kblocks < 1 || !(sparsity >= 0.0 && sparsity < 1.0)) return -1;
+  const double k = std::ceil((1.0 - sparsity) * n_kblocks - 1e-9);
+  return (int)std::min<double>(std::max<double>(k, 1.0), n_kblocks);
+}
+
+int sd_rope_default(int rank, double base, sd_rope_pair* out, int max_pairs) {
+  if (rank < 2 || !(base > 0.0) || max_pairs < 0 || (max_pairs > 0 && !out)) return -1;
+  const int n[3] = {rank - 2 * (rank / 3), rank / 3, rank / 3};
+  int cnt = 0, start = 0;
+  for (int ax = 0; ax < 3; ++ax) {
+    for (int m = 0; m < n[ax] / 2; ++m) {
+      if (cnt < max_pairs) {
+        out[cnt].dim = start + 2 * m;
+        out[cnt].axis = ax;
+        out[cnt].theta = (float)std::pow(base, -2.0 * m / n[ax]);
+      }
+      ++cnt;
+    }
+    start += n[ax];
+  }
+  return cnt;
+}
+
+size_t sd_block_select_workspace_size(const sd_attn_shape* shape) {
+  Geo g;
+  if (check_shape(shape, &g, false)) return 0;
+  Carve c(nullptr);
+  carve_select(c, g);
+  return align_up(c.off);
+}
+
+int sd_block_select(const sd_attn_shape* shape, const void* Q, const void* K, int k_keep, int32_t* idx, void* ws,
+                    size_t ws_bytes, void* stream) {
+  Geo g;
+  int rc;
+  if ((rc = check_shape(shape, &g, false))) return rc;
+  if ((rc = check_dev_ptr(Q, "Q")) || (rc = check_dev_ptr(K, "K")) || (rc = check_dev_ptr(idx, "idx", 4)))
+    return rc;
+  if (k_keep < 1 || k_keep > g.Nk) return fail(SD_ERR_INVALID_ARG, "k_keep = %d not in [1, %d]", k_keep, g.Nk);
+  const size_t need = sd_block_select_workspace_size(shape);
+  if (!ws || ws_bytes < need) return fail(SD_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  if (!aligned(ws, kAlign)) return fail(SD_ERR_ALIGN, "workspace must be 256-byte aligned");
+  Carve c(ws);
+  const SelectWs w = carve_select(c, g);
+  if ((rc = run_block_select(shape, g, Q, K, k_keep, idx, w, static_cast<hipStream_t>(stream)))) return rc;
+  return ok();
+}
+
+int sd_sparse_attn(const sd_attn_shape* shape, const void* Q, const void* K, const void* V, const int32_t* idx,
+                   int k_keep, float sm_scale, void* Os, int os_dtype, float* rms, void* stream) {
+  Geo g;
+  int rc;
+  if ((rc = check_shape(shape, &g, false))) return rc;
+  if ((rc = check_dev_ptr(Q, "Q")) || (rc = check_dev_ptr(K, "K")) || (rc = check_dev_ptr(V, "V")) ||
+      (rc = check_dev_ptr(idx, "idx", 4)) || (rc = check_dev_ptr(Os, "Os")))
+    return rc;
+  if (rms && !aligned(rms, 4)) return fail(SD_ERR_ALIGN, "rms misaligned");
+  if (k_keep < 1 || k_keep > g.Nk) return fail(SD_ERR_INVALID_ARG, "k_keep = %d not in [1, %d]", k_keep, g.Nk);
+  if (!valid_dtype(os_dtype)) return fail(SD_ERR_INVALID_ARG, "os_dtype = %d", os_dtype);
+  if (!(sm_scale > 0.f) || !std::isfinite(sm_scale)) return fail(SD_ERR_INVALID_ARG, "sm_scale must be > 0");
+  sd::AttnArgs a{};
+  fill_attn_common(a, shape, g);
+  a.Q = static_cast<const uint16_t*>(Q);
+  a.K = static_cast<const uint16_t*>(K);
+  a.V = static_cast<const uint16_t*>(V);
+  a.Qn = a.Q;
+  a.kkeep = k_keep;
+  a.idx = idx;
+  a.scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
+  a.out = Os;
+  a.out_f32 = os_dtype == SD_DTYPE_F32;
+  a.rms = rms;
+  const hipError_t e = sd::launch_sparse_attn(a, g.D, g.bq, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "sparse attention");
+  return ok();
+}
+
+size_t sd_lowrank_workspace_size(const sd_attn_shape* shape, const sd_lowrank_params* lr) {
+  Geo g;
+  if (check_shape(shape, &g, true)) return 0;
+  (void)lr;
+  Carve c(nullptr);
+  carve_lowrank(c, g, shape);
+  return align_up(c.off);
+}
+
+int sd_lowrank_attn(const sd_attn_shape* shape, const sd_lowrank_params* lr, const void* Qn, const void* Kn,
+                    const void* V, void* Olr, int olr_dtype, float* C_out, void* ws, size_t ws_bytes, void* stream) {
+  Geo g;
+  int rc;
+  if ((rc = check_shape(shape, &g, true))) return rc;
+  if ((rc = check_lowrank(lr, g))) return rc;
+  if ((rc = check_dev_ptr(Qn, "Qn")) || (rc = check_dev_ptr(Kn, "Kn")) || (rc = check_dev_ptr(V, "V")) ||
+      (rc = check_dev_ptr(Olr, "Olr")))
+    return rc;
+  if (C_out && !aligned(C_out, 4)) return fail(SD_ERR_ALIGN, "C_out misaligned");
+  if (!valid_dtype(olr_dtype)) return fail(SD_ERR_INVALID_ARG, "olr_dtype = %d", olr_dtype);
+  const size_t need = sd_lowrank_workspace_size(shape, lr);
+  if (!ws || ws_bytes < need) return fail(SD_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  if (!aligned(ws, kAlign)) return fail(SD_ERR_ALIGN, "workspace must be 256-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Carve c(ws);
+  const LowrankWs w = carve_lowrank(c, g, shape);
+  if ((rc = run_lowrank_state(shape, g, lr, Kn, V, C_out, w, st))) return rc;
+  sd::AttnArgs a{};
+  fill_attn_common(a, shape, g);
+  a.Qn = static_cast<const uint16_t*>(Qn);
+  a.Q = a.Qn;
+  fill_attn_lowrank(a, lr, shape, w);
+  a.out = Olr;
+  a.out_f32 = olr_dtype == SD_DTYPE_F32;
+  const hipError_t e = sd::launch_lowrank_query(a, g.D, g.bq, st);
+  if (e != hipSuccess) return hip_fail(e, "low-rank query");
+  return ok();
+}
+
+int sd_gate_fuse(const sd_attn_shape* shape, const void* Os, const void* Olr, int in_dtype, const float* g_ptr,
+                 int64_t g_stride_b, int64_t g_stride_l, int64_t g_stride_h, void* O, void* stream) {
+  Geo g;
+  int rc;
+  if ((rc = check_shape(shape, &g, false))) return rc;
+  if ((rc = check_dev_ptr(Os, "Os")) || (rc = check_dev_ptr(Olr, "Olr")) || (rc = check_dev_ptr(O, "O")) ||
+      (rc = check_dev_ptr(g_ptr, "g", 4)))
+    return rc;
+  if (!valid_dtype(in_dtype)) return fail(SD_ERR_INVALID_ARG, "in_dtype = %d", in_dtype);
+  if (g_stride_b < 0 || g_stride_l < 0 || g_stride_h < 0) return fail(SD_ERR_INVALID_ARG, "negative gate stride");
+  const hipError_t e = sd::launch_gate_fuse(Os, Olr, in_dtype == SD_DTYPE_F32, g_ptr, g_stride_b, g_stride_l,
+                                            g_stride_h, O, g.B, g.L, g.H, g.D, shape->so_b, shape->so_l,
+                                            shape->so_h, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gate fuse");
+  return ok();
+}
+
+int sd_quant_fp8_per_token(const void* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q, int64_t ldq,
+                           float* scales, void* stream) {
+  if (M < 0 || K < 8) return fail(SD_ERR_INVALID_ARG, "M = %lld, K = %lld", (long long)M, (long long)K);
+  if (K % 8 || ldx % 8 || ldq % 8) return fail(SD_ERR_ALIGN, "K, ldx, ldq must be multiples of 8");
+  if (K > 16384) return fail(SD_ERR_UNSUPPORTED, "K = %lld exceeds 16384", (long long)K);
+  if (ldx < K || ldq < K) return fail(SD_ERR_INVALID_ARG, "ldx and ldq must be >= K");
+  if (M > ((int64_t)1 << 31) * 4 - 4) return fail(SD_ERR_UNSUPPORTED, "M too large");
+  int rc;
+  if ((rc = check_dev_ptr(x, "x")) || (rc = check_dev_ptr(q, "q", 8)) || (rc = check_dev_ptr(scales, "scales", 4)))
+    return rc;
+  const hipError_t e = sd::launch_quant_fp8(static_cast<const uint16_t*>(x), M, K, ldx, q, ldq, scales,
+                                            static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "fp8 quant");
+  return ok();
+}
+
+size_t sd_rola_workspace_size(const sd_attn_shape* shape, const sd_lowrank_params* lr, int k_keep) {
+  Geo g;
+  if (check_shape(shape, &g, true)) return 0;
+  if (k_keep < 1 || k_keep > g.Nk) return 0;
+  (void)lr;
+  Carve c(nullptr);
+  carve_select(c, g);
+  c.take(sizeof(int32_t) * g.B * g.H * (size_t)g.Nq * k_keep);
+  carve_lowrank(c, g, shape);
+  return align_up(c.off);
+}
+
+int sd_rola_attention(const sd_attn_shape* shape, const sd_lowrank_params* lr, const void* Q, const void* K,
+                      const void* V, const void* Qn, const void* Kn, const float* g_ptr, int64_t g_stride_b,
+                      int64_t g_stride_l, int64_t g_stride_h, int k_keep, float sm_scale, void* O, int32_t* idx_out,
+                      void* ws, size_t ws_bytes, void* stream) {
+  Geo g;
+  int rc;
+  if ((rc = check_shape(shape, &g, true))) return rc;
+  if ((rc = check_lowrank(lr, g))) return rc;
+  if ((rc = check_dev_ptr(Q, "Q")) || (rc = check_dev_ptr(K, "K")) || (rc = check_dev_ptr(V, "V")) ||
+      (rc = check_dev_ptr(O, "O")) || (rc = check_dev_ptr(g_ptr, "g", 4)))
+    return rc;
+  if (Qn && (rc = check_dev_ptr(Qn, "Qn"))) return rc;
+  if (Kn && (rc = check_dev_ptr(Kn, "Kn"))) return rc;
+  if (idx_out && !aligned(idx_out, 4)) return fail(SD_ERR_ALIGN, "idx_out misaligned");
+  if (k_keep < 1 || k_keep > g.Nk) return fail(SD_ERR_INVALID_ARG, "k_keep = %d not in [1, %d]", k_keep, g.Nk);
+  if (!(sm_scale > 0.f) || !std::isfinite(sm_scale)) return fail(SD_ERR_INVALID_ARG, "sm_scale must be > 0");
+  if (g_stride_b < 0 || g_stride_l < 0 || g_stride_h < 0) return fail(SD_ERR_INVALID_ARG, "negative gate stride");
+  const size_t need = sd_rola_workspace_size(shape, lr, k_keep);
+  if (!ws || ws_bytes < need) return fail(SD_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  if (!aligned(ws, kAlign)) return fail(SD_ERR_ALIGN, "workspace must be 256-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Carve c(ws);
+  const SelectWs sw = carve_select(c, g);
+  int32_t* idx_ws = static_cast<int32_t*>(c.take(sizeof(int32_t) * g.B * g.H * (size_t)g.Nq * k_keep));
+  const LowrankWs lw = carve_lowrank(c, g, shape);
+  int32_t* idx = idx_out ? idx_out : idx_ws;
+  const void* qn = Qn ? Qn : Q;
+  const void* kn = Kn ? Kn : K;
+  if ((rc = run_block_select(shape, g, Q, K, k_keep, idx, sw, st))) return rc;
+  if ((rc = run_lowrank_state(shape, g, lr, kn, V, nullptr, lw, st))) return rc;
+  sd::AttnArgs a{};
+  fill_attn_common(a, shape, g);
+  a.Q = static_cast<const uint16_t*>(Q);
+  a.K = static_cast<const uint16_t*>(K);
+  a.V = static_cast<const uint16_t*>(V);
+  a.Qn = static_cast<const uint16_t*>(qn);
+  a.kkeep = k_keep;
+  a.idx = idx;
+  a.scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
+  fill_attn_lowrank(a, lr, shape, lw);
+  a.out = O;
+  a.out_f32 = 0;
+  a.g = g_ptr;
+  a.g_sb = g_stride_b;
+  a.g_sl = g_stride_l;
+  a.g_sh = g_stride_h;
+  const hipError_t e = sd::launch_rola_fused(a, g.D, g.bq, st);
+  if (e != hipSuccess) return hip_fail(e, "fused attention");
+  return ok();
+}
+
+const char* sd_status_string(int status) {
+  switch (status) {
+    case SD_OK: return "ok";
+    case SD_ERR_INVALID_ARG: return "invalid argument";
+    case SD_ERR_UNSUPPORTED: return "unsupported";
+    case SD_ERR_ALIGN: return "misaligned pointer or stride";
+    case SD_ERR_WORKSPACE: return "workspace too small";
+    case SD_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* sd_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

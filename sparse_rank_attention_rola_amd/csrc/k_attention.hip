@@ -1,0 +1,332 @@
+// Block-sparse softmax attention (A_M), the per-token low-rank query output
+// and the fused RoLA layer.
+//
+// robotworld.top SparkDiffusion write-up, section 2.1: A~ = A_M + g (.) C_psi.
+// A_M is softmax attention restricted to the kept 1-s of the key blocks of
+// each query block; the compensation branch gives O_lr,i = RMSNorm(q~_i^T C)
+// with q~_i = R_r(p_i) phi(P_q qn_i); the fusion is O_i = O_s,i + g_i r_i
+// O_lr,i with r_i the RMS of O_s,i.
+//
+// One workgroup owns one query block (block_q = 32 * waves queries) of one
+// (batch, head); each wave owns 32 queries. Work items are ordered
+// (batch, head, query block) and spread so each XCD takes a contiguous run,
+// which keeps one head's K/V blocks hot in that XCD's L2.
+//
+// Per kept key block (64 keys):
+//   * the K and V tiles are staged through LDS (double buffered: the next
+//     block's global loads are in flight while the current block computes);
+//   * S^T = K Q^T on 32x32x16 bf16 MFMA: the transposed product puts one
+//     query per lane column, so the online-softmax max/sum of a query is a
+//     32-register reduction plus one exchange with lane l^32;
+//   * P (bf16) feeds O^T += V^T P^T directly from the accumulator registers
+//     (keys permuted consistently in both operands), V^T read from the
+//     transposed LDS tile.
+// The epilogue (fused / low-rank modes) projects the wave's queries with
+// P_q on MFMA, applies phi and the rank-truncated RoPE through a small LDS
+// patch, multiplies by the head's state C (bf16 hi+lo split of both
+// operands, ~16-bit accurate), RMS-normalises per query, and blends.
+#include "sd_device.h"
+#include "sd_launch.h"
+#include "sd_tiles.h"
+
+namespace sd {
+
+enum AttnMode { kModeSparse = 0, kModeLowrank = 1, kModeFused = 2 };
+
+__device__ __forceinline__ float phi_elu1(float x) { return x > 0.f ? x + 1.f : __expf(x); }
+
+// Low-rank query output for the 32 queries of one wave.
+//   qreg: the wave's normalised queries in the B-operand layout
+//         (lane l32 = query, channels 16*s + 8*hf .. +7).
+//   Fw:   wave-private LDS patch of 32 x 33 floats.
+// Returns y / sqrt(mean(y^2) + eps) * w in the O^T accumulator layout.
+template <int D>
+__device__ __forceinline__ void lowrank_query_tile(const u32x4* qreg, const AttnArgs& a, int b, int h, int tok0,
+                                                   float* Fw, int lane, f32x16 (&out)[D / 32]) {
+  const int hf = lane >> 5, l32 = lane & 31;
+  const uint16_t* Pq = a.Pq + (int64_t)h * a.P_hs;
+  f32x16 acc = {};
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    const u32x4 pa = (l32 < a.rank) ? *reinterpret_cast<const u32x4*>(Pq + l32 * D + 16 * s + 8 * hf)
+                                    : u32x4{0, 0, 0, 0};
+    acc = mfma32(as_bf16x8(pa), as_bf16x8(qreg[s]), acc);
+  }
+  // acc: column = query l32, row = rank index 8*(r/4) + 4*hf + r%4
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int ri = 8 * (r >> 2) + 4 * hf + (r & 3);
+    Fw[l32 * 33 + ri] = ri < a.rank ? phi_elu1(acc[r]) : 0.f;
+  }
+  __syncthreads();
+  const int npairs = a.rope.n;
+  for (int it = lane; it < 32 * npairs; it += 64) {
+    const int tk = it / npairs, m = it - tk * npairs;
+    const int tok = tok0 + tk;
+    const int axis = a.rope.axis[m];
+    const int hw = a.Hg * a.Wg;
+    const int p = axis == 0 ? tok / hw : (axis == 1 ? (tok / a.Wg) % a.Hg : tok % a.Wg);
+    const float2 cs = a.rope_tab[m * a.rope.max_ext + min(p, a.rope.max_ext - 1)];
+    float* f = Fw + tk * 33 + a.rope.dim[m];
+    const float u = f[0], v = f[1];
+    f[0] = u * cs.x - v * cs.y;
+    f[1] = u * cs.y + v * cs.x;
+  }
+  __syncthreads();
+  bf16x8 qhi[2], qlo[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    float t8[8];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) t8[p] = Fw[l32 * 33 + 16 * s + 8 * hf + p];
+    split_bf16x8(t8, qhi[s], qlo[s]);
+  }
+  const int64_t cbase = ((int64_t)b * a.H + h) * D * 32;
+  float ss = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+    f32x16 y = {};
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int64_t off = cbase + (int64_t)(32 * dt + l32) * 32 + 16 * s + 8 * hf;
+      const bf16x8 ch = as_bf16x8(*reinterpret_cast<const u32x4*>(a.Ct_hi + off));
+      const bf16x8 cl = as_bf16x8(*reinterpret_cast<const u32x4*>(a.Ct_lo + off));
+      y = mfma32(ch, qhi[s], y);
+      y = mfma32(cl, qhi[s], y);
+      y = mfma32(ch, qlo[s], y);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ss += y[r] * y[r];
+    out[dt] = y;
+  }
+  ss += __shfl_xor(ss, 32);
+  const float inv = rsqrtf(ss * (1.0f / D) + a.eps);
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float w = inv;
+      if (a.rmsw) w *= bf16_bits_to_f32(a.rmsw[32 * dt + 8 * (r >> 2) + 4 * hf + (r & 3)]);
+      out[dt][r] *= w;
+    }
+}
+
+// Stores one lane's 64 (or 32) values of a [B, L, H, D] row in the O^T
+// accumulator layout: groups of 4 consecutive channels.
+template <int D>
+__device__ __forceinline__ void store_row(void* base, bool f32, int64_t off, const f32x16 (&v)[D / 32], int hf) {
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const int d0 = 32 * dt + 8 * rg + 4 * hf;
+      if (f32) {
+        f32x4 o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = v[dt][4 * rg + i];
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(base) + off + d0) = o;
+      } else {
+        u32x2 o;
+        o[0] = pack_bf16x2(v[dt][4 * rg], v[dt][4 * rg + 1]);
+        o[1] = pack_bf16x2(v[dt][4 * rg + 2], v[dt][4 * rg + 3]);
+        *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(base) + off + d0) = o;
+      }
+    }
+}
+
+template <int D, int BQ, int MODE>
+__global__ __launch_bounds__(BQ * 2) void attention_kernel(AttnArgs a) {
+  constexpr int NW = BQ / 32;
+  constexpr int NT = NW * 64;
+  constexpr bool kLoop = MODE != kModeLowrank;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2][TileSmem<D>::kElems];
+
+  const int64_t n_work = (int64_t)a.B * a.H * a.Nq;
+  const int64_t wi = xcd_work_index(blockIdx.x, n_work);
+  if (wi < 0) return;
+  const int qb = (int)(wi % a.Nq);
+  const int64_t bh = wi / a.Nq;
+  const int h = (int)(bh % a.H), b = (int)(bh / a.H);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
+  const int hf = lane >> 5, l32 = lane & 31;
+  const int tok0 = qb * BQ + wv * 32;
+  const int q_tok = tok0 + l32;
+  const bool q_ok = q_tok < a.L;
+
+  // queries in the B-operand layout
+  u32x4 qreg[D / 16];
+  {
+    const uint16_t* qsrc = (MODE == kModeLowrank) ? a.Qn : a.Q;
+    const uint16_t* qp = qsrc + (int64_t)b * a.sq_b + (int64_t)q_tok * a.sq_l + (int64_t)h * a.sq_h;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s)
+      qreg[s] = q_ok ? *reinterpret_cast<const u32x4*>(qp + 16 * s + 8 * hf) : u32x4{0, 0, 0, 0};
+  }
+
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
+  float ltot = 1.f;
+
+  if constexpr (kLoop) {
+    const int32_t* irow = a.idx + wi * a.kkeep;
+    const uint16_t* Kb = a.K + (int64_t)b * a.sk_b + (int64_t)h * a.sk_h;
+    const uint16_t* Vb = a.V + (int64_t)b * a.sv_b + (int64_t)h * a.sv_h;
+    TileLoader<D, NT> ld;
+    float m = -INFINITY, lsum = 0.f;
+
+    // first token of a kept block; an index outside [0, Nk) selects nothing
+    auto block_tok0 = [&](int c) { return (unsigned)c < (unsigned)a.Nk ? c * 64 : a.L; };
+    ld.load(Kb, a.sk_l, Vb, a.sv_l, block_tok0(irow[0]), a.L, tid);
+    ld.store(smem[0], tid, true);
+    __syncthreads();
+    for (int it = 0; it < a.kkeep; ++it) {
+      const int key0 = block_tok0(irow[it]);
+      const bool more = it + 1 < a.kkeep;
+      if (more) ld.load(Kb, a.sk_l, Vb, a.sv_l, block_tok0(irow[it + 1]), a.L, tid);
+      const uint16_t* Ks = smem[it & 1];
+      const uint16_t* Vt = Ks + TileSmem<D>::kKElems;
+
+      // S^T (64 keys x 32 queries) = K Q^T
+      f32x16 sacc[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        sacc[kt] = f32x16{};
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s)
+          sacc[kt] = mfma32(lds_k_chunk<D>(Ks, 32 * kt + l32, 2 * s + hf), as_bf16x8(qreg[s]), sacc[kt]);
+      }
+      // online softmax in the log2 domain; this lane holds 32 of the 64 keys
+      const bool tail = key0 + 64 > a.L;
+      float mloc = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float t = sacc[kt][r] * a.scale_log2;
+          if (tail && key0 + 32 * kt + 8 * (r >> 2) + 4 * hf + (r & 3) >= a.L) t = -INFINITY;
+          sacc[kt][r] = t;
+          mloc = fmaxf(mloc, t);
+        }
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+      // m_use stays finite while every key seen so far is masked
+      const float m_new = fmaxf(m, mloc);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = exp2f(m - m_use);
+      m = m_new;
+      lsum *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+      bf16x8 preg[4];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        float p16[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          p16[r] = exp2f(sacc[kt][r] - m_use);
+          lsum += p16[r];
+        }
+        preg[2 * kt] = to_bf16x8(p16);
+        preg[2 * kt + 1] = to_bf16x8(p16 + 8);
+      }
+      // O^T (D x 32 queries) += V^T P^T, keys of step s' in the order
+      // 16s'+4hf+{0..3}, 16s'+8+4hf+{0..3} on both operands
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const int d = 32 * dt + l32;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const bf16x8 va = cat_bf16x8(lds_vt_chunk(Vt, d, 4 * s + hf), lds_vt_chunk(Vt, d, 4 * s + 2 + hf));
+          oacc[dt] = mfma32(va, preg[s], oacc[dt]);
+        }
+      }
+      if (more) ld.store(smem[(it + 1) & 1], tid, true);
+      __syncthreads();
+    }
+    ltot = lsum + __shfl_xor(lsum, 32);
+  }
+
+  const int64_t obase = (int64_t)b * a.so_b + (int64_t)q_tok * a.so_l + (int64_t)h * a.so_h;
+  if constexpr (MODE == kModeSparse) {
+    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    float ss = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        oacc[dt][r] *= inv;
+        ss += oacc[dt][r] * oacc[dt][r];
+      }
+    ss += __shfl_xor(ss, 32);
+    if (q_ok) {
+      store_row<D>(a.out, a.out_f32, obase, oacc, hf);
+      if (a.rms && hf == 0) a.rms[((int64_t)b * a.L + q_tok) * a.H + h] = sqrtf(ss * (1.0f / D));
+    }
+  } else {
+    float* Fw = reinterpret_cast<float*>(&smem[0][0]) + wv * (32 * 33);
+    f32x16 olr[D / 32];
+    if constexpr (MODE == kModeFused) {
+      if (a.Qn != a.Q) {
+        const uint16_t* qp = a.Qn + (int64_t)b * a.sq_b + (int64_t)q_tok * a.sq_l + (int64_t)h * a.sq_h;
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s)
+          qreg[s] = q_ok ? *reinterpret_cast<const u32x4*>(qp + 16 * s + 8 * hf) : u32x4{0, 0, 0, 0};
+      }
+    }
+    lowrank_query_tile<D>(qreg, a, b, h, tok0, Fw, lane, olr);
+    if constexpr (MODE == kModeLowrank) {
+      if (q_ok) store_row<D>(a.out, a.out_f32, obase, olr, hf);
+    } else {
+      const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+      float ss = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          oacc[dt][r] *= inv;
+          ss += oacc[dt][r] * oacc[dt][r];
+        }
+      ss += __shfl_xor(ss, 32);
+      const float rr = sqrtf(ss * (1.0f / D));
+      const float gv = q_ok ? a.g[(int64_t)b * a.g_sb + (int64_t)q_tok * a.g_sl + (int64_t)h * a.g_sh] : 0.f;
+      const float coef = gv * rr;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[dt][r] = fmaf(coef, olr[dt][r], oacc[dt][r]);
+      if (q_ok) store_row<D>(a.out, false, obase, oacc, hf);
+    }
+  }
+}
+
+template <int D, int BQ, int MODE>
+static hipError_t launch_attention_t(const AttnArgs& a, hipStream_t stream) {
+  const int64_t n_work = (int64_t)a.B * a.H * a.Nq;
+  const int64_t grid = (n_work + kNumXcd - 1) / kNumXcd * kNumXcd;
+  hipLaunchKernelGGL((attention_kernel<D, BQ, MODE>), dim3((unsigned)grid), dim3(BQ * 2), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int MODE>
+static hipError_t launch_attention_mode(const AttnArgs& a, int D, int BQ, hipStream_t stream) {
+  if (D == 128 && BQ == 128) return launch_attention_t<128, 128, MODE>(a, stream);
+  if (D == 128 && BQ == 64) return launch_attention_t<128, 64, MODE>(a, stream);
+  if (D == 64 && BQ == 128) return launch_attention_t<64, 128, MODE>(a, stream);
+  if (D == 64 && BQ == 64) return launch_attention_t<64, 64, MODE>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_sparse_attn(const AttnArgs& a, int D, int BQ, hipStream_t stream) {
+  return launch_attention_mode<kModeSparse>(a, D, BQ, stream);
+}
+hipError_t launch_lowrank_query(const AttnArgs& a, int D, int BQ, hipStream_t stream) {
+  return launch_attention_mode<kModeLowrank>(a, D, BQ, stream);
+}
+hipError_t launch_rola_fused(const AttnArgs& a, int D, int BQ, hipStream_t stream) {
+  return launch_attention_mode<kModeFused>(a, D, BQ, stream);
+}
+
+}  // namespace sd

@@ -1,0 +1,245 @@
+// Block map of the sparse branch: mean pooling, block scores, exact top-k.
+//
+// robotworld.top SparkDiffusion write-up, section 2.1: the sparse branch A_M
+// keeps a 1-s fraction of the query/key blocks, chosen by top-k over a
+// block-level score. Here the score of query block b and key block c is the
+// dot product of the block means of Q and K.
+//
+// The score decides an integer (which blocks are kept), so it is formed in
+// float64: the block sums of <= 128 bf16 values are exact in float64, the
+// means are IEEE divisions, and only the summation order of the 64/128-term
+// dot product can differ from a plain float64 evaluation.
+//
+//  pool_blocks_kernel  Q or K [B, L, H, d] bf16 -> means [B, H, n_blocks, d] f64.
+//                      Each thread owns 8 adjacent channels of one head and
+//                      walks the tokens of one block; a wave reads 1 KB of a
+//                      token row per load (coalesced), HBM-bound.
+//  block_scores_kernel S[b, h] = qmean . kmean^T as a 64x64-tiled f64 GEMM
+//                      on the vector ALUs (4x4 register blocking, LDS tiles).
+//  topk_rows_kernel    one wavefront per score row: an 8-pass radix select
+//                      (8-bit digits of the order-preserving 64-bit image of
+//                      the scores) finds the k-th largest score exactly; the
+//                      row is then compacted in index order with ballots, so
+//                      the output is ascending and equal scores at the
+//                      threshold go to the lower block index.
+#include "sd_device.h"
+#include "sd_launch.h"
+
+namespace sd {
+
+__global__ __launch_bounds__(256) void pool_blocks_kernel(const uint16_t* __restrict__ X, int64_t sb, int64_t sl,
+                                                          int64_t sh, int L, int H, int D, int bs, int nblk,
+                                                          double* __restrict__ out) {
+  const int blk = blockIdx.x;
+  const int b = blockIdx.y;
+  const int cpr = D >> 3;  // 8-channel chunks per head
+  const int chunk = blockIdx.z * 256 + threadIdx.x;
+  if (chunk >= H * cpr) return;
+  const int h = chunk / cpr;
+  const int d0 = (chunk - h * cpr) * 8;
+  const int t0 = blk * bs;
+  const int t1 = min(L, t0 + bs);
+  const uint16_t* p = X + (int64_t)b * sb + (int64_t)h * sh + d0;
+  double acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.0;
+  int t = t0;
+  for (; t + 4 <= t1; t += 4) {
+    u32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const u32x4*>(p + (int64_t)(t + u) * sl);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        acc[2 * w] += (double)bf16_lo(v[u][w]);
+        acc[2 * w + 1] += (double)bf16_hi(v[u][w]);
+      }
+  }
+  for (; t < t1; ++t) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(p + (int64_t)t * sl);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      acc[2 * w] += (double)bf16_lo(v[w]);
+      acc[2 * w + 1] += (double)bf16_hi(v[w]);
+    }
+  }
+  const double n = (double)(t1 - t0);
+  double* o = out + (((int64_t)b * H + h) * nblk + blk) * D + d0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = acc[i] / n;
+}
+
+// S[bh][r][c] = sum_d A[bh][r][d] * Bm[bh][c][d]   (A: [R, D], Bm: [C, D])
+__global__ __launch_bounds__(256) void block_scores_kernel(const double* __restrict__ A, const double* __restrict__ Bm,
+                                                           int R, int C, int D, double* __restrict__ S) {
+  constexpr int TK = 16;
+  __shared__ double As[TK][64 + 2];
+  __shared__ double Bs[TK][64 + 2];
+  const int bh = blockIdx.z;
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const double* Ab = A + (int64_t)bh * R * D;
+  const double* Bb = Bm + (int64_t)bh * C * D;
+  const int tid = threadIdx.x;
+  const int tx = tid & 15, ty = tid >> 4;
+  double acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
+  const int lr = tid >> 2, lk = (tid & 3) * 4;  // loader: row lr, 4 channels at lk
+  for (int k0 = 0; k0 < D; k0 += TK) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      As[lk + i][lr] = (r0 + lr < R) ? Ab[(int64_t)(r0 + lr) * D + k0 + lk + i] : 0.0;
+      Bs[lk + i][lr] = (c0 + lr < C) ? Bb[(int64_t)(c0 + lr) * D + k0 + lk + i] : 0.0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < TK; ++kk) {
+      double a[4], bv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[i] = As[kk][ty * 4 + i];
+        bv[i] = Bs[kk][tx * 4 + i];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fma(a[i], bv[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+  double* Sb = S + (int64_t)bh * R * C;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = r0 + ty * 4 + i;
+    if (r >= R) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = c0 + tx * 4 + j;
+      if (c < C) Sb[(int64_t)r * C + c] = acc[i][j];
+    }
+  }
+}
+
+__device__ __forceinline__ uint64_t order_key(double x) {
+  const uint64_t u = __double_as_longlong(x);
+  return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+}
+
+template <int NPL>  // scores per lane (row length <= 64 * NPL)
+__global__ __launch_bounds__(256) void topk_rows_kernel(const double* __restrict__ S, int64_t n_rows, int C, int k,
+                                                        int32_t* __restrict__ idx) {
+  __shared__ uint32_t hist[4][256];
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int64_t row = (int64_t)blockIdx.x * 4 + wv;
+  const bool row_ok = row < n_rows;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+
+  uint64_t key[NPL];
+  bool valid[NPL];
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) {
+    const int c = j * 64 + lane;
+    valid[j] = row_ok && c < C;
+    key[j] = valid[j] ? order_key(S[row * C + c]) : 0ull;
+  }
+
+  uint64_t prefix = 0, pmask = 0;
+  int remaining = k;
+  for (int shift = 56; shift >= 0; shift -= 8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hist[wv][lane + 64 * i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < NPL; ++j)
+      if (valid[j] && (key[j] & pmask) == prefix) atomicAdd(&hist[wv][(uint32_t)(key[j] >> shift) & 255u], 1u);
+    __syncthreads();
+    // lane covers bins 255-4*lane .. 252-4*lane, i.e. digits in descending order
+    uint32_t cnt[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) cnt[i] = hist[wv][255 - 4 * lane - i];
+    const uint32_t s = cnt[0] + cnt[1] + cnt[2] + cnt[3];
+    uint32_t incl = s;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t up = (uint32_t)__shfl_up((int)incl, o);
+      if (lane >= o) incl += up;
+    }
+    const uint64_t hit = __ballot(incl >= (uint32_t)remaining);
+    const int src = hit ? (__builtin_ctzll(hit)) : 63;
+    uint32_t above = incl - s;
+    int digit = 255 - 4 * lane;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (above + cnt[i] >= (uint32_t)remaining) {
+        digit = 255 - 4 * lane - i;
+        break;
+      }
+      above += cnt[i];
+    }
+    digit = __shfl(digit, src);
+    above = (uint32_t)__shfl((int)above, src);
+    remaining -= (int)above;
+    prefix |= (uint64_t)digit << shift;
+    pmask |= 0xFFull << shift;
+    __syncthreads();
+  }
+
+  if (!row_ok) return;
+  // prefix is the exact k-th largest key; `remaining` keys equal to it are kept
+  int taken = 0, ties = 0;
+  int32_t* out = idx + row * k;
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) {
+    const bool gt = valid[j] && key[j] > prefix;
+    const bool eq = valid[j] && key[j] == prefix;
+    const uint64_t eqm = __ballot(eq);
+    const bool take = gt || (eq && ties + __popcll(eqm & lt_mask) < remaining);
+    const uint64_t tm = __ballot(take);
+    if (take) out[taken + __popcll(tm & lt_mask)] = j * 64 + lane;
+    taken += __popcll(tm);
+    ties += __popcll(eqm);
+  }
+}
+
+hipError_t launch_pool_blocks(const uint16_t* X, int64_t sb, int64_t sl, int64_t sh, int B, int L, int H, int D,
+                              int bs, double* out, hipStream_t stream) {
+  const int nblk = (L + bs - 1) / bs;
+  const int chunks = H * (D / 8);
+  const dim3 grid(nblk, B, (chunks + 255) / 256);
+  hipLaunchKernelGGL(pool_blocks_kernel, grid, dim3(256), 0, stream, X, sb, sl, sh, L, H, D, bs, nblk, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_scores(const double* qmean, const double* kmean, int BH, int Nq, int Nk, int D, double* S,
+                               hipStream_t stream) {
+  const dim3 grid((Nk + 63) / 64, (Nq + 63) / 64, BH);
+  hipLaunchKernelGGL(block_scores_kernel, grid, dim3(256), 0, stream, qmean, kmean, Nq, Nk, D, S);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_rows(const double* S, int64_t n_rows, int C, int k, int32_t* idx, hipStream_t stream) {
+  const int npl = (C + 63) / 64;
+  const dim3 grid((unsigned)((n_rows + 3) / 4)), block(256);
+#define SD_TOPK_CASE(N)                                                                       \
+  if (npl <= N) {                                                                             \
+    hipLaunchKernelGGL(topk_rows_kernel<N>, grid, block, 0, stream, S, n_rows, C, k, idx);    \
+    return hipGetLastError();                                                                 \
+  }
+  SD_TOPK_CASE(1)
+  SD_TOPK_CASE(2)
+  SD_TOPK_CASE(4)
+  SD_TOPK_CASE(8)
+  SD_TOPK_CASE(12)
+  SD_TOPK_CASE(16)
+  SD_TOPK_CASE(20)
+  SD_TOPK_CASE(24)
+  SD_TOPK_CASE(32)
+#undef SD_TOPK_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace sd

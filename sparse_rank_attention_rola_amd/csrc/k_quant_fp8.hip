@@ -1,0 +1,98 @@
+// Per-token dynamic FP8 E4M3 activation quantisation in one HBM pass.
+//
+// robotworld.top SparkDiffusion write-up, section 2.3: activations of the
+// W8A8 projections get a dynamic scale per token, and the scale and the type
+// conversion happen in a single memory pass.
+//
+// One wavefront owns one row: it streams the bf16 row into registers with
+// 16-byte loads, finds |x|max with an integer max on the magnitude bits
+// (for finite bf16, |a| < |b| iff (a & 0x7fff) < (b & 0x7fff)) and a
+// cross-lane reduction, forms the f32 reciprocal scale once, and writes the
+// codes with the hardware f32 -> E4M3FN converter. That converter rounds to
+// nearest even but turns overflow into NaN, so values are clamped to +-448
+// first (saturation); finite scaled values never exceed 448 * (1 + 2^-23).
+// The row is read from HBM exactly once and the codes are written once.
+#include "sd_device.h"
+#include "sd_launch.h"
+
+namespace sd {
+
+__device__ __forceinline__ float sat448(float v) { return __builtin_amdgcn_fmed3f(v, -448.0f, 448.0f); }
+
+template <int VPL>  // 16-byte vectors per lane (row length <= 512 * VPL)
+__global__ __launch_bounds__(256) void quant_fp8_rows_kernel(const uint16_t* __restrict__ x, int64_t M,
+                                                             int64_t K, int64_t ldx, uint8_t* __restrict__ q,
+                                                             int64_t ldq, float* __restrict__ scales) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const int nvec = (int)(K >> 3);
+  const u32x4* src = reinterpret_cast<const u32x4*>(x + row * ldx);
+
+  u32x4 v[VPL];
+  uint32_t amax_bits = 0;
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) {
+    const int vi = j * 64 + lane;
+    if (vi < nvec) {
+      v[j] = __builtin_nontemporal_load(src + vi);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        uint32_t a = v[j][w] & 0x7FFF7FFFu;
+        amax_bits = max(amax_bits, max(a & 0xFFFFu, a >> 16));
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) amax_bits = max(amax_bits, (uint32_t)__shfl_xor((int)amax_bits, o));
+
+  const float amax = fmaxf(bf16_bits_to_f32(amax_bits), 1e-12f);
+  const float inv = 448.0f / amax;  // IEEE division (correctly rounded)
+  if (lane == 0) scales[row] = amax / 448.0f;
+
+  u32x2* dst = reinterpret_cast<u32x2*>(q + row * ldq);
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) {
+    const int vi = j * 64 + lane;
+    if (vi < nvec) {
+      uint32_t out[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t w0 = v[j][2 * h], w1 = v[j][2 * h + 1];
+        int p = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(bf16_lo(w0) * inv), sat448(bf16_hi(w0) * inv), 0, false);
+        p = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(bf16_lo(w1) * inv), sat448(bf16_hi(w1) * inv), p, true);
+        out[h] = (uint32_t)p;
+      }
+      u32x2 o2;
+      o2[0] = out[0];
+      o2[1] = out[1];
+      __builtin_nontemporal_store(o2, dst + vi);
+    }
+  }
+}
+
+hipError_t launch_quant_fp8(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q, int64_t ldq,
+                            float* scales, hipStream_t stream) {
+  if (M == 0) return hipSuccess;
+  const int nvec = (int)(K >> 3);
+  const int vpl = (nvec + 63) / 64;
+  const dim3 grid((unsigned)((M + 3) / 4)), block(256);
+#define SD_QUANT_CASE(N)                                                                      \
+  if (vpl <= N) {                                                                             \
+    hipLaunchKernelGGL(quant_fp8_rows_kernel<N>, grid, block, 0, stream, x, M, K, ldx, q, ldq, \
+                       scales);                                                               \
+    return hipGetLastError();                                                                 \
+  }
+  SD_QUANT_CASE(1)
+  SD_QUANT_CASE(2)
+  SD_QUANT_CASE(4)
+  SD_QUANT_CASE(8)
+  SD_QUANT_CASE(10)
+  SD_QUANT_CASE(16)
+  SD_QUANT_CASE(24)
+  SD_QUANT_CASE(32)
+#undef SD_QUANT_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace sd

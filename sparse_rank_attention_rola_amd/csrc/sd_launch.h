@@ -1,0 +1,77 @@
+// Host-side launchers of the libsd kernels (internal; the public ABI is sd.h).
+// Every launcher assumes its arguments were validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sd_tiles.h"
+
+namespace sd {
+
+// Arguments of the attention-family kernels (sparse branch, low-rank query
+// output, fused layer). Strides are in elements.
+struct AttnArgs {
+  const uint16_t* Q;
+  const uint16_t* K;
+  const uint16_t* V;
+  const uint16_t* Qn;
+  int64_t sq_b, sq_l, sq_h, sk_b, sk_l, sk_h, sv_b, sv_l, sv_h, so_b, so_l, so_h;
+  int B, H, L, Nq, Nk, kkeep, Hg, Wg;
+  const int32_t* idx;  // [B, H, Nq, kkeep]
+  float scale_log2;    // softmax scale * log2(e)
+  void* out;
+  int out_f32;
+  float* rms;  // optional [B, L, H]
+  // low-rank branch
+  const uint16_t* Pq;
+  int64_t P_hs;
+  int rank;
+  const float2* rope_tab;  // [n pairs][max_ext] (cos, sin)
+  RopeArgs rope;
+  const uint16_t* Ct_hi;  // bf16 [B*H, D, 32], state C transposed, hi part
+  const uint16_t* Ct_lo;  // lo part
+  float eps;
+  const uint16_t* rmsw;  // optional bf16 [D]
+  // gate
+  const float* g;
+  int64_t g_sb, g_sl, g_sh;
+};
+
+struct LowrankKvArgs {
+  const uint16_t* Kn;
+  const uint16_t* V;
+  int64_t sk_b, sk_l, sk_h, sv_b, sv_l, sv_h;
+  int B, H, L, Hg, Wg;
+  int chunk_tiles;  // 64-token tiles per workgroup
+  int n_chunks;
+  const uint16_t* Pk;
+  int64_t P_hs;
+  int rank;
+  const float2* rope_tab;
+  RopeArgs rope;
+  float* partial;  // [B*H, n_chunks, 32, D]
+};
+
+hipError_t launch_quant_fp8(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q, int64_t ldq,
+                            float* scales, hipStream_t stream);
+hipError_t launch_pool_blocks(const uint16_t* X, int64_t sb, int64_t sl, int64_t sh, int B, int L, int H, int D,
+                              int bs, double* out, hipStream_t stream);
+hipError_t launch_block_scores(const double* qmean, const double* kmean, int BH, int Nq, int Nk, int D, double* S,
+                               hipStream_t stream);
+hipError_t launch_topk_rows(const double* S, int64_t n_rows, int C, int k, int32_t* idx, hipStream_t stream);
+hipError_t launch_sparse_attn(const AttnArgs& a, int D, int BQ, hipStream_t stream);
+hipError_t launch_lowrank_query(const AttnArgs& a, int D, int BQ, hipStream_t stream);
+hipError_t launch_rola_fused(const AttnArgs& a, int D, int BQ, hipStream_t stream);
+struct RopeThetas {
+  float theta[kMaxRopePairs];
+};
+hipError_t launch_rope_table(const RopeThetas& th, int n, int max_ext, float2* tab, hipStream_t stream);
+hipError_t launch_lowrank_kv(const LowrankKvArgs& a, int D, hipStream_t stream);
+hipError_t launch_lowrank_finalize(const float* partial, int BH, int n_chunks, int rank, int D, float* C_out,
+                                   uint16_t* Ct_hi, uint16_t* Ct_lo, hipStream_t stream);
+hipError_t launch_gate_fuse(const void* Os, const void* Olr, int in_f32, const float* g, int64_t g_sb, int64_t g_sl,
+                            int64_t g_sh, void* O, int B, int L, int H, int D, int64_t so_b, int64_t so_l,
+                            int64_t so_h, hipStream_t stream);
+
+}  // namespace sd

@@ -1,0 +1,106 @@
+"""GPU parity of the per-token FP8 E4M3 quantiser against the oracle.
+
+The code of every element is decided in float32 on both sides (x times the
+float32 reciprocal scale), so codes and scales must match bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_rank_attention_rola_amd as sd
+from workloads import synthetic
+from gpu_util import dev_bf16, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(x_bits):
+    q, s = sd.sd_quant_fp8_per_token(dev_bf16(x_bits))
+    torch.cuda.synchronize()
+    return q.cpu().numpy(), s.cpu().numpy()
+
+
+@pytest.mark.parametrize("M,K", [(1001, 5120), (37, 1024), (5, 136), (3, 8), (64, 16384)])
+def test_quant_random_rows_bit_exact(M, K):
+    say(f"quant M={M} K={K}")
+    x = synthetic.gen_activation(M, K, seed=M + K)
+    q, s = _run(x)
+    q_ref, s_ref = oracle.quant_fp8_per_token(x)
+    assert np.array_equal(s, s_ref)
+    bad = q != q_ref
+    assert not bad.any(), f"{bad.sum()} codes differ, first at {np.argwhere(bad)[:5]}"
+
+
+def _bf16_bits(v):
+    return synthetic.f32_to_bf16_bits(np.asarray(v, dtype=np.float32))
+
+
+def test_quant_codec_edges_through_kernel():
+    # Rows whose |x|max is 448 have a scale of exactly 1, so every value is
+    # converted as is: all E4M3 values, all midpoints between neighbours
+    # (ties to even), values just off the midpoints and tiny values.
+    vals = oracle.e4m3_decode(np.arange(127))
+    mids = (vals[:-1] + vals[1:]) / 2
+    pts = np.concatenate([vals, mids, [2.0 ** -10, 2.0 ** -11, 3 * 2.0 ** -11, 2.0 ** -100]])
+    bits = _bf16_bits(pts)
+    assert np.array_equal(oracle.bf16_bits_to_f64(bits), pts.astype(np.float32).astype(np.float64))
+    mb = _bf16_bits(mids[1:])
+    bits = np.concatenate([bits, mb + 1, mb - 1])  # one bf16 step either side of each midpoint
+    bits = np.concatenate([bits, bits | 0x8000])
+    K = 512
+    row = np.zeros(K, dtype=np.uint16)
+    n = len(bits)
+    rows = []
+    for s0 in range(0, n, K - 8):
+        r = row.copy()
+        chunk = bits[s0:s0 + K - 8]
+        r[:len(chunk)] = chunk
+        r[K - 1] = _bf16_bits([448.0])[0]
+        rows.append(r)
+    x = np.stack(rows)
+    q, s = _run(x)
+    q_ref, s_ref = oracle.quant_fp8_per_token(x)
+    assert (s == np.float32(1.0)).all()
+    assert np.array_equal(s, s_ref)
+    assert np.array_equal(q, q_ref)
+
+
+def test_quant_zero_and_constant_rows():
+    x = np.zeros((6, 64), dtype=np.uint16)
+    x[1] = _bf16_bits([-3.5])[0]
+    x[2, ::2] = _bf16_bits([1e-20])[0]
+    x[3, 5] = _bf16_bits([1e30])[0]
+    x[4] = _bf16_bits(np.linspace(-2, 2, 64))
+    q, s = _run(x)
+    q_ref, s_ref = oracle.quant_fp8_per_token(x)
+    assert np.array_equal(s, s_ref) and np.array_equal(q, q_ref)
+
+
+def test_quant_strided_rows():
+    M, K, ld = 40, 256, 320
+    x = synthetic.gen_activation(M, ld, seed=9)
+    xd = dev_bf16(x)[:, :K]
+    qbuf = torch.full((M, 264), 0xAA, dtype=torch.uint8, device="cuda")
+    q, s = sd.sd_quant_fp8_per_token(xd, q=qbuf[:, :K])
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.quant_fp8_per_token(x[:, :K])
+    assert np.array_equal(qbuf[:, :K].cpu().numpy(), q_ref)
+    assert (qbuf[:, K:].cpu().numpy() == 0xAA).all()  # nothing written past K
+    assert np.array_equal(s.cpu().numpy(), s_ref)
+
+
+def test_quant_480p_activation_sampled_rows():
+    M, K = synthetic.QUANT_480P
+    say(f"quant full size {M}x{K}")
+    x = synthetic.gen_activation(M, K, seed=0)
+    q, s = _run(x)
+    rng = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, 1024, replace=False)]))
+    q_ref, s_ref = oracle.quant_fp8_per_token(x[rows])
+    assert np.array_equal(s[rows], s_ref)
+    assert np.array_equal(q[rows], q_ref)
+    # every row's largest-magnitude element lands on +-448 (0x7E / 0xFE)
+    xf = oracle.bf16_bits_to_f64(x[rows])
+    arg = np.abs(xf).argmax(axis=1)
+    assert ((q[rows][np.arange(len(rows)), arg] & 0x7F) == 0x7E).all()
