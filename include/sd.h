@@ -128,8 +128,9 @@ int sd_block_select(const sd_attn_shape* shape, const void* Q, const void* K, in
 /* ---- (2) sparse softmax branch A_M --------------------------------------
  * robotworld.top write-up, section 2.1 (A_M over the kept 1-s of the
  * blocks; the dense-attention equation for the softmax form). Every query
- * of block b attends with softmax(q.k * sm_scale) to the valid keys of the
- * blocks idx[b, h, b, :] (bf16 operands, f32 accumulation).
+ * of query block qb of (batch b, head h) attends with softmax(q.k * sm_scale)
+ * to the valid keys of the blocks idx[b, h, qb, :] (bf16 operands, f32
+ * accumulation). Entries outside [0, Nk) select no keys.
  * Os: [B, L, H, d] at the so_* strides, bf16 or f32 (os_dtype).
  * rms: optional device f32 [B, L, H] (contiguous) = RMS over d of each
  * O_s row (the r_i of the fusion), or NULL. */
@@ -184,6 +185,23 @@ int sd_rola_attention(const sd_attn_shape* shape, const sd_lowrank_params* lr, c
                       int64_t g_stride_b, int64_t g_stride_l, int64_t g_stride_h, int k_keep,
                       float sm_scale, void* O, int32_t* idx_out, void* ws, size_t ws_bytes,
                       void* stream);
+
+/* The fused layer in two phases, for callers that schedule or time them
+ * apart (sd_rola_attention is exactly prepare followed by apply):
+ *  sd_rola_prepare  block map (into idx_out, or the workspace when NULL) and
+ *                   the low-rank state C (into the workspace);
+ *  sd_rola_apply    the fused sparse + low-rank + gate kernel; it reads the
+ *                   block map from idx (NULL: the workspace) and C from the
+ *                   workspace left by sd_rola_prepare with the same shape,
+ *                   parameters, k_keep and workspace, earlier on the stream.
+ * Arguments mean what they mean for sd_rola_attention. */
+int sd_rola_prepare(const sd_attn_shape* shape, const sd_lowrank_params* lr, const void* Q, const void* K,
+                    const void* V, const void* Qn, const void* Kn, int k_keep, int32_t* idx_out, void* ws,
+                    size_t ws_bytes, void* stream);
+int sd_rola_apply(const sd_attn_shape* shape, const sd_lowrank_params* lr, const void* Q, const void* K,
+                  const void* V, const void* Qn, const float* g, int64_t g_stride_b, int64_t g_stride_l,
+                  int64_t g_stride_h, int k_keep, float sm_scale, void* O, const int32_t* idx, void* ws,
+                  size_t ws_bytes, void* stream);
 
 const char* sd_status_string(int status);
 const char* sd_last_error(void);

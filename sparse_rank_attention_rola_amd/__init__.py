@@ -28,8 +28,8 @@ SD_PHI_ELU1 = 1
 EXPORTED = [
     "sd_keep_count", "sd_rope_default", "sd_block_select_workspace_size", "sd_block_select",
     "sd_sparse_attn", "sd_lowrank_workspace_size", "sd_lowrank_attn", "sd_gate_fuse",
-    "sd_quant_fp8_per_token", "sd_rola_workspace_size", "sd_rola_attention", "sd_status_string",
-    "sd_last_error",
+    "sd_quant_fp8_per_token", "sd_rola_workspace_size", "sd_rola_attention", "sd_rola_prepare",
+    "sd_rola_apply", "sd_status_string", "sd_last_error",
 ]
 
 
@@ -77,6 +77,8 @@ def _declare(lib):
         "sd_quant_fp8_per_token": (i32, [P, i64, i64, i64, P, i64, P, P]),
         "sd_rola_workspace_size": (sz, [S, LR, i32]),
         "sd_rola_attention": (i32, [S, LR, P, P, P, P, P, P, i64, i64, i64, i32, f32, P, P, P, sz, P]),
+        "sd_rola_prepare": (i32, [S, LR, P, P, P, P, P, i32, P, P, sz, P]),
+        "sd_rola_apply": (i32, [S, LR, P, P, P, P, P, i64, i64, i64, i32, f32, P, P, P, sz, P]),
         "sd_status_string": (ctypes.c_char_p, [i32]),
         "sd_last_error": (ctypes.c_char_p, []),
     }
@@ -280,4 +282,28 @@ def sd_rola_attention(Q, K, V, g, lr: LowrankParams, k_keep, *, grid, block_q=12
     _check(lib().sd_rola_attention(ctypes.byref(s), ctypes.byref(lr.p), _ptr(Q), _ptr(K), _ptr(V), _ptr(Qn), _ptr(Kn),
                                    _ptr(g), gb, gl, gh, int(k_keep), float(scale), _ptr(out), _ptr(idx_out), _ptr(ws),
                                    ws.numel(), _stream_ptr(stream)))
+    return out
+
+
+def sd_rola_prepare(Q, K, V, lr: LowrankParams, k_keep, workspace, *, grid, block_q=128, Qn=None, Kn=None,
+                    idx_out=None, stream=None):
+    """Phase 1 of the fused layer: block map and low-rank state."""
+    s = make_shape(Q, K, V, block_q=block_q, grid=grid)
+    _check(lib().sd_rola_prepare(ctypes.byref(s), ctypes.byref(lr.p), _ptr(Q), _ptr(K), _ptr(V), _ptr(Qn), _ptr(Kn),
+                                 int(k_keep), _ptr(idx_out), _ptr(workspace), workspace.numel(), _stream_ptr(stream)))
+
+
+def sd_rola_apply(Q, K, V, g, lr: LowrankParams, k_keep, workspace, *, grid, block_q=128, Qn=None, sm_scale=None,
+                  out=None, idx=None, stream=None):
+    """Phase 2 of the fused layer: the fused attention kernel; bf16 O."""
+    torch = _torch()
+    B, L, H, d = Q.shape
+    if out is None:
+        out = torch.empty((B, L, H, d), dtype=torch.bfloat16, device=Q.device)
+    s = make_shape(Q, K, V, out, block_q=block_q, grid=grid)
+    scale = sm_scale if sm_scale is not None else 1.0 / math.sqrt(d)
+    gb, gl, gh = _gate_strides(g, B, L, H)
+    _check(lib().sd_rola_apply(ctypes.byref(s), ctypes.byref(lr.p), _ptr(Q), _ptr(K), _ptr(V), _ptr(Qn), _ptr(g), gb,
+                               gl, gh, int(k_keep), float(scale), _ptr(out), _ptr(idx), _ptr(workspace),
+                               workspace.numel(), _stream_ptr(stream)))
     return out

@@ -431,54 +431,129 @@ size_t sd_rola_workspace_size(const sd_attn_shape* shape, const sd_lowrank_param
   return align_up(c.off);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Validation shared by the fused entry points.
+int check_rola(const sd_attn_shape* shape, const sd_lowrank_params* lr, const void* Q, const void* K, const void* V,
+               const void* Qn, const void* Kn, int k_keep, const void* idx, size_t ws_bytes, const void* ws,
+               Geo* g) {
+  int rc;
+  if ((rc = check_shape(shape, g, true))) return rc;
+  if ((rc = check_lowrank(lr, *g))) return rc;
+  if ((rc = check_dev_ptr(Q, "Q")) || (rc = check_dev_ptr(K, "K")) || (rc = check_dev_ptr(V, "V"))) return rc;
+  if (Qn && (rc = check_dev_ptr(Qn, "Qn"))) return rc;
+  if (Kn && (rc = check_dev_ptr(Kn, "Kn"))) return rc;
+  if (idx && !aligned(idx, 4)) return fail(SD_ERR_ALIGN, "block map pointer misaligned");
+  if (k_keep < 1 || k_keep > g->Nk) return fail(SD_ERR_INVALID_ARG, "k_keep = %d not in [1, %d]", k_keep, g->Nk);
+  const size_t need = sd_rola_workspace_size(shape, lr, k_keep);
+  if (!ws || ws_bytes < need) return fail(SD_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  if (!aligned(ws, kAlign)) return fail(SD_ERR_ALIGN, "workspace must be 256-byte aligned");
+  return SD_OK;
+}
+
+struct RolaWs {
+  SelectWs sel;
+  int32_t* idx;
+  LowrankWs lr;
+};
+
+RolaWs carve_rola(void* ws, const Geo& g, const sd_attn_shape* shape, int k_keep) {
+  Carve c(ws);
+  RolaWs w;
+  w.sel = carve_select(c, g);
+  w.idx = static_cast<int32_t*>(c.take(sizeof(int32_t) * g.B * g.H * (size_t)g.Nq * k_keep));
+  w.lr = carve_lowrank(c, g, shape);
+  return w;
+}
+
+int check_apply_extra(const void* O, const float* g_ptr, float sm_scale, int64_t gb, int64_t gl, int64_t gh) {
+  int rc;
+  if ((rc = check_dev_ptr(O, "O")) || (rc = check_dev_ptr(g_ptr, "g", 4))) return rc;
+  if (!(sm_scale > 0.f) || !std::isfinite(sm_scale)) return fail(SD_ERR_INVALID_ARG, "sm_scale must be > 0");
+  if (gb < 0 || gl < 0 || gh < 0) return fail(SD_ERR_INVALID_ARG, "negative gate stride");
+  return SD_OK;
+}
+
+int run_prepare(const sd_attn_shape* shape, const Geo& g, const sd_lowrank_params* lr, const void* Q, const void* K,
+                const void* V, const void* Kn, int k_keep, int32_t* idx, const RolaWs& w, hipStream_t st) {
+  int rc;
+  if ((rc = run_block_select(shape, g, Q, K, k_keep, idx, w.sel, st))) return rc;
+  return run_lowrank_state(shape, g, lr, Kn ? Kn : K, V, nullptr, w.lr, st);
+}
+
+int run_apply(const sd_attn_shape* shape, const Geo& g, const sd_lowrank_params* lr, const void* Q, const void* K,
+              const void* V, const void* Qn, const float* g_ptr, int64_t gb, int64_t gl, int64_t gh, int k_keep,
+              float sm_scale, void* O, const int32_t* idx, const RolaWs& w, hipStream_t st) {
+  sd::AttnArgs a{};
+  fill_attn_common(a, shape, g);
+  a.Q = static_cast<const uint16_t*>(Q);
+  a.K = static_cast<const uint16_t*>(K);
+  a.V = static_cast<const uint16_t*>(V);
+  a.Qn = static_cast<const uint16_t*>(Qn ? Qn : Q);
+  a.kkeep = k_keep;
+  a.idx = idx;
+  a.scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
+  fill_attn_lowrank(a, lr, shape, w.lr);
+  a.out = O;
+  a.out_f32 = 0;
+  a.g = g_ptr;
+  a.g_sb = gb;
+  a.g_sl = gl;
+  a.g_sh = gh;
+  const hipError_t e = sd::launch_rola_fused(a, g.D, g.bq, st);
+  if (e != hipSuccess) return hip_fail(e, "fused attention");
+  return SD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sd_rola_prepare(const sd_attn_shape* shape, const sd_lowrank_params* lr, const void* Q, const void* K,
+                    const void* V, const void* Qn, const void* Kn, int k_keep, int32_t* idx_out, void* ws,
+                    size_t ws_bytes, void* stream) {
+  Geo g;
+  int rc;
+  if ((rc = check_rola(shape, lr, Q, K, V, Qn, Kn, k_keep, idx_out, ws_bytes, ws, &g))) return rc;
+  const RolaWs w = carve_rola(ws, g, shape, k_keep);
+  if ((rc = run_prepare(shape, g, lr, Q, K, V, Kn, k_keep, idx_out ? idx_out : w.idx, w,
+                        static_cast<hipStream_t>(stream))))
+    return rc;
+  return ok();
+}
+
+int sd_rola_apply(const sd_attn_shape* shape, const sd_lowrank_params* lr, const void* Q, const void* K,
+                  const void* V, const void* Qn, const float* g_ptr, int64_t g_stride_b, int64_t g_stride_l,
+                  int64_t g_stride_h, int k_keep, float sm_scale, void* O, const int32_t* idx, void* ws,
+                  size_t ws_bytes, void* stream) {
+  Geo g;
+  int rc;
+  if ((rc = check_rola(shape, lr, Q, K, V, Qn, nullptr, k_keep, idx, ws_bytes, ws, &g))) return rc;
+  if ((rc = check_apply_extra(O, g_ptr, sm_scale, g_stride_b, g_stride_l, g_stride_h))) return rc;
+  const RolaWs w = carve_rola(ws, g, shape, k_keep);
+  if ((rc = run_apply(shape, g, lr, Q, K, V, Qn, g_ptr, g_stride_b, g_stride_l, g_stride_h, k_keep, sm_scale, O,
+                      idx ? idx : w.idx, w, static_cast<hipStream_t>(stream))))
+    return rc;
+  return ok();
+}
+
 int sd_rola_attention(const sd_attn_shape* shape, const sd_lowrank_params* lr, const void* Q, const void* K,
                       const void* V, const void* Qn, const void* Kn, const float* g_ptr, int64_t g_stride_b,
                       int64_t g_stride_l, int64_t g_stride_h, int k_keep, float sm_scale, void* O, int32_t* idx_out,
                       void* ws, size_t ws_bytes, void* stream) {
   Geo g;
   int rc;
-  if ((rc = check_shape(shape, &g, true))) return rc;
-  if ((rc = check_lowrank(lr, g))) return rc;
-  if ((rc = check_dev_ptr(Q, "Q")) || (rc = check_dev_ptr(K, "K")) || (rc = check_dev_ptr(V, "V")) ||
-      (rc = check_dev_ptr(O, "O")) || (rc = check_dev_ptr(g_ptr, "g", 4)))
-    return rc;
-  if (Qn && (rc = check_dev_ptr(Qn, "Qn"))) return rc;
-  if (Kn && (rc = check_dev_ptr(Kn, "Kn"))) return rc;
-  if (idx_out && !aligned(idx_out, 4)) return fail(SD_ERR_ALIGN, "idx_out misaligned");
-  if (k_keep < 1 || k_keep > g.Nk) return fail(SD_ERR_INVALID_ARG, "k_keep = %d not in [1, %d]", k_keep, g.Nk);
-  if (!(sm_scale > 0.f) || !std::isfinite(sm_scale)) return fail(SD_ERR_INVALID_ARG, "sm_scale must be > 0");
-  if (g_stride_b < 0 || g_stride_l < 0 || g_stride_h < 0) return fail(SD_ERR_INVALID_ARG, "negative gate stride");
-  const size_t need = sd_rola_workspace_size(shape, lr, k_keep);
-  if (!ws || ws_bytes < need) return fail(SD_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
-  if (!aligned(ws, kAlign)) return fail(SD_ERR_ALIGN, "workspace must be 256-byte aligned");
+  if ((rc = check_rola(shape, lr, Q, K, V, Qn, Kn, k_keep, idx_out, ws_bytes, ws, &g))) return rc;
+  if ((rc = check_apply_extra(O, g_ptr, sm_scale, g_stride_b, g_stride_l, g_stride_h))) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  Carve c(ws);
-  const SelectWs sw = carve_select(c, g);
-  int32_t* idx_ws = static_cast<int32_t*>(c.take(sizeof(int32_t) * g.B * g.H * (size_t)g.Nq * k_keep));
-  const LowrankWs lw = carve_lowrank(c, g, shape);
-  int32_t* idx = idx_out ? idx_out : idx_ws;
-  const void* qn = Qn ? Qn : Q;
-  const void* kn = Kn ? Kn : K;
-  if ((rc = run_block_select(shape, g, Q, K, k_keep, idx, sw, st))) return rc;
-  if ((rc = run_lowrank_state(shape, g, lr, kn, V, nullptr, lw, st))) return rc;
-  sd::AttnArgs a{};
-  fill_attn_common(a, shape, g);
-  a.Q = static_cast<const uint16_t*>(Q);
-  a.K = static_cast<const uint16_t*>(K);
-  a.V = static_cast<const uint16_t*>(V);
-  a.Qn = static_cast<const uint16_t*>(qn);
-  a.kkeep = k_keep;
-  a.idx = idx;
-  a.scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
-  fill_attn_lowrank(a, lr, shape, lw);
-  a.out = O;
-  a.out_f32 = 0;
-  a.g = g_ptr;
-  a.g_sb = g_stride_b;
-  a.g_sl = g_stride_l;
-  a.g_sh = g_stride_h;
-  const hipError_t e = sd::launch_rola_fused(a, g.D, g.bq, st);
-  if (e != hipSuccess) return hip_fail(e, "fused attention");
+  const RolaWs w = carve_rola(ws, g, shape, k_keep);
+  int32_t* idx = idx_out ? idx_out : w.idx;
+  if ((rc = run_prepare(shape, g, lr, Q, K, V, Kn, k_keep, idx, w, st))) return rc;
+  if ((rc = run_apply(shape, g, lr, Q, K, V, Qn, g_ptr, g_stride_b, g_stride_l, g_stride_h, k_keep, sm_scale, O, idx,
+                      w, st)))
+    return rc;
   return ok();
 }
 

@@ -133,24 +133,42 @@ def test_lowrank(cfg):
             assert_close(Olr[b, :, h], Or, f"O_lr b{b} h{h}")
 
 
+def _close_bf16_out(got, ref, name):
+    # O is stored as bf16: allow its rounding (half an ulp, 2^-9 relative)
+    # on top of the accuracy bound of the f32 result
+    err = np.abs(got - ref)
+    bound = 2e-2 + 2.0 ** -9 * np.abs(ref)
+    say(f"  {name}: max_abs={err.max():.3e} worst err/bound={(err / bound).max():.3f}")
+    assert (err <= bound).all(), name
+    assert_close(got, ref, name, max_abs=np.inf)
+
+
 def test_gate_fuse():
+    # O_s at the scale of attention outputs, O_lr of unit RMS, gates N(1, 1)
     cfg = RAGGED
     rng = np.random.default_rng(4)
-    Os = rng.standard_normal((1, cfg.L, cfg.H, cfg.d)).astype(np.float32)
+    Os = (0.5 * rng.standard_normal((1, cfg.L, cfg.H, cfg.d))).astype(np.float32)
     Olr = rng.standard_normal((1, cfg.L, cfg.H, cfg.d)).astype(np.float32)
     g = synthetic.gen_gate(cfg, amplified=True)
     O = host(sd.sd_gate_fuse(dev_f32(Os), dev_f32(Olr), dev_f32(g)))
     for h in range(cfg.H):
         os_, ol = Os[0, :, h].astype(np.float64), Olr[0, :, h].astype(np.float64)
         r = np.sqrt((os_ ** 2).mean(axis=1))
-        assert_close(O[0, :, h], oracle.gate_fuse(os_, r, g[0].astype(np.float64), ol), f"O h{h}")
+        _close_bf16_out(O[0, :, h], oracle.gate_fuse(os_, r, g[0].astype(np.float64), ol), f"O h{h}")
     # per-(token, head) gates
     g3 = rng.standard_normal((1, cfg.L, cfg.H)).astype(np.float32)
     O3 = host(sd.sd_gate_fuse(dev_f32(Os), dev_f32(Olr), dev_f32(g3)))
     for h in range(cfg.H):
         os_, ol = Os[0, :, h].astype(np.float64), Olr[0, :, h].astype(np.float64)
         r = np.sqrt((os_ ** 2).mean(axis=1))
-        assert_close(O3[0, :, h], oracle.gate_fuse(os_, r, g3[0, :, h].astype(np.float64), ol), f"O3 h{h}")
+        _close_bf16_out(O3[0, :, h], oracle.gate_fuse(os_, r, g3[0, :, h].astype(np.float64), ol), f"O3 h{h}")
+    # bf16 inputs
+    Ob = host(sd.sd_gate_fuse(dev_f32(Os).bfloat16(), dev_f32(Olr).bfloat16(), dev_f32(g)))
+    for h in range(cfg.H):
+        osb = host(dev_f32(Os[0, :, h]).bfloat16())
+        olb = host(dev_f32(Olr[0, :, h]).bfloat16())
+        r = np.sqrt((osb ** 2).mean(axis=1))
+        _close_bf16_out(Ob[0, :, h], oracle.gate_fuse(osb, r, g[0].astype(np.float64), olb), f"O bf16-in h{h}")
 
 
 def _fused(cfg, gate, seed=0, Qn=None, Kn=None):

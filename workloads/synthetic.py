@@ -8,11 +8,14 @@ Shapes follow the workloads on the pages: Wan2.1 latent grids of
 21 x 30 x 52 (480P) and 21 x 45 x 80 (720P, 81 frames) tokens, 12 heads
 (1.3B) or 40 heads (14B) of width 128, and 5120-wide activations.
 
-Recipe (one numpy PCG64 stream per call, fixed draw order):
-  1. four frequency triples f^m drawn without replacement from
-     {0,1,2}^3 minus the zero triple, shared by Q, K and V;
-  2. per tensor X in (Q, K, V), in that order: phases phi[m, head, chan]
-     ~ U[0, 2 pi), then noise z ~ N(0, 1);
+Recipe (numpy PCG64 streams, fixed draw order):
+  1. from the stream seeded by `seed`: four frequency triples f^m drawn
+     without replacement from {0,1,2}^3 minus the zero triple, shared by
+     Q, K and V; then per tensor X in (Q, K, V) the phases
+     phi[m, head, chan] ~ U[0, 2 pi);
+  2. noise z ~ N(0, 1), drawn per (tensor, batch, run of 4096 tokens) from
+     the stream seeded by SeedSequence(seed, spawn_key=(tensor, batch, run))
+     so that runs can be drawn in parallel;
      X = 0.5 z + sum_m 0.5 sin(2 pi (f_t t/T + f_h h/Hg + f_w w/Wg) + phi),
      with token i at raster position (t, h, w), i = (t*Hg + h)*Wg + w;
   3. values rounded to bfloat16 (round to nearest even).
@@ -91,6 +94,19 @@ def _positions(cfg: AttnConfig):
     return t, h, w
 
 
+_CHUNK = 4096
+
+
+def _pool():
+    import concurrent.futures as cf
+    import os
+    return cf.ThreadPoolExecutor(max_workers=max(1, min(16, os.cpu_count() or 1)))
+
+
+def _child(seed: int, *key) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed, spawn_key=key)))
+
+
 def gen_qkv(cfg: AttnConfig, seed: int = 0):
     """Q, K, V as bfloat16 bit patterns (uint16), layout [B, L, H, d]."""
     rng = np.random.Generator(np.random.PCG64(seed))
@@ -102,18 +118,24 @@ def gen_qkv(cfg: AttnConfig, seed: int = 0):
                            + np.outer(w / cfg.Wg, freqs[:, 2]))  # [L, 4]
     basis = np.concatenate([np.sin(ang), np.cos(ang)], axis=1).astype(np.float32)  # [L, 8]
     HD = cfg.H * cfg.d
-    out = []
+    coefs = []
     for _ in range(3):
         phase = rng.uniform(0.0, 2.0 * math.pi, size=(4, HD))
         # sin(a + p) = sin a cos p + cos a sin p
-        coef = 0.5 * np.concatenate([np.cos(phase), np.sin(phase)], axis=0).astype(np.float32)  # [8, HD]
-        x = np.empty((cfg.B, cfg.L, HD), dtype=np.float32)
-        for b in range(cfg.B):
-            x[b] = basis @ coef
-            x[b] += 0.5 * rng.standard_normal(size=(cfg.L, HD), dtype=np.float32)
-        out.append(f32_to_bf16_bits(x).reshape(cfg.B, cfg.L, cfg.H, cfg.d))
-        del x
-    return tuple(out)
+        coefs.append(0.5 * np.concatenate([np.cos(phase), np.sin(phase)], axis=0).astype(np.float32))  # [8, HD]
+    out = [np.empty((cfg.B, cfg.L, HD), dtype=np.uint16) for _ in range(3)]
+
+    def work(job):
+        x_i, b, s0 = job
+        e0 = min(cfg.L, s0 + _CHUNK)
+        x = basis[s0:e0] @ coefs[x_i]
+        x += 0.5 * _child(seed, x_i, b, s0 // _CHUNK).standard_normal(size=(e0 - s0, HD), dtype=np.float32)
+        out[x_i][b, s0:e0] = f32_to_bf16_bits(x)
+
+    jobs = [(x_i, b, s0) for x_i in range(3) for b in range(cfg.B) for s0 in range(0, cfg.L, _CHUNK)]
+    with _pool() as ex:
+        list(ex.map(work, jobs))
+    return tuple(o.reshape(cfg.B, cfg.L, cfg.H, cfg.d) for o in out)
 
 
 def gen_lowrank_params(cfg: AttnConfig, seed: int = 0):
@@ -135,16 +157,26 @@ def gen_gate(cfg: AttnConfig, seed: int = 0, amplified: bool = False) -> np.ndar
 
 def gen_activation(M: int, K: int, seed: int = 0, outlier_frac: float = 0.01,
                    outlier_gain: float = 20.0) -> np.ndarray:
-    """bf16 bits [M, K]: Student-t (nu=4) values, a fixed 1% of channels x20."""
-    rng = np.random.Generator(np.random.PCG64(seed + 3_000_003))
+    """bf16 bits [M, K]: Student-t (nu=4) values, a fixed 1% of channels x20.
+
+    The outlier channels come from the stream seeded by seed + 3000003; the
+    values of each run of rows from SeedSequence(seed + 3000003,
+    spawn_key=(run,)).
+    """
+    base = seed + 3_000_003
+    rng = np.random.Generator(np.random.PCG64(base))
     n_out = max(1, int(round(outlier_frac * K)))
     chans = rng.choice(K, size=n_out, replace=False)
     gain = np.ones(K, dtype=np.float32)
     gain[chans] = outlier_gain
     out = np.empty((M, K), dtype=np.uint16)
-    step = max(1, (1 << 24) // K)
-    for s in range(0, M, step):
-        e = min(M, s + step)
-        x = rng.standard_t(4.0, size=(e - s, K)).astype(np.float32) * gain
-        out[s:e] = f32_to_bf16_bits(x)
+    step = max(1, (1 << 22) // K)
+
+    def work(s0):
+        e0 = min(M, s0 + step)
+        x = _child(base, s0 // step).standard_t(4.0, size=(e0 - s0, K)).astype(np.float32) * gain
+        out[s0:e0] = f32_to_bf16_bits(x)
+
+    with _pool() as ex:
+        list(ex.map(work, range(0, M, step)))
     return out
