@@ -135,11 +135,13 @@ __device__ __forceinline__ void store_row(void* base, bool f32, int64_t off, con
 }
 
 template <int D, int BQ, int MODE>
-__global__ __launch_bounds__(BQ * 2) void attention_kernel(AttnArgs a) {
+__global__ __launch_bounds__(BQ * 2, 2) void attention_kernel(AttnArgs a) {
   constexpr int NW = BQ / 32;
   constexpr int NT = NW * 64;
   constexpr bool kLoop = MODE != kModeLowrank;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2][TileSmem<D>::kElems];
+  __shared__ __attribute__((aligned(16))) uint16_t smem0[TileSmem<D>::kElems];
+  __shared__ __attribute__((aligned(16))) uint16_t smem1[TileSmem<D>::kElems];
+  __shared__ int sidx[kMaxKeep];
 
   const int64_t n_work = (int64_t)a.B * a.H * a.Nq;
   const int64_t wi = xcd_work_index(blockIdx.x, n_work);
@@ -173,77 +175,88 @@ __global__ __launch_bounds__(BQ * 2) void attention_kernel(AttnArgs a) {
     const int32_t* irow = a.idx + wi * a.kkeep;
     const uint16_t* Kb = a.K + (int64_t)b * a.sk_b + (int64_t)h * a.sk_h;
     const uint16_t* Vb = a.V + (int64_t)b * a.sv_b + (int64_t)h * a.sv_h;
-    TileLoader<D, NT> ld;
+    DirectTileLoader<D, NW> ld;
+    ld.init(lane, wv, a.sk_l, a.sv_l);
     float m = -INFINITY, lsum = 0.f;
 
-    // first token of a kept block; an index outside [0, Nk) selects nothing
-    auto block_tok0 = [&](int c) { return (unsigned)c < (unsigned)a.Nk ? c * 64 : a.L; };
-    ld.load(Kb, a.sk_l, Vb, a.sv_l, block_tok0(irow[0]), a.L, tid);
-    ld.store(smem[0], tid, true);
+    // The block row goes to LDS once: reading it there (lgkm counter) never
+    // waits on the tile prefetches in flight (vm counter, completed in order).
+    for (int i = tid; i < a.kkeep; i += NT) sidx[i] = irow[i];
     __syncthreads();
-    for (int it = 0; it < a.kkeep; ++it) {
-      const int key0 = block_tok0(irow[it]);
-      const bool more = it + 1 < a.kkeep;
-      if (more) ld.load(Kb, a.sk_l, Vb, a.sv_l, block_tok0(irow[it + 1]), a.L, tid);
-      const uint16_t* Ks = smem[it & 1];
-      const uint16_t* Vt = Ks + TileSmem<D>::kKElems;
+    // first token of a kept block; an index outside [0, Nk) selects nothing
+    auto block_tok0 = [&](int i) {
+      const int c = __builtin_amdgcn_readfirstlane(sidx[i]);
+      return (unsigned)c < (unsigned)a.Nk ? c * 64 : a.L;
+    };
 
-      // S^T (64 keys x 32 queries) = K Q^T
-      f32x16 sacc[2];
+    // One kept block of 64 keys, as two half-tiles of 32. For each: S^T
+    // (32 keys x 32 queries) = K Q^T, the online-softmax update in the log2
+    // domain, then O^T += V^T P^T. This lane holds 16 of the 32 keys.
+    auto compute = [&](const uint16_t* tile, int key0) {
+      const uint16_t* Ks = tile;
+      const uint16_t* Vs = tile + 64 * D;
+      const bool tail = key0 + 64 > a.L;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        sacc[kt] = f32x16{};
+        f32x16 sacc = {};
 #pragma unroll
         for (int s = 0; s < D / 16; ++s)
-          sacc[kt] = mfma32(lds_k_chunk<D>(Ks, 32 * kt + l32, 2 * s + hf), as_bf16x8(qreg[s]), sacc[kt]);
-      }
-      // online softmax in the log2 domain; this lane holds 32 of the 64 keys
-      const bool tail = key0 + 64 > a.L;
-      float mloc = -INFINITY;
+          sacc = mfma32(lds_k_chunk<D>(Ks, 32 * kt + l32, 2 * s + hf), as_bf16x8(qreg[s]), sacc);
+        if (tail) {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float t = sacc[kt][r] * a.scale_log2;
-          if (tail && key0 + 32 * kt + 8 * (r >> 2) + 4 * hf + (r & 3) >= a.L) t = -INFINITY;
-          sacc[kt][r] = t;
-          mloc = fmaxf(mloc, t);
+          for (int r = 0; r < 16; ++r)
+            if (key0 + 32 * kt + 8 * (r >> 2) + 4 * hf + (r & 3) >= a.L) sacc[r] = -INFINITY;
         }
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-      // m_use stays finite while every key seen so far is masked
-      const float m_new = fmaxf(m, mloc);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = exp2f(m - m_use);
-      m = m_new;
-      lsum *= alpha;
+        float mloc = sacc[0];
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
+        for (int r = 1; r < 16; ++r) mloc = fmaxf(mloc, sacc[r]);
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 32)) * a.scale_log2;
+        // Lazy rescaling: the reference max only moves when a score exceeds
+        // it by more than 2^8, so P <= 256 and O, l stay well inside f32.
+        if (__ballot(mloc > m + 8.f)) {
+          const float m_new = mloc > m + 8.f ? mloc : m;
+          const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+          lsum *= alpha;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
-      bf16x8 preg[4];
+          for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
+            for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+          m = m_new;
+        }
+        const float neg_m = m == -INFINITY ? 0.f : -m;
         float p16[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          p16[r] = exp2f(sacc[kt][r] - m_use);
+          p16[r] = __builtin_amdgcn_exp2f(fmaf(sacc[r], a.scale_log2, neg_m));
           lsum += p16[r];
         }
-        preg[2 * kt] = to_bf16x8(p16);
-        preg[2 * kt + 1] = to_bf16x8(p16 + 8);
-      }
-      // O^T (D x 32 queries) += V^T P^T, keys of step s' in the order
-      // 16s'+4hf+{0..3}, 16s'+8+4hf+{0..3} on both operands
+        const bf16x8 p0 = to_bf16x8(p16), p1 = to_bf16x8(p16 + 8);
+        // keys of each 16-key step in the order 4hf+{0..3}, 8+4hf+{0..3} on
+        // both operands
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-        const int d = 32 * dt + l32;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const bf16x8 va = cat_bf16x8(lds_vt_chunk(Vt, d, 4 * s + hf), lds_vt_chunk(Vt, d, 4 * s + 2 + hf));
-          oacc[dt] = mfma32(va, preg[s], oacc[dt]);
+        for (int dt = 0; dt < D / 32; ++dt) {
+          oacc[dt] = mfma32(lds_v_operand<D>(Vs, lane, dt, 32 * kt), p0, oacc[dt]);
+          oacc[dt] = mfma32(lds_v_operand<D>(Vs, lane, dt, 32 * kt + 16), p1, oacc[dt]);
         }
       }
-      if (more) ld.store(smem[(it + 1) & 1], tid, true);
+    };
+
+    ld.issue(smem0, Kb, a.sk_l, Vb, a.sv_l, block_tok0(0), a.L, lane, wv);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    int it = 0;
+    for (; it + 1 < a.kkeep; it += 2) {
+      ld.issue(smem1, Kb, a.sk_l, Vb, a.sv_l, block_tok0(it + 1), a.L, lane, wv);
+      compute(smem0, block_tok0(it));
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (it + 2 < a.kkeep) ld.issue(smem0, Kb, a.sk_l, Vb, a.sv_l, block_tok0(it + 2), a.L, lane, wv);
+      compute(smem1, block_tok0(it + 1));
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    }
+    if (it < a.kkeep) {
+      compute(smem0, block_tok0(it));
       __syncthreads();
     }
     ltot = lsum + __shfl_xor(lsum, 32);
@@ -266,7 +279,7 @@ __global__ __launch_bounds__(BQ * 2) void attention_kernel(AttnArgs a) {
       if (a.rms && hf == 0) a.rms[((int64_t)b * a.L + q_tok) * a.H + h] = sqrtf(ss * (1.0f / D));
     }
   } else {
-    float* Fw = reinterpret_cast<float*>(&smem[0][0]) + wv * (32 * 33);
+    float* Fw = reinterpret_cast<float*>(smem0) + wv * (32 * 33);
     f32x16 olr[D / 32];
     if constexpr (MODE == kModeFused) {
       if (a.Qn != a.Q) {
@@ -301,6 +314,17 @@ __global__ __launch_bounds__(BQ * 2) void attention_kernel(AttnArgs a) {
     }
   }
 }
+
+// Explicit instantiation of every variant: the host pass must emit each
+// kernel's launch stub.
+#define SD_ATTN_INST(D, BQ, MODE) template __global__ void attention_kernel<D, BQ, MODE>(AttnArgs);
+#define SD_ATTN_INST_MODES(D, BQ) SD_ATTN_INST(D, BQ, 0) SD_ATTN_INST(D, BQ, 1) SD_ATTN_INST(D, BQ, 2)
+SD_ATTN_INST_MODES(128, 128)
+SD_ATTN_INST_MODES(128, 64)
+SD_ATTN_INST_MODES(64, 128)
+SD_ATTN_INST_MODES(64, 64)
+#undef SD_ATTN_INST_MODES
+#undef SD_ATTN_INST
 
 template <int D, int BQ, int MODE>
 static hipError_t launch_attention_t(const AttnArgs& a, hipStream_t stream) {

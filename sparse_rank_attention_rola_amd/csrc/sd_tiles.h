@@ -120,6 +120,104 @@ __device__ __forceinline__ bf16x8 cat_bf16x8(u32x2 a, u32x2 b) {
   return as_bf16x8(v);
 }
 
+
+// ---------------------------------------------------------------------------
+// Direct (global -> LDS) staging of one 64-token K tile and one 64-token V
+// tile, both row-major [token][D] bf16. A wave instruction writes 1 KB of
+// LDS: lane l's 16 bytes land at base + 16*l, so the swizzle is realised by
+// choosing which global 16-byte chunk each lane fetches:
+//   K tile: 16-byte chunk c of row t stored at c ^ (t % 8)  (conflict-free
+//           reads of one chunk column by 32 consecutive rows);
+//   V tile: 16-byte chunk c of row t stored at c ^ 2*(t % 4) (conflict-free
+//           transposing reads of 4 rows x 32 bytes per 16-lane group).
+// Rows past the end of the sequence are fetched from the last valid row;
+// their scores are masked, so they contribute nothing.
+template <int D, int NW>
+struct DirectTileLoader {
+  static constexpr int kSegs = D / 8;          // 1 KB segments per tile
+  static constexpr int kSpw = kSegs / NW;      // segments per wave per tile
+  static constexpr int kRowBytes = 2 * D;
+  static_assert(kSpw >= 1, "tile smaller than the workgroup");
+
+  int koff[kSpw];  // element offset of this lane's K chunk, relative to the tile's first row
+  int voff[kSpw];
+
+  __device__ __forceinline__ static void seg_row_chunk(int sg, int lane, int& row, int& p16) {
+    const int byte = sg * 1024 + 16 * lane;
+    row = byte / kRowBytes;
+    p16 = (byte % kRowBytes) / 16;
+  }
+
+  __device__ __forceinline__ void init(int lane, int wv, int64_t sk_l, int64_t sv_l) {
+#pragma unroll
+    for (int i = 0; i < kSpw; ++i) {
+      int row, p16;
+      seg_row_chunk(wv + NW * i, lane, row, p16);
+      koff[i] = row * (int)sk_l + ((p16 ^ (row & 7)) * 8);
+      voff[i] = row * (int)sv_l + ((p16 ^ ((row & 3) << 1)) * 8);
+    }
+  }
+
+  __device__ __forceinline__ void issue(uint16_t* tile, const uint16_t* Kb, int64_t sk_l, const uint16_t* Vb,
+                                        int64_t sv_l, int tok0, int L, int lane, int wv) const {
+    uint16_t* Ks = tile;
+    uint16_t* Vs = tile + 64 * D;
+    if (tok0 + 64 <= L) {
+      const uint16_t* kb = Kb + (int64_t)tok0 * sk_l;
+      const uint16_t* vb = Vb + (int64_t)tok0 * sv_l;
+#pragma unroll
+      for (int i = 0; i < kSpw; ++i) {
+        const int sg = wv + NW * i;
+        __builtin_amdgcn_global_load_lds(kb + koff[i], (__attribute__((address_space(3))) void*)(Ks + sg * 512),
+                                         16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vb + voff[i], (__attribute__((address_space(3))) void*)(Vs + sg * 512),
+                                         16, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kSpw; ++i) {
+        const int sg = wv + NW * i;
+        int row, p16;
+        seg_row_chunk(sg, lane, row, p16);
+        const int64_t t = min(tok0 + row, L - 1);
+        __builtin_amdgcn_global_load_lds(Kb + t * sk_l + ((p16 ^ (row & 7)) * 8),
+                                         (__attribute__((address_space(3))) void*)(Ks + sg * 512), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(Vb + t * sv_l + ((p16 ^ ((row & 3) << 1)) * 8),
+                                         (__attribute__((address_space(3))) void*)(Vs + sg * 512), 16, 0, 0);
+      }
+    }
+  }
+};
+
+typedef short short4_t __attribute__((ext_vector_type(4)));
+
+// Transposing LDS read (ds_read_b64_tr_b16). Within each 16-lane group,
+// lane 4q+k receives element k of the 8-byte chunks addressed by lanes
+// q, 4+q, 8+q and 12+q (checked on the hardware).
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+  const short4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) short4_t*)((__attribute__((address_space(3))) uint16_t*)p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// A operand (32 channels x 16 keys) of O^T += V^T P^T from the row-major
+// V tile: lane l receives V[kbase + r][32*dt + l%32] for r = 0..3 (first
+// read) and V[kbase + 8 + r][...] (second read), kbase = 16*step + 4*(l/32).
+template <int D>
+__device__ __forceinline__ bf16x8 lds_v_operand(const uint16_t* Vs, int lane, int dt, int key_base) {
+  const int G = lane >> 4, j = lane & 15;
+  const int r = j >> 2, q = j & 3;
+  const int row = key_base + 4 * (G >> 1) + r;       // (row & 3) == r
+  const int c8 = 8 * dt + 4 * (G & 1) + q;           // 8-byte chunk of the channel
+  const int off = ((c8 >> 1) ^ (r << 1)) * 8 + (c8 & 1) * 4;
+  const u32x2 lo = lds_read_tr16(Vs + row * D + off);
+  const u32x2 hi = lds_read_tr16(Vs + (row + 8) * D + off);
+  return cat_bf16x8(lo, hi);
+}
+
+// Largest number of kept key blocks per query block (L <= 131072, 64-key blocks).
+constexpr int kMaxKeep = 2048;
+
 // Compile-time description of the rank-truncated 3D RoPE pairs.
 constexpr int kMaxRopePairs = 16;
 struct RopeArgs {
