@@ -13,7 +13,7 @@ import math
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libsd.so")
+LIB_PATH = os.environ.get("SD_LIBRARY", os.path.join(_PKG, "libsd.so"))
 
 SD_OK = 0
 SD_ERR_INVALID_ARG = 1

@@ -64,6 +64,14 @@ int check_shape(const sd_attn_shape* s, Geo* g, bool need_grid) {
     if (st[i] < 0) return fail(SD_ERR_INVALID_ARG, "negative stride");
     if (st[i] % 8) return fail(SD_ERR_ALIGN, "strides must be multiples of 8 elements (16 bytes)");
   }
+  // offsets inside a 64-token tile are 32-bit
+  if (std::max(std::max(s->sq_l, s->sk_l), std::max(s->sv_l, s->so_l)) > ((int64_t)1 << 31) / 128)
+    return fail(SD_ERR_UNSUPPORTED, "token stride too large");
+  // K and V of one (batch, head) are read through 32-bit buffer offsets, and a
+  // token row must not overlap the next one
+  if (s->sk_l < s->d || s->sv_l < s->d) return fail(SD_ERR_UNSUPPORTED, "K/V token stride smaller than d");
+  if ((int64_t)(s->L + 64) * std::max(s->sk_l, s->sv_l) * 2 >= ((int64_t)1 << 32))
+    return fail(SD_ERR_UNSUPPORTED, "K/V of one head exceed 4 GiB");
   g->B = s->B;
   g->H = s->H;
   g->L = s->L;

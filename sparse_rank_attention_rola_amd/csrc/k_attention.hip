@@ -33,6 +33,25 @@ namespace sd {
 
 enum AttnMode { kModeSparse = 0, kModeLowrank = 1, kModeFused = 2 };
 
+#ifndef SD_ATTN_PIPE
+#define SD_ATTN_PIPE 2  // 1: issue both halves' QK^T before the first softmax
+#endif
+// Wave priority around the MFMA chains: while one wave of a SIMD runs its
+// softmax on the VALU, the other wave's matrix work is issued first.
+#ifndef SD_ATTN_PRIO
+#define SD_ATTN_PRIO 0
+#endif
+#if SD_ATTN_PRIO
+#define SD_PRIO_HI() __builtin_amdgcn_s_setprio(1)
+#define SD_PRIO_LO() __builtin_amdgcn_s_setprio(0)
+#else
+#define SD_PRIO_HI()
+#define SD_PRIO_LO()
+#endif
+#ifndef SD_ATTN_WAVES
+#define SD_ATTN_WAVES 2  // minimum waves per SIMD the register budget must allow
+#endif
+
 __device__ __forceinline__ float phi_elu1(float x) { return x > 0.f ? x + 1.f : __expf(x); }
 
 // Low-rank query output for the 32 queries of one wave.
@@ -135,7 +154,7 @@ __device__ __forceinline__ void store_row(void* base, bool f32, int64_t off, con
 }
 
 template <int D, int BQ, int MODE>
-__global__ __launch_bounds__(BQ * 2, 2) void attention_kernel(AttnArgs a) {
+__global__ __launch_bounds__(BQ * 2, SD_ATTN_WAVES) void attention_kernel(AttnArgs a) {
   constexpr int NW = BQ / 32;
   constexpr int NT = NW * 64;
   constexpr bool kLoop = MODE != kModeLowrank;
@@ -150,7 +169,8 @@ __global__ __launch_bounds__(BQ * 2, 2) void attention_kernel(AttnArgs a) {
   const int64_t bh = wi / a.Nq;
   const int h = (int)(bh % a.H), b = (int)(bh / a.H);
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wv = tid >> 6;
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int hf = lane >> 5, l32 = lane & 31;
   const int tok0 = qb * BQ + wv * 32;
   const int q_tok = tok0 + l32;
@@ -176,7 +196,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void attention_kernel(AttnArgs a) {
     const uint16_t* Kb = a.K + (int64_t)b * a.sk_b + (int64_t)h * a.sk_h;
     const uint16_t* Vb = a.V + (int64_t)b * a.sv_b + (int64_t)h * a.sv_h;
     DirectTileLoader<D, NW> ld;
-    ld.init(lane, wv, a.sk_l, a.sv_l);
+    ld.init(Kb, a.sk_l, Vb, a.sv_l, a.L, lane, wv);
     float m = -INFINITY, lsum = 0.f;
 
     // The block row goes to LDS once: reading it there (lgkm counter) never
@@ -189,68 +209,153 @@ __global__ __launch_bounds__(BQ * 2, 2) void attention_kernel(AttnArgs a) {
       return (unsigned)c < (unsigned)a.Nk ? c * 64 : a.L;
     };
 
-    // One kept block of 64 keys, as two half-tiles of 32. For each: S^T
-    // (32 keys x 32 queries) = K Q^T, the online-softmax update in the log2
-    // domain, then O^T += V^T P^T. This lane holds 16 of the 32 keys.
+    // One kept block of 64 keys, as two half-tiles of 32. S^T (32 keys x 32
+    // queries) = K Q^T for both halves is issued first, so the second
+    // half's MFMAs run while the first half's softmax is on the VALU; then
+    // per half: online-softmax update in the log2 domain and O^T += V^T P^T.
+    // This lane holds 16 of the 32 keys of its query per half.
+    auto softmax_half = [&](f32x16& sacc, int key0, int kt, bool tail, bf16x8& p0, bf16x8& p1) {
+      if (tail) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (key0 + 32 * kt + 8 * (r >> 2) + 4 * hf + (r & 3) >= a.L) sacc[r] = -INFINITY;
+      }
+      float mloc = sacc[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mloc = fmaxf(mloc, sacc[r]);
+      mloc = fmaxf(mloc, partner32(mloc, hf)) * a.scale_log2;
+      // Lazy rescaling: the reference max only moves when a score exceeds it
+      // by more than 2^8, so P <= 256 and O, l stay well inside f32.
+      if (__ballot(mloc > m + 8.f)) {
+        const float m_new = mloc > m + 8.f ? mloc : m;
+        const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+        lsum *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+        m = m_new;
+      }
+      const float neg_m = m == -INFINITY ? 0.f : -m;
+      float p16[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) p16[r] = __builtin_amdgcn_exp2f(fmaf(sacc[r], a.scale_log2, neg_m));
+      p0 = to_bf16x8(p16);
+      p1 = to_bf16x8(p16 + 8);
+      // the normaliser sums the bf16 values the PV product consumes
+      lsum = sum_bf16x8(p1, sum_bf16x8(p0, lsum));
+    };
+    auto pv_half = [&](const uint16_t* Vs, int kt, bf16x8 p0, bf16x8 p1) {
+      // keys of each 16-key step in the order 4hf+{0..3}, 8+4hf+{0..3} on
+      // both operands
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        oacc[dt] = mfma32(lds_v_operand<D>(Vs, lane, dt, 32 * kt), p0, oacc[dt]);
+        oacc[dt] = mfma32(lds_v_operand<D>(Vs, lane, dt, 32 * kt + 16), p1, oacc[dt]);
+      }
+    };
     auto compute = [&](const uint16_t* tile, int key0) {
       const uint16_t* Ks = tile;
       const uint16_t* Vs = tile + 64 * D;
       const bool tail = key0 + 64 > a.L;
+#if SD_ATTN_PIPE
+      f32x16 s0 = {}, s1 = {};
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) s0 = mfma32(lds_k_chunk<D>(Ks, l32, 2 * s + hf), as_bf16x8(qreg[s]), s0);
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) s1 = mfma32(lds_k_chunk<D>(Ks, 32 + l32, 2 * s + hf), as_bf16x8(qreg[s]), s1);
+      bf16x8 pa, pb;
+      softmax_half(s0, key0, 0, tail, pa, pb);
+      pv_half(Vs, 0, pa, pb);
+      softmax_half(s1, key0, 1, tail, pa, pb);
+      pv_half(Vs, 1, pa, pb);
+#elif SD_ATTN_PIPE == 2
+      // operands are read from LDS a stage ahead of the MFMAs that use them
+      bf16x8 kop[D / 16];
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) kop[s] = lds_k_chunk<D>(Ks, l32, 2 * s + hf);
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         f32x16 sacc = {};
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s)
-          sacc = mfma32(lds_k_chunk<D>(Ks, 32 * kt + l32, 2 * s + hf), as_bf16x8(qreg[s]), sacc);
-        if (tail) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (key0 + 32 * kt + 8 * (r >> 2) + 4 * hf + (r & 3) >= a.L) sacc[r] = -INFINITY;
-        }
-        float mloc = sacc[0];
-#pragma unroll
-        for (int r = 1; r < 16; ++r) mloc = fmaxf(mloc, sacc[r]);
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 32)) * a.scale_log2;
-        // Lazy rescaling: the reference max only moves when a score exceeds
-        // it by more than 2^8, so P <= 256 and O, l stay well inside f32.
-        if (__ballot(mloc > m + 8.f)) {
-          const float m_new = mloc > m + 8.f ? mloc : m;
-          const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-          lsum *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
-          m = m_new;
-        }
-        const float neg_m = m == -INFINITY ? 0.f : -m;
-        float p16[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          p16[r] = __builtin_amdgcn_exp2f(fmaf(sacc[r], a.scale_log2, neg_m));
-          lsum += p16[r];
-        }
-        const bf16x8 p0 = to_bf16x8(p16), p1 = to_bf16x8(p16 + 8);
-        // keys of each 16-key step in the order 4hf+{0..3}, 8+4hf+{0..3} on
-        // both operands
+        for (int s = 0; s < D / 16; ++s) sacc = mfma32(kop[s], as_bf16x8(qreg[s]), sacc);
+        bf16x8 vop[D / 32][2];
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
-          oacc[dt] = mfma32(lds_v_operand<D>(Vs, lane, dt, 32 * kt), p0, oacc[dt]);
-          oacc[dt] = mfma32(lds_v_operand<D>(Vs, lane, dt, 32 * kt + 16), p1, oacc[dt]);
+          vop[dt][0] = lds_v_operand<D>(Vs, lane, dt, 32 * kt);
+          vop[dt][1] = lds_v_operand<D>(Vs, lane, dt, 32 * kt + 16);
+        }
+        if (kt == 0) {
+#pragma unroll
+          for (int s = 0; s < D / 16; ++s) kop[s] = lds_k_chunk<D>(Ks, 32 + l32, 2 * s + hf);
+        }
+        bf16x8 pa, pb;
+        softmax_half(sacc, key0, kt, tail, pa, pb);
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+          oacc[dt] = mfma32(vop[dt][0], pa, oacc[dt]);
+          oacc[dt] = mfma32(vop[dt][1], pb, oacc[dt]);
         }
       }
+#elif SD_ATTN_PIPE == 3
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        // QK chain: each K operand read is issued one MFMA ahead
+        f32x16 sacc = {};
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s)
+          sacc = mfma32(lds_k_chunk<D>(Ks, 32 * kt + l32, 2 * s + hf), as_bf16x8(qreg[s]), sacc);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+        for (int s = 0; s < D / 16 - 2; ++s) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        bf16x8 pa, pb;
+        softmax_half(sacc, key0, kt, tail, pa, pb);
+        // PV chain: the two transposing reads of each V operand one MFMA ahead
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+          oacc[dt] = mfma32(lds_v_operand<D>(Vs, lane, dt, 32 * kt), pa, oacc[dt]);
+          oacc[dt] = mfma32(lds_v_operand<D>(Vs, lane, dt, 32 * kt + 16), pb, oacc[dt]);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+        for (int i = 0; i < D / 16 - 1; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      }
+#else
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        f32x16 sacc = {};
+        SD_PRIO_HI();
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s)
+          sacc = mfma32(lds_k_chunk<D>(Ks, 32 * kt + l32, 2 * s + hf), as_bf16x8(qreg[s]), sacc);
+        SD_PRIO_LO();
+        bf16x8 pa, pb;
+        softmax_half(sacc, key0, kt, tail, pa, pb);
+        SD_PRIO_HI();
+        pv_half(Vs, kt, pa, pb);
+        SD_PRIO_LO();
+      }
+#endif
     };
 
-    ld.issue(smem0, Kb, a.sk_l, Vb, a.sv_l, block_tok0(0), a.L, lane, wv);
+    ld.issue(smem0, block_tok0(0), lane, wv);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     int it = 0;
     for (; it + 1 < a.kkeep; it += 2) {
-      ld.issue(smem1, Kb, a.sk_l, Vb, a.sv_l, block_tok0(it + 1), a.L, lane, wv);
+      ld.issue(smem1, block_tok0(it + 1), lane, wv);
       compute(smem0, block_tok0(it));
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      if (it + 2 < a.kkeep) ld.issue(smem0, Kb, a.sk_l, Vb, a.sv_l, block_tok0(it + 2), a.L, lane, wv);
+      if (it + 2 < a.kkeep) ld.issue(smem0, block_tok0(it + 2), lane, wv);
       compute(smem1, block_tok0(it + 1));
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();

@@ -64,6 +64,26 @@ __device__ __forceinline__ int64_t xcd_work_index(int64_t wg, int64_t n_work) {
   return w < n_work ? w : -1;
 }
 
+// Value of lane l ^ 32 (v_permlane32_swap: one VALU op, no LDS traffic).
+__device__ __forceinline__ float partner32(float x, int hf) {
+  const int xi = __float_as_int(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
+  return __int_as_float(hf ? r[0] : r[1]);
+}
+
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+
+// Sum of the 8 bf16 values of an MFMA operand, accumulated into acc (f32).
+__device__ __forceinline__ float sum_bf16x8(bf16x8 v, float acc) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bf16x2 pr = {v[2 * i], v[2 * i + 1]};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(pr, one, acc, false);
+  }
+  return acc;
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));

@@ -8,13 +8,12 @@
 // With l32 = lane % 32 and hf = lane / 32, the accumulator register r of a
 // lane holds row i = 8*(r/4) + 4*hf + r%4 of column j = l32.
 //
-// A 64-token tile of K (or any [tokens, d] operand read along d) is kept in
-// LDS row-major, 16-byte chunk c of row t stored at chunk c ^ (t % 8): the
-// 32 lanes that read one chunk column of 32 rows hit distinct banks.
-// A 64-token tile of V is kept transposed, Vt[d][token], in 8-byte chunks of
-// 4 tokens; chunk c of row d is stored at c ^ f(d), f(d) = (d%16) ^ (d/16),
-// which keeps both the transposing stores and the MFMA operand reads free
-// of bank conflicts.
+// LDS has 64 banks of 4 bytes on gfx950. A 64-token tile of K (or any
+// [tokens, d] operand read along d) is kept row-major with 16-byte chunk c
+// of row t stored at c ^ k_swz(t): the lanes that read one chunk column of
+// consecutive rows hit distinct banks. The register-staged loader below keeps
+// V transposed, Vt[d][token], in 8-byte chunks of 4 tokens (chunk c of row d
+// stored at c ^ f(d), f(d) = (d%16) ^ (d/16)).
 #pragma once
 
 #include "sd_device.h"
@@ -29,6 +28,20 @@ struct TileSmem {
 };
 
 __device__ __forceinline__ int vt_swz(int d) { return (d & 15) ^ ((d >> 4) & 15); }
+
+// 16-byte-chunk swizzle of row t of a row-major K tile: 16 consecutive rows
+// (one 16-lane LDS cycle of a b128 read) land on 16 distinct bank groups.
+template <int D>
+__device__ __forceinline__ int k_swz(int t) {
+  return D == 128 ? (t & 15) : ((t >> 1) & 7);  // D = 64: two 128-byte rows share a bank row
+}
+
+// 16-byte-chunk swizzle of row t of a row-major V tile read by transposing
+// reads: the 4 rows x 64 bytes of one 32-lane LDS cycle hit distinct banks.
+template <int D>
+__device__ __forceinline__ int v_swz(int t) {
+  return D == 128 ? 4 * (t & 3) : 4 * ((t & 3) >> 1);
+}
 
 // Global -> registers -> LDS staging of one 64-token tile of K (row-major,
 // swizzled) and V (transposed, swizzled) by NT threads.
@@ -74,7 +87,7 @@ struct TileLoader {
     for (int i = 0; i < KPT; ++i) {
       const int chunk = i * NT + tid;
       const int t = chunk / DC, dc = chunk % DC;
-      *reinterpret_cast<u32x4*>(Ks + t * D + ((dc ^ (t & 7)) * 8)) = kreg[i];
+      *reinterpret_cast<u32x4*>(Ks + t * D + ((dc ^ k_swz<D>(t)) * 8)) = kreg[i];
     }
     if (!with_v) return;
     uint16_t* Vt = smem + TileSmem<D>::kKElems;
@@ -103,7 +116,7 @@ struct TileLoader {
 // 8 bf16 of K-layout row t (tokens), channels 8*c .. 8*c+7.
 template <int D>
 __device__ __forceinline__ bf16x8 lds_k_chunk(const uint16_t* Ks, int t, int c) {
-  return as_bf16x8(*reinterpret_cast<const u32x4*>(Ks + t * D + ((c ^ (t & 7)) * 8)));
+  return as_bf16x8(*reinterpret_cast<const u32x4*>(Ks + t * D + ((c ^ k_swz<D>(t)) * 8)));
 }
 
 // 4 bf16 of Vt row d, tokens 4*c .. 4*c+3.
@@ -123,24 +136,28 @@ __device__ __forceinline__ bf16x8 cat_bf16x8(u32x2 a, u32x2 b) {
 
 // ---------------------------------------------------------------------------
 // Direct (global -> LDS) staging of one 64-token K tile and one 64-token V
-// tile, both row-major [token][D] bf16. A wave instruction writes 1 KB of
-// LDS: lane l's 16 bytes land at base + 16*l, so the swizzle is realised by
-// choosing which global 16-byte chunk each lane fetches:
-//   K tile: 16-byte chunk c of row t stored at c ^ (t % 8)  (conflict-free
-//           reads of one chunk column by 32 consecutive rows);
-//   V tile: 16-byte chunk c of row t stored at c ^ 2*(t % 4) (conflict-free
-//           transposing reads of 4 rows x 32 bytes per 16-lane group).
-// Rows past the end of the sequence are fetched from the last valid row;
-// their scores are masked, so they contribute nothing.
+// tile, both row-major [token][D] bf16, with raw buffer loads into LDS. A wave
+// instruction writes 1 KB of LDS: lane l's 16 bytes land at base + 16*l, so
+// the swizzle is realised by choosing which 16-byte chunk each lane fetches:
+//   K tile: 16-byte chunk c of row t stored at c ^ k_swz(t);
+//   V tile: 16-byte chunk c of row t stored at c ^ v_swz(t).
+// The buffer descriptor of each (batch, head) ends at the last valid token,
+// so rows past the end of the sequence read as zeros (hardware range check);
+// their scores are masked and their zero values contribute nothing.
+// Per-load offsets are uniform (SGPR); each lane keeps one 32-bit offset per
+// tensor (both swizzles repeat every 16 rows, the distance between a wave's
+// consecutive segments when 4 waves share a 128-channel tile).
 template <int D, int NW>
 struct DirectTileLoader {
   static constexpr int kSegs = D / 8;          // 1 KB segments per tile
   static constexpr int kSpw = kSegs / NW;      // segments per wave per tile
   static constexpr int kRowBytes = 2 * D;
+  static constexpr int kRowsPerStep = NW * 1024 / kRowBytes;  // rows between a wave's segments
   static_assert(kSpw >= 1, "tile smaller than the workgroup");
 
-  int koff[kSpw];  // element offset of this lane's K chunk, relative to the tile's first row
-  int voff[kSpw];
+  __amdgpu_buffer_rsrc_t krsrc, vrsrc;
+  unsigned kvoff, vvoff;  // byte offsets of this lane's chunks in its first segment
+  unsigned kstride, vstride;  // token strides in bytes
 
   __device__ __forceinline__ static void seg_row_chunk(int sg, int lane, int& row, int& p16) {
     const int byte = sg * 1024 + 16 * lane;
@@ -148,43 +165,39 @@ struct DirectTileLoader {
     p16 = (byte % kRowBytes) / 16;
   }
 
-  __device__ __forceinline__ void init(int lane, int wv, int64_t sk_l, int64_t sv_l) {
-#pragma unroll
-    for (int i = 0; i < kSpw; ++i) {
-      int row, p16;
-      seg_row_chunk(wv + NW * i, lane, row, p16);
-      koff[i] = row * (int)sk_l + ((p16 ^ (row & 7)) * 8);
-      voff[i] = row * (int)sv_l + ((p16 ^ ((row & 3) << 1)) * 8);
-    }
+  // Kb, Vb: first element of this (batch, head); L valid tokens.
+  __device__ __forceinline__ void init(const uint16_t* Kb, int64_t sk_l, const uint16_t* Vb, int64_t sv_l, int L,
+                                       int lane, int wv) {
+    kstride = (unsigned)(sk_l * 2);
+    vstride = (unsigned)(sv_l * 2);
+    krsrc = __builtin_amdgcn_make_buffer_rsrc((void*)Kb, 0, (int)((L - 1) * kstride + 2 * D), 0x00020000);
+    vrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)Vb, 0, (int)((L - 1) * vstride + 2 * D), 0x00020000);
+    int row, p16;
+    seg_row_chunk(wv, lane, row, p16);
+    kvoff = row * kstride + ((p16 ^ k_swz<D>(row)) * 16);
+    vvoff = row * vstride + ((p16 ^ v_swz<D>(row)) * 16);
   }
 
-  __device__ __forceinline__ void issue(uint16_t* tile, const uint16_t* Kb, int64_t sk_l, const uint16_t* Vb,
-                                        int64_t sv_l, int tok0, int L, int lane, int wv) const {
+  // tok0: first token of the block (a value >= L loads nothing but zeros).
+  __device__ __forceinline__ void issue(uint16_t* tile, int tok0, int lane, int wv) const {
     uint16_t* Ks = tile;
     uint16_t* Vs = tile + 64 * D;
-    if (tok0 + 64 <= L) {
-      const uint16_t* kb = Kb + (int64_t)tok0 * sk_l;
-      const uint16_t* vb = Vb + (int64_t)tok0 * sv_l;
 #pragma unroll
-      for (int i = 0; i < kSpw; ++i) {
-        const int sg = wv + NW * i;
-        __builtin_amdgcn_global_load_lds(kb + koff[i], (__attribute__((address_space(3))) void*)(Ks + sg * 512),
-                                         16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vb + voff[i], (__attribute__((address_space(3))) void*)(Vs + sg * 512),
-                                         16, 0, 0);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < kSpw; ++i) {
-        const int sg = wv + NW * i;
+    for (int i = 0; i < kSpw; ++i) {
+      const int sg = wv + NW * i;
+      unsigned kv = kvoff;
+      if constexpr (kRowsPerStep % 16 != 0) {  // the K swizzle does not repeat: recompute
         int row, p16;
         seg_row_chunk(sg, lane, row, p16);
-        const int64_t t = min(tok0 + row, L - 1);
-        __builtin_amdgcn_global_load_lds(Kb + t * sk_l + ((p16 ^ (row & 7)) * 8),
-                                         (__attribute__((address_space(3))) void*)(Ks + sg * 512), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(Vb + t * sv_l + ((p16 ^ ((row & 3) << 1)) * 8),
-                                         (__attribute__((address_space(3))) void*)(Vs + sg * 512), 16, 0, 0);
+        kv = (row - i * kRowsPerStep) * kstride + ((p16 ^ k_swz<D>(row)) * 16);
       }
+      const unsigned rows = (unsigned)(tok0 + i * kRowsPerStep);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          krsrc, (__attribute__((address_space(3))) void*)((__attribute__((address_space(3))) uint16_t*)(Ks + sg * 512)),
+          16, kv, rows * kstride, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          vrsrc, (__attribute__((address_space(3))) void*)((__attribute__((address_space(3))) uint16_t*)(Vs + sg * 512)),
+          16, vvoff, rows * vstride, 0, 0);
     }
   }
 };
@@ -209,7 +222,7 @@ __device__ __forceinline__ bf16x8 lds_v_operand(const uint16_t* Vs, int lane, in
   const int r = j >> 2, q = j & 3;
   const int row = key_base + 4 * (G >> 1) + r;       // (row & 3) == r
   const int c8 = 8 * dt + 4 * (G & 1) + q;           // 8-byte chunk of the channel
-  const int off = ((c8 >> 1) ^ (r << 1)) * 8 + (c8 & 1) * 4;
+  const int off = ((c8 >> 1) ^ v_swz<D>(r)) * 8 + (c8 & 1) * 4;
   const u32x2 lo = lds_read_tr16(Vs + row * D + off);
   const u32x2 hi = lds_read_tr16(Vs + (row + 8) * D + off);
   return cat_bf16x8(lo, hi);
