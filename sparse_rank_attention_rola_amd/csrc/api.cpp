@@ -155,6 +155,19 @@ int lowrank_chunks(const Geo& g, int* chunk_tiles) {
   return (ntiles + ct - 1) / ct;
 }
 
+// Runs of 64-token tiles for the fused prepare pass: aligned to query blocks,
+// about 2048 workgroups in all.
+int prepare_chunks(const Geo& g, int* chunk_tiles) {
+  const int ntiles = (g.L + 63) / 64;
+  const int q_tiles = g.bq / 64;
+  const int64_t bh = (int64_t)g.B * g.H;
+  const int want = (int)std::min<int64_t>(ntiles, std::max<int64_t>(1, (2048 + bh - 1) / bh));
+  int ct = (ntiles + want - 1) / want;
+  ct = (ct + q_tiles - 1) / q_tiles * q_tiles;
+  *chunk_tiles = ct;
+  return (ntiles + ct - 1) / ct;
+}
+
 int max_extent(const sd_attn_shape* s) { return std::max(s->T, std::max(s->Hg, s->Wg)); }
 
 struct LowrankWs {
@@ -435,7 +448,12 @@ size_t sd_rola_workspace_size(const sd_attn_shape* shape, const sd_lowrank_param
   Carve c(nullptr);
   carve_select(c, g);
   c.take(sizeof(int32_t) * g.B * g.H * (size_t)g.Nq * k_keep);
-  carve_lowrank(c, g, shape);
+  int ct;
+  const int nc = prepare_chunks(g, &ct);
+  c.take(sizeof(float2) * sd::kMaxRopePairs * max_extent(shape));
+  c.take(sizeof(float) * g.B * g.H * (size_t)nc * 32 * g.D);
+  c.take(sizeof(uint16_t) * g.B * g.H * g.D * 32);
+  c.take(sizeof(uint16_t) * g.B * g.H * g.D * 32);
   return align_up(c.off);
 }
 
@@ -472,7 +490,15 @@ RolaWs carve_rola(void* ws, const Geo& g, const sd_attn_shape* shape, int k_keep
   RolaWs w;
   w.sel = carve_select(c, g);
   w.idx = static_cast<int32_t*>(c.take(sizeof(int32_t) * g.B * g.H * (size_t)g.Nq * k_keep));
-  w.lr = carve_lowrank(c, g, shape);
+  // the fused pass writes one partial state per run of tiles
+  int ct;
+  const int nc = prepare_chunks(g, &ct);
+  w.lr.n_chunks = nc;
+  w.lr.chunk_tiles = ct;
+  w.lr.rope_tab = static_cast<float2*>(c.take(sizeof(float2) * sd::kMaxRopePairs * max_extent(shape)));
+  w.lr.partial = static_cast<float*>(c.take(sizeof(float) * g.B * g.H * (size_t)nc * 32 * g.D));
+  w.lr.ct_hi = static_cast<uint16_t*>(c.take(sizeof(uint16_t) * g.B * g.H * g.D * 32));
+  w.lr.ct_lo = static_cast<uint16_t*>(c.take(sizeof(uint16_t) * g.B * g.H * g.D * 32));
   return w;
 }
 
@@ -484,11 +510,63 @@ int check_apply_extra(const void* O, const float* g_ptr, float sm_scale, int64_t
   return SD_OK;
 }
 
-int run_prepare(const sd_attn_shape* shape, const Geo& g, const sd_lowrank_params* lr, const void* Q, const void* K,
+// Block map and low-rank state: one streaming pass over Q, K (Kn), V for the
+// block means and partial states, then scores, top-k and the state sum.
+int run_prepare(const sd_attn_shape* s, const Geo& g, const sd_lowrank_params* lr, const void* Q, const void* K,
                 const void* V, const void* Kn, int k_keep, int32_t* idx, const RolaWs& w, hipStream_t st) {
-  int rc;
-  if ((rc = run_block_select(shape, g, Q, K, k_keep, idx, w.sel, st))) return rc;
-  return run_lowrank_state(shape, g, lr, Kn ? Kn : K, V, nullptr, w.lr, st);
+  sd::RopeThetas th{};
+  for (int i = 0; i < lr->n_rope; ++i) th.theta[i] = lr->rope[i].theta;
+  hipError_t e = sd::launch_rope_table(th, lr->n_rope, max_extent(s), w.lr.rope_tab, st);
+  if (e != hipSuccess) return hip_fail(e, "rope table");
+  sd::PrepareArgs a{};
+  a.Q = static_cast<const uint16_t*>(Q);
+  a.K = static_cast<const uint16_t*>(K);
+  a.Kn = static_cast<const uint16_t*>(Kn ? Kn : K);
+  a.V = static_cast<const uint16_t*>(V);
+  a.sq_b = s->sq_b;
+  a.sq_l = s->sq_l;
+  a.sq_h = s->sq_h;
+  a.sk_b = s->sk_b;
+  a.sk_l = s->sk_l;
+  a.sk_h = s->sk_h;
+  a.sv_b = s->sv_b;
+  a.sv_l = s->sv_l;
+  a.sv_h = s->sv_h;
+  a.B = g.B;
+  a.H = g.H;
+  a.L = g.L;
+  a.Nq = g.Nq;
+  a.Nk = g.Nk;
+  a.block_q = g.bq;
+  a.Hg = s->Hg;
+  a.Wg = s->Wg;
+  a.chunk_tiles = w.lr.chunk_tiles;
+  a.n_chunks = w.lr.n_chunks;
+  a.Pk = static_cast<const uint16_t*>(lr->Pk);
+  a.P_hs = lr->P_head_stride;
+  a.rank = lr->rank;
+  a.rope_tab = w.lr.rope_tab;
+  a.rope = rope_args(lr, s);
+  // key-block means come from the stream pass when it reads K itself
+  const bool k_in_stream = a.Kn == a.K;
+  a.kmean = k_in_stream ? w.sel.kmean : nullptr;
+  a.partial = w.lr.partial;
+  e = sd::launch_pool_blocks(a.Q, s->sq_b, s->sq_l, s->sq_h, g.B, g.L, g.H, g.D, g.bq, w.sel.qmean, st);
+  if (e != hipSuccess) return hip_fail(e, "pool Q");
+  if (!k_in_stream) {
+    e = sd::launch_pool_blocks(a.K, s->sk_b, s->sk_l, s->sk_h, g.B, g.L, g.H, g.D, g.bk, w.sel.kmean, st);
+    if (e != hipSuccess) return hip_fail(e, "pool K");
+  }
+  e = sd::launch_prepare_stream(a, g.D, st);
+  if (e != hipSuccess) return hip_fail(e, "prepare pass");
+  e = sd::launch_block_scores(w.sel.qmean, w.sel.kmean, g.B * g.H, g.Nq, g.Nk, g.D, w.sel.S, st);
+  if (e != hipSuccess) return hip_fail(e, "block scores");
+  e = sd::launch_topk_rows(w.sel.S, (int64_t)g.B * g.H * g.Nq, g.Nk, k_keep, idx, st);
+  if (e != hipSuccess) return hip_fail(e, "top-k");
+  e = sd::launch_lowrank_finalize(w.lr.partial, g.B * g.H, w.lr.n_chunks, lr->rank, g.D, nullptr, w.lr.ct_hi,
+                                  w.lr.ct_lo, st);
+  if (e != hipSuccess) return hip_fail(e, "low-rank finalize");
+  return SD_OK;
 }
 
 int run_apply(const sd_attn_shape* shape, const Geo& g, const sd_lowrank_params* lr, const void* Q, const void* K,

@@ -8,9 +8,9 @@
 // O_lr,i with r_i the RMS of O_s,i.
 //
 // One workgroup owns one query block (block_q = 32 * waves queries) of one
-// (batch, head); each wave owns 32 queries. Work items are ordered
-// (batch, head, query block) and spread so each XCD takes a contiguous run,
-// which keeps one head's K/V blocks hot in that XCD's L2.
+// (batch, head); each wave owns 32 queries. All XCDs work on the same head at
+// a time, each on a contiguous eighth of its query blocks, so the last-level
+// cache holds one head's K/V and each L2 sees spatially close query blocks.
 //
 // Per kept key block (64 keys):
 //   * the K and V tiles are staged through LDS (double buffered: the next
@@ -78,18 +78,23 @@ __device__ __forceinline__ void lowrank_query_tile(const u32x4* qreg, const Attn
     Fw[l32 * 33 + ri] = ri < a.rank ? phi_elu1(acc[r]) : 0.f;
   }
   __syncthreads();
-  const int npairs = a.rope.n;
-  for (int it = lane; it < 32 * npairs; it += 64) {
-    const int tk = it / npairs, m = it - tk * npairs;
-    const int tok = tok0 + tk;
-    const int axis = a.rope.axis[m];
+  // RoPE: lane l32 = token; the two lane halves take the even and odd pairs
+  {
+    const int tok = tok0 + l32;
     const int hw = a.Hg * a.Wg;
-    const int p = axis == 0 ? tok / hw : (axis == 1 ? (tok / a.Wg) % a.Hg : tok % a.Wg);
-    const float2 cs = a.rope_tab[m * a.rope.max_ext + min(p, a.rope.max_ext - 1)];
-    float* f = Fw + tk * 33 + a.rope.dim[m];
-    const float u = f[0], v = f[1];
-    f[0] = u * cs.x - v * cs.y;
-    f[1] = u * cs.y + v * cs.x;
+    const int pos[3] = {min(tok / hw, a.rope.max_ext - 1), (tok / a.Wg) % a.Hg, tok % a.Wg};
+    for (int m0 = 0; m0 < a.rope.n; m0 += 2) {
+      const int m = m0 + hf;
+      if (m < a.rope.n) {
+        const int axis = hf ? a.rope.axis[m0 + 1] : a.rope.axis[m0];
+        const int dim = hf ? a.rope.dim[m0 + 1] : a.rope.dim[m0];
+        const float2 cs = a.rope_tab[m * a.rope.max_ext + (axis == 0 ? pos[0] : axis == 1 ? pos[1] : pos[2])];
+        float* f = Fw + l32 * 33 + dim;
+        const float u = f[0], v = f[1];
+        f[0] = u * cs.x - v * cs.y;
+        f[1] = u * cs.y + v * cs.x;
+      }
+    }
   }
   __syncthreads();
   bf16x8 qhi[2], qlo[2];
@@ -162,11 +167,10 @@ __global__ __launch_bounds__(BQ * 2, SD_ATTN_WAVES) void attention_kernel(AttnAr
   __shared__ __attribute__((aligned(16))) uint16_t smem1[TileSmem<D>::kElems];
   __shared__ int sidx[kMaxKeep];
 
-  const int64_t n_work = (int64_t)a.B * a.H * a.Nq;
-  const int64_t wi = xcd_work_index(blockIdx.x, n_work);
-  if (wi < 0) return;
-  const int qb = (int)(wi % a.Nq);
-  const int64_t bh = wi / a.Nq;
+  int64_t bh;
+  int qb;
+  if (!xcd_group_item(blockIdx.x, a.Nq, (int64_t)a.B * a.H, bh, qb)) return;
+  const int64_t wi = bh * a.Nq + qb;
   const int h = (int)(bh % a.H), b = (int)(bh / a.H);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -433,8 +437,7 @@ SD_ATTN_INST_MODES(64, 64)
 
 template <int D, int BQ, int MODE>
 static hipError_t launch_attention_t(const AttnArgs& a, hipStream_t stream) {
-  const int64_t n_work = (int64_t)a.B * a.H * a.Nq;
-  const int64_t grid = (n_work + kNumXcd - 1) / kNumXcd * kNumXcd;
+  const int64_t grid = (int64_t)kNumXcd * ((a.Nq + kNumXcd - 1) / kNumXcd) * a.B * a.H;
   hipLaunchKernelGGL((attention_kernel<D, BQ, MODE>), dim3((unsigned)grid), dim3(BQ * 2), 0, stream, a);
   return hipGetLastError();
 }

@@ -154,8 +154,27 @@ __global__ __launch_bounds__(256) void topk_rows_kernel(const double* __restrict
     for (int i = 0; i < 4; ++i) hist[wv][lane + 64 * i] = 0;
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < NPL; ++j)
-      if (valid[j] && (key[j] & pmask) == prefix) atomicAdd(&hist[wv][(uint32_t)(key[j] >> shift) & 255u], 1u);
+    for (int j = 0; j < NPL; ++j) {
+      const bool f = valid[j] && (key[j] & pmask) == prefix;
+      if (shift < 48) {
+        if (f) atomicAdd(&hist[wv][(uint32_t)(key[j] >> shift) & 255u], 1u);
+        continue;
+      }
+      const uint64_t fm = __ballot(f);
+      if (fm) {
+        const uint32_t dg = (uint32_t)(key[j] >> shift) & 255u;
+        const int lead = __builtin_ctzll(fm);
+        const uint32_t d0 = (uint32_t)__shfl((int)dg, lead);
+        if (__ballot(f && dg != d0) == 0) {
+          // one digit for every candidate of this chunk (the rule in the two
+          // leading digits, sign and exponent): one update instead of 64
+          // contended LDS atomics
+          if (lane == lead) atomicAdd(&hist[wv][d0], (uint32_t)__popcll(fm));
+        } else if (f) {
+          atomicAdd(&hist[wv][dg], 1u);
+        }
+      }
+    }
     __syncthreads();
     // lane covers bins 255-4*lane .. 252-4*lane, i.e. digits in descending order
     uint32_t cnt[4];

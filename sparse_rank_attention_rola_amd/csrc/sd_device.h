@@ -64,6 +64,20 @@ __device__ __forceinline__ int64_t xcd_work_index(int64_t wg, int64_t n_work) {
   return w < n_work ? w : -1;
 }
 
+// Workgroup -> (group, item) map that keeps all XCDs on the same group at a
+// time: group g (a batch-head) is split into 8 contiguous runs of items (query
+// blocks), run x going to XCD x. Concurrent workgroups then share one head's
+// K/V in the last-level cache while each XCD's L2 sees a contiguous run.
+// The grid must have 8 * ceil(items / 8) * groups workgroups; returns false
+// for padding workgroups.
+__device__ __forceinline__ bool xcd_group_item(int64_t wg, int items, int64_t groups, int64_t& group, int& item) {
+  const int per = (items + kNumXcd - 1) / kNumXcd;
+  const int64_t j = wg / kNumXcd;
+  group = j / per;
+  item = (int)(wg % kNumXcd) * per + (int)(j % per);
+  return group < groups && item < items;
+}
+
 // Value of lane l ^ 32 (v_permlane32_swap: one VALU op, no LDS traffic).
 __device__ __forceinline__ float partner32(float x, int hf) {
   const int xi = __float_as_int(x);
@@ -72,6 +86,52 @@ __device__ __forceinline__ float partner32(float x, int hf) {
 }
 
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef int int2v __attribute__((ext_vector_type(2)));
+
+// Lane-exchange helpers for float64 values (two 32-bit moves each, VALU only).
+template <int CTRL>  // DPP control, e.g. 0x120 + n = rotate right by n within a row of 16
+__device__ __forceinline__ double dpp_f64(double v) {
+  const int2v p = __builtin_bit_cast(int2v, v);
+  int2v r;
+  r[0] = __builtin_amdgcn_update_dpp(0, p[0], CTRL, 0xF, 0xF, false);
+  r[1] = __builtin_amdgcn_update_dpp(0, p[1], CTRL, 0xF, 0xF, false);
+  return __builtin_bit_cast(double, r);
+}
+
+// value of lane l ^ 16 (v_permlane16_swap exchanges the odd and even rows)
+__device__ __forceinline__ double partner16_f64(double v, int lane) {
+  const int2v p = __builtin_bit_cast(int2v, v);
+  const auto a = __builtin_amdgcn_permlane16_swap(p[0], p[0], false, false);
+  const auto b = __builtin_amdgcn_permlane16_swap(p[1], p[1], false, false);
+  const bool odd = (lane >> 4) & 1;
+  int2v r;
+  r[0] = odd ? a[0] : a[1];
+  r[1] = odd ? b[0] : b[1];
+  return __builtin_bit_cast(double, r);
+}
+
+__device__ __forceinline__ double partner32_f64(double v, int lane) {
+  const int2v p = __builtin_bit_cast(int2v, v);
+  const auto a = __builtin_amdgcn_permlane32_swap(p[0], p[0], false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(p[1], p[1], false, false);
+  const bool up = lane >= 32;
+  int2v r;
+  r[0] = up ? a[0] : a[1];
+  r[1] = up ? b[0] : b[1];
+  return __builtin_bit_cast(double, r);
+}
+
+// Sum of v over the lanes of a wave that agree on lane % G (G = 2 or 4), in a
+// fixed order; every lane receives its class's sum.
+template <int G>
+__device__ __forceinline__ double sum_lanes_mod(double v, int lane) {
+  if constexpr (G == 2) v += dpp_f64<0x122>(v);
+  v += dpp_f64<0x124>(v);
+  v += dpp_f64<0x128>(v);
+  v += partner16_f64(v, lane);
+  v += partner32_f64(v, lane);
+  return v;
+}
 
 // Sum of the 8 bf16 values of an MFMA operand, accumulated into acc (f32).
 __device__ __forceinline__ float sum_bf16x8(bf16x8 v, float acc) {

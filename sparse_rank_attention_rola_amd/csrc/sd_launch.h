@@ -53,6 +53,26 @@ struct LowrankKvArgs {
   float* partial;  // [B*H, n_chunks, 32, D]
 };
 
+// One streaming pass over Kn, V: block means of K (when Kn is K and kmean is
+// set) plus the partial low-rank states of each run of tiles.
+struct PrepareArgs {
+  const uint16_t* Q;
+  const uint16_t* K;
+  const uint16_t* Kn;  // may equal K
+  const uint16_t* V;
+  int64_t sq_b, sq_l, sq_h, sk_b, sk_l, sk_h, sv_b, sv_l, sv_h;
+  int B, H, L, Nq, Nk, block_q, Hg, Wg;
+  int chunk_tiles;  // 64-token tiles per workgroup (a multiple of block_q / 64)
+  int n_chunks;
+  const uint16_t* Pk;
+  int64_t P_hs;
+  int rank;
+  const float2* rope_tab;
+  RopeArgs rope;
+  double* kmean;   // [B*H, Nk, D] or null
+  float* partial;  // [B*H, n_chunks, 32, D]
+};
+
 hipError_t launch_quant_fp8(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q, int64_t ldq,
                             float* scales, hipStream_t stream);
 hipError_t launch_pool_blocks(const uint16_t* X, int64_t sb, int64_t sl, int64_t sh, int B, int L, int H, int D,
@@ -70,6 +90,7 @@ hipError_t launch_rope_table(const RopeThetas& th, int n, int max_ext, float2* t
 hipError_t launch_lowrank_kv(const LowrankKvArgs& a, int D, hipStream_t stream);
 hipError_t launch_lowrank_finalize(const float* partial, int BH, int n_chunks, int rank, int D, float* C_out,
                                    uint16_t* Ct_hi, uint16_t* Ct_lo, hipStream_t stream);
+hipError_t launch_prepare_stream(const PrepareArgs& a, int D, hipStream_t stream);
 hipError_t launch_gate_fuse(const void* Os, const void* Olr, int in_f32, const float* g, int64_t g_sb, int64_t g_sl,
                             int64_t g_sh, void* O, int B, int L, int H, int D, int64_t so_b, int64_t so_l,
                             int64_t so_h, hipStream_t stream);
