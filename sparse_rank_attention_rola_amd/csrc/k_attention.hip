@@ -33,21 +33,6 @@ namespace sd {
 
 enum AttnMode { kModeSparse = 0, kModeLowrank = 1, kModeFused = 2 };
 
-#ifndef SD_ATTN_PIPE
-#define SD_ATTN_PIPE 2  // 1: issue both halves' QK^T before the first softmax
-#endif
-// Wave priority around the MFMA chains: while one wave of a SIMD runs its
-// softmax on the VALU, the other wave's matrix work is issued first.
-#ifndef SD_ATTN_PRIO
-#define SD_ATTN_PRIO 0
-#endif
-#if SD_ATTN_PRIO
-#define SD_PRIO_HI() __builtin_amdgcn_s_setprio(1)
-#define SD_PRIO_LO() __builtin_amdgcn_s_setprio(0)
-#else
-#define SD_PRIO_HI()
-#define SD_PRIO_LO()
-#endif
 #ifndef SD_ATTN_WAVES
 #define SD_ATTN_WAVES 2  // minimum waves per SIMD the register budget must allow
 #endif
@@ -159,7 +144,7 @@ __device__ __forceinline__ void store_row(void* base, bool f32, int64_t off, con
 }
 
 template <int D, int BQ, int MODE>
-__global__ __launch_bounds__(BQ * 2, SD_ATTN_WAVES) void attention_kernel(AttnArgs a) {
+__global__ __launch_bounds__(BQ * 2, BQ == 128 ? SD_ATTN_WAVES : 1) void attention_kernel(AttnArgs a) {
   constexpr int NW = BQ / 32;
   constexpr int NT = NW * 64;
   constexpr bool kLoop = MODE != kModeLowrank;
@@ -213,143 +198,84 @@ __global__ __launch_bounds__(BQ * 2, SD_ATTN_WAVES) void attention_kernel(AttnAr
       return (unsigned)c < (unsigned)a.Nk ? c * 64 : a.L;
     };
 
-    // One kept block of 64 keys, as two half-tiles of 32. S^T (32 keys x 32
-    // queries) = K Q^T for both halves is issued first, so the second
-    // half's MFMAs run while the first half's softmax is on the VALU; then
-    // per half: online-softmax update in the log2 domain and O^T += V^T P^T.
-    // This lane holds 16 of the 32 keys of its query per half.
-    auto softmax_half = [&](f32x16& sacc, int key0, int kt, bool tail, bf16x8& p0, bf16x8& p1) {
-      if (tail) {
+    // One kept block of 64 keys, as two half-tiles of 32 keys. The lane
+    // holds 16 of the 32 keys of its query per half-tile.
+    auto mask_half = [&](f32x16& sacc, int key0, int kt) {
+      // key of register r: key0 + 32 kt + 4 hf + 8 (r / 4) + r % 4, compared
+      // as a constant against one per-lane limit
+      const int lim = a.L - key0 - 32 * kt - 4 * hf;
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (key0 + 32 * kt + 8 * (r >> 2) + 4 * hf + (r & 3) >= a.L) sacc[r] = -INFINITY;
-      }
+      for (int r = 0; r < 16; ++r)
+        if (8 * (r >> 2) + (r & 3) >= lim) sacc[r] = -INFINITY;
+    };
+    // Online softmax of a half-tile in the log2 domain, without touching O:
+    // returns whether the reference maximum moves (for some lane), the new
+    // maximum and the sum of the bf16 probabilities the PV product consumes.
+    // Lazy rescaling: the maximum only moves when a score exceeds it by more
+    // than 2^8, so P <= 256 and O, l stay well inside f32.
+    auto softmax_half = [&](const f32x16& sacc, bf16x8& p0, bf16x8& p1, float& m_new, float& rs) {
       float mloc = sacc[0];
 #pragma unroll
       for (int r = 1; r < 16; ++r) mloc = fmaxf(mloc, sacc[r]);
       mloc = fmaxf(mloc, partner32(mloc, hf)) * a.scale_log2;
-      // Lazy rescaling: the reference max only moves when a score exceeds it
-      // by more than 2^8, so P <= 256 and O, l stay well inside f32.
-      if (__ballot(mloc > m + 8.f)) {
-        const float m_new = mloc > m + 8.f ? mloc : m;
-        const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-        lsum *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
-        m = m_new;
-      }
-      const float neg_m = m == -INFINITY ? 0.f : -m;
+      const bool up = mloc > m + 8.f;
+      m_new = up ? mloc : m;
+      const float neg_m = m_new == -INFINITY ? 0.f : -m_new;
       float p16[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) p16[r] = __builtin_amdgcn_exp2f(fmaf(sacc[r], a.scale_log2, neg_m));
       p0 = to_bf16x8(p16);
       p1 = to_bf16x8(p16 + 8);
-      // the normaliser sums the bf16 values the PV product consumes
-      lsum = sum_bf16x8(p1, sum_bf16x8(p0, lsum));
+      rs = sum_bf16x8(p1, sum_bf16x8(p0, 0.f));
+      return up;
     };
-    auto pv_half = [&](const uint16_t* Vs, int kt, bf16x8 p0, bf16x8 p1) {
-      // keys of each 16-key step in the order 4hf+{0..3}, 8+4hf+{0..3} on
-      // both operands
+    auto rescale = [&](bool up, float m_new, float rs) {
+      if (__ballot(up)) {
+        const float alpha = up ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;
+        lsum *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-        oacc[dt] = mfma32(lds_v_operand<D>(Vs, lane, dt, 32 * kt), p0, oacc[dt]);
-        oacc[dt] = mfma32(lds_v_operand<D>(Vs, lane, dt, 32 * kt + 16), p1, oacc[dt]);
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
       }
+      m = m_new;
+      lsum += rs;
     };
+    // S^T (32 keys x 32 queries) = K Q^T for both halves, then per half the
+    // softmax and O^T += V^T P^T (keys of each 16-key step in the order
+    // 4hf+{0..3}, 8+4hf+{0..3} on both operands). Independent accumulators
+    // alternate in every MFMA sequence (the two halves' S^T chains; the
+    // channel tiles of O^T): no MFMA waits on the result of the one issued
+    // just before it.
     auto compute = [&](const uint16_t* tile, int key0) {
       const uint16_t* Ks = tile;
       const uint16_t* Vs = tile + 64 * D;
-      const bool tail = key0 + 64 > a.L;
-#if SD_ATTN_PIPE
       f32x16 s0 = {}, s1 = {};
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s) s0 = mfma32(lds_k_chunk<D>(Ks, l32, 2 * s + hf), as_bf16x8(qreg[s]), s0);
-#pragma unroll
-      for (int s = 0; s < D / 16; ++s) s1 = mfma32(lds_k_chunk<D>(Ks, 32 + l32, 2 * s + hf), as_bf16x8(qreg[s]), s1);
-      bf16x8 pa, pb;
-      softmax_half(s0, key0, 0, tail, pa, pb);
-      pv_half(Vs, 0, pa, pb);
-      softmax_half(s1, key0, 1, tail, pa, pb);
-      pv_half(Vs, 1, pa, pb);
-#elif SD_ATTN_PIPE == 2
-      // operands are read from LDS a stage ahead of the MFMAs that use them
-      bf16x8 kop[D / 16];
-#pragma unroll
-      for (int s = 0; s < D / 16; ++s) kop[s] = lds_k_chunk<D>(Ks, l32, 2 * s + hf);
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        f32x16 sacc = {};
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s) sacc = mfma32(kop[s], as_bf16x8(qreg[s]), sacc);
-        bf16x8 vop[D / 32][2];
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          vop[dt][0] = lds_v_operand<D>(Vs, lane, dt, 32 * kt);
-          vop[dt][1] = lds_v_operand<D>(Vs, lane, dt, 32 * kt + 16);
-        }
-        if (kt == 0) {
-#pragma unroll
-          for (int s = 0; s < D / 16; ++s) kop[s] = lds_k_chunk<D>(Ks, 32 + l32, 2 * s + hf);
-        }
-        bf16x8 pa, pb;
-        softmax_half(sacc, key0, kt, tail, pa, pb);
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          oacc[dt] = mfma32(vop[dt][0], pa, oacc[dt]);
-          oacc[dt] = mfma32(vop[dt][1], pb, oacc[dt]);
-        }
+      for (int s = 0; s < D / 16; ++s) {
+        s0 = mfma32(lds_k_chunk<D>(Ks, l32, 2 * s + hf), as_bf16x8(qreg[s]), s0);
+        s1 = mfma32(lds_k_chunk<D>(Ks, 32 + l32, 2 * s + hf), as_bf16x8(qreg[s]), s1);
       }
-#elif SD_ATTN_PIPE == 3
+      if (key0 + 64 > a.L) {
+        mask_half(s0, key0, 0);
+        mask_half(s1, key0, 1);
+      }
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        // QK chain: each K operand read is issued one MFMA ahead
-        f32x16 sacc = {};
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s)
-          sacc = mfma32(lds_k_chunk<D>(Ks, 32 * kt + l32, 2 * s + hf), as_bf16x8(qreg[s]), sacc);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-        for (int s = 0; s < D / 16 - 2; ++s) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
         bf16x8 pa, pb;
-        softmax_half(sacc, key0, kt, tail, pa, pb);
-        // PV chain: the two transposing reads of each V operand one MFMA ahead
+        float mn, rs;
+        const bool up = softmax_half(kt ? s1 : s0, pa, pb, mn, rs);
+        rescale(up, mn, rs);
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          oacc[dt] = mfma32(lds_v_operand<D>(Vs, lane, dt, 32 * kt), pa, oacc[dt]);
+        for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = mfma32(lds_v_operand<D>(Vs, lane, dt, 32 * kt), pa, oacc[dt]);
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
           oacc[dt] = mfma32(lds_v_operand<D>(Vs, lane, dt, 32 * kt + 16), pb, oacc[dt]);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
-#pragma unroll
-        for (int i = 0; i < D / 16 - 1; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
       }
-#else
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        f32x16 sacc = {};
-        SD_PRIO_HI();
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s)
-          sacc = mfma32(lds_k_chunk<D>(Ks, 32 * kt + l32, 2 * s + hf), as_bf16x8(qreg[s]), sacc);
-        SD_PRIO_LO();
-        bf16x8 pa, pb;
-        softmax_half(sacc, key0, kt, tail, pa, pb);
-        SD_PRIO_HI();
-        pv_half(Vs, kt, pa, pb);
-        SD_PRIO_LO();
-      }
-#endif
     };
 
+    // Double-buffered tiles: block i+1's loads are in flight while block i
+    // computes; one wait + barrier per block.
     ld.issue(smem0, block_tok0(0), lane, wv);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();

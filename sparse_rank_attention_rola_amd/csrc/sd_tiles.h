@@ -178,10 +178,9 @@ struct DirectTileLoader {
     vvoff = row * vstride + ((p16 ^ v_swz<D>(row)) * 16);
   }
 
-  // tok0: first token of the block (a value >= L loads nothing but zeros).
-  __device__ __forceinline__ void issue(uint16_t* tile, int tok0, int lane, int wv) const {
-    uint16_t* Ks = tile;
-    uint16_t* Vs = tile + 64 * D;
+  // K tile of the block starting at token tok0 into Ks (64 x D, swizzled);
+  // a tok0 >= L loads nothing but zeros.
+  __device__ __forceinline__ void issue_k(uint16_t* Ks, int tok0, int lane, int wv) const {
 #pragma unroll
     for (int i = 0; i < kSpw; ++i) {
       const int sg = wv + NW * i;
@@ -195,10 +194,23 @@ struct DirectTileLoader {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           krsrc, (__attribute__((address_space(3))) void*)((__attribute__((address_space(3))) uint16_t*)(Ks + sg * 512)),
           16, kv, rows * kstride, 0, 0);
+    }
+  }
+  // V tile of the block starting at token tok0 into Vs (64 x D, swizzled).
+  __device__ __forceinline__ void issue_v(uint16_t* Vs, int tok0, int wv) const {
+#pragma unroll
+    for (int i = 0; i < kSpw; ++i) {
+      const int sg = wv + NW * i;
+      const unsigned rows = (unsigned)(tok0 + i * kRowsPerStep);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           vrsrc, (__attribute__((address_space(3))) void*)((__attribute__((address_space(3))) uint16_t*)(Vs + sg * 512)),
           16, vvoff, rows * vstride, 0, 0);
     }
+  }
+  // K and V tiles of one block into a tile buffer (K rows, then V rows).
+  __device__ __forceinline__ void issue(uint16_t* tile, int tok0, int lane, int wv) const {
+    issue_k(tile, tok0, lane, wv);
+    issue_v(tile + 64 * D, tok0, wv);
   }
 };
 
