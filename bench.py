@@ -87,6 +87,63 @@ def cpu_baseline(cfg, Qb, Kb, Vb, Pqb, Pkb, g, k, n_heads):
                       f"scaled by {cfg.B * cfg.H / len(heads):g} to one layer"}
 
 
+def _rocpd(path):
+    """Open the rocprofv3 result database under `path` (a directory or a .db file)."""
+    import glob
+    import sqlite3
+    dbs = [path] if path.endswith(".db") else sorted(glob.glob(os.path.join(path, "**", "*.db"), recursive=True))
+    if not dbs:
+        raise SystemExit(f"no rocprofv3 database under {path}")
+    return sqlite3.connect(dbs[0])
+
+
+def trace_summary(path, cmd, skip):
+    """Markdown table of a rocprofv3 --kernel-trace database: per kernel the
+    launches, mean / min / max duration and the mean over the launches after
+    the first `skip` (the warmup steps of the profiled bench)."""
+    db = _rocpd(path)
+    rows = {}
+    for name, dur in db.execute("select name, duration from kernels order by start"):
+        rows.setdefault(name, []).append(dur / 1e3)
+    lines = [f"Command: `{cmd}`", "",
+             f"| kernel | launches | mean us | min us | max us | mean us after {skip} warmup launches |",
+             "|---|---|---|---|---|---|"]
+    for name, d in sorted(rows.items(), key=lambda kv: -sum(kv[1])):
+        warm = d[skip:] or d
+        short = name.split("(")[0].replace("void ", "")
+        lines.append(f"| `{short}` | {len(d)} | {sum(d) / len(d):.1f} | {min(d):.1f} | {max(d):.1f} | "
+                     f"{sum(warm) / len(warm):.1f} |")
+    return "\n".join(lines)
+
+
+def pmc_traffic(fetch_path, write_path, kernel="attention_kernel", copy_bytes=1 << 30):
+    """HBM bytes per launch of `kernel` from a FETCH_SIZE run and a WRITE_SIZE
+    run (KiB per dispatch), each scaled by what the counter reads for the
+    1 GiB device copies of --calib-copy."""
+    def per_dispatch(path, counter):
+        db = _rocpd(path)
+        out = {}
+        for did, name, val in db.execute(
+                "select dispatch_id, name, sum(counter_value) from pmc_events where counter_name = ? "
+                "group by dispatch_id", (counter,)):
+            out[did] = (name, val)
+        return out
+    res = {}
+    for counter, path in (("FETCH_SIZE", fetch_path), ("WRITE_SIZE", write_path)):
+        d = per_dispatch(path, counter)
+        copies = sorted(v for n, v in d.values() if "copyBuffer" in n)
+        big = [v for v in copies if v > 0.25 * copy_bytes / 1024]
+        if not big:
+            raise SystemExit(f"no calibration copy found in the {counter} run")
+        big = big[-3:]
+        factor = (copy_bytes / 1024) / (sum(big) / len(big))
+        vals = [v for n, v in d.values() if kernel in n]
+        res[counter] = {"kib_per_dispatch": sum(vals) / len(vals), "dispatches": len(vals),
+                        "copy_kib_read": sum(big) / len(big), "scale": factor}
+    total = sum(r["kib_per_dispatch"] * r["scale"] for r in res.values()) * 1024
+    return res, total
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -94,10 +151,28 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--sparsity", type=float, default=0.97)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=4, help="whole heads in the oracle sample")
+    ap.add_argument("--cpu-heads", type=int, default=8, help="whole heads in the oracle sample")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter calibration)")
+    ap.add_argument("--trace-summary", metavar="DB", help="print a kernel table of a rocprofv3 trace and exit")
+    ap.add_argument("--pmc-traffic", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
+                    help="write the fused kernel's HBM bytes per launch from two rocprofv3 --pmc runs "
+                         "(FETCH_SIZE, WRITE_SIZE, each with --calib-copy) to the traffic record and exit")
+    ap.add_argument("--cmd", default="", help="command line recorded with --trace-summary / --pmc-traffic")
     args = ap.parse_args()
+
+    if args.trace_summary:
+        print(trace_summary(args.trace_summary, args.cmd, args.warmup))
+        return
+    if args.pmc_traffic:
+        res, total = pmc_traffic(*args.pmc_traffic)
+        rec = {"kernel": "attention_kernel<128, 128, 2> (fused sparse/low-rank/gate)", "sparsity": args.sparsity,
+               "source_hash": kernel_source_hash(), "bytes_per_launch": round(total), "counters": res,
+               "command": args.cmd}
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(rec, f, indent=1)
+        print(json.dumps(rec, indent=1))
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
