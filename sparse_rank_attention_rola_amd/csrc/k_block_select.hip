@@ -14,14 +14,16 @@
 //                      Each thread owns 8 adjacent channels of one head and
 //                      walks the tokens of one block; a wave reads 1 KB of a
 //                      token row per load (coalesced), HBM-bound.
-//  block_scores_kernel S[b, h] = qmean . kmean^T as a 64x64-tiled f64 GEMM
-//                      on the vector ALUs (4x4 register blocking, LDS tiles).
-//  topk_rows_kernel    one wavefront per score row: an 8-pass radix select
-//                      (8-bit digits of the order-preserving 64-bit image of
-//                      the scores) finds the k-th largest score exactly; the
-//                      row is then compacted in index order with ballots, so
-//                      the output is ascending and equal scores at the
-//                      threshold go to the lower block index.
+//  block_scores_kernel S[b, h] = qmean . kmean^T as a 128x128-tiled f64 GEMM
+//                      on the vector ALUs (8x8 register blocking, LDS panels).
+//  topk_rows_kernel    one wavefront per score row: a radix select on 8-bit
+//                      digits of the order-preserving 64-bit image of the
+//                      scores, from the top, finds the k-th largest score
+//                      exactly (it stops early once every candidate left in
+//                      the chosen bin is kept); the row is then compacted in
+//                      index order with ballots, so the output is ascending
+//                      and equal scores at the threshold go to the lower
+//                      block index.
 #include "sd_device.h"
 #include "sd_launch.h"
 
@@ -70,54 +72,73 @@ __global__ __launch_bounds__(256) void pool_blocks_kernel(const uint16_t* __rest
   for (int i = 0; i < 8; ++i) o[i] = acc[i] / n;
 }
 
-// S[bh][r][c] = sum_d A[bh][r][d] * Bm[bh][c][d]   (A: [R, D], Bm: [C, D])
+// S[bh][r][c] = sum_d A[bh][r][d] * Bm[bh][c][d]   (A: [R, D], Bm: [C, D]).
+// 128 x 128 output tile per workgroup; thread (tx, ty) of a 16 x 16 grid
+// owns rows ty + 16 i and columns tx + 16 j (i, j < 8): per 16 x 8-byte
+// LDS reads it issues 64 float64 FMAs, and its stores are 128-byte runs.
+// The d-loop goes in steps of 16 through k-major LDS panels.
 __global__ __launch_bounds__(256) void block_scores_kernel(const double* __restrict__ A, const double* __restrict__ Bm,
                                                            int R, int C, int D, double* __restrict__ S) {
-  constexpr int TK = 16;
-  __shared__ double As[TK][64 + 2];
-  __shared__ double Bs[TK][64 + 2];
+  constexpr int TM = 128, TK = 16;
+  __shared__ double As[TK][TM + 1];
+  __shared__ double Bs[TK][TM + 1];
   const int bh = blockIdx.z;
-  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int r0 = blockIdx.y * TM, c0 = blockIdx.x * TM;
   const double* Ab = A + (int64_t)bh * R * D;
   const double* Bb = Bm + (int64_t)bh * C * D;
   const int tid = threadIdx.x;
   const int tx = tid & 15, ty = tid >> 4;
-  double acc[4][4];
+  double acc[8][8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
-  const int lr = tid >> 2, lk = (tid & 3) * 4;  // loader: row lr, 4 channels at lk
+    for (int j = 0; j < 8; ++j) acc[i][j] = 0.0;
+  // loader: 128 rows x 16 d per panel = 2048 values, 8 per thread: row lr,
+  // d = lk .. lk + 7 (64 contiguous bytes of the row)
+  const int lr = tid >> 1, lk = (tid & 1) * 8;
+  const bool a_ok = r0 + lr < R, b_ok = c0 + lr < C;
+  const double* ap = Ab + (int64_t)(a_ok ? r0 + lr : 0) * D + lk;
+  const double* bp = Bb + (int64_t)(b_ok ? c0 + lr : 0) * D + lk;
+  double av[8], bv[8];
+  auto load_panel = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      av[i] = a_ok ? ap[k0 + i] : 0.0;
+      bv[i] = b_ok ? bp[k0 + i] : 0.0;
+    }
+  };
+  load_panel(0);
   for (int k0 = 0; k0 < D; k0 += TK) {
+    __syncthreads();  // the previous panel's readers are done
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      As[lk + i][lr] = (r0 + lr < R) ? Ab[(int64_t)(r0 + lr) * D + k0 + lk + i] : 0.0;
-      Bs[lk + i][lr] = (c0 + lr < C) ? Bb[(int64_t)(c0 + lr) * D + k0 + lk + i] : 0.0;
+    for (int i = 0; i < 8; ++i) {
+      As[lk + i][lr] = av[i];
+      Bs[lk + i][lr] = bv[i];
     }
     __syncthreads();
+    if (k0 + TK < D) load_panel(k0 + TK);  // in flight during this panel's FMAs
 #pragma unroll
     for (int kk = 0; kk < TK; ++kk) {
-      double a[4], bv[4];
+      double a[8], b[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        a[i] = As[kk][ty * 4 + i];
-        bv[i] = Bs[kk][tx * 4 + i];
+      for (int i = 0; i < 8; ++i) {
+        a[i] = As[kk][ty + 16 * i];
+        b[i] = Bs[kk][tx + 16 * i];
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fma(a[i], bv[j], acc[i][j]);
+        for (int j = 0; j < 8; ++j) acc[i][j] = fma(a[i], b[j], acc[i][j]);
     }
-    __syncthreads();
   }
   double* Sb = S + (int64_t)bh * R * C;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = r0 + ty * 4 + i;
+  for (int i = 0; i < 8; ++i) {
+    const int r = r0 + ty + 16 * i;
     if (r >= R) continue;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int c = c0 + tx * 4 + j;
+    for (int j = 0; j < 8; ++j) {
+      const int c = c0 + tx + 16 * j;
       if (c < C) Sb[(int64_t)r * C + c] = acc[i][j];
     }
   }
@@ -126,6 +147,15 @@ __global__ __launch_bounds__(256) void block_scores_kernel(const double* __restr
 __device__ __forceinline__ uint64_t order_key(double x) {
   const uint64_t u = __double_as_longlong(x);
   return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+}
+
+// Orders this wave's LDS accesses (the histogram of a row is private to its
+// wave, so no workgroup barrier is needed and waves may leave the radix
+// loop at different passes).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 template <int NPL>  // scores per lane (row length <= 64 * NPL)
@@ -152,7 +182,7 @@ __global__ __launch_bounds__(256) void topk_rows_kernel(const double* __restrict
   for (int shift = 56; shift >= 0; shift -= 8) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) hist[wv][lane + 64 * i] = 0;
-    __syncthreads();
+    wave_lds_sync();
 #pragma unroll
     for (int j = 0; j < NPL; ++j) {
       const bool f = valid[j] && (key[j] & pmask) == prefix;
@@ -175,7 +205,7 @@ __global__ __launch_bounds__(256) void topk_rows_kernel(const double* __restrict
         }
       }
     }
-    __syncthreads();
+    wave_lds_sync();
     // lane covers bins 255-4*lane .. 252-4*lane, i.e. digits in descending order
     uint32_t cnt[4];
 #pragma unroll
@@ -199,22 +229,34 @@ __global__ __launch_bounds__(256) void topk_rows_kernel(const double* __restrict
       }
       above += cnt[i];
     }
+    uint32_t in_bin = 0;  // candidates in the chosen bin
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (digit == 255 - 4 * lane - i) in_bin = cnt[i];
     digit = __shfl(digit, src);
     above = (uint32_t)__shfl((int)above, src);
+    in_bin = (uint32_t)__shfl((int)in_bin, src);
     remaining -= (int)above;
     prefix |= (uint64_t)digit << shift;
     pmask |= 0xFFull << shift;
-    __syncthreads();
+    wave_lds_sync();
+    // every candidate left in the chosen bin is kept: the bits below do not
+    // change the selection (wave-uniform exit)
+    if (in_bin == (uint32_t)remaining) break;
   }
 
   if (!row_ok) return;
-  // prefix is the exact k-th largest key; `remaining` keys equal to it are kept
+  // keys whose leading bits (pmask) exceed the prefix are kept, and of those
+  // equal to it on those bits the first `remaining` in index order (all of
+  // them when the loop ended early); with every bit examined, prefix is the
+  // exact k-th largest key
   int taken = 0, ties = 0;
   int32_t* out = idx + row * k;
 #pragma unroll
   for (int j = 0; j < NPL; ++j) {
-    const bool gt = valid[j] && key[j] > prefix;
-    const bool eq = valid[j] && key[j] == prefix;
+    const uint64_t km = key[j] & pmask;
+    const bool gt = valid[j] && km > prefix;
+    const bool eq = valid[j] && km == prefix;
     const uint64_t eqm = __ballot(eq);
     const bool take = gt || (eq && ties + __popcll(eqm & lt_mask) < remaining);
     const uint64_t tm = __ballot(take);
@@ -235,7 +277,7 @@ hipError_t launch_pool_blocks(const uint16_t* X, int64_t sb, int64_t sl, int64_t
 
 hipError_t launch_block_scores(const double* qmean, const double* kmean, int BH, int Nq, int Nk, int D, double* S,
                                hipStream_t stream) {
-  const dim3 grid((Nk + 63) / 64, (Nq + 63) / 64, BH);
+  const dim3 grid((Nk + 127) / 128, (Nq + 127) / 128, BH);
   hipLaunchKernelGGL(block_scores_kernel, grid, dim3(256), 0, stream, qmean, kmean, Nq, Nk, D, S);
   return hipGetLastError();
 }

@@ -33,9 +33,11 @@ __global__ __launch_bounds__(256) void prepare_stream_kernel(PrepareArgs a) {
   __shared__ float F[64 * 33];
   __shared__ double kred[D];
 
-  int64_t bh;
-  int chunk;
-  if (!xcd_group_item(blockIdx.x, a.n_chunks, (int64_t)a.B * a.H, bh, chunk)) return;
+  // All heads of a run of tokens run side by side, so that together the
+  // workgroups read whole token rows of K and V (DRAM-friendly).
+  const int64_t nbh = (int64_t)a.B * a.H;
+  const int64_t bh = blockIdx.x % nbh;
+  const int chunk = (int)(blockIdx.x / nbh);
   const int h = (int)(bh % a.H), b = (int)(bh / a.H);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -172,7 +174,7 @@ __global__ __launch_bounds__(256) void prepare_stream_kernel(PrepareArgs a) {
 }
 
 hipError_t launch_prepare_stream(const PrepareArgs& a, int D, hipStream_t stream) {
-  const int64_t grid = (int64_t)kNumXcd * ((a.n_chunks + kNumXcd - 1) / kNumXcd) * a.B * a.H;
+  const int64_t grid = (int64_t)a.n_chunks * a.B * a.H;
   if (D == 128)
     hipLaunchKernelGGL(prepare_stream_kernel<128>, dim3((unsigned)grid), dim3(256), 0, stream, a);
   else if (D == 64)
