@@ -13,7 +13,9 @@ Sources (the page, then the section / equation):
   * SparkDiffusion README_zh (github raw), single-sample inference section:
     `topk` is the keep ratio (0.1/0.05/0.03 <-> 90/95/97% sparsity);
   * kais-engine portability report, section 2.1 (three-stage recipe:
-    proj_q/proj_k map head_dim -> rank, gate_proj/gate_bias is a scalar gate).
+    proj_q/proj_k map head_dim -> rank, gate_proj/gate_bias is a scalar gate);
+  * the same write-up, section 2.3, for the W8A8 projection fed by the
+    per-token quantiser (gemm.py).
 
 Where the pages leave a step open, the reading taken is stated in the
 docstring of the function that takes it.
@@ -50,4 +52,9 @@ from .fp8 import (  # noqa: F401
     e4m3_encode,
     quant_fp8_per_token,
     AMAX_FLOOR,
+)
+from .gemm import (  # noqa: F401
+    quant_weight_per_channel,
+    w8a8_gemm,
+    w8a8_abs_products,
 )
