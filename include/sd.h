@@ -173,6 +173,23 @@ int sd_gate_fuse(const sd_attn_shape* shape, const void* Os, const void* Olr, in
 int sd_quant_fp8_per_token(const void* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
                            int64_t ldq, float* scales, void* stream);
 
+/* ---- (6) W8A8 FP8 projection ------------------------------------------------
+ * robotworld.top write-up, section 2.3: the linear projections run W8A8 in
+ * FP8 E4M3, weights with a static scale per output channel, activations with
+ * the dynamic per-token scale of sd_quant_fp8_per_token:
+ *   y[m, n] = sx[m] * sw[n] * sum_k E4M3(xq[m, k]) * E4M3(wq[n, k])
+ * xq: uint8 codes [M, K], row stride ldx bytes (the quantiser's q);
+ * sx: f32 [M] (its scales); wq: uint8 codes [N, K], row stride ldw bytes,
+ * one row per output channel (W quantised row by row, e.g. by
+ * sd_quant_fp8_per_token on W once, offline); sw: f32 [N]; y: bf16 [M, N],
+ * row stride ldy elements, rounded to nearest even. Accumulation is f32.
+ * Needs K % 64 == 0, ldx and ldw multiples of 16 (>= K), ldy % 4 == 0
+ * (>= N), 16-byte aligned xq, wq, sw and 8-byte aligned y; K <= 65536 and
+ * 256 * max(ldx, ldw) < 2^31. All buffers are caller-owned device memory. */
+int sd_gemm_fp8_w8a8(const uint8_t* xq, int64_t M, int64_t K, int64_t ldx, const float* sx,
+                     const uint8_t* wq, int64_t N, int64_t ldw, const float* sw, void* y, int64_t ldy,
+                     void* stream);
+
 /* ---- fused layer -------------------------------------------------------------
  * The whole path of section 2.1 in one call: block map, sparse branch,
  * low-rank branch and gated fusion. O: bf16 [B, L, H, d] at the so_*

@@ -28,7 +28,7 @@ SD_PHI_ELU1 = 1
 EXPORTED = [
     "sd_keep_count", "sd_rope_default", "sd_block_select_workspace_size", "sd_block_select",
     "sd_sparse_attn", "sd_lowrank_workspace_size", "sd_lowrank_attn", "sd_gate_fuse",
-    "sd_quant_fp8_per_token", "sd_rola_workspace_size", "sd_rola_attention", "sd_rola_prepare",
+    "sd_quant_fp8_per_token", "sd_gemm_fp8_w8a8", "sd_rola_workspace_size", "sd_rola_attention", "sd_rola_prepare",
     "sd_rola_apply", "sd_status_string", "sd_last_error",
 ]
 
@@ -75,6 +75,7 @@ def _declare(lib):
         "sd_lowrank_attn": (i32, [S, LR, P, P, P, P, i32, P, P, sz, P]),
         "sd_gate_fuse": (i32, [S, P, P, i32, P, i64, i64, i64, P, P]),
         "sd_quant_fp8_per_token": (i32, [P, i64, i64, i64, P, i64, P, P]),
+        "sd_gemm_fp8_w8a8": (i32, [P, i64, i64, i64, P, P, i64, i64, P, P, i64, P]),
         "sd_rola_workspace_size": (sz, [S, LR, i32]),
         "sd_rola_attention": (i32, [S, LR, P, P, P, P, P, P, i64, i64, i64, i32, f32, P, P, P, sz, P]),
         "sd_rola_prepare": (i32, [S, LR, P, P, P, P, P, i32, P, P, sz, P]),
@@ -257,6 +258,25 @@ def sd_quant_fp8_per_token(x, *, q=None, scales=None, stream=None):
     _check(lib().sd_quant_fp8_per_token(_ptr(x), M, K, x.stride(0), _ptr(q), q.stride(0), _ptr(scales),
                                         _stream_ptr(stream)))
     return q, scales
+
+
+def sd_gemm_fp8_w8a8(xq, sx, wq, sw, *, out=None, stream=None):
+    """bf16 y [M, N] = diag(sx) (E4M3(xq) E4M3(wq)^T) diag(sw) for uint8 codes
+    xq [M, K] and wq [N, K] (one row per output channel)."""
+    torch = _torch()
+    M, K = xq.shape
+    N, K2 = wq.shape
+    if K2 != K:
+        raise ValueError("xq and wq must have the same K")
+    if xq.stride(1) != 1 or wq.stride(1) != 1:
+        raise ValueError("rows of xq and wq must be contiguous")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
+    if out.stride(1) != 1:
+        raise ValueError("rows of out must be contiguous")
+    _check(lib().sd_gemm_fp8_w8a8(_ptr(xq), M, K, xq.stride(0), _ptr(sx), _ptr(wq), N, wq.stride(0), _ptr(sw),
+                                  _ptr(out), out.stride(0), _stream_ptr(stream)))
+    return out
 
 
 def rola_workspace(Q, lr: LowrankParams, k_keep, *, grid, block_q=128):

@@ -1,5 +1,6 @@
 // libsd C ABI: host-side validation, workspace layout and kernel dispatch.
 // Semantics of every entry point are documented in include/sd.h.
+#include <algorithm>
 #include "sd.h"
 
 #include <hip/hip_runtime.h>
@@ -437,6 +438,27 @@ int sd_quant_fp8_per_token(const void* x, int64_t M, int64_t K, int64_t ldx, uin
   const hipError_t e = sd::launch_quant_fp8(static_cast<const uint16_t*>(x), M, K, ldx, q, ldq, scales,
                                             static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "fp8 quant");
+  return ok();
+}
+
+int sd_gemm_fp8_w8a8(const uint8_t* xq, int64_t M, int64_t K, int64_t ldx, const float* sx, const uint8_t* wq,
+                     int64_t N, int64_t ldw, const float* sw, void* y, int64_t ldy, void* stream) {
+  if (M < 0 || N < 0 || K <= 0)
+    return fail(SD_ERR_INVALID_ARG, "M = %lld, N = %lld, K = %lld", (long long)M, (long long)N, (long long)K);
+  if (K % 64) return fail(SD_ERR_UNSUPPORTED, "K = %lld is not a multiple of 64", (long long)K);
+  if (K > 65536) return fail(SD_ERR_UNSUPPORTED, "K = %lld exceeds 65536", (long long)K);
+  if (ldx < K || ldw < K || ldy < N) return fail(SD_ERR_INVALID_ARG, "ldx, ldw must be >= K and ldy >= N");
+  if (ldx % 16 || ldw % 16 || ldy % 4) return fail(SD_ERR_ALIGN, "ldx, ldw must be multiples of 16, ldy of 4");
+  if (256 * std::max(ldx, ldw) >= ((int64_t)1 << 31))
+    return fail(SD_ERR_UNSUPPORTED, "row strides too large for 32-bit tile offsets");
+  if (M == 0 || N == 0) return ok();
+  int rc;
+  if ((rc = check_dev_ptr(xq, "xq")) || (rc = check_dev_ptr(wq, "wq")) || (rc = check_dev_ptr(sx, "sx", 4)) ||
+      (rc = check_dev_ptr(sw, "sw")) || (rc = check_dev_ptr(y, "y", 8)))
+    return rc;
+  sd::GemmFp8Args a{xq, wq, sx, sw, static_cast<uint16_t*>(y), M, N, K, ldx, ldw, ldy};
+  const hipError_t e = sd::launch_gemm_fp8(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "fp8 gemm");
   return ok();
 }
 

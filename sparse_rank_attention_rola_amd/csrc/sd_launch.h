@@ -73,6 +73,17 @@ struct PrepareArgs {
   float* partial;  // [B*H, n_chunks, 32, D]
 };
 
+// W8A8 FP8 projection y = diag(sx) (xq wq^T) diag(sw), bf16 out.
+struct GemmFp8Args {
+  const uint8_t* xq;  // [M, K], row stride ldx bytes
+  const uint8_t* wq;  // [N, K], row stride ldw bytes
+  const float* sx;    // [M]
+  const float* sw;    // [N]
+  uint16_t* y;        // [M, N] bf16, row stride ldy elements
+  int64_t M, N, K, ldx, ldw, ldy;
+};
+hipError_t launch_gemm_fp8(const GemmFp8Args& a, hipStream_t stream);
+
 hipError_t launch_quant_fp8(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q, int64_t ldq,
                             float* scales, hipStream_t stream);
 hipError_t launch_pool_blocks(const uint16_t* X, int64_t sb, int64_t sl, int64_t sh, int B, int L, int H, int D,

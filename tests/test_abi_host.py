@@ -166,6 +166,27 @@ def test_gate_fuse_and_quant_validation():
 
 
 @host_only
+def test_gemm_fp8_validation():
+    lib = sd.lib()
+
+    def g(M=300, N=200, K=128, ldx=128, ldw=128, ldy=200, xq=FAKE, y=FAKE):
+        return lib.sd_gemm_fp8_w8a8(xq, M, K, ldx, FAKE, FAKE, N, ldw, FAKE, y, ldy, None)
+
+    assert g(K=100, ldx=112, ldw=112) == sd.SD_ERR_UNSUPPORTED  # K % 64
+    assert g(K=131072, ldx=131072, ldw=131072) == sd.SD_ERR_UNSUPPORTED
+    assert g(ldx=64) == sd.SD_ERR_INVALID_ARG  # ldx < K
+    assert g(ldy=100) == sd.SD_ERR_INVALID_ARG  # ldy < N
+    assert g(ldx=136) == sd.SD_ERR_ALIGN  # ldx % 16
+    assert g(ldy=202) == sd.SD_ERR_ALIGN  # ldy % 4
+    assert g(M=-1) == sd.SD_ERR_INVALID_ARG
+    assert g(xq=None) == sd.SD_ERR_INVALID_ARG
+    assert g(xq=FAKE + 8) == sd.SD_ERR_ALIGN
+    assert g(y=FAKE + 4) == sd.SD_ERR_ALIGN
+    assert g(ldx=1 << 24, ldw=1 << 24) == sd.SD_ERR_UNSUPPORTED
+    assert g(M=0) == sd.SD_OK  # nothing to do, nothing touched
+
+
+@host_only
 def test_rola_validation():
     lib = sd.lib()
     s = _shape()

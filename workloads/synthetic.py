@@ -180,3 +180,45 @@ def gen_activation(M: int, K: int, seed: int = 0, outlier_frac: float = 0.01,
     with _pool() as ex:
         list(ex.map(work, range(0, M, step)))
     return out
+
+
+# Config-5 projections of the 720P block: QKV (3 x 5120 outputs) and output.
+PROJ_QKV_720P = (75600, 15360, 5120)  # (M tokens, N outputs, K inputs)
+PROJ_OUT_720P = (75600, 5120, 5120)
+
+
+def gen_weight(N: int, K: int, seed: int = 0) -> np.ndarray:
+    """bf16 bits [N, K] ~ N(0, 1/K) (one row per output channel), from the
+    stream seeded by seed + 4000003 (rows in runs, like gen_activation)."""
+    base = seed + 4_000_003
+    out = np.empty((N, K), dtype=np.uint16)
+    step = max(1, (1 << 22) // K)
+
+    def work(s0):
+        e0 = min(N, s0 + step)
+        w = (_child(base, s0 // step).standard_normal((e0 - s0, K)) / np.sqrt(K)).astype(np.float32)
+        out[s0:e0] = f32_to_bf16_bits(w)
+
+    with _pool() as ex:
+        list(ex.map(work, range(0, N, step)))
+    return out
+
+
+def gen_fp8_codes(M: int, K: int, seed: int = 0):
+    """(uint8 [M, K] random finite E4M3FN codes, float32 [M] scales in
+    [2^-8, 2^-4)): operands of the projection at full size, drawn directly
+    (stream seed + 5000003)."""
+    base = seed + 5_000_003
+    out = np.empty((M, K), dtype=np.uint8)
+    step = max(1, (1 << 23) // K)
+
+    def work(s0):
+        e0 = min(M, s0 + step)
+        c = _child(base, s0 // step).integers(0, 254, size=(e0 - s0, K), dtype=np.uint8)
+        c[c >= 0x7F] += 1  # skip 0x7F (NaN); 254 values map onto 0..0xFE minus 0x7F
+        out[s0:e0] = c
+    with _pool() as ex:
+        list(ex.map(work, range(0, M, step)))
+    rng = np.random.Generator(np.random.PCG64(base))
+    scales = np.exp2(rng.uniform(-8.0, -4.0, M)).astype(np.float32)
+    return out, scales
