@@ -7,7 +7,9 @@ sparse attention layer of Wan2.1-T2V-14B at 720P -- B=1, 40 heads of width
 blocks, sparsity 0.97 (36 of 1182 key blocks kept per query block), rank 32
 -- plus the per-token FP8 E4M3 quantisation of the layer's 75600 x 5120
 bf16 activation. One step = quantise the activation, then the fused layer
-(block map + low-rank state, then the fused sparse/low-rank/gate kernel).
+(block map + low-rank state, then the fused sparse/low-rank/gate kernel). The
+W8A8 QKV projection that consumes the quantised activation (75600 x 15360 x
+5120) is timed on its own after the steps and reported beside them.
 Inputs are seeded synthetic tensors of those shapes, resident in HBM before
 the timed region.
 
@@ -26,6 +28,7 @@ sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+MFMA_FP8_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 MFMA
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_rola_fused_720p.json")
 FUSED_KERNEL_SOURCES = ["k_attention.hip", "sd_tiles.h", "sd_device.h", "sd_launch.h"]
 
@@ -152,6 +155,7 @@ def main():
     ap.add_argument("--sparsity", type=float, default=0.97)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=8, help="whole heads in the oracle sample")
+    ap.add_argument("--no-gemm", action="store_true", help="skip the FP8 projection measurement")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter calibration)")
     ap.add_argument("--trace-summary", metavar="DB", help="print a kernel table of a rocprofv3 trace and exit")
@@ -242,6 +246,34 @@ def main():
     t_apply = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
     t_layer = float(np.mean([e[1].elapsed_time(e[3]) for e in evs]))
 
+    # W8A8 FP8 QKV projection of the same layer (the step that consumes the
+    # quantised activation): weights quantised per output channel once,
+    # outside the timed region, then the projection timed on its own
+    gemm = None
+    if not args.no_gemm:
+        Mg, Ng, Kg = synthetic.PROJ_QKV_720P
+        log(f"fp8 projection: {Mg}x{Ng}x{Kg}")
+        W = to_dev(synthetic.gen_weight(Ng, Kg, 0))
+        wq, sw = sd.sd_quant_fp8_per_token(W)
+        del W
+        y = torch.empty((Mg, Ng), dtype=torch.bfloat16, device=dev)
+        for _ in range(max(1, args.warmup)):
+            sd.sd_gemm_fp8_w8a8(codes, scales, wq, sw, out=y)
+        torch.cuda.synchronize()
+        gev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        n_g = max(3, args.steps // 2)
+        gev[0].record()
+        for _ in range(n_g):
+            sd.sd_gemm_fp8_w8a8(codes, scales, wq, sw, out=y)
+        gev[1].record()
+        torch.cuda.synchronize()
+        t_g = gev[0].elapsed_time(gev[1]) / n_g
+        gflop = 2.0 * Mg * Ng * Kg
+        gemm = {"shape_MxNxK": [Mg, Ng, Kg], "ms": round(t_g, 4),
+                "tflops": round(gflop / (t_g * 1e-3) / 1e12, 1),
+                "fp8_mfma_peak_frac": round(gflop / (t_g * 1e-3) / 1e12 / MFMA_FP8_PEAK_TFLOPS, 4)}
+        del y, wq, sw
+
     if args.calib_copy:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)
@@ -295,6 +327,7 @@ def main():
                      "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
                      "algorithmic_flops_per_launch": flops},
+        "w8a8_qkv_projection": gemm,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
