@@ -157,12 +157,15 @@ int lowrank_chunks(const Geo& g, int* chunk_tiles) {
 }
 
 // Runs of 64-token tiles for the fused prepare pass: aligned to query blocks,
-// about 2048 workgroups in all.
+// at most kPrepareSlots workgroups in all where the shape allows it, so that
+// every run is resident at once (three 4-wave workgroups per CU on 256 CUs)
+// and none waits for a second round.
+constexpr int64_t kPrepareSlots = 768;
 int prepare_chunks(const Geo& g, int* chunk_tiles) {
   const int ntiles = (g.L + 63) / 64;
   const int q_tiles = g.bq / 64;
   const int64_t bh = (int64_t)g.B * g.H;
-  const int want = (int)std::min<int64_t>(ntiles, std::max<int64_t>(1, (2048 + bh - 1) / bh));
+  const int want = (int)std::min<int64_t>(ntiles, std::max<int64_t>(1, kPrepareSlots / bh));
   int ct = (ntiles + want - 1) / want;
   ct = (ct + q_tiles - 1) / q_tiles * q_tiles;
   *chunk_tiles = ct;
@@ -231,7 +234,9 @@ int run_lowrank_state(const sd_attn_shape* s, const Geo& g, const sd_lowrank_par
   a.partial = w.partial;
   e = sd::launch_lowrank_kv(a, g.D, st);
   if (e != hipSuccess) return hip_fail(e, "low-rank state");
-  e = sd::launch_lowrank_finalize(w.partial, g.B * g.H, w.n_chunks, lr->rank, g.D, C_out, w.ct_hi, w.ct_lo, st);
+  sd::RankRows rows{};
+  for (int r = 0; r < 32; ++r) rows.row[r] = (int8_t)(r < lr->rank ? r : -1);
+  e = sd::launch_lowrank_finalize(w.partial, g.B * g.H, w.n_chunks, lr->rank, g.D, rows, C_out, w.ct_hi, w.ct_lo, st);
   if (e != hipSuccess) return hip_fail(e, "low-rank finalize");
   return SD_OK;
 }
@@ -562,6 +567,8 @@ int run_prepare(const sd_attn_shape* s, const Geo& g, const sd_lowrank_params* l
   a.block_q = g.bq;
   a.Hg = s->Hg;
   a.Wg = s->Wg;
+  a.rcp_hw = 1.0f / (float)(s->Hg * s->Wg);
+  a.rcp_wg = 1.0f / (float)s->Wg;
   a.chunk_tiles = w.lr.chunk_tiles;
   a.n_chunks = w.lr.n_chunks;
   a.Pk = static_cast<const uint16_t*>(lr->Pk);
@@ -569,6 +576,30 @@ int run_prepare(const sd_attn_shape* s, const Geo& g, const sd_lowrank_params* l
   a.rank = lr->rank;
   a.rope_tab = w.lr.rope_tab;
   a.rope = rope_args(lr, s);
+  // rank slots: each RoPE pair takes the next two slots, then each rank
+  // outside every pair one slot; the rest stay empty
+  sd::RankRows rows{};
+  for (int r = 0; r < 32; ++r) rows.row[r] = -1;
+  for (int i = 0; i < 32; ++i) a.slot_rank[i] = -1;
+  for (int p = 0; p < 16; ++p) a.slot_pair[p] = -1;
+  int nslot = 0;
+  for (int m = 0; m < lr->n_rope; ++m) {
+    a.slot_pair[nslot / 2] = (int8_t)m;
+    for (int k = 0; k < 2; ++k) {
+      a.slot_rank[nslot] = (int8_t)(lr->rope[m].dim + k);
+      rows.row[lr->rope[m].dim + k] = (int8_t)nslot;
+      ++nslot;
+    }
+  }
+  for (int r = 0; r < lr->rank; ++r)
+    if (rows.row[r] < 0) {
+      a.slot_rank[nslot] = (int8_t)r;
+      rows.row[r] = (int8_t)nslot;
+      ++nslot;
+    }
+  a.slot_mask = 0;
+  for (int i = 0; i < 32; ++i)
+    if (a.slot_rank[i] >= 0) a.slot_mask |= 1u << i;
   // key-block means come from the stream pass when it reads K itself
   const bool k_in_stream = a.Kn == a.K;
   a.kmean = k_in_stream ? w.sel.kmean : nullptr;
@@ -585,7 +616,7 @@ int run_prepare(const sd_attn_shape* s, const Geo& g, const sd_lowrank_params* l
   if (e != hipSuccess) return hip_fail(e, "block scores");
   e = sd::launch_topk_rows(w.sel.S, (int64_t)g.B * g.H * g.Nq, g.Nk, k_keep, idx, st);
   if (e != hipSuccess) return hip_fail(e, "top-k");
-  e = sd::launch_lowrank_finalize(w.lr.partial, g.B * g.H, w.lr.n_chunks, lr->rank, g.D, nullptr, w.lr.ct_hi,
+  e = sd::launch_lowrank_finalize(w.lr.partial, g.B * g.H, w.lr.n_chunks, lr->rank, g.D, rows, nullptr, w.lr.ct_hi,
                                   w.lr.ct_lo, st);
   if (e != hipSuccess) return hip_fail(e, "low-rank finalize");
   return SD_OK;

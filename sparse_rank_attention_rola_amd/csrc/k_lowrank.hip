@@ -122,16 +122,19 @@ __global__ __launch_bounds__(256) void lowrank_kv_kernel(LowrankKvArgs a) {
 }
 
 __global__ void lowrank_finalize_kernel(const float* __restrict__ partial, int64_t BH, int n_chunks, int rank,
-                                        int D, float* __restrict__ C_out, uint16_t* __restrict__ Ct_hi,
+                                        int D, RankRows rows, float* __restrict__ C_out, uint16_t* __restrict__ Ct_hi,
                                         uint16_t* __restrict__ Ct_lo) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= BH * 32 * D) return;
   const int d = (int)(i % D);
   const int r = (int)((i / D) % 32);
   const int64_t bh = i / (32 * D);
-  const float* p = partial + (bh * n_chunks * 32 + r) * D + d;
+  const int row = rows.row[r];
   float s = 0.f;
-  for (int c = 0; c < n_chunks; ++c) s += p[(int64_t)c * 32 * D];
+  if (row >= 0) {
+    const float* p = partial + (bh * n_chunks * 32 + row) * D + d;
+    for (int c = 0; c < n_chunks; ++c) s += p[(int64_t)c * 32 * D];
+  }
   if (C_out && r < rank) C_out[(bh * rank + r) * D + d] = s;
   const __bf16 hi = (__bf16)s;
   const __bf16 lo = (__bf16)(s - (float)hi);
@@ -158,11 +161,11 @@ hipError_t launch_lowrank_kv(const LowrankKvArgs& a, int D, hipStream_t stream) 
   return hipGetLastError();
 }
 
-hipError_t launch_lowrank_finalize(const float* partial, int BH, int n_chunks, int rank, int D, float* C_out,
-                                   uint16_t* Ct_hi, uint16_t* Ct_lo, hipStream_t stream) {
+hipError_t launch_lowrank_finalize(const float* partial, int BH, int n_chunks, int rank, int D, const RankRows& rows,
+                                   float* C_out, uint16_t* Ct_hi, uint16_t* Ct_lo, hipStream_t stream) {
   const int64_t total = (int64_t)BH * 32 * D;
   hipLaunchKernelGGL(lowrank_finalize_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, partial,
-                     (int64_t)BH, n_chunks, rank, D, C_out, Ct_hi, Ct_lo);
+                     (int64_t)BH, n_chunks, rank, D, rows, C_out, Ct_hi, Ct_lo);
   return hipGetLastError();
 }
 

@@ -5,15 +5,23 @@
 // phi; C linear in the sequence length).
 //
 // One workgroup (4 waves) owns a run of 64-token tiles of one (batch, head),
-// aligned to query blocks. Per tile:
-//   * Kn and V tiles are staged into LDS with raw buffer loads (double
-//     buffered, the next tile in flight during the current one);
-//   * waves 0-1 project 32 tokens each onto the rank dims with P_k on MFMA,
-//     apply phi, and park k~ in an LDS patch, while waves 2-3 sum the staged
-//     K tile's columns in float64 (exact for bf16 values) for the key-block
-//     means; all threads rotate the RoPE pairs; each wave then owns 32
-//     channels of C^T and accumulates V^T k~ on MFMA (V^T operands from
-//     transposing LDS reads, k~ split into bf16 hi + lo parts).
+// aligned to query blocks; about three workgroups per CU, all resident at
+// once. Per tile:
+//   * each thread prefetches its share of the next tile's K and V rows into
+//     registers (buffer loads) and writes them into the LDS tile when the
+//     tile's turn comes;
+//   * each wave projects 16 tokens onto the rank dims with P_k on MFMA and
+//     applies phi into a float patch F, and sums 16 of the tile's K rows in
+//     float64 (exact for bf16 values) for the key-block means;
+//   * thread (token, wave w) rotates the RoPE pairs of rank slots
+//     8w .. 8w+7, splits the features into bf16 hi + lo parts once, and
+//     stores them as MFMA operands (in the K half of the tile, dead by then);
+//   * each wave owns 32 channels of C^T and accumulates V^T k~ on MFMA (V^T
+//     operands from transposing LDS reads).
+// The rank dims are held in slot order: every RoPE pair occupies two
+// adjacent slots starting at an even slot, so a pair never straddles two
+// threads' 8-slot groups; the partial states are written in slot order and
+// the finalising sum maps slots back to ranks.
 // K and V are each read from HBM once. (The query-block means come from the
 // pooling kernel, which streams Q once.)
 #include "sd_device.h"
@@ -24,14 +32,81 @@ namespace sd {
 
 __device__ __forceinline__ float phi_elu1_p(float x) { return x > 0.f ? x + 1.f : __expf(x); }
 
+// x / d and x % d for 0 <= x < 2^24, d >= 1, with rcp = 1/d rounded to
+// float: the float quotient is off by at most one, and one correction step
+// each way makes it exact.
+__device__ __forceinline__ int div_small(int x, int d, float rcp, int& rem) {
+  int q = (int)((float)x * rcp);
+  int r = x - q * d;
+  if (r < 0) {
+    --q;
+    r += d;
+  } else if (r >= d) {
+    ++q;
+    r -= d;
+  }
+  rem = r;
+  return q;
+}
+
+// Register staging of one 64-token K and V tile: thread tid owns 16-byte
+// chunk tid % kCpr of rows tid / kCpr + kRows * i.
 template <int D>
-__global__ __launch_bounds__(256) void prepare_stream_kernel(PrepareArgs a) {
+struct RegTile {
+  static constexpr int kCpr = D / 8;              // 16-byte chunks per row
+  static constexpr int kPer = 64 * kCpr / 256;    // chunks per thread per tensor
+  static constexpr int kRows = 256 / kCpr;        // rows covered by one pass of the workgroup
+  static_assert(kRows % 16 == 0, "swizzles must repeat within kRows");
+  u32x4 k[kPer], v[kPer];
+
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr, unsigned kstr,
+                                       unsigned vstr, int tok0, int tid) {
+    const int row = tid / kCpr, col = tid % kCpr;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+      k[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           kr, (int)(row * kstr + 16 * col), (int)((tok0 + kRows * i) * kstr), 0));
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+      v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           vr, (int)(row * vstr + 16 * col), (int)((tok0 + kRows * i) * vstr), 0));
+  }
+  // Both swizzles depend on the row only through bits that kRows leaves
+  // unchanged, so the LDS addresses of the chunks differ by constants.
+  __device__ __forceinline__ void store(uint16_t* tile, int tid) const {
+    const int row = tid / kCpr, col = tid % kCpr;
+    uint16_t* kd = tile + row * D + ((col ^ k_swz<D>(row)) * 8);
+    uint16_t* vd = tile + 64 * D + row * D + ((col ^ v_swz<D>(row)) * 8);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      *reinterpret_cast<u32x4*>(kd + kRows * i * D) = k[i];
+      *reinterpret_cast<u32x4*>(vd + kRows * i * D) = v[i];
+    }
+  }
+};
+
+// Feature operands of the C^T update, bf16 [32 slots][64 tokens]: row j
+// holds in its 16-byte chunk 2s + h the tokens 16s + 4h + {0..3} and
+// 16s + 8 + 4h + {0..3} (the key order of the transposing V read), chunk c
+// stored at c ^ ((j / 2) % 8) so that 16 rows read one chunk column without
+// bank conflicts.
+__device__ __forceinline__ int fop_index(int j, int t) {
+  const int s = t >> 4, u = t & 15;
+  const int c = 2 * s + ((u >> 2) & 1);
+  const int e = (u & 3) + 4 * (u >> 3);
+  return j * 64 + ((c ^ ((j >> 1) & 7)) << 3) + e;
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 3) void prepare_stream_kernel(PrepareArgs a) {
   constexpr int NW = 4;
-  constexpr int CH = D / 64;  // channels per lane in the K block sums
-  __shared__ __attribute__((aligned(16))) uint16_t tile0[TileSmem<D>::kElems];
-  __shared__ __attribute__((aligned(16))) uint16_t tile1[TileSmem<D>::kElems];
-  __shared__ float F[64 * 33];
-  __shared__ double kred[D];
+  constexpr int CH = D / 64;
+  constexpr int FS = 36;  // F row stride (floats): 16-byte aligned rows, conflict-free b128 access
+  static_assert(2 * 32 * 64 <= 64 * D, "feature operands must fit in the K half of the tile");
+  __shared__ __attribute__((aligned(16))) uint16_t tile[TileSmem<D>::kElems];
+  __shared__ __attribute__((aligned(16))) float F[64 * FS];
+  __shared__ double kred[3][D];
+  __shared__ __attribute__((aligned(16))) uint16_t Ps[32 * D];
 
   // All heads of a run of tokens run side by side, so that together the
   // workgroups read whole token rows of K and V (DRAM-friendly).
@@ -49,123 +124,185 @@ __global__ __launch_bounds__(256) void prepare_stream_kernel(PrepareArgs a) {
 
   const uint16_t* Knb = a.Kn + (int64_t)b * a.sk_b + (int64_t)h * a.sk_h;
   const uint16_t* Vb = a.V + (int64_t)b * a.sv_b + (int64_t)h * a.sv_h;
-  // the K tile is staged for the block sums too; when the low-rank branch
-  // reads a separate Kn, the sums come from the pooling kernel instead
+  // the K tile is summed for the block means too; when the low-rank branch
+  // reads a separate Kn, the means come from the pooling kernel instead
   const bool pool_k = a.kmean != nullptr;
+  const unsigned kstr = (unsigned)(a.sk_l * 2), vstr = (unsigned)(a.sv_l * 2);
+  // rows past L read as zeros (range-checked buffers); the empty buffers
+  // serve loads past the workgroup's run
+  const __amdgpu_buffer_rsrc_t kr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)Knb, 0, (int)((a.L - 1) * kstr + 2 * D), 0x00020000);
+  const __amdgpu_buffer_rsrc_t vr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)Vb, 0, (int)((a.L - 1) * vstr + 2 * D), 0x00020000);
+  const __amdgpu_buffer_rsrc_t kr0 = __builtin_amdgcn_make_buffer_rsrc((void*)Knb, 0, 0, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vr0 = __builtin_amdgcn_make_buffer_rsrc((void*)Vb, 0, 0, 0x00020000);
 
-  DirectTileLoader<D, NW> ld;
-  ld.init(Knb, a.sk_l, Vb, a.sv_l, a.L, lane, wv);
-
-  u32x4 P[D / 16];
+  // P_k rows in slot order (empty slots zero), laid out like a K tile
   {
     const uint16_t* Pk = a.Pk + (int64_t)h * a.P_hs;
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s)
-      P[s] = (wv < 2 && l32 < a.rank) ? *reinterpret_cast<const u32x4*>(Pk + l32 * D + 16 * s + 8 * hf)
-                                      : u32x4{0, 0, 0, 0};
+    for (int c = tid; c < 32 * (D / 8); c += 256) {
+      const int row = c / (D / 8), col = c % (D / 8);
+      const int rk = a.slot_rank[row];
+      *reinterpret_cast<u32x4*>(Ps + row * D + ((col ^ k_swz<D>(row)) * 8)) =
+          rk >= 0 ? *reinterpret_cast<const u32x4*>(Pk + rk * D + 8 * col) : u32x4{0, 0, 0, 0};
+    }
   }
   f32x16 cacc = {};
 
-  if (t_begin < t_end) ld.issue(tile0, t_begin * 64, lane, wv);
-  for (int tl = t_begin; tl < t_end; ++tl) {
-    const int tok0 = tl * 64;
-    uint16_t* cur = ((tl - t_begin) & 1) ? tile1 : tile0;
-    uint16_t* nxt = ((tl - t_begin) & 1) ? tile0 : tile1;
-
-    // RoPE factors of this lane's token for the pairs of this wave (issued
-    // early so their latency overlaps the projections)
-    constexpr int kMaxPW = kMaxRopePairs / NW;
-    float2 cs[kMaxPW];
-    const int rtok = tok0 + lane;
-    {
-      const int tc = min(rtok, a.L - 1);
-      const int pos[3] = {tc / hw, (tc / a.Wg) % a.Hg, tc % a.Wg};
+  // K block sums: wave wv sums rows 16 wv .. +15, lane = CH adjacent
+  // channels; LDS offsets of the lane's channels in rows 0..15 (the K
+  // swizzle of row 16 wv + t depends on t only)
+  const int c0 = lane * CH;
+  int koff[16];
 #pragma unroll
-      for (int j = 0; j < kMaxPW; ++j) {
-        const int m = wv + NW * j;
-        if (m < a.rope.n) {
-          const int axis = a.rope.axis[m];
-          cs[j] = a.rope_tab[m * a.rope.max_ext + (axis == 0 ? pos[0] : axis == 1 ? pos[1] : pos[2])];
+  for (int t = 0; t < 16; ++t) koff[t] = t * D + (((c0 >> 3) ^ k_swz<D>(t)) << 3) + (c0 & 7);
+
+  // cos/sin at this lane's token of the tile at tok0 for the RoPE pairs of
+  // slot pairs 4 wv + j (slot pairs without a RoPE pair load row 0, unused)
+  auto load_cs = [&](float2(&cs)[4], int tok0) __attribute__((always_inline)) {
+    const int tc = min(tok0 + lane, a.L - 1);
+    int pos[3], rest;
+    pos[0] = div_small(tc, hw, a.rcp_hw, rest);
+    pos[1] = div_small(rest, a.Wg, a.rcp_wg, pos[2]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int m = max((int)a.slot_pair[4 * wv + j], 0);
+      const int axis = a.rope.axis[m];
+      cs[j] = a.rope_tab[m * a.rope.max_ext + (axis == 0 ? pos[0] : axis == 1 ? pos[1] : pos[2])];
+    }
+  };
+
+  // One 64-token tile. Vector-memory operations complete in issue order, so
+  // each step issues its global stores after every load that a later wait
+  // needs: a wait never has to cover a store.
+  auto step = [&](RegTile<D>& rt, int tl, float2(&cs)[4]) __attribute__((always_inline)) {
+    const int tok0 = tl * 64;
+    __syncthreads();  // the previous tile's readers are done with the tile
+    rt.store(tile, tid);
+    // refill the registers with tile tl + 1; past the run the loads go to
+    // empty buffers (zeros, no memory access), so every path issues the
+    // same loads and the waits stay counted
+    const bool more = tl + 1 < t_end;
+    rt.load(more ? kr : kr0, more ? vr : vr0, kstr, vstr, (tl + 1) * 64, tid);
+    __syncthreads();
+
+    {
+      // phi(P_k k) of tokens 16 wv .. +15 on 16x16x32 MFMAs, both 16-slot
+      // halves; lane (token l16, group g = lane / 16) holds slots
+      // 16 rh + 4 g + {0..3}; empty slots and tokens past L are zero
+      const int l16 = lane & 15, g = lane >> 4;
+      f32x4 acc[2] = {};
+#pragma unroll
+      for (int s = 0; s < D / 32; ++s) {
+        const bf16x8 kop = lds_k_chunk<D>(tile, 16 * wv + l16, 4 * s + g);
+#pragma unroll
+        for (int rh = 0; rh < 2; ++rh)
+          acc[rh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_k_chunk<D>(Ps, 16 * rh + l16, 4 * s + g), kop,
+                                                            acc[rh], 0, 0, 0);
+      }
+      const int tk = 16 * wv + l16;
+      const bool tok_ok = tok0 + tk < a.L;
+#pragma unroll
+      for (int rh = 0; rh < 2; ++rh) {
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int sl = 16 * rh + 4 * g + e;
+          v[e] = (tok_ok && ((a.slot_mask >> sl) & 1u)) ? phi_elu1_p(acc[rh][e]) : 0.f;
         }
+        *reinterpret_cast<f32x4*>(F + tk * FS + 16 * rh + 4 * g) = v;
       }
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();  // tile `cur` is in; last tile's readers are done
-    if (tl + 1 < t_end) ld.issue(nxt, tok0 + 64, lane, wv);
-
+    // exact float64 sums of K rows 16 wv .. 16 wv + 15 (rows past L were
+    // loaded as zeros)
     double ks[CH];
 #pragma unroll
     for (int c = 0; c < CH; ++c) ks[c] = 0.0;
-    const int c0 = lane * CH;
-    if (wv < 2) {
-      // low-rank features of 32 tokens per wave
-      f32x16 acc = {};
+    if (pool_k) {
+      const uint16_t* rows = tile + 16 * wv * D;
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s)
-        acc = mfma32(as_bf16x8(P[s]), lds_k_chunk<D>(cur, 32 * wv + l32, 2 * s + hf), acc);
-      const bool tok_ok = tok0 + 32 * wv + l32 < a.L;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int ri = 8 * (r >> 2) + 4 * hf + (r & 3);
-        F[(32 * wv + l32) * 33 + ri] = (ri < a.rank && tok_ok) ? phi_elu1_p(acc[r]) : 0.f;
-      }
-    } else if (pool_k) {
-      // exact float64 block sums of K: wave 2 rows 0..31, wave 3 rows 32..63,
-      // CH channels per lane (rows past L were loaded as zeros)
-#pragma unroll 8
-      for (int t = 32 * (wv - 2); t < 32 * (wv - 1); ++t) {
-        const uint16_t* src = cur + t * D + (((c0 >> 3) ^ k_swz<D>(t)) << 3) + (c0 & 7);
+      for (int t = 0; t < 16; ++t) {
         if constexpr (CH == 2) {
-          const uint32_t w = *reinterpret_cast<const uint32_t*>(src);
+          const uint32_t w = *reinterpret_cast<const uint32_t*>(rows + koff[t]);
           ks[0] += (double)bf16_lo(w);
           ks[1] += (double)bf16_hi(w);
         } else {
-          ks[0] += (double)bf16_bits_to_f32(*src);
+          ks[0] += (double)bf16_bits_to_f32(rows[koff[t]]);
         }
       }
-      if (wv == 3) {
+      if (wv > 0) {
 #pragma unroll
-        for (int c = 0; c < CH; ++c) kred[c0 + c] = ks[c];
+        for (int c = 0; c < CH; ++c) kred[wv - 1][c0 + c] = ks[c];
       }
     }
     __syncthreads();
-    if (pool_k && wv == 2) {
-      const int kb_tok = min(64, a.L - tok0);
+    // rank-truncated RoPE on slots 8 wv .. +7 of token `lane`, then the hi/lo
+    // split into the feature operands (K half of the tile: K is dead now)
+    {
+      float f[8];
+      const f32x4 f0 = *reinterpret_cast<const f32x4*>(F + lane * FS + 8 * wv);
+      const f32x4 f1 = *reinterpret_cast<const f32x4*>(F + lane * FS + 8 * wv + 4);
 #pragma unroll
-      for (int c = 0; c < CH; ++c) a.kmean[(bh * a.Nk + tl) * D + c0 + c] = (ks[c] + kred[c0 + c]) / kb_tok;
-    }
-    // rank-truncated RoPE on the feature patch: lane = token, pairs split over waves
-    if (rtok < a.L) {
+      for (int e = 0; e < 4; ++e) {
+        f[e] = f0[e];
+        f[4 + e] = f1[e];
+      }
 #pragma unroll
-      for (int j = 0; j < kMaxPW; ++j) {
-        const int m = wv + NW * j;
-        if (m < a.rope.n) {
-          float* f = F + lane * 33 + a.rope.dim[m];
-          const float u = f[0], v = f[1];
-          f[0] = u * cs[j].x - v * cs[j].y;
-          f[1] = u * cs[j].y + v * cs[j].x;
+      for (int j = 0; j < 4; ++j) {
+        if (a.slot_pair[4 * wv + j] >= 0) {
+          const float u = f[2 * j], v = f[2 * j + 1];
+          f[2 * j] = u * cs[j].x - v * cs[j].y;
+          f[2 * j + 1] = u * cs[j].y + v * cs[j].x;
         }
+      }
+      uint16_t* Fh = tile;
+      uint16_t* Fl = tile + 32 * 64;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const __bf16 hi = (__bf16)f[e];
+        const __bf16 lo = (__bf16)(f[e] - (float)hi);
+        const int ix = fop_index(8 * wv + e, lane);
+        Fh[ix] = __builtin_bit_cast(uint16_t, hi);
+        Fl[ix] = __builtin_bit_cast(uint16_t, lo);
       }
     }
     __syncthreads();
-    // C^T[d][r] += sum over the tile's tokens of V[tok][d] k~[tok][r]
+    // C^T[d][slot] += sum over the tile's tokens of V[tok][d] k~[tok][slot]
     if (wv < D / 32) {
-      const uint16_t* Vs = cur + 64 * D;
+      const uint16_t* Vs = tile + 64 * D;
+      const uint16_t* Fh = tile;
+      const uint16_t* Fl = tile + 32 * 64;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        // token order of the transposing V read: 16s + 4hf + {0..3}, 16s + 8 + 4hf + {0..3}
-        float f8[8];
-#pragma unroll
-        for (int p = 0; p < 8; ++p) f8[p] = F[(16 * s + 8 * (p >> 2) + 4 * hf + (p & 3)) * 33 + l32];
-        bf16x8 fhi, flo;
-        split_bf16x8(f8, fhi, flo);
+        const int off = l32 * 64 + (((2 * s + hf) ^ ((l32 >> 1) & 7)) << 3);
+        const bf16x8 fhi = as_bf16x8(*reinterpret_cast<const u32x4*>(Fh + off));
+        const bf16x8 flo = as_bf16x8(*reinterpret_cast<const u32x4*>(Fl + off));
         const bf16x8 vop = lds_v_operand<D>(Vs, lane, wv, 16 * s);
         cacc = mfma32(vop, fhi, cacc);
         cacc = mfma32(vop, flo, cacc);
       }
     }
-  }
-  // partial C of this chunk: lane holds r = l32, channels 32*wv + 8*(r/4) + 4*hf + r%4
+    // the next tile's RoPE factors, then this tile's key-block means (kred
+    // is rewritten only after the next step's first two barriers)
+    load_cs(cs, tok0 + 64);
+    if (pool_k && wv == 0) {
+      // (a full block divides by 64 exactly as a multiplication)
+      const int kb_tok = min(64, a.L - tok0);
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        const double sum = ((ks[c] + kred[0][c0 + c]) + kred[1][c0 + c]) + kred[2][c0 + c];
+        a.kmean[(bh * a.Nk + tl) * D + c0 + c] = kb_tok == 64 ? sum * 0.015625 : sum / kb_tok;
+      }
+    }
+  };
+
+  float2 cs[4];
+  load_cs(cs, t_begin * 64);
+  RegTile<D> rt;
+  rt.load(kr, vr, kstr, vstr, t_begin * 64, tid);
+  for (int tl = t_begin; tl < t_end; ++tl) step(rt, tl, cs);
+  // partial C of this run in slot order: lane holds slot l32, channels
+  // 32 wv + 8 (r / 4) + 4 hf + r % 4
   if (wv < D / 32) {
     float* out = a.partial + ((int64_t)bh * a.n_chunks + chunk) * 32 * D;
 #pragma unroll

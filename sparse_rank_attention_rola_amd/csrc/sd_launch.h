@@ -62,6 +62,7 @@ struct PrepareArgs {
   const uint16_t* V;
   int64_t sq_b, sq_l, sq_h, sk_b, sk_l, sk_h, sv_b, sv_l, sv_h;
   int B, H, L, Nq, Nk, block_q, Hg, Wg;
+  float rcp_hw, rcp_wg;  // 1 / (Hg * Wg) and 1 / Wg rounded to float
   int chunk_tiles;  // 64-token tiles per workgroup (a multiple of block_q / 64)
   int n_chunks;
   const uint16_t* Pk;
@@ -69,6 +70,11 @@ struct PrepareArgs {
   int rank;
   const float2* rope_tab;
   RopeArgs rope;
+  // rank slots of the stream pass: slot i holds rank slot_rank[i] (-1:
+  // empty); slots 2p, 2p+1 form RoPE pair slot_pair[p] (-1: not rotated)
+  int8_t slot_rank[32];
+  int8_t slot_pair[16];
+  uint32_t slot_mask;  // bit i set where slot_rank[i] >= 0
   double* kmean;   // [B*H, Nk, D] or null
   float* partial;  // [B*H, n_chunks, 32, D]
 };
@@ -99,8 +105,13 @@ struct RopeThetas {
 };
 hipError_t launch_rope_table(const RopeThetas& th, int n, int max_ext, float2* tab, hipStream_t stream);
 hipError_t launch_lowrank_kv(const LowrankKvArgs& a, int D, hipStream_t stream);
-hipError_t launch_lowrank_finalize(const float* partial, int BH, int n_chunks, int rank, int D, float* C_out,
-                                   uint16_t* Ct_hi, uint16_t* Ct_lo, hipStream_t stream);
+// Row of the partial states that holds each rank (-1: none, the rank's
+// state is zero).
+struct RankRows {
+  int8_t row[32];
+};
+hipError_t launch_lowrank_finalize(const float* partial, int BH, int n_chunks, int rank, int D, const RankRows& rows,
+                                   float* C_out, uint16_t* Ct_hi, uint16_t* Ct_lo, hipStream_t stream);
 hipError_t launch_prepare_stream(const PrepareArgs& a, int D, hipStream_t stream);
 hipError_t launch_gate_fuse(const void* Os, const void* Olr, int in_f32, const float* g, int64_t g_sb, int64_t g_sl,
                             int64_t g_sh, void* O, int B, int L, int H, int D, int64_t so_b, int64_t so_l,
