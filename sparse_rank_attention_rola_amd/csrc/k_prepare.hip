@@ -10,18 +10,17 @@
 //   * each thread prefetches its share of the next tile's K and V rows into
 //     registers (buffer loads) and writes them into the LDS tile when the
 //     tile's turn comes;
-//   * each wave projects 16 tokens onto the rank dims with P_k on MFMA and
-//     applies phi into a float patch F, and sums 16 of the tile's K rows in
-//     float64 (exact for bf16 values) for the key-block means;
-//   * thread (token, wave w) rotates the RoPE pairs of rank slots
-//     8w .. 8w+7, splits the features into bf16 hi + lo parts once, and
-//     stores them as MFMA operands (in the K half of the tile, dead by then);
+//   * each wave projects 16 tokens onto the rank dims with P_k on MFMA,
+//     applies phi, rotates the RoPE pairs in registers, splits the features
+//     into bf16 hi + lo parts once and stores them as MFMA operands; it also
+//     sums 16 of the tile's K rows in float64 (exact for bf16 values) for
+//     the key-block means;
 //   * each wave owns 32 channels of C^T and accumulates V^T k~ on MFMA (V^T
 //     operands from transposing LDS reads).
 // The rank dims are held in slot order: every RoPE pair occupies two
-// adjacent slots starting at an even slot, so a pair never straddles two
-// threads' 8-slot groups; the partial states are written in slot order and
-// the finalising sum maps slots back to ranks.
+// adjacent slots starting at an even slot, so both features of a pair land
+// in one lane of the projection's output; the partial states are written in
+// slot order and the finalising sum maps slots back to ranks.
 // K and V are each read from HBM once. (The query-block means come from the
 // pooling kernel, which streams Q once.)
 #include "sd_device.h"
@@ -99,13 +98,11 @@ __device__ __forceinline__ int fop_index(int j, int t) {
 
 template <int D>
 __global__ __launch_bounds__(256, 3) void prepare_stream_kernel(PrepareArgs a) {
-  constexpr int NW = 4;
   constexpr int CH = D / 64;
-  constexpr int FS = 36;  // F row stride (floats): 16-byte aligned rows, conflict-free b128 access
-  static_assert(2 * 32 * 64 <= 64 * D, "feature operands must fit in the K half of the tile");
+  constexpr int kFop = 32 * 64;  // elements of one feature operand array
   __shared__ __attribute__((aligned(16))) uint16_t tile[TileSmem<D>::kElems];
-  __shared__ __attribute__((aligned(16))) float F[64 * FS];
-  __shared__ double kred[3][D];
+  __shared__ __attribute__((aligned(16))) uint16_t Fop[2 * kFop];  // feature operands: hi, then lo
+  __shared__ double kred[3 * D];                                  // block-sum partials of waves 1..3
   __shared__ __attribute__((aligned(16))) uint16_t Ps[32 * D];
 
   // All heads of a run of tokens run side by side, so that together the
@@ -150,26 +147,39 @@ __global__ __launch_bounds__(256, 3) void prepare_stream_kernel(PrepareArgs a) {
   f32x16 cacc = {};
 
   // K block sums: wave wv sums rows 16 wv .. +15, lane = CH adjacent
-  // channels; LDS offsets of the lane's channels in rows 0..15 (the K
-  // swizzle of row 16 wv + t depends on t only)
+  // channels (the K swizzle of row 16 wv + t depends on t only)
   const int c0 = lane * CH;
-  int koff[16];
-#pragma unroll
-  for (int t = 0; t < 16; ++t) koff[t] = t * D + (((c0 >> 3) ^ k_swz<D>(t)) << 3) + (c0 & 7);
 
-  // cos/sin at this lane's token of the tile at tok0 for the RoPE pairs of
-  // slot pairs 4 wv + j (slot pairs without a RoPE pair load row 0, unused)
+  // Projection layout (16x16x32 MFMA): lane (token 16 wv + l16, group g)
+  // holds slots 16 rh + 4 g + {0..3}, i.e. slot pairs 8 rh + 2 g + q. Per
+  // lane, the RoPE table row and axis of those 4 slot pairs (j = 2 rh + q);
+  // slot pairs without a RoPE pair rotate by the identity.
+  const int l16 = lane & 15, g = lane >> 4;
+  int cs_row[4], cs_axis[4];
+  bool cs_on[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int p = 8 * (j >> 1) + 2 * g + (j & 1);
+    int m = -1;
+#pragma unroll
+    for (int pp = 0; pp < 16; ++pp) m = pp == p ? a.slot_pair[pp] : m;
+    cs_on[j] = m >= 0;
+    m = max(m, 0);
+    int ax = 0;
+#pragma unroll
+    for (int mm = 0; mm < kMaxRopePairs; ++mm) ax = mm == m ? a.rope.axis[mm] : ax;
+    cs_row[j] = m * a.rope.max_ext;
+    cs_axis[j] = ax;
+  }
+  // cos/sin of those pairs at this lane's token of the tile at tok0
   auto load_cs = [&](float2(&cs)[4], int tok0) __attribute__((always_inline)) {
-    const int tc = min(tok0 + lane, a.L - 1);
+    const int tc = min(tok0 + 16 * wv + l16, a.L - 1);
     int pos[3], rest;
     pos[0] = div_small(tc, hw, a.rcp_hw, rest);
     pos[1] = div_small(rest, a.Wg, a.rcp_wg, pos[2]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int m = max((int)a.slot_pair[4 * wv + j], 0);
-      const int axis = a.rope.axis[m];
-      cs[j] = a.rope_tab[m * a.rope.max_ext + (axis == 0 ? pos[0] : axis == 1 ? pos[1] : pos[2])];
-    }
+    for (int j = 0; j < 4; ++j)
+      cs[j] = a.rope_tab[cs_row[j] + (cs_axis[j] == 0 ? pos[0] : cs_axis[j] == 1 ? pos[1] : pos[2])];
   };
 
   // One 64-token tile. Vector-memory operations complete in issue order, so
@@ -186,11 +196,30 @@ __global__ __launch_bounds__(256, 3) void prepare_stream_kernel(PrepareArgs a) {
     rt.load(more ? kr : kr0, more ? vr : vr0, kstr, vstr, (tl + 1) * 64, tid);
     __syncthreads();
 
+    // exact float64 sums of K rows 16 wv .. 16 wv + 15 (rows past L were
+    // loaded as zeros)
+    double ks[CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) ks[c] = 0.0;
+    if (pool_k) {
+      const uint16_t* rows = tile + 16 * wv * D;
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        if constexpr (CH == 2) {
+          const uint32_t w =
+              *reinterpret_cast<const uint32_t*>(rows + t * D + (((c0 >> 3) ^ k_swz<D>(t)) << 3) + (c0 & 7));
+          ks[0] += (double)bf16_lo(w);
+          ks[1] += (double)bf16_hi(w);
+        } else {
+          ks[0] += (double)bf16_bits_to_f32(rows[t * D + (((c0 >> 3) ^ k_swz<D>(t)) << 3) + (c0 & 7)]);
+        }
+      }
+    }
     {
-      // phi(P_k k) of tokens 16 wv .. +15 on 16x16x32 MFMAs, both 16-slot
-      // halves; lane (token l16, group g = lane / 16) holds slots
-      // 16 rh + 4 g + {0..3}; empty slots and tokens past L are zero
-      const int l16 = lane & 15, g = lane >> 4;
+      // k~ of tokens 16 wv .. +15: phi(P_k k) on 16x16x32 MFMAs (both
+      // 16-slot halves), the RoPE pairs rotated in registers (a pair sits in
+      // one lane), split into bf16 hi + lo once and stored as the operands of
+      // the C^T update; empty slots and tokens past L are zero
       f32x4 acc[2] = {};
 #pragma unroll
       for (int s = 0; s < D / 32; ++s) {
@@ -202,76 +231,51 @@ __global__ __launch_bounds__(256, 3) void prepare_stream_kernel(PrepareArgs a) {
       }
       const int tk = 16 * wv + l16;
       const bool tok_ok = tok0 + tk < a.L;
+      uint16_t fh[8], fl[8];
 #pragma unroll
       for (int rh = 0; rh < 2; ++rh) {
-        f32x4 v;
+        float f[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int sl = 16 * rh + 4 * g + e;
-          v[e] = (tok_ok && ((a.slot_mask >> sl) & 1u)) ? phi_elu1_p(acc[rh][e]) : 0.f;
+          f[e] = (tok_ok && ((a.slot_mask >> sl) & 1u)) ? phi_elu1_p(acc[rh][e]) : 0.f;
         }
-        *reinterpret_cast<f32x4*>(F + tk * FS + 16 * rh + 4 * g) = v;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int j = 2 * rh + q;
+          if (cs_on[j]) {
+            const float u = f[2 * q], v = f[2 * q + 1];
+            f[2 * q] = u * cs[j].x - v * cs[j].y;
+            f[2 * q + 1] = u * cs[j].y + v * cs[j].x;
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const __bf16 hi = (__bf16)f[e];
+          const __bf16 lo = (__bf16)(f[e] - (float)hi);
+          fh[4 * rh + e] = __builtin_bit_cast(uint16_t, hi);
+          fl[4 * rh + e] = __builtin_bit_cast(uint16_t, lo);
+        }
       }
+#pragma unroll
+      for (int rh = 0; rh < 2; ++rh)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int ix = fop_index(16 * rh + 4 * g + e, tk);
+          Fop[ix] = fh[4 * rh + e];
+          Fop[kFop + ix] = fl[4 * rh + e];
+        }
     }
-    // exact float64 sums of K rows 16 wv .. 16 wv + 15 (rows past L were
-    // loaded as zeros)
-    double ks[CH];
+    if (pool_k && wv > 0) {
 #pragma unroll
-    for (int c = 0; c < CH; ++c) ks[c] = 0.0;
-    if (pool_k) {
-      const uint16_t* rows = tile + 16 * wv * D;
-#pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        if constexpr (CH == 2) {
-          const uint32_t w = *reinterpret_cast<const uint32_t*>(rows + koff[t]);
-          ks[0] += (double)bf16_lo(w);
-          ks[1] += (double)bf16_hi(w);
-        } else {
-          ks[0] += (double)bf16_bits_to_f32(rows[koff[t]]);
-        }
-      }
-      if (wv > 0) {
-#pragma unroll
-        for (int c = 0; c < CH; ++c) kred[wv - 1][c0 + c] = ks[c];
-      }
-    }
-    __syncthreads();
-    // rank-truncated RoPE on slots 8 wv .. +7 of token `lane`, then the hi/lo
-    // split into the feature operands (K half of the tile: K is dead now)
-    {
-      float f[8];
-      const f32x4 f0 = *reinterpret_cast<const f32x4*>(F + lane * FS + 8 * wv);
-      const f32x4 f1 = *reinterpret_cast<const f32x4*>(F + lane * FS + 8 * wv + 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        f[e] = f0[e];
-        f[4 + e] = f1[e];
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (a.slot_pair[4 * wv + j] >= 0) {
-          const float u = f[2 * j], v = f[2 * j + 1];
-          f[2 * j] = u * cs[j].x - v * cs[j].y;
-          f[2 * j + 1] = u * cs[j].y + v * cs[j].x;
-        }
-      }
-      uint16_t* Fh = tile;
-      uint16_t* Fl = tile + 32 * 64;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const __bf16 hi = (__bf16)f[e];
-        const __bf16 lo = (__bf16)(f[e] - (float)hi);
-        const int ix = fop_index(8 * wv + e, lane);
-        Fh[ix] = __builtin_bit_cast(uint16_t, hi);
-        Fl[ix] = __builtin_bit_cast(uint16_t, lo);
-      }
+      for (int c = 0; c < CH; ++c) kred[(wv - 1) * D + c0 + c] = ks[c];
     }
     __syncthreads();
     // C^T[d][slot] += sum over the tile's tokens of V[tok][d] k~[tok][slot]
     if (wv < D / 32) {
       const uint16_t* Vs = tile + 64 * D;
-      const uint16_t* Fh = tile;
-      const uint16_t* Fl = tile + 32 * 64;
+      const uint16_t* Fh = Fop;
+      const uint16_t* Fl = Fop + kFop;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const int off = l32 * 64 + (((2 * s + hf) ^ ((l32 >> 1) & 7)) << 3);
@@ -283,14 +287,14 @@ __global__ __launch_bounds__(256, 3) void prepare_stream_kernel(PrepareArgs a) {
       }
     }
     // the next tile's RoPE factors, then this tile's key-block means (kred
-    // is rewritten only after the next step's first two barriers)
+    // is rewritten only after the next step's two barriers)
     load_cs(cs, tok0 + 64);
     if (pool_k && wv == 0) {
       // (a full block divides by 64 exactly as a multiplication)
       const int kb_tok = min(64, a.L - tok0);
 #pragma unroll
       for (int c = 0; c < CH; ++c) {
-        const double sum = ((ks[c] + kred[0][c0 + c]) + kred[1][c0 + c]) + kred[2][c0 + c];
+        const double sum = ((ks[c] + kred[c0 + c]) + kred[D + c0 + c]) + kred[2 * D + c0 + c];
         a.kmean[(bh * a.Nk + tl) * D + c0 + c] = kb_tok == 64 ? sum * 0.015625 : sum / kb_tok;
       }
     }
