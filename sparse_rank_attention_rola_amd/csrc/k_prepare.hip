@@ -29,6 +29,8 @@
 
 namespace sd {
 
+typedef double f64x2 __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ float phi_elu1_p(float x) { return x > 0.f ? x + 1.f : __expf(x); }
 
 // x / d and x % d for 0 <= x < 2^24, d >= 1, with rcp = 1/d rounded to
@@ -96,13 +98,13 @@ __device__ __forceinline__ int fop_index(int j, int t) {
   return j * 64 + ((c ^ ((j >> 1) & 7)) << 3) + e;
 }
 
-template <int D>
+template <int D, bool POOL>
 __global__ __launch_bounds__(256, 3) void prepare_stream_kernel(PrepareArgs a) {
   constexpr int CH = D / 64;
   constexpr int kFop = 32 * 64;  // elements of one feature operand array
   __shared__ __attribute__((aligned(16))) uint16_t tile[TileSmem<D>::kElems];
   __shared__ __attribute__((aligned(16))) uint16_t Fop[2 * kFop];  // feature operands: hi, then lo
-  __shared__ double kred[3 * D];                                  // block-sum partials of waves 1..3
+  __shared__ double kred[4 * D];                                  // block-sum partials of the 4 waves
   __shared__ __attribute__((aligned(16))) uint16_t Ps[32 * D];
 
   // All heads of a run of tokens run side by side, so that together the
@@ -121,9 +123,9 @@ __global__ __launch_bounds__(256, 3) void prepare_stream_kernel(PrepareArgs a) {
 
   const uint16_t* Knb = a.Kn + (int64_t)b * a.sk_b + (int64_t)h * a.sk_h;
   const uint16_t* Vb = a.V + (int64_t)b * a.sv_b + (int64_t)h * a.sv_h;
-  // the K tile is summed for the block means too; when the low-rank branch
-  // reads a separate Kn, the means come from the pooling kernel instead
-  const bool pool_k = a.kmean != nullptr;
+  // POOL: the K tile is summed for the block means too (when the low-rank
+  // branch reads a separate Kn, the means come from the pooling kernel)
+  constexpr bool pool_k = POOL;
   const unsigned kstr = (unsigned)(a.sk_l * 2), vstr = (unsigned)(a.sv_l * 2);
   // rows past L read as zeros (range-checked buffers); the empty buffers
   // serve loads past the workgroup's run
@@ -182,9 +184,7 @@ __global__ __launch_bounds__(256, 3) void prepare_stream_kernel(PrepareArgs a) {
       cs[j] = a.rope_tab[cs_row[j] + (cs_axis[j] == 0 ? pos[0] : cs_axis[j] == 1 ? pos[1] : pos[2])];
   };
 
-  // One 64-token tile. Vector-memory operations complete in issue order, so
-  // each step issues its global stores after every load that a later wait
-  // needs: a wait never has to cover a store.
+  // One 64-token tile (its key-block partial sums are left in kred).
   auto step = [&](RegTile<D>& rt, int tl, float2(&cs)[4]) __attribute__((always_inline)) {
     const int tok0 = tl * 64;
     __syncthreads();  // the previous tile's readers are done with the tile
@@ -201,7 +201,7 @@ __global__ __launch_bounds__(256, 3) void prepare_stream_kernel(PrepareArgs a) {
     double ks[CH];
 #pragma unroll
     for (int c = 0; c < CH; ++c) ks[c] = 0.0;
-    if (pool_k) {
+    if constexpr (pool_k) {
       const uint16_t* rows = tile + 16 * wv * D;
 #pragma unroll
       for (int t = 0; t < 16; ++t) {
@@ -266,9 +266,9 @@ __global__ __launch_bounds__(256, 3) void prepare_stream_kernel(PrepareArgs a) {
           Fop[kFop + ix] = fl[4 * rh + e];
         }
     }
-    if (pool_k && wv > 0) {
+    if constexpr (pool_k) {
 #pragma unroll
-      for (int c = 0; c < CH; ++c) kred[(wv - 1) * D + c0 + c] = ks[c];
+      for (int c = 0; c < CH; ++c) kred[wv * D + c0 + c] = ks[c];
     }
     __syncthreads();
     // C^T[d][slot] += sum over the tile's tokens of V[tok][d] k~[tok][slot]
@@ -286,25 +286,51 @@ __global__ __launch_bounds__(256, 3) void prepare_stream_kernel(PrepareArgs a) {
         cacc = mfma32(vop, flo, cacc);
       }
     }
-    // the next tile's RoPE factors, then this tile's key-block means (kred
-    // is rewritten only after the next step's two barriers)
+    // the next tile's RoPE factors (kred is rewritten only after the next
+    // step's two barriers)
     load_cs(cs, tok0 + 64);
-    if (pool_k && wv == 0) {
-      // (a full block divides by 64 exactly as a multiplication)
-      const int kb_tok = min(64, a.L - tok0);
-#pragma unroll
-      for (int c = 0; c < CH; ++c) {
-        const double sum = ((ks[c] + kred[c0 + c]) + kred[D + c0 + c]) + kred[2 * D + c0 + c];
-        a.kmean[(bh * a.Nk + tl) * D + c0 + c] = kb_tok == 64 ? sum * 0.015625 : sum / kb_tok;
-      }
-    }
   };
 
-  float2 cs[4];
-  load_cs(cs, t_begin * 64);
+  // The key-block means go out in groups of 4 tiles: wave w finishes the
+  // means of the group's tile w (CH channels per lane, a full block divides
+  // by 64 exactly as a multiplication) and holds them until the group's
+  // last step, then every wave stores its tile's row with one instruction.
   RegTile<D> rt;
   rt.load(kr, vr, kstr, vstr, t_begin * 64, tid);
-  for (int tl = t_begin; tl < t_end; ++tl) step(rt, tl, cs);
+  float2 cs[4];
+  load_cs(cs, t_begin * 64);
+  double km[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) km[c] = 0.0;
+  const int c0k = lane * CH;
+  auto store_means = [&](int tl) __attribute__((always_inline)) {
+    double* dst = a.kmean + (bh * a.Nk + tl) * D + c0k;
+    if constexpr (CH == 2) {
+      *reinterpret_cast<f64x2*>(dst) = f64x2{km[0], km[1]};
+    } else {
+      dst[0] = km[0];
+    }
+  };
+  for (int tl = t_begin; tl < t_end; ++tl) {
+    step(rt, tl, cs);
+    if constexpr (pool_k) {
+      const int pos = (tl - t_begin) & 3;
+      if (pos == wv) {
+        const int kb_tok = min(64, a.L - tl * 64);
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+          const int cc = c0k + c;
+          const double sum = ((kred[cc] + kred[D + cc]) + kred[2 * D + cc]) + kred[3 * D + cc];
+          km[c] = kb_tok == 64 ? sum * 0.015625 : sum / kb_tok;
+        }
+      }
+      if (pos == 3) store_means(tl - 3 + wv);
+    }
+  }
+  if constexpr (pool_k) {
+    const int rem = (t_end - t_begin) & 3;  // tiles of the last, unfinished group
+    if (rem != 0 && wv < rem) store_means(t_end - rem + wv);
+  }
   // partial C of this run in slot order: lane holds slot l32, channels
   // 32 wv + 8 (r / 4) + 4 hf + r % 4
   if (wv < D / 32) {
@@ -315,11 +341,16 @@ __global__ __launch_bounds__(256, 3) void prepare_stream_kernel(PrepareArgs a) {
 }
 
 hipError_t launch_prepare_stream(const PrepareArgs& a, int D, hipStream_t stream) {
-  const int64_t grid = (int64_t)a.n_chunks * a.B * a.H;
-  if (D == 128)
-    hipLaunchKernelGGL(prepare_stream_kernel<128>, dim3((unsigned)grid), dim3(256), 0, stream, a);
+  const dim3 grid((unsigned)((int64_t)a.n_chunks * a.B * a.H));
+  const bool pool = a.kmean != nullptr;
+  if (D == 128 && pool)
+    hipLaunchKernelGGL((prepare_stream_kernel<128, true>), grid, dim3(256), 0, stream, a);
+  else if (D == 128)
+    hipLaunchKernelGGL((prepare_stream_kernel<128, false>), grid, dim3(256), 0, stream, a);
+  else if (D == 64 && pool)
+    hipLaunchKernelGGL((prepare_stream_kernel<64, true>), grid, dim3(256), 0, stream, a);
   else if (D == 64)
-    hipLaunchKernelGGL(prepare_stream_kernel<64>, dim3((unsigned)grid), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((prepare_stream_kernel<64, false>), grid, dim3(256), 0, stream, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
