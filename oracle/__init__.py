@@ -15,7 +15,10 @@ Sources (the page, then the section / equation):
   * kais-engine portability report, section 2.1 (three-stage recipe:
     proj_q/proj_k map head_dim -> rank, gate_proj/gate_bias is a scalar gate);
   * the same write-up, section 2.3, for the W8A8 projection fed by the
-    per-token quantiser (gemm.py).
+    per-token quantiser (gemm.py);
+  * the same write-up, section 2.1 (q_norm reused by the low-rank branch),
+    and the kais-engine report, section 2.1 (fused QKV + RoPE, scalar gate),
+    for the producer steps of the deployment block (block.py).
 
 Where the pages leave a step open, the reading taken is stated in the
 docstring of the function that takes it.
@@ -52,6 +55,12 @@ from .fp8 import (  # noqa: F401
     e4m3_encode,
     quant_fp8_per_token,
     AMAX_FLOOR,
+)
+from .block import (  # noqa: F401
+    rms_norm_rows,
+    qk_norm_rope,
+    gate_gemv,
+    gate_abs_terms,
 )
 from .gemm import (  # noqa: F401
     quant_weight_per_channel,
