@@ -190,6 +190,27 @@ int sd_gemm_fp8_w8a8(const uint8_t* xq, int64_t M, int64_t K, int64_t ldx, const
                      const uint8_t* wq, int64_t N, int64_t ldw, const float* sw, void* y, int64_t ldy,
                      void* stream);
 
+/* ---- (7) q/k producer of the attention block --------------------------------
+ * robotworld.top write-up, section 2.1: the low-rank branch reuses the
+ * normalised q/k from before the backbone attention, which applies its own
+ * 3D RoPE; kais-engine report, section 2.1: fused QKV + RoPE operator.
+ * For every token row x (H*d channels) of q and of k (bf16, rows of B*L
+ * tokens in (b, l) order, row stride ld_in elements, e.g. slices of the
+ * W8A8 QKV projection's output):
+ *   y_c = x_c / sqrt(mean_c' x_c'^2 + eps) * gamma_c      -> Qn, Kn (bf16)
+ *   per head: pairs (dim, dim+1) of y rotated by p_axis * theta -> Q, K
+ * with p = (t, h, w) of token l = (t*Hg + h)*Wg + w. Computation in f32,
+ * each output rounded once to bf16 (nearest even). Outputs are contiguous
+ * [B, L, H, d]. gamma_q / gamma_k: bf16 [H*d], or NULL for ones. rope: host
+ * array of n_rope pairs (e.g. sd_rope_default(d, 10000, ...)); channels in
+ * no pair are copied unrotated.
+ * Needs d in {64, 128}, H*d <= 8192, T*Hg*Wg == L, every pair's dim even
+ * (pairs inside 8-channel groups), ld_in >= H*d and a multiple of 8, all
+ * device buffers 16-byte aligned. Errors leave the outputs unwritten. */
+int sd_qk_norm_rope(int B, int L, int H, int d, int T, int Hg, int Wg, const void* q, const void* k,
+                    int64_t ld_in, const void* gamma_q, const void* gamma_k, float eps, const sd_rope_pair* rope,
+                    int n_rope, void* Q, void* K, void* Qn, void* Kn, void* stream);
+
 /* ---- fused layer -------------------------------------------------------------
  * The whole path of section 2.1 in one call: block map, sparse branch,
  * low-rank branch and gated fusion. O: bf16 [B, L, H, d] at the so_*

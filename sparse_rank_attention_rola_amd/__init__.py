@@ -28,7 +28,7 @@ SD_PHI_ELU1 = 1
 EXPORTED = [
     "sd_keep_count", "sd_rope_default", "sd_block_select_workspace_size", "sd_block_select",
     "sd_sparse_attn", "sd_lowrank_workspace_size", "sd_lowrank_attn", "sd_gate_fuse",
-    "sd_quant_fp8_per_token", "sd_gemm_fp8_w8a8", "sd_rola_workspace_size", "sd_rola_attention", "sd_rola_prepare",
+    "sd_quant_fp8_per_token", "sd_gemm_fp8_w8a8", "sd_qk_norm_rope", "sd_rola_workspace_size", "sd_rola_attention", "sd_rola_prepare",
     "sd_rola_apply", "sd_status_string", "sd_last_error",
 ]
 
@@ -76,6 +76,8 @@ def _declare(lib):
         "sd_gate_fuse": (i32, [S, P, P, i32, P, i64, i64, i64, P, P]),
         "sd_quant_fp8_per_token": (i32, [P, i64, i64, i64, P, i64, P, P]),
         "sd_gemm_fp8_w8a8": (i32, [P, i64, i64, i64, P, P, i64, i64, P, P, i64, P]),
+        "sd_qk_norm_rope": (i32, [i32, i32, i32, i32, i32, i32, i32, P, P, i64, P, P, f32,
+                                  ctypes.POINTER(sd_rope_pair), i32, P, P, P, P, P]),
         "sd_rola_workspace_size": (sz, [S, LR, i32]),
         "sd_rola_attention": (i32, [S, LR, P, P, P, P, P, P, i64, i64, i64, i32, f32, P, P, P, sz, P]),
         "sd_rola_prepare": (i32, [S, LR, P, P, P, P, P, i32, P, P, sz, P]),
@@ -114,8 +116,8 @@ def sd_keep_count(sparsity: float, n_kblocks: int) -> int:
 
 
 def sd_rope_default(rank: int, base: float = 10000.0):
-    buf = (sd_rope_pair * 32)()
-    n = lib().sd_rope_default(int(rank), float(base), buf, 32)
+    buf = (sd_rope_pair * 64)()
+    n = lib().sd_rope_default(int(rank), float(base), buf, 64)
     if n < 0:
         raise SdError(SD_ERR_INVALID_ARG, "bad rope arguments")
     return [(buf[i].dim, buf[i].axis, buf[i].theta) for i in range(n)]
@@ -277,6 +279,34 @@ def sd_gemm_fp8_w8a8(xq, sx, wq, sw, *, out=None, stream=None):
     _check(lib().sd_gemm_fp8_w8a8(_ptr(xq), M, K, xq.stride(0), _ptr(sx), _ptr(wq), N, wq.stride(0), _ptr(sw),
                                   _ptr(out), out.stride(0), _stream_ptr(stream)))
     return out
+
+
+def sd_qk_norm_rope(q, k, *, heads, grid, batch=1, gamma_q=None, gamma_k=None, eps=1e-6, rope=None, stream=None):
+    """q/k producer: RMSNorm of every token row of q and k (bf16 [B*L, H*d]
+    row views, e.g. slices of the QKV projection's output) and the backbone
+    3D RoPE per head. Returns (Q, K, Qn, Kn), bf16 [B, L, H, d]; rope
+    defaults to sd_rope_default(d)."""
+    torch = _torch()
+    rows, C = q.shape
+    if k.shape != q.shape or k.stride() != q.stride():
+        raise ValueError("q and k must be row views of the same shape and strides")
+    if q.stride(1) != 1:
+        raise ValueError("rows of q and k must be contiguous")
+    H = int(heads)
+    if C % H:
+        raise ValueError("H must divide the row length")
+    d = C // H
+    T, Hg, Wg = grid
+    L = rows // batch
+    pairs = rope if rope is not None else sd_rope_default(d)
+    rp = (sd_rope_pair * max(1, len(pairs)))(*[sd_rope_pair(dm, a, t) for dm, a, t in pairs])
+    outs = [torch.empty((batch, L, H, d), dtype=torch.bfloat16, device=q.device) for _ in range(4)]
+    _check(lib().sd_qk_norm_rope(batch, L, H, d, T, Hg, Wg, _ptr(q), _ptr(k), q.stride(0),
+                                 _ptr(gamma_q) if gamma_q is not None else None,
+                                 _ptr(gamma_k) if gamma_k is not None else None, float(eps),
+                                 ctypes.cast(rp, ctypes.POINTER(sd_rope_pair)), len(pairs),
+                                 *[_ptr(o) for o in outs], _stream_ptr(stream)))
+    return tuple(outs)
 
 
 def rola_workspace(Q, lr: LowrankParams, k_keep, *, grid, block_q=128):

@@ -467,6 +467,59 @@ int sd_gemm_fp8_w8a8(const uint8_t* xq, int64_t M, int64_t K, int64_t ldx, const
   return ok();
 }
 
+int sd_qk_norm_rope(int B, int L, int H, int d, int T, int Hg, int Wg, const void* q, const void* k,
+                    int64_t ld_in, const void* gamma_q, const void* gamma_k, float eps, const sd_rope_pair* rope,
+                    int n_rope, void* Q, void* K, void* Qn, void* Kn, void* stream) {
+  if (B < 1 || L < 1 || H < 1) return fail(SD_ERR_INVALID_ARG, "B, L, H must be >= 1");
+  if (d != 64 && d != 128) return fail(SD_ERR_UNSUPPORTED, "d = %d (supported: 64, 128)", d);
+  if ((int64_t)H * d > 8192) return fail(SD_ERR_UNSUPPORTED, "H*d = %d exceeds 8192", H * d);
+  if (T < 1 || Hg < 1 || Wg < 1 || (int64_t)T * Hg * Wg != L)
+    return fail(SD_ERR_INVALID_ARG, "T*Hg*Wg (%d*%d*%d) must equal L = %d", T, Hg, Wg, L);
+  if (ld_in < (int64_t)H * d) return fail(SD_ERR_INVALID_ARG, "ld_in must be >= H*d");
+  if (ld_in % 8) return fail(SD_ERR_ALIGN, "ld_in must be a multiple of 8");
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(SD_ERR_INVALID_ARG, "eps invalid");
+  if (n_rope < 0 || n_rope > d / 2) return fail(SD_ERR_INVALID_ARG, "n_rope = %d out of range", n_rope);
+  if (n_rope > 0 && !rope) return fail(SD_ERR_INVALID_ARG, "rope is NULL");
+  sd::QkNormRopeArgs a{};
+  for (int i = 0; i < sd::kQkMaxPairs; ++i) {
+    a.pair_axis[i] = -1;
+    a.pair_theta[i] = 0.f;
+  }
+  for (int i = 0; i < n_rope; ++i) {
+    const sd_rope_pair& p = rope[i];
+    if (p.dim < 0 || p.dim + 1 >= d || p.dim % 2 || p.axis < 0 || p.axis > 2 || !std::isfinite(p.theta))
+      return fail(SD_ERR_INVALID_ARG, "rope pair %d invalid (dims must be even, inside the head)", i);
+    if (a.pair_axis[p.dim / 2] >= 0) return fail(SD_ERR_INVALID_ARG, "rope pairs overlap at pair %d", i);
+    a.pair_axis[p.dim / 2] = (int8_t)p.axis;
+    a.pair_theta[p.dim / 2] = p.theta;
+  }
+  int rc;
+  if ((rc = check_dev_ptr(q, "q")) || (rc = check_dev_ptr(k, "k")) || (rc = check_dev_ptr(Q, "Q")) ||
+      (rc = check_dev_ptr(K, "K")) || (rc = check_dev_ptr(Qn, "Qn")) || (rc = check_dev_ptr(Kn, "Kn")))
+    return rc;
+  if ((gamma_q && !aligned(gamma_q, 16)) || (gamma_k && !aligned(gamma_k, 16)))
+    return fail(SD_ERR_ALIGN, "gamma must be 16-byte aligned");
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.ld_in = ld_in;
+  a.gamma_q = static_cast<const uint16_t*>(gamma_q);
+  a.gamma_k = static_cast<const uint16_t*>(gamma_k);
+  a.eps = eps;
+  a.B = B;
+  a.L = L;
+  a.H = H;
+  a.d = d;
+  a.Hg = Hg;
+  a.Wg = Wg;
+  a.Q = static_cast<uint16_t*>(Q);
+  a.K = static_cast<uint16_t*>(K);
+  a.Qn = static_cast<uint16_t*>(Qn);
+  a.Kn = static_cast<uint16_t*>(Kn);
+  const hipError_t e = sd::launch_qk_norm_rope(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "q/k norm + rope");
+  return ok();
+}
+
 size_t sd_rola_workspace_size(const sd_attn_shape* shape, const sd_lowrank_params* lr, int k_keep) {
   Geo g;
   if (check_shape(shape, &g, true)) return 0;

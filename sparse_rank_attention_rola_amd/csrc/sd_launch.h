@@ -79,6 +79,27 @@ struct PrepareArgs {
   float* partial;  // [B*H, n_chunks, 32, D]
 };
 
+// Fused q/k RMSNorm + backbone 3D RoPE.
+constexpr int kQkMaxPairs = 64;  // pairs per head (d <= 128)
+struct QkNormRopeArgs {
+  const uint16_t* q;  // [B*L rows][H*d], row stride ld_in elements
+  const uint16_t* k;
+  int64_t ld_in;
+  const uint16_t* gamma_q;  // bf16 [H*d] or null (ones)
+  const uint16_t* gamma_k;
+  float eps;
+  int B, L, H, d, Hg, Wg;
+  // per pair index m = dim / 2 of a head: axis of the pair starting at
+  // dim 2m (-1: the channels are not rotated) and its frequency
+  int8_t pair_axis[kQkMaxPairs];
+  float pair_theta[kQkMaxPairs];
+  uint16_t* Q;  // outputs, bf16 [B, L, H, d] contiguous
+  uint16_t* K;
+  uint16_t* Qn;
+  uint16_t* Kn;
+};
+hipError_t launch_qk_norm_rope(const QkNormRopeArgs& a, hipStream_t stream);
+
 // W8A8 FP8 projection y = diag(sx) (xq wq^T) diag(sw), bf16 out.
 struct GemmFp8Args {
   const uint8_t* xq;  // [M, K], row stride ldx bytes

@@ -187,6 +187,31 @@ def test_gemm_fp8_validation():
 
 
 @host_only
+def test_qk_norm_rope_validation():
+    lib = sd.lib()
+    pairs = sd.sd_rope_default(128)
+    rp = (sd.sd_rope_pair * 64)(*[sd.sd_rope_pair(a, b, c) for a, b, c in pairs])
+    rptr = ctypes.cast(rp, ctypes.POINTER(sd.sd_rope_pair))
+    odd = (sd.sd_rope_pair * 1)(sd.sd_rope_pair(43, 2, 1.0))
+
+    def c(B=1, L=60, H=4, d=128, T=3, Hg=4, Wg=5, q=FAKE, ld=512, eps=1e-6, rope=rptr, n=64, gq=None, Q=FAKE):
+        return lib.sd_qk_norm_rope(B, L, H, d, T, Hg, Wg, q, FAKE, ld, gq, None, eps, rope, n, Q, FAKE, FAKE, FAKE,
+                                   None)
+
+    assert c(d=96) == sd.SD_ERR_UNSUPPORTED
+    assert c(H=80) == sd.SD_ERR_UNSUPPORTED  # H*d > 8192
+    assert c(L=61) == sd.SD_ERR_INVALID_ARG  # T*Hg*Wg != L
+    assert c(ld=256) == sd.SD_ERR_INVALID_ARG  # ld_in < H*d
+    assert c(ld=516) == sd.SD_ERR_ALIGN
+    assert c(eps=-1.0) == sd.SD_ERR_INVALID_ARG
+    assert c(n=65) == sd.SD_ERR_INVALID_ARG
+    assert c(d=64, H=8, rope=ctypes.cast(odd, ctypes.POINTER(sd.sd_rope_pair)), n=1) == sd.SD_ERR_INVALID_ARG
+    assert c(q=None) == sd.SD_ERR_INVALID_ARG
+    assert c(Q=FAKE + 8) == sd.SD_ERR_ALIGN
+    assert c(gq=FAKE + 2) == sd.SD_ERR_ALIGN
+
+
+@host_only
 def test_rola_validation():
     lib = sd.lib()
     s = _shape()

@@ -1,0 +1,112 @@
+"""GPU parity of the q/k producer (sd_qk_norm_rope: RMSNorm of each
+projection row, then the backbone 3D RoPE per head) against the oracle's
+float64 values.
+
+Acceptance per element (derived from the arithmetic): the kernel computes
+in f32 and rounds once to bf16, so it is within one bf16 ulp of the exact
+value, 2^-7 |ref|, once its f32 error is counted (the rounding can land on
+the other neighbour). The f32 error of a rotated channel is dominated by the
+angle p*theta formed in f32 (|p| <= 80: 80 * 2^-24 rad) and by cancellation
+in u cos - v sin, both at most about 2^-18 (|u| + |v|) of the pair's
+unrotated values; the bound takes 2^-16 (|u| + |v|) with margin. For the
+unrotated output the second term is 2^-20 |ref| (the f32 sum of squares
+over at most 8192 channels)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_rank_attention_rola_amd as sd
+from gpu_util import dev_bf16, say
+from workloads import synthetic
+
+pytestmark = pytest.mark.gpu
+
+
+def _f(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def _pair_mag(Xn):
+    # |u| + |v| of the pair each channel belongs to (pairs (2m, 2m+1))
+    a = np.abs(Xn)
+    s = a[..., 0::2] + a[..., 1::2]
+    return np.repeat(s, 2, axis=-1)
+
+
+def _check(name, got, ref, extra):
+    err = np.abs(got - ref)
+    bound = 2.0 ** -7 * np.abs(ref) + extra + 2.0 ** -126
+    worst = float((err / bound).max())
+    say(f"{name}: max |err| {err.max():.3e}, worst err/bound {worst:.3f}")
+    assert np.isfinite(got).all() and worst <= 1.0, name
+
+
+def _run_case(B, T, Hg, Wg, H, d, seed, strided=False, with_gamma=True):
+    L = T * Hg * Wg
+    C = H * d
+    qb = synthetic.gen_qk_rows(B * L, C, seed)
+    kb = synthetic.gen_qk_rows(B * L, C, seed + 1)
+    gq = synthetic.gen_norm_weight(C, seed) if with_gamma else None
+    gk = synthetic.gen_norm_weight(C, seed + 1) if with_gamma else None
+    if strided:  # q and k as slices of one [rows, 3C] projection output
+        buf = np.zeros((B * L, 3 * C), dtype=np.uint16)
+        buf[:, :C], buf[:, C:2 * C] = qb, kb
+        dbuf = dev_bf16(buf)
+        q, k = dbuf[:, :C], dbuf[:, C:2 * C]
+    else:
+        q, k = dev_bf16(qb), dev_bf16(kb)
+    Q, K, Qn, Kn = sd.sd_qk_norm_rope(q, k, heads=H, grid=(T, Hg, Wg), batch=B,
+                                      gamma_q=dev_bf16(gq) if with_gamma else None,
+                                      gamma_k=dev_bf16(gk) if with_gamma else None)
+    torch.cuda.synchronize()
+    pos = oracle.token_positions(T, Hg, Wg)
+    for name, xb, g, outr, outn in (("q", qb, gq, Q, Qn), ("k", kb, gk, K, Kn)):
+        gam = oracle.bf16_bits_to_f64(g) if g is not None else None
+        for b in range(B):
+            X = oracle.bf16_bits_to_f64(xb[b * L:(b + 1) * L])
+            Xn, Xr = oracle.qk_norm_rope(X, H, d, pos, gam, 1e-6)
+            _check(f"{name}n b{b}", _f(outn[b]), Xn, 2.0 ** -20 * np.abs(Xn))
+            _check(f"{name} rope b{b}", _f(outr[b]), Xr, 2.0 ** -16 * _pair_mag(Xn))
+
+
+@pytest.mark.parametrize("B,T,Hg,Wg,H", [(1, 3, 5, 7, 4), (2, 2, 4, 9, 12), (1, 4, 6, 10, 40)])
+def test_qk_norm_rope_small(B, T, Hg, Wg, H):
+    say(f"case B={B} grid={T}x{Hg}x{Wg} H={H}")
+    _run_case(B, T, Hg, Wg, H, 128, seed=B * 100 + H)
+
+
+def test_qk_norm_rope_strided_rows_no_gamma():
+    _run_case(1, 3, 4, 5, 8, 128, seed=9, strided=True, with_gamma=False)
+
+
+def test_qk_norm_rope_720p_sampled_rows():
+    # 75600 tokens x 40 heads x 128: q and k at full size, rows sampled
+    # across the sequence (all heads and channels of each sampled row)
+    T, Hg, Wg, H, d = 21, 45, 80, 40, 128
+    L, C = T * Hg * Wg, H * d
+    qb = synthetic.gen_qk_rows(L, C, 31)
+    kb = synthetic.gen_qk_rows(L, C, 32)
+    gq, gk = synthetic.gen_norm_weight(C, 31), synthetic.gen_norm_weight(C, 32)
+    Q, K, Qn, Kn = sd.sd_qk_norm_rope(dev_bf16(qb), dev_bf16(kb), heads=H, grid=(T, Hg, Wg),
+                                      gamma_q=dev_bf16(gq), gamma_k=dev_bf16(gk))
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(0, L, 997), [L - 1, 3599, 3600, 79, 80]]))
+    pos = oracle.token_positions(T, Hg, Wg)[rows]
+    ridx = torch.from_numpy(rows).cuda()
+    for name, xb, g, outr, outn in (("q", qb, gq, Q, Qn), ("k", kb, gk, K, Kn)):
+        Xn, Xr = oracle.qk_norm_rope(oracle.bf16_bits_to_f64(xb[rows]), H, d, pos, oracle.bf16_bits_to_f64(g))
+        _check(f"{name}n 720p", _f(outn[0][ridx]), Xn, 2.0 ** -20 * np.abs(Xn))
+        _check(f"{name} rope 720p", _f(outr[0][ridx]), Xr, 2.0 ** -16 * _pair_mag(Xn))
+
+
+def test_qk_norm_rope_deterministic():
+    qb = synthetic.gen_qk_rows(2 * 60, 1024, 5)
+    q = dev_bf16(qb)
+    a = sd.sd_qk_norm_rope(q, q, heads=8, grid=(3, 4, 5), batch=2)
+    b = sd.sd_qk_norm_rope(q, q, heads=8, grid=(3, 4, 5), batch=2)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+    # q and k from the same rows give the same outputs
+    assert torch.equal(a[0].view(torch.int16), a[1].view(torch.int16))

@@ -222,3 +222,27 @@ def gen_fp8_codes(M: int, K: int, seed: int = 0):
     rng = np.random.Generator(np.random.PCG64(base))
     scales = np.exp2(rng.uniform(-8.0, -4.0, M)).astype(np.float32)
     return out, scales
+
+
+def gen_qk_rows(M: int, C: int, seed: int = 0) -> np.ndarray:
+    """bf16 bits [M, C]: rows of a q or k projection, N(0, 1) times a per-row
+    scale 2^U(-3, 3) (stream seed + 6000007, rows in runs)."""
+    base = seed + 6_000_007
+    out = np.empty((M, C), dtype=np.uint16)
+    step = max(1, (1 << 22) // C)
+
+    def work(s0):
+        e0 = min(M, s0 + step)
+        rng = _child(base, s0 // step)
+        scale = np.exp2(rng.uniform(-3.0, 3.0, size=(e0 - s0, 1)))
+        out[s0:e0] = f32_to_bf16_bits((rng.standard_normal((e0 - s0, C)) * scale).astype(np.float32))
+
+    with _pool() as ex:
+        list(ex.map(work, range(0, M, step)))
+    return out
+
+
+def gen_norm_weight(C: int, seed: int = 0) -> np.ndarray:
+    """bf16 bits [C]: an RMSNorm weight 1 + 0.1 N(0, 1) (stream seed + 7000003)."""
+    rng = np.random.Generator(np.random.PCG64(seed + 7_000_003))
+    return f32_to_bf16_bits((1.0 + 0.1 * rng.standard_normal(C)).astype(np.float32))
