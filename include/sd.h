@@ -173,6 +173,16 @@ int sd_gate_fuse(const sd_attn_shape* shape, const void* Os, const void* Olr, in
 int sd_quant_fp8_per_token(const void* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
                            int64_t ldq, float* scales, void* stream);
 
+/* The same quantiser with the block's scalar gate computed from the same
+ * row in the same pass (kais-engine report, section 2.1: the gate is
+ * gate_proj(x) + gate_bias, one scalar per token; robotworld.top write-up,
+ * section 2.1: O_i = O_s,i + g_i r_i O_lr,i):
+ *   g[m] = b_gate + sum_k w_gate[k] * x_mk      (f32 accumulation)
+ * w_gate: bf16 [K], 16-byte aligned; g: f32 [M]. Codes and scales as in
+ * sd_quant_fp8_per_token (bit-identical), same requirements. */
+int sd_quant_fp8_gate(const void* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q, int64_t ldq, float* scales,
+                      const void* w_gate, float b_gate, float* g, void* stream);
+
 /* ---- (6) W8A8 FP8 projection ------------------------------------------------
  * robotworld.top write-up, section 2.3: the linear projections run W8A8 in
  * FP8 E4M3, weights with a static scale per output channel, activations with

@@ -28,7 +28,7 @@ SD_PHI_ELU1 = 1
 EXPORTED = [
     "sd_keep_count", "sd_rope_default", "sd_block_select_workspace_size", "sd_block_select",
     "sd_sparse_attn", "sd_lowrank_workspace_size", "sd_lowrank_attn", "sd_gate_fuse",
-    "sd_quant_fp8_per_token", "sd_gemm_fp8_w8a8", "sd_qk_norm_rope", "sd_rola_workspace_size", "sd_rola_attention", "sd_rola_prepare",
+    "sd_quant_fp8_per_token", "sd_quant_fp8_gate", "sd_gemm_fp8_w8a8", "sd_qk_norm_rope", "sd_rola_workspace_size", "sd_rola_attention", "sd_rola_prepare",
     "sd_rola_apply", "sd_status_string", "sd_last_error",
 ]
 
@@ -75,6 +75,7 @@ def _declare(lib):
         "sd_lowrank_attn": (i32, [S, LR, P, P, P, P, i32, P, P, sz, P]),
         "sd_gate_fuse": (i32, [S, P, P, i32, P, i64, i64, i64, P, P]),
         "sd_quant_fp8_per_token": (i32, [P, i64, i64, i64, P, i64, P, P]),
+        "sd_quant_fp8_gate": (i32, [P, i64, i64, i64, P, i64, P, P, f32, P, P]),
         "sd_gemm_fp8_w8a8": (i32, [P, i64, i64, i64, P, P, i64, i64, P, P, i64, P]),
         "sd_qk_norm_rope": (i32, [i32, i32, i32, i32, i32, i32, i32, P, P, i64, P, P, f32,
                                   ctypes.POINTER(sd_rope_pair), i32, P, P, P, P, P]),
@@ -260,6 +261,24 @@ def sd_quant_fp8_per_token(x, *, q=None, scales=None, stream=None):
     _check(lib().sd_quant_fp8_per_token(_ptr(x), M, K, x.stride(0), _ptr(q), q.stride(0), _ptr(scales),
                                         _stream_ptr(stream)))
     return q, scales
+
+
+def sd_quant_fp8_gate(x, w_gate, b_gate, *, q=None, scales=None, g=None, stream=None):
+    """Per-token FP8 quant of x (bf16 [M, K]) plus the scalar gate
+    g = x @ w_gate + b_gate (w_gate bf16 [K]) in one pass: (q, scales, g)."""
+    torch = _torch()
+    M, K = x.shape
+    if x.stride(1) != 1:
+        raise ValueError("rows of x must be contiguous")
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((M,), dtype=torch.float32, device=x.device)
+    if g is None:
+        g = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _check(lib().sd_quant_fp8_gate(_ptr(x), M, K, x.stride(0), _ptr(q), q.stride(0), _ptr(scales), _ptr(w_gate),
+                                   float(b_gate), _ptr(g), _stream_ptr(stream)))
+    return q, scales, g
 
 
 def sd_gemm_fp8_w8a8(xq, sx, wq, sw, *, out=None, stream=None):

@@ -446,6 +446,24 @@ int sd_quant_fp8_per_token(const void* x, int64_t M, int64_t K, int64_t ldx, uin
   return ok();
 }
 
+int sd_quant_fp8_gate(const void* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q, int64_t ldq, float* scales,
+                      const void* w_gate, float b_gate, float* g, void* stream) {
+  if (M < 0 || K < 8) return fail(SD_ERR_INVALID_ARG, "M = %lld, K = %lld", (long long)M, (long long)K);
+  if (K % 8 || ldx % 8 || ldq % 8) return fail(SD_ERR_ALIGN, "K, ldx, ldq must be multiples of 8");
+  if (K > 16384) return fail(SD_ERR_UNSUPPORTED, "K = %lld exceeds 16384", (long long)K);
+  if (ldx < K || ldq < K) return fail(SD_ERR_INVALID_ARG, "ldx and ldq must be >= K");
+  if (!std::isfinite(b_gate)) return fail(SD_ERR_INVALID_ARG, "b_gate must be finite");
+  int rc;
+  if ((rc = check_dev_ptr(x, "x")) || (rc = check_dev_ptr(q, "q", 8)) || (rc = check_dev_ptr(scales, "scales", 4)) ||
+      (rc = check_dev_ptr(w_gate, "w_gate")) || (rc = check_dev_ptr(g, "g", 4)))
+    return rc;
+  const hipError_t e = sd::launch_quant_fp8_gate(static_cast<const uint16_t*>(x), M, K, ldx, q, ldq, scales,
+                                                 static_cast<const uint16_t*>(w_gate), b_gate, g,
+                                                 static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "fp8 quant + gate");
+  return ok();
+}
+
 int sd_gemm_fp8_w8a8(const uint8_t* xq, int64_t M, int64_t K, int64_t ldx, const float* sx, const uint8_t* wq,
                      int64_t N, int64_t ldw, const float* sw, void* y, int64_t ldy, void* stream) {
   if (M < 0 || N < 0 || K <= 0)

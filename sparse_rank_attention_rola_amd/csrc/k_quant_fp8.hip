@@ -19,18 +19,16 @@ namespace sd {
 
 __device__ __forceinline__ float sat448(float v) { return __builtin_amdgcn_fmed3f(v, -448.0f, 448.0f); }
 
-template <int VPL>  // 16-byte vectors per lane (row length <= 512 * VPL)
-__global__ __launch_bounds__(256) void quant_fp8_rows_kernel(const uint16_t* __restrict__ x, int64_t M,
-                                                             int64_t K, int64_t ldx, uint8_t* __restrict__ q,
-                                                             int64_t ldq, float* __restrict__ scales) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= M) return;
-  const int nvec = (int)(K >> 3);
+// One row by one wavefront: codes and scale, and with GATE the dot product
+// of the row with the gate weight (its slice wg held by the lane).
+template <int VPL, bool GATE>
+__device__ __forceinline__ void quant_row(const uint16_t* __restrict__ x, int64_t row, int nvec, int64_t ldx,
+                                          uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ scales,
+                                          const u32x4* wg, float gate_bias, float* __restrict__ g, int lane) {
   const u32x4* src = reinterpret_cast<const u32x4*>(x + row * ldx);
-
   u32x4 v[VPL];
   uint32_t amax_bits = 0;
+  float dot = 0.f;
 #pragma unroll
   for (int j = 0; j < VPL; ++j) {
     const int vi = j * 64 + lane;
@@ -40,11 +38,20 @@ __global__ __launch_bounds__(256) void quant_fp8_rows_kernel(const uint16_t* __r
       for (int w = 0; w < 4; ++w) {
         uint32_t a = v[j][w] & 0x7FFF7FFFu;
         amax_bits = max(amax_bits, max(a & 0xFFFFu, a >> 16));
+        if constexpr (GATE) {
+          dot = fmaf(bf16_lo(v[j][w]), bf16_lo(wg[j][w]), dot);
+          dot = fmaf(bf16_hi(v[j][w]), bf16_hi(wg[j][w]), dot);
+        }
       }
     }
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) amax_bits = max(amax_bits, (uint32_t)__shfl_xor((int)amax_bits, o));
+  if constexpr (GATE) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) dot += __shfl_xor(dot, o);
+    if (lane == 0) g[row] = dot + gate_bias;
+  }
 
   const float amax = fmaxf(bf16_bits_to_f32(amax_bits), 1e-12f);
   const float inv = 448.0f / amax;  // IEEE division (correctly rounded)
@@ -71,6 +78,39 @@ __global__ __launch_bounds__(256) void quant_fp8_rows_kernel(const uint16_t* __r
   }
 }
 
+template <int VPL>  // 16-byte vectors per lane (row length <= 512 * VPL)
+__global__ __launch_bounds__(256) void quant_fp8_rows_kernel(const uint16_t* __restrict__ x, int64_t M,
+                                                             int64_t K, int64_t ldx, uint8_t* __restrict__ q,
+                                                             int64_t ldq, float* __restrict__ scales) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;
+  quant_row<VPL, false>(x, row, (int)(K >> 3), ldx, q, ldq, scales, nullptr, 0.f, nullptr, lane);
+}
+
+// The quantiser with the scalar gate of the block folded in (kais-engine
+// report, section 2.1: g = gate_proj(x) + gate_bias from the same input
+// row): the row is in registers anyway, so the gate costs no extra pass.
+template <int VPL>
+__global__ __launch_bounds__(256) void quant_fp8_gate_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
+                                                             int64_t ldx, uint8_t* __restrict__ q, int64_t ldq,
+                                                             float* __restrict__ scales,
+                                                             const uint16_t* __restrict__ wgate, float gate_bias,
+                                                             float* __restrict__ g) {
+  const int lane = threadIdx.x & 63;
+  const int nvec = (int)(K >> 3);
+  // one row per wave; the weight slice comes from the cache each row
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;
+  u32x4 wg[VPL];
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) {
+    const int vi = j * 64 + lane;
+    wg[j] = vi < nvec ? reinterpret_cast<const u32x4*>(wgate)[vi] : u32x4{0, 0, 0, 0};
+  }
+  quant_row<VPL, true>(x, row, nvec, ldx, q, ldq, scales, wg, gate_bias, g, lane);
+}
+
 hipError_t launch_quant_fp8(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q, int64_t ldq,
                             float* scales, hipStream_t stream) {
   if (M == 0) return hipSuccess;
@@ -92,6 +132,30 @@ hipError_t launch_quant_fp8(const uint16_t* x, int64_t M, int64_t K, int64_t ldx
   SD_QUANT_CASE(24)
   SD_QUANT_CASE(32)
 #undef SD_QUANT_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_quant_fp8_gate(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q, int64_t ldq,
+                                 float* scales, const uint16_t* wgate, float gate_bias, float* g, hipStream_t stream) {
+  if (M == 0) return hipSuccess;
+  const int nvec = (int)(K >> 3);
+  const int vpl = (nvec + 63) / 64;
+  const dim3 grid((unsigned)((M + 3) / 4)), block(256);
+#define SD_QUANT_GATE_CASE(N)                                                                          \
+  if (vpl <= N) {                                                                                      \
+    hipLaunchKernelGGL(quant_fp8_gate_kernel<N>, grid, block, 0, stream, x, M, K, ldx, q, ldq, scales, \
+                       wgate, gate_bias, g);                                                           \
+    return hipGetLastError();                                                                          \
+  }
+  SD_QUANT_GATE_CASE(1)
+  SD_QUANT_GATE_CASE(2)
+  SD_QUANT_GATE_CASE(4)
+  SD_QUANT_GATE_CASE(8)
+  SD_QUANT_GATE_CASE(10)
+  SD_QUANT_GATE_CASE(16)
+  SD_QUANT_GATE_CASE(24)
+  SD_QUANT_GATE_CASE(32)
+#undef SD_QUANT_GATE_CASE
   return hipErrorInvalidValue;
 }
 

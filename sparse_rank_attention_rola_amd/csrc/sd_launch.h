@@ -113,6 +113,8 @@ hipError_t launch_gemm_fp8(const GemmFp8Args& a, hipStream_t stream);
 
 hipError_t launch_quant_fp8(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q, int64_t ldq,
                             float* scales, hipStream_t stream);
+hipError_t launch_quant_fp8_gate(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q, int64_t ldq,
+                                 float* scales, const uint16_t* wgate, float gate_bias, float* g, hipStream_t stream);
 hipError_t launch_pool_blocks(const uint16_t* X, int64_t sb, int64_t sl, int64_t sh, int B, int L, int H, int D,
                               int bs, double* out, hipStream_t stream);
 hipError_t launch_block_scores(const double* qmean, const double* kmean, int BH, int Nq, int Nk, int D, double* S,

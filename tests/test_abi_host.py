@@ -166,6 +166,23 @@ def test_gate_fuse_and_quant_validation():
 
 
 @host_only
+def test_quant_gate_validation():
+    lib = sd.lib()
+
+    def c(M=10, K=128, ldx=128, ldq=128, x=FAKE, w=FAKE, g=FAKE, b=0.05):
+        return lib.sd_quant_fp8_gate(x, M, K, ldx, FAKE, ldq, FAKE, w, b, g, None)
+
+    assert c(K=4) == sd.SD_ERR_INVALID_ARG
+    assert c(K=132, ldx=136, ldq=136) == sd.SD_ERR_ALIGN
+    assert c(K=32768, ldx=32768, ldq=32768) == sd.SD_ERR_UNSUPPORTED
+    assert c(ldx=64) == sd.SD_ERR_INVALID_ARG
+    assert c(b=float("nan")) == sd.SD_ERR_INVALID_ARG
+    assert c(w=None) == sd.SD_ERR_INVALID_ARG
+    assert c(w=FAKE + 2) == sd.SD_ERR_ALIGN
+    assert c(g=FAKE + 2) == sd.SD_ERR_ALIGN
+
+
+@host_only
 def test_gemm_fp8_validation():
     lib = sd.lib()
 

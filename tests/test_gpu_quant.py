@@ -104,3 +104,51 @@ def test_quant_480p_activation_sampled_rows():
     xf = oracle.bf16_bits_to_f64(x[rows])
     arg = np.abs(xf).argmax(axis=1)
     assert ((q[rows][np.arange(len(rows)), arg] & 0x7F) == 0x7E).all()
+
+
+# --- the quantiser with the scalar gate folded in ----------------------------
+# Codes and scales must equal the plain quantiser's bit for bit. The gate is
+# an f32 sum of K products: each lane adds its 8*VPL <= 80 terms in order,
+# then a 6-level tree adds the 64 lane sums and the bias is added once, so
+# |g - ref| <= 88 * 2^-24 * sum |w x| + 2^-24 |ref| (f32 rounding of each
+# step); the test takes 2^-17 sum |w x| + 2^-23 |ref|.
+
+def _gate_bound(xb, wb, ref):
+    absx = oracle.bf16_bits_to_f64(xb)
+    absw = oracle.bf16_bits_to_f64(wb)
+    return 2.0 ** -17 * oracle.gate_abs_terms(absx, absw) + 2.0 ** -23 * np.abs(ref) + 1e-30
+
+
+@pytest.mark.parametrize("M,K", [(1000, 5120), (37, 1024), (5, 136), (64, 16384)])
+def test_quant_gate_matches_quant_and_oracle(M, K):
+    say(f"quant+gate M={M} K={K}")
+    x = synthetic.gen_activation(M, K, seed=M + 3 * K)
+    w = synthetic.gen_gate_weight(K, seed=K)
+    xd = dev_bf16(x)
+    q, s, g = sd.sd_quant_fp8_gate(xd, dev_bf16(w), synthetic.GATE_BIAS)
+    q0, s0 = sd.sd_quant_fp8_per_token(xd)
+    torch.cuda.synchronize()
+    assert torch.equal(q, q0) and torch.equal(s.view(torch.int32), s0.view(torch.int32))
+    ref = oracle.gate_gemv(oracle.bf16_bits_to_f64(x), oracle.bf16_bits_to_f64(w), synthetic.GATE_BIAS)
+    got = g.cpu().numpy().astype(np.float64)
+    err = np.abs(got - ref)
+    worst = float((err / _gate_bound(x, w, ref)).max())
+    say(f"gate: max |err| {err.max():.3e}, worst err/bound {worst:.3f}")
+    assert worst <= 1.0
+
+
+def test_quant_gate_720p_full_rows_sampled():
+    M, K = synthetic.QUANT_720P
+    x = synthetic.gen_activation(M, K, seed=77)
+    w = synthetic.gen_gate_weight(K, seed=77)
+    xd = dev_bf16(x)
+    q, s, g = sd.sd_quant_fp8_gate(xd, dev_bf16(w), synthetic.GATE_BIAS)
+    q0, s0 = sd.sd_quant_fp8_per_token(xd)
+    torch.cuda.synchronize()
+    assert torch.equal(q, q0) and torch.equal(s.view(torch.int32), s0.view(torch.int32))
+    rows = np.unique(np.concatenate([np.arange(0, M, 331), [M - 1]]))
+    ref = oracle.gate_gemv(oracle.bf16_bits_to_f64(x[rows]), oracle.bf16_bits_to_f64(w), synthetic.GATE_BIAS)
+    got = g.cpu().numpy().astype(np.float64)[rows]
+    worst = float((np.abs(got - ref) / _gate_bound(x[rows], w, ref)).max())
+    say(f"gate 720p: worst err/bound {worst:.3f}")
+    assert worst <= 1.0

@@ -246,3 +246,13 @@ def gen_norm_weight(C: int, seed: int = 0) -> np.ndarray:
     """bf16 bits [C]: an RMSNorm weight 1 + 0.1 N(0, 1) (stream seed + 7000003)."""
     rng = np.random.Generator(np.random.PCG64(seed + 7_000_003))
     return f32_to_bf16_bits((1.0 + 0.1 * rng.standard_normal(C)).astype(np.float32))
+
+
+def gen_gate_weight(K: int, seed: int = 0) -> np.ndarray:
+    """bf16 bits [K]: the gate projection weight, N(0, 1e-2 / K) (variance
+    notation, stream seed + 8000009); the bias is 0.05."""
+    rng = np.random.Generator(np.random.PCG64(seed + 8_000_009))
+    return f32_to_bf16_bits((rng.standard_normal(K) * np.sqrt(1e-2 / K)).astype(np.float32))
+
+
+GATE_BIAS = 0.05
