@@ -156,6 +156,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=8, help="whole heads in the oracle sample")
     ap.add_argument("--no-gemm", action="store_true", help="skip the FP8 projection measurement")
+    ap.add_argument("--no-block", action="store_true", help="skip the deployment block measurement")
+    ap.add_argument("--block-timesteps", type=int, default=3, help="timesteps of the deployment block")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter calibration)")
     ap.add_argument("--trace-summary", metavar="DB", help="print a kernel table of a rocprofv3 trace and exit")
@@ -272,7 +274,67 @@ def main():
         gemm = {"shape_MxNxK": [Mg, Ng, Kg], "ms": round(t_g, 4),
                 "tflops": round(gflop / (t_g * 1e-3) / 1e12, 1),
                 "fp8_mfma_peak_frac": round(gflop / (t_g * 1e-3) / 1e12 / MFMA_FP8_PEAK_TFLOPS, 4)}
-        del y, wq, sw
+        del y
+
+    # The whole 720P attention block in deployment precision, the layer
+    # repeated for a few timesteps: x -> FP8 quant with the scalar gate ->
+    # W8A8 QKV -> q/k RMSNorm + 3D RoPE -> RoLA prepare + fused attention
+    # (low-rank branch on the pre-RoPE Qn/Kn) -> FP8 quant -> W8A8 output
+    # projection. Weights quantised once, outside the timed region.
+    block = None
+    if not args.no_block and not args.no_gemm:
+        C = cfg.H * cfg.d
+        log(f"deployment block: {args.block_timesteps} timesteps of the 720P layer")
+        Wo = to_dev(synthetic.gen_weight(C, C, 1))
+        woq, swo = sd.sd_quant_fp8_per_token(Wo)
+        del Wo
+        wgate = to_dev(synthetic.gen_gate_weight(Kc, 0))
+        gam_q, gam_k = to_dev(synthetic.gen_norm_weight(C, 0)), to_dev(synthetic.gen_norm_weight(C, 1))
+        y = torch.empty((M, 3 * C), dtype=torch.bfloat16, device=dev)
+        gts = torch.empty((M,), dtype=torch.float32, device=dev)
+        qkn = [torch.empty((1, cfg.L, cfg.H, cfg.d), dtype=torch.bfloat16, device=dev) for _ in range(4)]
+        V5 = y[:, 2 * C:].unflatten(1, (cfg.H, cfg.d)).unsqueeze(0)
+        Ob = torch.empty((1, cfg.L, cfg.H, cfg.d), dtype=torch.bfloat16, device=dev)
+        ocodes = torch.empty((M, C), dtype=torch.uint8, device=dev)
+        oscales = torch.empty((M,), dtype=torch.float32, device=dev)
+        yout = torch.empty((M, C), dtype=torch.bfloat16, device=dev)
+
+        def block_step(ev=None):
+            if ev: ev[0].record()
+            sd.sd_quant_fp8_gate(X, wgate, synthetic.GATE_BIAS, q=codes, scales=scales, g=gts)
+            if ev: ev[1].record()
+            sd.sd_gemm_fp8_w8a8(codes, scales, wq, sw, out=y)
+            if ev: ev[2].record()
+            Q5, K5, Qn5, Kn5 = sd.sd_qk_norm_rope(y[:, :C], y[:, C:2 * C], heads=cfg.H, grid=grid, gamma_q=gam_q,
+                                                  gamma_k=gam_k, out=qkn)
+            if ev: ev[3].record()
+            sd.sd_rola_prepare(Q5, K5, V5, lr, k, ws, grid=grid, block_q=cfg.block_q, Qn=Qn5, Kn=Kn5, idx_out=idx)
+            if ev: ev[4].record()
+            sd.sd_rola_apply(Q5, K5, V5, gts.view(1, cfg.L), lr, k, ws, grid=grid, block_q=cfg.block_q, Qn=Qn5,
+                             out=Ob, idx=idx)
+            if ev: ev[5].record()
+            sd.sd_quant_fp8_per_token(Ob.view(M, C), q=ocodes, scales=oscales)
+            if ev: ev[6].record()
+            sd.sd_gemm_fp8_w8a8(ocodes, oscales, woq, swo, out=yout)
+            if ev: ev[7].record()
+
+        block_step()
+        torch.cuda.synchronize()
+        bev = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(args.block_timesteps)]
+        for i in range(args.block_timesteps):
+            block_step(bev[i])
+        torch.cuda.synchronize()
+        names = ["fp8 quant + gate", "W8A8 QKV projection", "q/k RMSNorm + 3D RoPE",
+                 "rola prepare (block map + low-rank state)", "rola fused attention", "fp8 quant of O",
+                 "W8A8 output projection"]
+        per = {n: round(float(np.mean([e[j].elapsed_time(e[j + 1]) for e in bev])), 4) for j, n in enumerate(names)}
+        t_step = float(np.mean([e[0].elapsed_time(e[7]) for e in bev]))
+        block = {"workload": "wan2.1-14b-720p attention block, fp8 W8A8 projections, s=%.2f" % cfg.sparsity,
+                 "timesteps": args.block_timesteps, "ms_per_timestep": round(t_step, 4),
+                 "ms_total": round(t_step * args.block_timesteps, 4), "breakdown_ms": per}
+        del y, qkn, Ob, ocodes, oscales, yout, woq, swo
+    if gemm is not None:
+        del wq, sw
 
     if args.calib_copy:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -328,6 +390,7 @@ def main():
                      "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
                      "algorithmic_flops_per_launch": flops},
         "w8a8_qkv_projection": gemm,
+        "deployment_block_720p": block,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

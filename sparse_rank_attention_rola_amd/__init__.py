@@ -300,11 +300,12 @@ def sd_gemm_fp8_w8a8(xq, sx, wq, sw, *, out=None, stream=None):
     return out
 
 
-def sd_qk_norm_rope(q, k, *, heads, grid, batch=1, gamma_q=None, gamma_k=None, eps=1e-6, rope=None, stream=None):
+def sd_qk_norm_rope(q, k, *, heads, grid, batch=1, gamma_q=None, gamma_k=None, eps=1e-6, rope=None, out=None,
+                    stream=None):
     """q/k producer: RMSNorm of every token row of q and k (bf16 [B*L, H*d]
     row views, e.g. slices of the QKV projection's output) and the backbone
-    3D RoPE per head. Returns (Q, K, Qn, Kn), bf16 [B, L, H, d]; rope
-    defaults to sd_rope_default(d)."""
+    3D RoPE per head. Returns (Q, K, Qn, Kn), bf16 [B, L, H, d] contiguous
+    (or the given out tuple); rope defaults to sd_rope_default(d)."""
     torch = _torch()
     rows, C = q.shape
     if k.shape != q.shape or k.stride() != q.stride():
@@ -319,7 +320,12 @@ def sd_qk_norm_rope(q, k, *, heads, grid, batch=1, gamma_q=None, gamma_k=None, e
     L = rows // batch
     pairs = rope if rope is not None else sd_rope_default(d)
     rp = (sd_rope_pair * max(1, len(pairs)))(*[sd_rope_pair(dm, a, t) for dm, a, t in pairs])
-    outs = [torch.empty((batch, L, H, d), dtype=torch.bfloat16, device=q.device) for _ in range(4)]
+    if out is not None:
+        outs = list(out)
+        if any(o.shape != (batch, L, H, d) or not o.is_contiguous() or o.dtype != torch.bfloat16 for o in outs):
+            raise ValueError("out must be four contiguous bf16 [B, L, H, d] tensors")
+    else:
+        outs = [torch.empty((batch, L, H, d), dtype=torch.bfloat16, device=q.device) for _ in range(4)]
     _check(lib().sd_qk_norm_rope(batch, L, H, d, T, Hg, Wg, _ptr(q), _ptr(k), q.stride(0),
                                  _ptr(gamma_q) if gamma_q is not None else None,
                                  _ptr(gamma_k) if gamma_k is not None else None, float(eps),
