@@ -18,7 +18,10 @@ Sources (the page, then the section / equation):
     per-token quantiser (gemm.py);
   * the same write-up, section 2.1 (q_norm reused by the low-rank branch),
     and the kais-engine report, section 2.1 (fused QKV + RoPE, scalar gate),
-    for the producer steps of the deployment block (block.py).
+    for the producer steps of the deployment block (block.py);
+  * the same write-up, section 2.1 (a fixed spatio-temporal pattern as the
+    selector) and section 4 (the causal-window restriction for
+    autoregressive video diffusion), for the variants (variants.py).
 
 Where the pages leave a step open, the reading taken is stated in the
 docstring of the function that takes it.
@@ -61,6 +64,16 @@ from .block import (  # noqa: F401
     qk_norm_rope,
     gate_gemv,
     gate_abs_terms,
+)
+from .variants import (  # noqa: F401
+    block_centroids,
+    fixed_block_scores,
+    causal_window_mask,
+    block_allowed,
+    topk_block_map_allowed,
+    sparse_attention_masked,
+    lowrank_states_masked,
+    rola_attention_head_variant,
 )
 from .gemm import (  # noqa: F401
     quant_weight_per_channel,
