@@ -53,12 +53,38 @@ enum sd_dtype { SD_DTYPE_BF16 = 1, SD_DTYPE_F32 = 2 };
 
 enum sd_phi { SD_PHI_ELU1 = 1 }; /* phi(x) = ELU(x) + 1 */
 
+/* Selector of the sparse branch (robotworld.top write-up, section 2.1: the
+ * kept 1-s of the blocks come from top-k over block-level scores or from a
+ * fixed spatio-temporal pattern). */
+enum sd_select {
+  SD_SELECT_TOPK = 0,  /* top-k of mean(Q block) . mean(K block)            */
+  SD_SELECT_FIXED = 1  /* the k key blocks whose centroids in latent
+                          (t, h, w) units are nearest the query block's
+                          (squared distance -((dt^2 + dh^2) + dw^2), float64
+                          without fused multiply-add; needs the grid)       */
+};
+
 /* Geometry of one attention layer. Supported: d in {64, 128},
  * block_q in {64, 128}, block_k == 64, L <= 131072, B, H >= 1.
- * T, Hg, Wg are needed (T*Hg*Wg == L) only by the low-rank branch and the
- * fused entry; the block map and the sparse branch ignore them.
+ * T, Hg, Wg are needed (T*Hg*Wg == L) only by the low-rank branch, the fused
+ * entry and SD_SELECT_FIXED; the scored block map and the sparse branch
+ * ignore them.
  * s?_b, s?_l, s?_h: element strides of Q, K, V and of every output tensor
- * (so_*) in [B, L, H, d] layout. */
+ * (so_*) in [B, L, H, d] layout.
+ * select: SD_SELECT_TOPK or SD_SELECT_FIXED (used by the block map).
+ * chunk_tokens, window: causal window for autoregressive generation
+ * (robotworld.top write-up, section 4: compensated sparse attention
+ * restricted to a causal window). chunk_tokens = 0: bidirectional (window
+ * must be 0). Otherwise tokens form chunks of chunk_tokens consecutive
+ * tokens (a chunk of f latent frames is f*Hg*Wg tokens; at most 4096
+ * chunks) and a query of chunk c sees exactly the keys of chunks
+ * c-window+1 .. c (window 0: 0 .. c), in both branches: the block map keeps
+ * only key blocks some query of the block sees (rows with fewer than k_keep
+ * such blocks keep them all and are padded with -1), the sparse branch
+ * masks the other keys of a kept block (a query that sees none of the kept
+ * keys gets O_s = 0), and the low-rank state of a chunk sums k~ v^T over
+ * the keys its queries see. Zero-initialised fields give the bidirectional
+ * scored layer. */
 typedef struct sd_attn_shape {
   int32_t B, H, L, d;
   int32_t T, Hg, Wg;
@@ -67,6 +93,9 @@ typedef struct sd_attn_shape {
   int64_t sk_b, sk_l, sk_h;
   int64_t sv_b, sv_l, sv_h;
   int64_t so_b, so_l, so_h;
+  int32_t select;
+  int32_t chunk_tokens;
+  int32_t window;
 } sd_attn_shape;
 
 /* One rotated pair of the rank-truncated 3D RoPE R_r(p): feature dims
@@ -120,7 +149,11 @@ int sd_rope_default(int rank, double base, sd_rope_pair* out, int max_pairs);
  * tokens of (possibly partial) blocks, accumulated and compared in float64.
  * idx: device int32 [B, H, Nq, k_keep], Nq = ceil(L/block_q); each row lists
  * the k_keep highest-scoring key blocks (equal scores: lower index first)
- * in ascending order. 1 <= k_keep <= Nk = ceil(L/block_k). */
+ * in ascending order. 1 <= k_keep <= Nk = ceil(L/block_k).
+ * shape->select = SD_SELECT_FIXED scores by the fixed spatio-temporal
+ * pattern instead (Q and K are not read; every (b, h) gets the same map).
+ * Under a causal window only allowed blocks are candidates and short rows
+ * end in -1 (see sd_attn_shape). */
 size_t sd_block_select_workspace_size(const sd_attn_shape* shape);
 int sd_block_select(const sd_attn_shape* shape, const void* Q, const void* K, int k_keep,
                     int32_t* idx, void* ws, size_t ws_bytes, void* stream);
@@ -141,10 +174,12 @@ int sd_sparse_attn(const sd_attn_shape* shape, const void* Q, const void* K, con
 /* ---- (3) low-rank branch ---------------------------------------------------
  * robotworld.top write-up, section 2.1, the q~/k~ and C/O_lr equations:
  * C[b,h] = sum over all L tokens of k~_j v_j^T (f32 [rank, d]), then
- * O_lr,i = w * y / sqrt(mean(y^2) + eps) with y = q~_i^T C.
+ * O_lr,i = w * y / sqrt(mean(y^2) + eps) with y = q~_i^T C. Under a causal
+ * window every chunk c has its own C (the keys its queries see).
  * Qn, Kn: the normalised q/k the branch reads (strides of Q and K).
  * Olr: [B, L, H, d] at the so_* strides, bf16 or f32 (olr_dtype).
- * C_out: optional device f32 [B, H, rank, d], or NULL. */
+ * C_out: optional device f32 [B, H, n_chunks, rank, d] (n_chunks =
+ * ceil(L / chunk_tokens), 1 without a causal window), or NULL. */
 size_t sd_lowrank_workspace_size(const sd_attn_shape* shape, const sd_lowrank_params* lr);
 int sd_lowrank_attn(const sd_attn_shape* shape, const sd_lowrank_params* lr, const void* Qn,
                     const void* Kn, const void* V, void* Olr, int olr_dtype, float* C_out,

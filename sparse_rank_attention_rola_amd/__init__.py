@@ -24,6 +24,9 @@ SD_ERR_HIP = 5
 SD_DTYPE_BF16 = 1
 SD_DTYPE_F32 = 2
 SD_PHI_ELU1 = 1
+SD_SELECT_TOPK = 0
+SD_SELECT_FIXED = 1
+_SELECT = {"topk": SD_SELECT_TOPK, "fixed": SD_SELECT_FIXED}
 
 EXPORTED = [
     "sd_keep_count", "sd_rope_default", "sd_block_select_workspace_size", "sd_block_select",
@@ -42,7 +45,8 @@ class SdError(RuntimeError):
 class sd_attn_shape(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("B", "H", "L", "d", "T", "Hg", "Wg", "block_q", "block_k")] + \
                [(n, ctypes.c_int64) for n in ("sq_b", "sq_l", "sq_h", "sk_b", "sk_l", "sk_h",
-                                              "sv_b", "sv_l", "sv_h", "so_b", "so_l", "so_h")]
+                                              "sv_b", "sv_l", "sv_h", "so_b", "so_l", "so_h")] + \
+               [(n, ctypes.c_int32) for n in ("select", "chunk_tokens", "window")]
 
 
 class sd_rope_pair(ctypes.Structure):
@@ -139,11 +143,18 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
 
-def make_shape(Q, K, V, out_like=None, *, block_q=128, block_k=64, grid=(0, 0, 0)) -> sd_attn_shape:
-    """sd_attn_shape from [B, L, H, d] tensors (out_like gives the so_* strides)."""
+def make_shape(Q, K, V, out_like=None, *, block_q=128, block_k=64, grid=(0, 0, 0), select="topk", chunk_tokens=0,
+               window=0) -> sd_attn_shape:
+    """sd_attn_shape from [B, L, H, d] tensors (out_like gives the so_* strides).
+
+    select: "topk" (scored) or "fixed" (spatio-temporal pattern); chunk_tokens
+    and window: the causal window (0: bidirectional)."""
     B, L, H, d = Q.shape
     T, Hg, Wg = grid
     s = sd_attn_shape(B, H, L, d, T, Hg, Wg, block_q, block_k)
+    s.select = _SELECT[select]
+    s.chunk_tokens = int(chunk_tokens)
+    s.window = int(window)
     o_strides = out_like.stride() if out_like is not None else (L * H * d, H * d, d, 1)
     for pre, st in (("sq", Q.stride()), ("sk", K.stride()), ("sv", V.stride()), ("so", o_strides)):
         if st[3] != 1:
@@ -177,11 +188,14 @@ def _workspace(nbytes: int, device):
 # entry points (same names as the C ABI)
 # --------------------------------------------------------------------------
 
-def sd_block_select(Q, K, k_keep, *, block_q=128, block_k=64, idx=None, stream=None):
-    """int32 [B, H, Nq, k_keep] block map (ascending rows)."""
+def sd_block_select(Q, K, k_keep, *, block_q=128, block_k=64, idx=None, grid=(0, 0, 0), select="topk",
+                    chunk_tokens=0, window=0, stream=None):
+    """int32 [B, H, Nq, k_keep] block map (ascending rows, -1 padded under a
+    causal window); the fixed pattern needs the latent grid."""
     torch = _torch()
     B, L, H, d = Q.shape
-    s = make_shape(Q, K, K, block_q=block_q, block_k=block_k)
+    s = make_shape(Q, K, K, block_q=block_q, block_k=block_k, grid=grid, select=select, chunk_tokens=chunk_tokens,
+                   window=window)
     nq = -(-L // block_q)
     if idx is None:
         idx = torch.empty((B, H, nq, k_keep), dtype=torch.int32, device=Q.device)
@@ -193,14 +207,14 @@ def sd_block_select(Q, K, k_keep, *, block_q=128, block_k=64, idx=None, stream=N
 
 
 def sd_sparse_attn(Q, K, V, idx, *, block_q=128, block_k=64, sm_scale=None, out_dtype=None, want_rms=True,
-                   out=None, stream=None):
+                   out=None, chunk_tokens=0, window=0, stream=None):
     """(O_s [B, L, H, d], rms [B, L, H] or None)."""
     torch = _torch()
     B, L, H, d = Q.shape
     out_dtype = out_dtype or torch.float32
     if out is None:
         out = torch.empty((B, L, H, d), dtype=out_dtype, device=Q.device)
-    s = make_shape(Q, K, V, out, block_q=block_q, block_k=block_k)
+    s = make_shape(Q, K, V, out, block_q=block_q, block_k=block_k, chunk_tokens=chunk_tokens, window=window)
     rms = torch.empty((B, L, H), dtype=torch.float32, device=Q.device) if want_rms else None
     scale = sm_scale if sm_scale is not None else 1.0 / math.sqrt(d)
     dt = SD_DTYPE_F32 if out.dtype == torch.float32 else SD_DTYPE_BF16
@@ -210,15 +224,17 @@ def sd_sparse_attn(Q, K, V, idx, *, block_q=128, block_k=64, sm_scale=None, out_
 
 
 def sd_lowrank_attn(Qn, Kn, V, lr: LowrankParams, *, grid, block_q=128, out_dtype=None, want_C=True, out=None,
-                    stream=None):
-    """(O_lr [B, L, H, d], C [B, H, rank, d] or None)."""
+                    chunk_tokens=0, window=0, stream=None):
+    """(O_lr [B, L, H, d], C or None): C is [B, H, rank, d], or one state
+    per autoregressive chunk [B, H, n_chunks, rank, d] under a causal window."""
     torch = _torch()
     B, L, H, d = Qn.shape
     out_dtype = out_dtype or torch.float32
     if out is None:
         out = torch.empty((B, L, H, d), dtype=out_dtype, device=Qn.device)
-    s = make_shape(Qn, Kn, V, out, block_q=block_q, grid=grid)
-    C = torch.empty((B, H, lr.p.rank, d), dtype=torch.float32, device=Qn.device) if want_C else None
+    s = make_shape(Qn, Kn, V, out, block_q=block_q, grid=grid, chunk_tokens=chunk_tokens, window=window)
+    c_shape = (B, H, lr.p.rank, d) if chunk_tokens <= 0 else (B, H, -(-L // min(chunk_tokens, L)), lr.p.rank, d)
+    C = torch.empty(c_shape, dtype=torch.float32, device=Qn.device) if want_C else None
     ws = _workspace(lib().sd_lowrank_workspace_size(ctypes.byref(s), ctypes.byref(lr.p)), Qn.device)
     dt = SD_DTYPE_F32 if out.dtype == torch.float32 else SD_DTYPE_BF16
     _check(lib().sd_lowrank_attn(ctypes.byref(s), ctypes.byref(lr.p), _ptr(Qn), _ptr(Kn), _ptr(V), _ptr(out), dt,
@@ -334,14 +350,16 @@ def sd_qk_norm_rope(q, k, *, heads, grid, batch=1, gamma_q=None, gamma_k=None, e
     return tuple(outs)
 
 
-def rola_workspace(Q, lr: LowrankParams, k_keep, *, grid, block_q=128):
-    s = make_shape(Q, Q, Q, block_q=block_q, grid=grid)
+def rola_workspace(Q, lr: LowrankParams, k_keep, *, grid, block_q=128, select="topk", chunk_tokens=0, window=0):
+    s = make_shape(Q, Q, Q, block_q=block_q, grid=grid, select=select, chunk_tokens=chunk_tokens, window=window)
     return _workspace(lib().sd_rola_workspace_size(ctypes.byref(s), ctypes.byref(lr.p), int(k_keep)), Q.device)
 
 
 def sd_rola_attention(Q, K, V, g, lr: LowrankParams, k_keep, *, grid, block_q=128, Qn=None, Kn=None,
-                      sm_scale=None, out=None, idx_out=None, workspace=None, stream=None):
+                      sm_scale=None, out=None, idx_out=None, workspace=None, select="topk", chunk_tokens=0, window=0,
+                      stream=None):
     """Fused layer: bf16 O [B, L, H, d]."""
+    var = dict(select=select, chunk_tokens=chunk_tokens, window=window)
     torch = _torch()
     B, L, H, d = Q.shape
     if out is None:
@@ -350,8 +368,8 @@ def sd_rola_attention(Q, K, V, g, lr: LowrankParams, k_keep, *, grid, block_q=12
         raise ValueError("Qn must have the strides of Q")
     if Kn is not None and Kn.stride() != K.stride():
         raise ValueError("Kn must have the strides of K")
-    s = make_shape(Q, K, V, out, block_q=block_q, grid=grid)
-    ws = workspace if workspace is not None else rola_workspace(Q, lr, k_keep, grid=grid, block_q=block_q)
+    s = make_shape(Q, K, V, out, block_q=block_q, grid=grid, **var)
+    ws = workspace if workspace is not None else rola_workspace(Q, lr, k_keep, grid=grid, block_q=block_q, **var)
     scale = sm_scale if sm_scale is not None else 1.0 / math.sqrt(d)
     gb, gl, gh = _gate_strides(g, B, L, H)
     _check(lib().sd_rola_attention(ctypes.byref(s), ctypes.byref(lr.p), _ptr(Q), _ptr(K), _ptr(V), _ptr(Qn), _ptr(Kn),
@@ -361,21 +379,21 @@ def sd_rola_attention(Q, K, V, g, lr: LowrankParams, k_keep, *, grid, block_q=12
 
 
 def sd_rola_prepare(Q, K, V, lr: LowrankParams, k_keep, workspace, *, grid, block_q=128, Qn=None, Kn=None,
-                    idx_out=None, stream=None):
+                    idx_out=None, select="topk", chunk_tokens=0, window=0, stream=None):
     """Phase 1 of the fused layer: block map and low-rank state."""
-    s = make_shape(Q, K, V, block_q=block_q, grid=grid)
+    s = make_shape(Q, K, V, block_q=block_q, grid=grid, select=select, chunk_tokens=chunk_tokens, window=window)
     _check(lib().sd_rola_prepare(ctypes.byref(s), ctypes.byref(lr.p), _ptr(Q), _ptr(K), _ptr(V), _ptr(Qn), _ptr(Kn),
                                  int(k_keep), _ptr(idx_out), _ptr(workspace), workspace.numel(), _stream_ptr(stream)))
 
 
 def sd_rola_apply(Q, K, V, g, lr: LowrankParams, k_keep, workspace, *, grid, block_q=128, Qn=None, sm_scale=None,
-                  out=None, idx=None, stream=None):
+                  out=None, idx=None, select="topk", chunk_tokens=0, window=0, stream=None):
     """Phase 2 of the fused layer: the fused attention kernel; bf16 O."""
     torch = _torch()
     B, L, H, d = Q.shape
     if out is None:
         out = torch.empty((B, L, H, d), dtype=torch.bfloat16, device=Q.device)
-    s = make_shape(Q, K, V, out, block_q=block_q, grid=grid)
+    s = make_shape(Q, K, V, out, block_q=block_q, grid=grid, select=select, chunk_tokens=chunk_tokens, window=window)
     scale = sm_scale if sm_scale is not None else 1.0 / math.sqrt(d)
     gb, gl, gh = _gate_strides(g, B, L, H)
     _check(lib().sd_rola_apply(ctypes.byref(s), ctypes.byref(lr.p), _ptr(Q), _ptr(K), _ptr(V), _ptr(Qn), _ptr(g), gb,

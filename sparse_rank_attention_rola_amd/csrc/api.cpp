@@ -41,8 +41,12 @@ constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+constexpr int kMaxArChunks = 4096;
+
 struct Geo {
   int B, H, L, D, bq, bk, Nq, Nk;
+  int select;  // SD_SELECT_*
+  int ar, win, n_ar;  // causal window: tokens per chunk (L: none), window, chunks
 };
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -55,6 +59,14 @@ int check_shape(const sd_attn_shape* s, Geo* g, bool need_grid) {
     return fail(SD_ERR_UNSUPPORTED, "block_q = %d (supported: 64, 128)", s->block_q);
   if (s->block_k != 64) return fail(SD_ERR_UNSUPPORTED, "block_k = %d (supported: 64)", s->block_k);
   if (s->L > kMaxL) return fail(SD_ERR_UNSUPPORTED, "L = %d exceeds %d", s->L, kMaxL);
+  if (s->select != SD_SELECT_TOPK && s->select != SD_SELECT_FIXED)
+    return fail(SD_ERR_INVALID_ARG, "select = %d", s->select);
+  if (s->chunk_tokens < 0 || s->window < 0) return fail(SD_ERR_INVALID_ARG, "chunk_tokens and window must be >= 0");
+  if (s->chunk_tokens == 0 && s->window != 0) return fail(SD_ERR_INVALID_ARG, "window needs chunk_tokens > 0");
+  const int ar = (s->chunk_tokens > 0 && s->chunk_tokens < s->L) ? s->chunk_tokens : s->L;
+  if ((s->L + ar - 1) / ar > kMaxArChunks)
+    return fail(SD_ERR_UNSUPPORTED, "more than %d autoregressive chunks", kMaxArChunks);
+  if (s->select == SD_SELECT_FIXED) need_grid = true;  // the pattern lives on the latent grid
   if (need_grid) {
     if (s->T < 1 || s->Hg < 1 || s->Wg < 1 || (int64_t)s->T * s->Hg * s->Wg != s->L)
       return fail(SD_ERR_INVALID_ARG, "T*Hg*Wg (%d*%d*%d) must equal L = %d", s->T, s->Hg, s->Wg, s->L);
@@ -81,6 +93,10 @@ int check_shape(const sd_attn_shape* s, Geo* g, bool need_grid) {
   g->bk = s->block_k;
   g->Nq = (s->L + s->block_q - 1) / s->block_q;
   g->Nk = (s->L + s->block_k - 1) / s->block_k;
+  g->select = s->select;
+  g->ar = ar;
+  g->win = s->chunk_tokens > 0 ? s->window : 0;
+  g->n_ar = (s->L + ar - 1) / ar;
   if ((int64_t)g->B * g->H * g->Nq >= (int64_t)1 << 31) return fail(SD_ERR_UNSUPPORTED, "too many query blocks");
   if ((int64_t)g->B * g->H > 65535) return fail(SD_ERR_UNSUPPORTED, "B*H exceeds 65535");
   return SD_OK;
@@ -147,48 +163,50 @@ SelectWs carve_select(Carve& c, const Geo& g) {
   return w;
 }
 
-int lowrank_chunks(const Geo& g, int* chunk_tiles) {
-  const int ntiles = (g.L + 63) / 64;
+// Runs of 64-token tiles that each write one partial low-rank state: about
+// `slots` workgroups in all, `align` tiles a multiple of the run length.
+// Each autoregressive chunk gets its own runs (it spans at most
+// ceil(ar / 64) + 1 tiles); without a causal window there is one chunk.
+sd::RunGeo make_runs(const Geo& g, int64_t slots, int align) {
   const int64_t bh = (int64_t)g.B * g.H;
-  int n_chunks = (int)std::min<int64_t>(ntiles, std::max<int64_t>(1, (2048 + bh - 1) / bh));
-  const int ct = (ntiles + n_chunks - 1) / n_chunks;
-  *chunk_tiles = ct;
-  return (ntiles + ct - 1) / ct;
+  const int span = g.n_ar == 1 ? (g.L + 63) / 64 : (g.ar + 63) / 64 + 1;
+  const int want = (int)std::min<int64_t>(span, std::max<int64_t>(1, slots / (bh * g.n_ar)));
+  int rt = (span + want - 1) / want;
+  rt = (rt + align - 1) / align * align;
+  sd::RunGeo r;
+  r.ar_tokens = g.ar;
+  r.run_tiles = rt;
+  r.runs_per_ar = (span + rt - 1) / rt;
+  r.n_runs = g.n_ar * r.runs_per_ar;
+  return r;
 }
 
-// Runs of 64-token tiles for the fused prepare pass: aligned to query blocks,
-// at most kPrepareSlots workgroups in all where the shape allows it, so that
-// every run is resident at once (three 4-wave workgroups per CU on 256 CUs)
-// and none waits for a second round.
+sd::RunGeo lowrank_runs(const Geo& g) { return make_runs(g, 2048, 1); }
+
+// Runs of the fused prepare pass: at most kPrepareSlots workgroups in all
+// where the shape allows it, so that every run is resident at once (three
+// 4-wave workgroups per CU on 256 CUs) and none waits for a second round.
+// Without a causal window they are aligned to query blocks.
 constexpr int64_t kPrepareSlots = 768;
-int prepare_chunks(const Geo& g, int* chunk_tiles) {
-  const int ntiles = (g.L + 63) / 64;
-  const int q_tiles = g.bq / 64;
-  const int64_t bh = (int64_t)g.B * g.H;
-  const int want = (int)std::min<int64_t>(ntiles, std::max<int64_t>(1, kPrepareSlots / bh));
-  int ct = (ntiles + want - 1) / want;
-  ct = (ct + q_tiles - 1) / q_tiles * q_tiles;
-  *chunk_tiles = ct;
-  return (ntiles + ct - 1) / ct;
-}
+sd::RunGeo prepare_runs(const Geo& g) { return make_runs(g, kPrepareSlots, g.n_ar == 1 ? g.bq / 64 : 1); }
 
 int max_extent(const sd_attn_shape* s) { return std::max(s->T, std::max(s->Hg, s->Wg)); }
 
 struct LowrankWs {
   float2* rope_tab;
   float* partial;
-  uint16_t* ct_hi;
+  uint16_t* ct_hi;  // [B*H, n_ar, D, 32]
   uint16_t* ct_lo;
-  int n_chunks, chunk_tiles;
+  sd::RunGeo runs;
 };
 
-LowrankWs carve_lowrank(Carve& c, const Geo& g, const sd_attn_shape* s) {
+LowrankWs carve_lowrank(Carve& c, const Geo& g, const sd_attn_shape* s, const sd::RunGeo& runs) {
   LowrankWs w;
-  w.n_chunks = lowrank_chunks(g, &w.chunk_tiles);
+  w.runs = runs;
   w.rope_tab = static_cast<float2*>(c.take(sizeof(float2) * sd::kMaxRopePairs * max_extent(s)));
-  w.partial = static_cast<float*>(c.take(sizeof(float) * g.B * g.H * (size_t)w.n_chunks * 32 * g.D));
-  w.ct_hi = static_cast<uint16_t*>(c.take(sizeof(uint16_t) * g.B * g.H * g.D * 32));
-  w.ct_lo = static_cast<uint16_t*>(c.take(sizeof(uint16_t) * g.B * g.H * g.D * 32));
+  w.partial = static_cast<float*>(c.take(sizeof(float) * g.B * g.H * (size_t)runs.n_runs * 32 * g.D));
+  w.ct_hi = static_cast<uint16_t*>(c.take(sizeof(uint16_t) * g.B * g.H * (size_t)g.n_ar * g.D * 32));
+  w.ct_lo = static_cast<uint16_t*>(c.take(sizeof(uint16_t) * g.B * g.H * (size_t)g.n_ar * g.D * 32));
   return w;
 }
 
@@ -224,8 +242,7 @@ int run_lowrank_state(const sd_attn_shape* s, const Geo& g, const sd_lowrank_par
   a.L = g.L;
   a.Hg = s->Hg;
   a.Wg = s->Wg;
-  a.chunk_tiles = w.chunk_tiles;
-  a.n_chunks = w.n_chunks;
+  a.runs = w.runs;
   a.Pk = static_cast<const uint16_t*>(lr->Pk);
   a.P_hs = lr->P_head_stride;
   a.rank = lr->rank;
@@ -236,24 +253,62 @@ int run_lowrank_state(const sd_attn_shape* s, const Geo& g, const sd_lowrank_par
   if (e != hipSuccess) return hip_fail(e, "low-rank state");
   sd::RankRows rows{};
   for (int r = 0; r < 32; ++r) rows.row[r] = (int8_t)(r < lr->rank ? r : -1);
-  e = sd::launch_lowrank_finalize(w.partial, g.B * g.H, w.n_chunks, lr->rank, g.D, rows, C_out, w.ct_hi, w.ct_lo, st);
+  e = sd::launch_lowrank_finalize(w.partial, g.B * g.H, w.runs, g.n_ar, g.win, lr->rank, g.D, rows, C_out, w.ct_hi,
+                                  w.ct_lo, st);
   if (e != hipSuccess) return hip_fail(e, "low-rank finalize");
+  return SD_OK;
+}
+
+sd::MapRule map_rule(const Geo& g, int k_keep) {
+  sd::MapRule r;
+  r.Nq = g.Nq;
+  r.bq = g.bq;
+  r.bk = g.bk;
+  r.L = g.L;
+  r.ar_tokens = g.ar;
+  r.ar_window = g.win;
+  if (g.select == SD_SELECT_FIXED) {  // one map, copied to every (batch, head)
+    r.s_rows = g.Nq;
+    r.n_rep = g.B * g.H;
+    r.rep_stride = (int64_t)g.Nq * k_keep;
+  } else {
+    r.s_rows = (int64_t)g.B * g.H * g.Nq;
+    r.n_rep = 1;
+    r.rep_stride = 0;
+  }
+  return r;
+}
+
+// Scores of the selector (block means are ready for SD_SELECT_TOPK), then the
+// top-k under the causal window.
+int run_scores_topk(const sd_attn_shape* s, const Geo& g, int k_keep, int32_t* idx, const SelectWs& w,
+                    hipStream_t st) {
+  hipError_t e;
+  const sd::MapRule rule = map_rule(g, k_keep);
+  if (g.select == SD_SELECT_FIXED) {
+    e = sd::launch_fixed_scores(g.L, g.Nq, g.Nk, g.bq, g.bk, s->Hg, s->Wg, w.qmean, w.kmean, w.S, st);
+    if (e != hipSuccess) return hip_fail(e, "fixed scores");
+    e = sd::launch_topk_rows(w.S, g.Nq, g.Nk, k_keep, rule, idx, st);
+  } else {
+    e = sd::launch_block_scores(w.qmean, w.kmean, g.B * g.H, g.Nq, g.Nk, g.D, w.S, st);
+    if (e != hipSuccess) return hip_fail(e, "block scores");
+    e = sd::launch_topk_rows(w.S, (int64_t)g.B * g.H * g.Nq, g.Nk, k_keep, rule, idx, st);
+  }
+  if (e != hipSuccess) return hip_fail(e, "top-k");
   return SD_OK;
 }
 
 int run_block_select(const sd_attn_shape* s, const Geo& g, const void* Q, const void* K, int k_keep, int32_t* idx,
                      const SelectWs& w, hipStream_t st) {
-  hipError_t e = sd::launch_pool_blocks(static_cast<const uint16_t*>(Q), s->sq_b, s->sq_l, s->sq_h, g.B, g.L, g.H,
-                                        g.D, g.bq, w.qmean, st);
-  if (e != hipSuccess) return hip_fail(e, "pool Q");
-  e = sd::launch_pool_blocks(static_cast<const uint16_t*>(K), s->sk_b, s->sk_l, s->sk_h, g.B, g.L, g.H, g.D, g.bk,
-                             w.kmean, st);
-  if (e != hipSuccess) return hip_fail(e, "pool K");
-  e = sd::launch_block_scores(w.qmean, w.kmean, g.B * g.H, g.Nq, g.Nk, g.D, w.S, st);
-  if (e != hipSuccess) return hip_fail(e, "block scores");
-  e = sd::launch_topk_rows(w.S, (int64_t)g.B * g.H * g.Nq, g.Nk, k_keep, idx, st);
-  if (e != hipSuccess) return hip_fail(e, "top-k");
-  return SD_OK;
+  if (g.select == SD_SELECT_TOPK) {
+    hipError_t e = sd::launch_pool_blocks(static_cast<const uint16_t*>(Q), s->sq_b, s->sq_l, s->sq_h, g.B, g.L, g.H,
+                                          g.D, g.bq, w.qmean, st);
+    if (e != hipSuccess) return hip_fail(e, "pool Q");
+    e = sd::launch_pool_blocks(static_cast<const uint16_t*>(K), s->sk_b, s->sk_l, s->sk_h, g.B, g.L, g.H, g.D, g.bk,
+                               w.kmean, st);
+    if (e != hipSuccess) return hip_fail(e, "pool K");
+  }
+  return run_scores_topk(s, g, k_keep, idx, w, st);
 }
 
 void fill_attn_common(sd::AttnArgs& a, const sd_attn_shape* s, const Geo& g) {
@@ -276,6 +331,8 @@ void fill_attn_common(sd::AttnArgs& a, const sd_attn_shape* s, const Geo& g) {
   a.Nk = g.Nk;
   a.Hg = s->Hg;
   a.Wg = s->Wg;
+  a.ar_tokens = g.ar;
+  a.ar_window = g.win;
 }
 
 void fill_attn_lowrank(sd::AttnArgs& a, const sd_lowrank_params* lr, const sd_attn_shape* s, const LowrankWs& w) {
@@ -379,7 +436,7 @@ size_t sd_lowrank_workspace_size(const sd_attn_shape* shape, const sd_lowrank_pa
   if (check_shape(shape, &g, true)) return 0;
   (void)lr;
   Carve c(nullptr);
-  carve_lowrank(c, g, shape);
+  carve_lowrank(c, g, shape, lowrank_runs(g));
   return align_up(c.off);
 }
 
@@ -399,7 +456,7 @@ int sd_lowrank_attn(const sd_attn_shape* shape, const sd_lowrank_params* lr, con
   if (!aligned(ws, kAlign)) return fail(SD_ERR_ALIGN, "workspace must be 256-byte aligned");
   hipStream_t st = static_cast<hipStream_t>(stream);
   Carve c(ws);
-  const LowrankWs w = carve_lowrank(c, g, shape);
+  const LowrankWs w = carve_lowrank(c, g, shape, lowrank_runs(g));
   if ((rc = run_lowrank_state(shape, g, lr, Kn, V, C_out, w, st))) return rc;
   sd::AttnArgs a{};
   fill_attn_common(a, shape, g);
@@ -538,21 +595,39 @@ int sd_qk_norm_rope(int B, int L, int H, int d, int T, int Hg, int Wg, const voi
   return ok();
 }
 
+}  // extern "C"
+
+namespace {
+
+struct RolaWs {
+  SelectWs sel;
+  int32_t* idx;
+  LowrankWs lr;
+  size_t bytes;
+};
+
+// Workspace of the fused entry points (sizes only when ws is NULL).
+RolaWs carve_rola(void* ws, const Geo& g, const sd_attn_shape* shape, int k_keep) {
+  Carve c(ws);
+  RolaWs w;
+  w.sel = carve_select(c, g);
+  w.idx = static_cast<int32_t*>(c.take(sizeof(int32_t) * g.B * g.H * (size_t)g.Nq * k_keep));
+  // the fused pass writes one partial state per run of tiles
+  w.lr = carve_lowrank(c, g, shape, prepare_runs(g));
+  w.bytes = align_up(c.off);
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
 size_t sd_rola_workspace_size(const sd_attn_shape* shape, const sd_lowrank_params* lr, int k_keep) {
   Geo g;
   if (check_shape(shape, &g, true)) return 0;
   if (k_keep < 1 || k_keep > g.Nk) return 0;
   (void)lr;
-  Carve c(nullptr);
-  carve_select(c, g);
-  c.take(sizeof(int32_t) * g.B * g.H * (size_t)g.Nq * k_keep);
-  int ct;
-  const int nc = prepare_chunks(g, &ct);
-  c.take(sizeof(float2) * sd::kMaxRopePairs * max_extent(shape));
-  c.take(sizeof(float) * g.B * g.H * (size_t)nc * 32 * g.D);
-  c.take(sizeof(uint16_t) * g.B * g.H * g.D * 32);
-  c.take(sizeof(uint16_t) * g.B * g.H * g.D * 32);
-  return align_up(c.off);
+  return carve_rola(nullptr, g, shape, k_keep).bytes;
 }
 
 }  // extern "C"
@@ -575,29 +650,6 @@ int check_rola(const sd_attn_shape* shape, const sd_lowrank_params* lr, const vo
   if (!ws || ws_bytes < need) return fail(SD_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
   if (!aligned(ws, kAlign)) return fail(SD_ERR_ALIGN, "workspace must be 256-byte aligned");
   return SD_OK;
-}
-
-struct RolaWs {
-  SelectWs sel;
-  int32_t* idx;
-  LowrankWs lr;
-};
-
-RolaWs carve_rola(void* ws, const Geo& g, const sd_attn_shape* shape, int k_keep) {
-  Carve c(ws);
-  RolaWs w;
-  w.sel = carve_select(c, g);
-  w.idx = static_cast<int32_t*>(c.take(sizeof(int32_t) * g.B * g.H * (size_t)g.Nq * k_keep));
-  // the fused pass writes one partial state per run of tiles
-  int ct;
-  const int nc = prepare_chunks(g, &ct);
-  w.lr.n_chunks = nc;
-  w.lr.chunk_tiles = ct;
-  w.lr.rope_tab = static_cast<float2*>(c.take(sizeof(float2) * sd::kMaxRopePairs * max_extent(shape)));
-  w.lr.partial = static_cast<float*>(c.take(sizeof(float) * g.B * g.H * (size_t)nc * 32 * g.D));
-  w.lr.ct_hi = static_cast<uint16_t*>(c.take(sizeof(uint16_t) * g.B * g.H * g.D * 32));
-  w.lr.ct_lo = static_cast<uint16_t*>(c.take(sizeof(uint16_t) * g.B * g.H * g.D * 32));
-  return w;
 }
 
 int check_apply_extra(const void* O, const float* g_ptr, float sm_scale, int64_t gb, int64_t gl, int64_t gh) {
@@ -640,8 +692,7 @@ int run_prepare(const sd_attn_shape* s, const Geo& g, const sd_lowrank_params* l
   a.Wg = s->Wg;
   a.rcp_hw = 1.0f / (float)(s->Hg * s->Wg);
   a.rcp_wg = 1.0f / (float)s->Wg;
-  a.chunk_tiles = w.lr.chunk_tiles;
-  a.n_chunks = w.lr.n_chunks;
+  a.runs = w.lr.runs;
   a.Pk = static_cast<const uint16_t*>(lr->Pk);
   a.P_hs = lr->P_head_stride;
   a.rank = lr->rank;
@@ -671,24 +722,28 @@ int run_prepare(const sd_attn_shape* s, const Geo& g, const sd_lowrank_params* l
   a.slot_mask = 0;
   for (int i = 0; i < 32; ++i)
     if (a.slot_rank[i] >= 0) a.slot_mask |= 1u << i;
-  // key-block means come from the stream pass when it reads K itself
-  const bool k_in_stream = a.Kn == a.K;
+  // The scored selector needs the block means: those of K come from the
+  // stream pass when it reads K itself and its runs are whole key blocks
+  // (no causal window), else from the pooling kernel. The fixed pattern
+  // needs none.
+  const bool scored = g.select == SD_SELECT_TOPK;
+  const bool k_in_stream = scored && a.Kn == a.K && g.n_ar == 1;
   a.kmean = k_in_stream ? w.sel.kmean : nullptr;
   a.partial = w.lr.partial;
-  e = sd::launch_pool_blocks(a.Q, s->sq_b, s->sq_l, s->sq_h, g.B, g.L, g.H, g.D, g.bq, w.sel.qmean, st);
-  if (e != hipSuccess) return hip_fail(e, "pool Q");
-  if (!k_in_stream) {
-    e = sd::launch_pool_blocks(a.K, s->sk_b, s->sk_l, s->sk_h, g.B, g.L, g.H, g.D, g.bk, w.sel.kmean, st);
-    if (e != hipSuccess) return hip_fail(e, "pool K");
+  if (scored) {
+    e = sd::launch_pool_blocks(a.Q, s->sq_b, s->sq_l, s->sq_h, g.B, g.L, g.H, g.D, g.bq, w.sel.qmean, st);
+    if (e != hipSuccess) return hip_fail(e, "pool Q");
+    if (!k_in_stream) {
+      e = sd::launch_pool_blocks(a.K, s->sk_b, s->sk_l, s->sk_h, g.B, g.L, g.H, g.D, g.bk, w.sel.kmean, st);
+      if (e != hipSuccess) return hip_fail(e, "pool K");
+    }
   }
   e = sd::launch_prepare_stream(a, g.D, st);
   if (e != hipSuccess) return hip_fail(e, "prepare pass");
-  e = sd::launch_block_scores(w.sel.qmean, w.sel.kmean, g.B * g.H, g.Nq, g.Nk, g.D, w.sel.S, st);
-  if (e != hipSuccess) return hip_fail(e, "block scores");
-  e = sd::launch_topk_rows(w.sel.S, (int64_t)g.B * g.H * g.Nq, g.Nk, k_keep, idx, st);
-  if (e != hipSuccess) return hip_fail(e, "top-k");
-  e = sd::launch_lowrank_finalize(w.lr.partial, g.B * g.H, w.lr.n_chunks, lr->rank, g.D, rows, nullptr, w.lr.ct_hi,
-                                  w.lr.ct_lo, st);
+  int rc = run_scores_topk(s, g, k_keep, idx, w.sel, st);
+  if (rc) return rc;
+  e = sd::launch_lowrank_finalize(w.lr.partial, g.B * g.H, w.lr.runs, g.n_ar, g.win, lr->rank, g.D, rows, nullptr,
+                                  w.lr.ct_hi, w.lr.ct_lo, st);
   if (e != hipSuccess) return hip_fail(e, "low-rank finalize");
   return SD_OK;
 }

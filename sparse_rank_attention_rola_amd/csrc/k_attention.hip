@@ -5,7 +5,10 @@
 // A_M is softmax attention restricted to the kept 1-s of the key blocks of
 // each query block; the compensation branch gives O_lr,i = RMSNorm(q~_i^T C)
 // with q~_i = R_r(p_i) phi(P_q qn_i); the fusion is O_i = O_s,i + g_i r_i
-// O_lr,i with r_i the RMS of O_s,i.
+// O_lr,i with r_i the RMS of O_s,i. Section 4 (autoregressive extension):
+// both branches may be restricted to a causal window over chunks of tokens;
+// a query then sees only the keys of its window, in the kept blocks and in
+// the state C of its chunk.
 //
 // One workgroup owns one query block (block_q = 32 * waves queries) of one
 // (batch, head); each wave owns 32 queries. All XCDs work on the same head at
@@ -43,10 +46,12 @@ __device__ __forceinline__ float phi_elu1(float x) { return x > 0.f ? x + 1.f : 
 //   qreg: the wave's normalised queries in the B-operand layout
 //         (lane l32 = query, channels 16*s + 8*hf .. +7).
 //   Fw:   wave-private LDS patch of 32 x 33 floats.
+//   q_chunk: the autoregressive chunk of the lane's query (0 without a
+//         causal window); the state C of that chunk is used.
 // Returns y / sqrt(mean(y^2) + eps) * w in the O^T accumulator layout.
 template <int D>
 __device__ __forceinline__ void lowrank_query_tile(const u32x4* qreg, const AttnArgs& a, int b, int h, int tok0,
-                                                   float* Fw, int lane, f32x16 (&out)[D / 32]) {
+                                                   int q_chunk, float* Fw, int lane, f32x16 (&out)[D / 32]) {
   const int hf = lane >> 5, l32 = lane & 31;
   const uint16_t* Pq = a.Pq + (int64_t)h * a.P_hs;
   f32x16 acc = {};
@@ -90,24 +95,36 @@ __device__ __forceinline__ void lowrank_query_tile(const u32x4* qreg, const Attn
     for (int p = 0; p < 8; ++p) t8[p] = Fw[l32 * 33 + 16 * s + 8 * hf + p];
     split_bf16x8(t8, qhi[s], qlo[s]);
   }
-  const int64_t cbase = ((int64_t)b * a.H + h) * D * 32;
+  // The wave's queries may fall in several autoregressive chunks (the
+  // chunk index grows with the token): the product is formed once per chunk
+  // with that chunk's state and each lane keeps the one of its own chunk.
+  const int n_ar = (a.L + a.ar_tokens - 1) / a.ar_tokens;
+  const int c_first = __builtin_amdgcn_readfirstlane(q_chunk);
+  const int c_last = __builtin_amdgcn_readlane(q_chunk, 31);
+  for (int c = c_first; c <= c_last; ++c) {
+    const int64_t cbase = (((int64_t)b * a.H + h) * n_ar + c) * D * 32;
+    const bool mine = q_chunk == c;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      f32x16 y = {};
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int64_t off = cbase + (int64_t)(32 * dt + l32) * 32 + 16 * s + 8 * hf;
+        const bf16x8 ch = as_bf16x8(*reinterpret_cast<const u32x4*>(a.Ct_hi + off));
+        const bf16x8 cl = as_bf16x8(*reinterpret_cast<const u32x4*>(a.Ct_lo + off));
+        y = mfma32(ch, qhi[s], y);
+        y = mfma32(cl, qhi[s], y);
+        y = mfma32(ch, qlo[s], y);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) out[dt][r] = (c == c_first || mine) ? y[r] : out[dt][r];
+    }
+  }
   float ss = 0.f;
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) {
-    f32x16 y = {};
+  for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int64_t off = cbase + (int64_t)(32 * dt + l32) * 32 + 16 * s + 8 * hf;
-      const bf16x8 ch = as_bf16x8(*reinterpret_cast<const u32x4*>(a.Ct_hi + off));
-      const bf16x8 cl = as_bf16x8(*reinterpret_cast<const u32x4*>(a.Ct_lo + off));
-      y = mfma32(ch, qhi[s], y);
-      y = mfma32(cl, qhi[s], y);
-      y = mfma32(ch, qlo[s], y);
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) ss += y[r] * y[r];
-    out[dt] = y;
-  }
+    for (int r = 0; r < 16; ++r) ss += out[dt][r] * out[dt][r];
   ss += __shfl_xor(ss, 32);
   const float inv = rsqrtf(ss * (1.0f / D) + a.eps);
 #pragma unroll
@@ -164,6 +181,12 @@ __global__ __launch_bounds__(BQ * 2, BQ == 128 ? SD_ATTN_WAVES : 1) void attenti
   const int tok0 = qb * BQ + wv * 32;
   const int q_tok = tok0 + l32;
   const bool q_ok = q_tok < a.L;
+  // keys the lane's query may see: [key_lo, key_hi) of its causal window
+  // ([0, L) without one); the bounds grow with the token, so the wave's
+  // tightest limits are those of its first and last query
+  const int q_chunk = min(q_tok, a.L - 1) / a.ar_tokens;
+  const int key_hi = min(a.L, (q_chunk + 1) * a.ar_tokens);
+  const int key_lo = a.ar_window > 0 ? max(0, (q_chunk - a.ar_window + 1) * a.ar_tokens) : 0;
 
   // queries in the B-operand layout
   u32x4 qreg[D / 16];
@@ -201,13 +224,18 @@ __global__ __launch_bounds__(BQ * 2, BQ == 128 ? SD_ATTN_WAVES : 1) void attenti
     // One kept block of 64 keys, as two half-tiles of 32 keys. The lane
     // holds 16 of the 32 keys of its query per half-tile.
     auto mask_half = [&](f32x16& sacc, int key0, int kt) {
-      // key of register r: key0 + 32 kt + 4 hf + 8 (r / 4) + r % 4, compared
-      // as a constant against one per-lane limit
-      const int lim = a.L - key0 - 32 * kt - 4 * hf;
+      // key of register r: key0 + 32 kt + 4 hf + 8 (r / 4) + r % 4, its
+      // offset compared as a constant against two per-lane limits
+      const int base = key0 + 32 * kt + 4 * hf;
+      const int lim_hi = key_hi - base, lim_lo = key_lo - base;
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (8 * (r >> 2) + (r & 3) >= lim) sacc[r] = -INFINITY;
+      for (int r = 0; r < 16; ++r) {
+        const int o = 8 * (r >> 2) + (r & 3);
+        if (o >= lim_hi || o < lim_lo) sacc[r] = -INFINITY;
+      }
     };
+    const int wave_hi = __builtin_amdgcn_readfirstlane(key_hi);
+    const int wave_lo = __builtin_amdgcn_readlane(key_lo, 31);
     // Online softmax of a half-tile in the log2 domain, without touching O:
     // returns whether the reference maximum moves (for some lane), the new
     // maximum and the sum of the bf16 probabilities the PV product consumes.
@@ -256,7 +284,7 @@ __global__ __launch_bounds__(BQ * 2, BQ == 128 ? SD_ATTN_WAVES : 1) void attenti
         s0 = mfma32(lds_k_chunk<D>(Ks, l32, 2 * s + hf), as_bf16x8(qreg[s]), s0);
         s1 = mfma32(lds_k_chunk<D>(Ks, 32 + l32, 2 * s + hf), as_bf16x8(qreg[s]), s1);
       }
-      if (key0 + 64 > a.L) {
+      if (key0 + 64 > wave_hi || key0 < wave_lo) {
         mask_half(s0, key0, 0);
         mask_half(s1, key0, 1);
       }
@@ -324,7 +352,7 @@ __global__ __launch_bounds__(BQ * 2, BQ == 128 ? SD_ATTN_WAVES : 1) void attenti
           qreg[s] = q_ok ? *reinterpret_cast<const u32x4*>(qp + 16 * s + 8 * hf) : u32x4{0, 0, 0, 0};
       }
     }
-    lowrank_query_tile<D>(qreg, a, b, h, tok0, Fw, lane, olr);
+    lowrank_query_tile<D>(qreg, a, b, h, tok0, q_chunk, Fw, lane, olr);
     if constexpr (MODE == kModeLowrank) {
       if (q_ok) store_row<D>(a.out, a.out_f32, obase, olr, hf);
     } else {

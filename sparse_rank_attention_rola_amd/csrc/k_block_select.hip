@@ -16,6 +16,10 @@
 //                      token row per load (coalesced), HBM-bound.
 //  block_scores_kernel S[b, h] = qmean . kmean^T as a 128x128-tiled f64 GEMM
 //                      on the vector ALUs (8x8 register blocking, LDS panels).
+//  fixed_scores_kernel the fixed spatio-temporal pattern (same section: a
+//                      fixed pattern may replace the scored selection):
+//                      minus the squared distance of the block centroids in
+//                      latent (t, h, w) coordinates.
 //  topk_rows_kernel    one wavefront per score row: a radix select on 8-bit
 //                      digits of the order-preserving 64-bit image of the
 //                      scores, from the top, finds the k-th largest score
@@ -23,7 +27,11 @@
 //                      the chosen bin is kept); the row is then compacted in
 //                      index order with ballots, so the output is ascending
 //                      and equal scores at the threshold go to the lower
-//                      block index.
+//                      block index. Under a causal window (section 4 of the
+//                      write-up, autoregressive extension) only the key
+//                      blocks some query of the row's block may see are
+//                      candidates; a row with fewer than k of them keeps
+//                      them all and is padded with -1.
 #include "sd_device.h"
 #include "sd_launch.h"
 
@@ -158,9 +166,15 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Chunk range [first, last] of the tokens [t0, t1) (t1 > t0).
+__device__ __forceinline__ void chunk_span(int t0, int t1, int ar, int& first, int& last) {
+  first = t0 / ar;
+  last = (t1 - 1) / ar;
+}
+
 template <int NPL>  // scores per lane (row length <= 64 * NPL)
 __global__ __launch_bounds__(256) void topk_rows_kernel(const double* __restrict__ S, int64_t n_rows, int C, int k,
-                                                        int32_t* __restrict__ idx) {
+                                                        MapRule rule, int32_t* __restrict__ idx) {
   __shared__ uint32_t hist[4][256];
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
@@ -168,18 +182,36 @@ __global__ __launch_bounds__(256) void topk_rows_kernel(const double* __restrict
   const bool row_ok = row < n_rows;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
+  // Causal window: key block c may be kept by query block qb when its
+  // chunks [ck0, ck1] meet [cq0 - W + 1, cq1], the chunks the queries of qb
+  // see (no lower limit for W = 0); without a window every block is allowed.
+  const int qb = (int)(row % rule.Nq);
+  int cq0, cq1;
+  chunk_span(qb * rule.bq, min(rule.L, (qb + 1) * rule.bq), rule.ar_tokens, cq0, cq1);
+  const int lo_chunk = rule.ar_window > 0 ? cq0 - rule.ar_window + 1 : -1;
+  const double* Srow = S + (row % rule.s_rows) * (int64_t)C;
   uint64_t key[NPL];
   bool valid[NPL];
+  int n_ok = 0;
 #pragma unroll
   for (int j = 0; j < NPL; ++j) {
     const int c = j * 64 + lane;
-    valid[j] = row_ok && c < C;
-    key[j] = valid[j] ? order_key(S[row * C + c]) : 0ull;
+    bool ok = row_ok && c < C;
+    if (ok) {
+      int ck0, ck1;
+      chunk_span(c * rule.bk, min(rule.L, (c + 1) * rule.bk), rule.ar_tokens, ck0, ck1);
+      ok = ck0 <= cq1 && ck1 >= lo_chunk;
+    }
+    valid[j] = ok;
+    key[j] = ok ? order_key(Srow[c]) : 0ull;
+    n_ok += __popcll(__ballot(ok));
   }
+  // fewer allowed blocks than k: all of them are kept, the rest is -1
+  const int kk = min(k, n_ok);
 
   uint64_t prefix = 0, pmask = 0;
-  int remaining = k;
-  for (int shift = 56; shift >= 0; shift -= 8) {
+  int remaining = kk;
+  for (int shift = 56; shift >= 0 && kk > 0; shift -= 8) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) hist[wv][lane + 64 * i] = 0;
     wave_lds_sync();
@@ -250,20 +282,59 @@ __global__ __launch_bounds__(256) void topk_rows_kernel(const double* __restrict
   // equal to it on those bits the first `remaining` in index order (all of
   // them when the loop ended early); with every bit examined, prefix is the
   // exact k-th largest key
-  int taken = 0, ties = 0;
-  int32_t* out = idx + row * k;
+  for (int rep = 0; rep < rule.n_rep; ++rep) {
+    int taken = 0, ties = 0;
+    int32_t* out = idx + rep * rule.rep_stride + row * k;
+    if (kk > 0) {
 #pragma unroll
-  for (int j = 0; j < NPL; ++j) {
-    const uint64_t km = key[j] & pmask;
-    const bool gt = valid[j] && km > prefix;
-    const bool eq = valid[j] && km == prefix;
-    const uint64_t eqm = __ballot(eq);
-    const bool take = gt || (eq && ties + __popcll(eqm & lt_mask) < remaining);
-    const uint64_t tm = __ballot(take);
-    if (take) out[taken + __popcll(tm & lt_mask)] = j * 64 + lane;
-    taken += __popcll(tm);
-    ties += __popcll(eqm);
+      for (int j = 0; j < NPL; ++j) {
+        const uint64_t km = key[j] & pmask;
+        const bool gt = valid[j] && km > prefix;
+        const bool eq = valid[j] && km == prefix;
+        const uint64_t eqm = __ballot(eq);
+        const bool take = gt || (eq && ties + __popcll(eqm & lt_mask) < remaining);
+        const uint64_t tm = __ballot(take);
+        if (take) out[taken + __popcll(tm & lt_mask)] = j * 64 + lane;
+        taken += __popcll(tm);
+        ties += __popcll(eqm);
+      }
+    }
+    for (int i = kk + lane; i < k; i += 64) out[i] = -1;
   }
+}
+
+// Centroid (t, h, w) of each block of bs raster tokens: exact integer sums
+// of the coordinates, one float64 division each.
+__global__ void block_centroids_kernel(int L, int bs, int n, int Hg, int Wg, double* __restrict__ cen) {
+  const int blk = blockIdx.x * blockDim.x + threadIdx.x;
+  if (blk >= n) return;
+  const int t0 = blk * bs, t1 = min(L, t0 + bs);
+  const int hw = Hg * Wg;
+  int64_t st = 0, sh = 0, sw = 0;
+  for (int i = t0; i < t1; ++i) {
+    st += i / hw;
+    sh += (i / Wg) % Hg;
+    sw += i % Wg;
+  }
+  const double cnt = (double)(t1 - t0);
+  cen[3 * blk + 0] = (double)st / cnt;
+  cen[3 * blk + 1] = (double)sh / cnt;
+  cen[3 * blk + 2] = (double)sw / cnt;
+}
+
+// S[r][c] = -((dt*dt + dh*dh) + dw*dw) of the two centroids, rounded after
+// every operation (no fused multiply-add), so the value is reproducible.
+__global__ void fixed_scores_kernel(const double* __restrict__ cq, const double* __restrict__ ck, int Nq, int Nk,
+                                    double* __restrict__ S) {
+#pragma clang fp contract(off)
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)Nq * Nk) return;
+  const int r = (int)(i / Nk), c = (int)(i - (int64_t)r * Nk);
+  const double dt = cq[3 * r] - ck[3 * c];
+  const double dh = cq[3 * r + 1] - ck[3 * c + 1];
+  const double dw = cq[3 * r + 2] - ck[3 * c + 2];
+  const double sq_t = dt * dt, sq_h = dh * dh, sq_w = dw * dw;
+  S[i] = -((sq_t + sq_h) + sq_w);
 }
 
 hipError_t launch_pool_blocks(const uint16_t* X, int64_t sb, int64_t sl, int64_t sh, int B, int L, int H, int D,
@@ -282,13 +353,14 @@ hipError_t launch_block_scores(const double* qmean, const double* kmean, int BH,
   return hipGetLastError();
 }
 
-hipError_t launch_topk_rows(const double* S, int64_t n_rows, int C, int k, int32_t* idx, hipStream_t stream) {
+hipError_t launch_topk_rows(const double* S, int64_t n_rows, int C, int k, const MapRule& rule, int32_t* idx,
+                            hipStream_t stream) {
   const int npl = (C + 63) / 64;
   const dim3 grid((unsigned)((n_rows + 3) / 4)), block(256);
-#define SD_TOPK_CASE(N)                                                                       \
-  if (npl <= N) {                                                                             \
-    hipLaunchKernelGGL(topk_rows_kernel<N>, grid, block, 0, stream, S, n_rows, C, k, idx);    \
-    return hipGetLastError();                                                                 \
+#define SD_TOPK_CASE(N)                                                                          \
+  if (npl <= N) {                                                                                \
+    hipLaunchKernelGGL(topk_rows_kernel<N>, grid, block, 0, stream, S, n_rows, C, k, rule, idx); \
+    return hipGetLastError();                                                                    \
   }
   SD_TOPK_CASE(1)
   SD_TOPK_CASE(2)
@@ -301,6 +373,16 @@ hipError_t launch_topk_rows(const double* S, int64_t n_rows, int C, int k, int32
   SD_TOPK_CASE(32)
 #undef SD_TOPK_CASE
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_fixed_scores(int L, int Nq, int Nk, int bq, int bk, int Hg, int Wg, double* cq, double* ck,
+                               double* S, hipStream_t stream) {
+  hipLaunchKernelGGL(block_centroids_kernel, dim3((Nq + 255) / 256), dim3(256), 0, stream, L, bq, Nq, Hg, Wg, cq);
+  hipLaunchKernelGGL(block_centroids_kernel, dim3((Nk + 255) / 256), dim3(256), 0, stream, L, bk, Nk, Hg, Wg, ck);
+  const int64_t n = (int64_t)Nq * Nk;
+  hipLaunchKernelGGL(fixed_scores_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, cq, ck, Nq, Nk,
+                     S);
+  return hipGetLastError();
 }
 
 }  // namespace sd

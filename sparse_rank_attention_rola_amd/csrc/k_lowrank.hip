@@ -37,11 +37,11 @@ template <int D>
 __global__ __launch_bounds__(256) void lowrank_kv_kernel(LowrankKvArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[TileSmem<D>::kElems];
   __shared__ float F[64 * 33];
-  const int64_t n_work = (int64_t)a.B * a.H * a.n_chunks;
+  const int64_t n_work = (int64_t)a.B * a.H * a.runs.n_runs;
   const int64_t wi = xcd_work_index(blockIdx.x, n_work);
   if (wi < 0) return;
-  const int chunk = (int)(wi % a.n_chunks);
-  const int64_t bh = wi / a.n_chunks;
+  const int run = (int)(wi % a.runs.n_runs);
+  const int64_t bh = wi / a.runs.n_runs;
   const int h = (int)(bh % a.H), b = (int)(bh / a.H);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int hf = lane >> 5, l32 = lane & 31;
@@ -58,9 +58,8 @@ __global__ __launch_bounds__(256) void lowrank_kv_kernel(LowrankKvArgs a) {
   TileLoader<D, 256> ld;
   const uint16_t* Kb = a.Kn + (int64_t)b * a.sk_b + (int64_t)h * a.sk_h;
   const uint16_t* Vb = a.V + (int64_t)b * a.sv_b + (int64_t)h * a.sv_h;
-  const int ntiles = (a.L + 63) / 64;
-  const int t_begin = chunk * a.chunk_tiles;
-  const int t_end = min(ntiles, t_begin + a.chunk_tiles);
+  int t_begin, t_end, tok_lo, tok_hi;  // tiles of the run, tokens of its chunk
+  run_extent(a.runs, a.L, run, t_begin, t_end, tok_lo, tok_hi);
   const int hw = a.Hg * a.Wg;
   for (int tl = t_begin; tl < t_end; ++tl) {
     const int tok0 = tl * 64;
@@ -73,7 +72,8 @@ __global__ __launch_bounds__(256) void lowrank_kv_kernel(LowrankKvArgs a) {
 #pragma unroll
       for (int s = 0; s < D / 16; ++s)
         acc = mfma32(as_bf16x8(pk[s]), lds_k_chunk<D>(tile, 32 * wv + l32, 2 * s + hf), acc);
-      const bool tok_ok = tok0 + 32 * wv + l32 < a.L;
+      const int tk = tok0 + 32 * wv + l32;
+      const bool tok_ok = tk >= tok_lo && tk < tok_hi;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int ri = 8 * (r >> 2) + 4 * hf + (r & 3);
@@ -85,7 +85,7 @@ __global__ __launch_bounds__(256) void lowrank_kv_kernel(LowrankKvArgs a) {
     for (int it = tid; it < 64 * np; it += 256) {
       const int tk = it / np, m = it - tk * np;
       const int tok = tok0 + tk;
-      if (tok >= a.L) continue;
+      if (tok < tok_lo || tok >= tok_hi) continue;
       const int axis = a.rope.axis[m];
       const int p = axis == 0 ? tok / hw : (axis == 1 ? (tok / a.Wg) % a.Hg : tok % a.Wg);
       const float2 cs = a.rope_tab[m * a.rope.max_ext + p];
@@ -112,7 +112,7 @@ __global__ __launch_bounds__(256) void lowrank_kv_kernel(LowrankKvArgs a) {
     }
   }
   if (wv < D / 32) {
-    float* out = a.partial + ((int64_t)bh * a.n_chunks + chunk) * 32 * D;
+    float* out = a.partial + ((int64_t)bh * a.runs.n_runs + run) * 32 * D;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int ri = 8 * (r >> 2) + 4 * hf + (r & 3);
@@ -121,25 +121,30 @@ __global__ __launch_bounds__(256) void lowrank_kv_kernel(LowrankKvArgs a) {
   }
 }
 
-__global__ void lowrank_finalize_kernel(const float* __restrict__ partial, int64_t BH, int n_chunks, int rank,
-                                        int D, RankRows rows, float* __restrict__ C_out, uint16_t* __restrict__ Ct_hi,
-                                        uint16_t* __restrict__ Ct_lo) {
+// One thread per (batch*head, chunk, rank slot, channel); the runs of the
+// chunk's window are summed in run order (bitwise reproducible).
+__global__ void lowrank_finalize_kernel(const float* __restrict__ partial, int64_t BH, RunGeo runs, int n_ar,
+                                        int window, int rank, int D, RankRows rows, float* __restrict__ C_out,
+                                        uint16_t* __restrict__ Ct_hi, uint16_t* __restrict__ Ct_lo) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= BH * 32 * D) return;
+  if (i >= BH * n_ar * 32 * D) return;
   const int d = (int)(i % D);
   const int r = (int)((i / D) % 32);
-  const int64_t bh = i / (32 * D);
+  const int64_t bc = i / (32 * D);  // (batch*head) * n_ar + chunk
+  const int c = (int)(bc % n_ar);
+  const int64_t bh = bc / n_ar;
   const int row = rows.row[r];
   float s = 0.f;
   if (row >= 0) {
-    const float* p = partial + (bh * n_chunks * 32 + row) * D + d;
-    for (int c = 0; c < n_chunks; ++c) s += p[(int64_t)c * 32 * D];
+    const int c0 = window > 0 ? max(0, c - window + 1) : 0;
+    const float* p = partial + (bh * runs.n_runs * 32 + row) * D + d;
+    for (int u = c0 * runs.runs_per_ar; u < (c + 1) * runs.runs_per_ar; ++u) s += p[(int64_t)u * 32 * D];
   }
-  if (C_out && r < rank) C_out[(bh * rank + r) * D + d] = s;
+  if (C_out && r < rank) C_out[(bc * rank + r) * D + d] = s;
   const __bf16 hi = (__bf16)s;
   const __bf16 lo = (__bf16)(s - (float)hi);
-  Ct_hi[(bh * D + d) * 32 + r] = __builtin_bit_cast(uint16_t, hi);
-  Ct_lo[(bh * D + d) * 32 + r] = __builtin_bit_cast(uint16_t, lo);
+  Ct_hi[(bc * D + d) * 32 + r] = __builtin_bit_cast(uint16_t, hi);
+  Ct_lo[(bc * D + d) * 32 + r] = __builtin_bit_cast(uint16_t, lo);
 }
 
 hipError_t launch_rope_table(const RopeThetas& th, int n, int max_ext, float2* tab, hipStream_t stream) {
@@ -150,7 +155,7 @@ hipError_t launch_rope_table(const RopeThetas& th, int n, int max_ext, float2* t
 }
 
 hipError_t launch_lowrank_kv(const LowrankKvArgs& a, int D, hipStream_t stream) {
-  const int64_t n_work = (int64_t)a.B * a.H * a.n_chunks;
+  const int64_t n_work = (int64_t)a.B * a.H * a.runs.n_runs;
   const int64_t grid = (n_work + kNumXcd - 1) / kNumXcd * kNumXcd;
   if (D == 128)
     hipLaunchKernelGGL(lowrank_kv_kernel<128>, dim3((unsigned)grid), dim3(256), 0, stream, a);
@@ -161,11 +166,12 @@ hipError_t launch_lowrank_kv(const LowrankKvArgs& a, int D, hipStream_t stream) 
   return hipGetLastError();
 }
 
-hipError_t launch_lowrank_finalize(const float* partial, int BH, int n_chunks, int rank, int D, const RankRows& rows,
-                                   float* C_out, uint16_t* Ct_hi, uint16_t* Ct_lo, hipStream_t stream) {
-  const int64_t total = (int64_t)BH * 32 * D;
+hipError_t launch_lowrank_finalize(const float* partial, int BH, const RunGeo& runs, int n_ar, int window, int rank,
+                                   int D, const RankRows& rows, float* C_out, uint16_t* Ct_hi, uint16_t* Ct_lo,
+                                   hipStream_t stream) {
+  const int64_t total = (int64_t)BH * n_ar * 32 * D;
   hipLaunchKernelGGL(lowrank_finalize_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, partial,
-                     (int64_t)BH, n_chunks, rank, D, rows, C_out, Ct_hi, Ct_lo);
+                     (int64_t)BH, runs, n_ar, window, rank, D, rows, C_out, Ct_hi, Ct_lo);
   return hipGetLastError();
 }
 

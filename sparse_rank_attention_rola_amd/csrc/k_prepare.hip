@@ -111,14 +111,13 @@ __global__ __launch_bounds__(256, 3) void prepare_stream_kernel(PrepareArgs a) {
   // workgroups read whole token rows of K and V (DRAM-friendly).
   const int64_t nbh = (int64_t)a.B * a.H;
   const int64_t bh = blockIdx.x % nbh;
-  const int chunk = (int)(blockIdx.x / nbh);
+  const int run = (int)(blockIdx.x / nbh);
   const int h = (int)(bh % a.H), b = (int)(bh / a.H);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hf = lane >> 5, l32 = lane & 31;
-  const int ntiles = (a.L + 63) / 64;
-  const int t_begin = chunk * a.chunk_tiles;
-  const int t_end = min(ntiles, t_begin + a.chunk_tiles);
+  int t_begin, t_end, tok_lo, tok_hi;  // tiles of the run, tokens of its chunk
+  run_extent(a.runs, a.L, run, t_begin, t_end, tok_lo, tok_hi);
   const int hw = a.Hg * a.Wg;
 
   const uint16_t* Knb = a.Kn + (int64_t)b * a.sk_b + (int64_t)h * a.sk_h;
@@ -230,7 +229,7 @@ __global__ __launch_bounds__(256, 3) void prepare_stream_kernel(PrepareArgs a) {
                                                             acc[rh], 0, 0, 0);
       }
       const int tk = 16 * wv + l16;
-      const bool tok_ok = tok0 + tk < a.L;
+      const bool tok_ok = tok0 + tk >= tok_lo && tok0 + tk < tok_hi;
       uint16_t fh[8], fl[8];
 #pragma unroll
       for (int rh = 0; rh < 2; ++rh) {
@@ -334,14 +333,14 @@ __global__ __launch_bounds__(256, 3) void prepare_stream_kernel(PrepareArgs a) {
   // partial C of this run in slot order: lane holds slot l32, channels
   // 32 wv + 8 (r / 4) + 4 hf + r % 4
   if (wv < D / 32) {
-    float* out = a.partial + ((int64_t)bh * a.n_chunks + chunk) * 32 * D;
+    float* out = a.partial + ((int64_t)bh * a.runs.n_runs + run) * 32 * D;
 #pragma unroll
     for (int r = 0; r < 16; ++r) out[l32 * D + 32 * wv + 8 * (r >> 2) + 4 * hf + (r & 3)] = cacc[r];
   }
 }
 
 hipError_t launch_prepare_stream(const PrepareArgs& a, int D, hipStream_t stream) {
-  const dim3 grid((unsigned)((int64_t)a.n_chunks * a.B * a.H));
+  const dim3 grid((unsigned)((int64_t)a.runs.n_runs * a.B * a.H));
   const bool pool = a.kmean != nullptr;
   if (D == 128 && pool)
     hipLaunchKernelGGL((prepare_stream_kernel<128, true>), grid, dim3(256), 0, stream, a);

@@ -9,6 +9,29 @@
 
 namespace sd {
 
+// Runs of 64-token tiles, each accumulating one partial low-rank state.
+// Autoregressive chunk c holds tokens [c * ar_tokens, min(L, (c+1) * ar_tokens))
+// (one chunk of L tokens without a causal window) and is split into
+// runs_per_ar runs of at most run_tiles tiles, counted from the tile that
+// holds its first token; a run counts only the tokens of its chunk, so a
+// tile across a chunk boundary is read by both chunks' runs.
+struct RunGeo {
+  int ar_tokens;
+  int runs_per_ar;
+  int run_tiles;
+  int n_runs;  // runs per (batch, head) = chunks * runs_per_ar
+};
+
+__host__ __device__ inline void run_extent(const RunGeo& g, int L, int run, int& t_begin, int& t_end, int& lo,
+                                           int& hi) {
+  const int c = run / g.runs_per_ar, j = run - c * g.runs_per_ar;
+  lo = c * g.ar_tokens;
+  hi = lo + g.ar_tokens < L ? lo + g.ar_tokens : L;
+  const int ta = lo / 64, tb = (hi + 63) / 64;
+  t_begin = ta + j * g.run_tiles < tb ? ta + j * g.run_tiles : tb;
+  t_end = t_begin + g.run_tiles < tb ? t_begin + g.run_tiles : tb;
+}
+
 // Arguments of the attention-family kernels (sparse branch, low-rank query
 // output, fused layer). Strides are in elements.
 struct AttnArgs {
@@ -36,6 +59,11 @@ struct AttnArgs {
   // gate
   const float* g;
   int64_t g_sb, g_sl, g_sh;
+  // causal window: query i sees the keys of autoregressive chunks
+  // i/ar_tokens - ar_window + 1 .. i/ar_tokens (ar_window 0: all earlier
+  // chunks); ar_tokens = L and ar_window = 0 without one. The state of the
+  // chunk is Ct_*[(b*H + h) * n_ar + chunk].
+  int ar_tokens, ar_window;
 };
 
 struct LowrankKvArgs {
@@ -43,14 +71,13 @@ struct LowrankKvArgs {
   const uint16_t* V;
   int64_t sk_b, sk_l, sk_h, sv_b, sv_l, sv_h;
   int B, H, L, Hg, Wg;
-  int chunk_tiles;  // 64-token tiles per workgroup
-  int n_chunks;
+  RunGeo runs;
   const uint16_t* Pk;
   int64_t P_hs;
   int rank;
   const float2* rope_tab;
   RopeArgs rope;
-  float* partial;  // [B*H, n_chunks, 32, D]
+  float* partial;  // [B*H, runs.n_runs, 32, D]
 };
 
 // One streaming pass over Kn, V: block means of K (when Kn is K and kmean is
@@ -63,8 +90,7 @@ struct PrepareArgs {
   int64_t sq_b, sq_l, sq_h, sk_b, sk_l, sk_h, sv_b, sv_l, sv_h;
   int B, H, L, Nq, Nk, block_q, Hg, Wg;
   float rcp_hw, rcp_wg;  // 1 / (Hg * Wg) and 1 / Wg rounded to float
-  int chunk_tiles;  // 64-token tiles per workgroup (a multiple of block_q / 64)
-  int n_chunks;
+  RunGeo runs;  // without a causal window, run_tiles is a multiple of block_q / 64
   const uint16_t* Pk;
   int64_t P_hs;
   int rank;
@@ -76,7 +102,7 @@ struct PrepareArgs {
   int8_t slot_pair[16];
   uint32_t slot_mask;  // bit i set where slot_rank[i] >= 0
   double* kmean;   // [B*H, Nk, D] or null
-  float* partial;  // [B*H, n_chunks, 32, D]
+  float* partial;  // [B*H, runs.n_runs, 32, D]
 };
 
 // Fused q/k RMSNorm + backbone 3D RoPE.
@@ -119,7 +145,24 @@ hipError_t launch_pool_blocks(const uint16_t* X, int64_t sb, int64_t sl, int64_t
                               int bs, double* out, hipStream_t stream);
 hipError_t launch_block_scores(const double* qmean, const double* kmean, int BH, int Nq, int Nk, int D, double* S,
                                hipStream_t stream);
-hipError_t launch_topk_rows(const double* S, int64_t n_rows, int C, int k, int32_t* idx, hipStream_t stream);
+// Which key blocks a row of the block map may keep, and where it goes.
+// Row r of the map belongs to query block r % Nq; it is computed from row
+// r % s_rows of S and written to every one of n_rep copies of the map
+// (rep_stride int32 apart). Key block c is allowed for query block b when
+// some query of b sees some key of c under the causal window (AttnArgs).
+struct MapRule {
+  int Nq, bq, bk, L;
+  int ar_tokens, ar_window;
+  int64_t s_rows;
+  int n_rep;
+  int64_t rep_stride;
+};
+hipError_t launch_topk_rows(const double* S, int64_t n_rows, int C, int k, const MapRule& rule, int32_t* idx,
+                            hipStream_t stream);
+// Fixed spatio-temporal scores: S[b][c] = -|centroid_q(b) - centroid_k(c)|^2
+// in latent (t, h, w) units; cq / ck: scratch of 3 * Nq / 3 * Nk doubles.
+hipError_t launch_fixed_scores(int L, int Nq, int Nk, int bq, int bk, int Hg, int Wg, double* cq, double* ck,
+                               double* S, hipStream_t stream);
 hipError_t launch_sparse_attn(const AttnArgs& a, int D, int BQ, hipStream_t stream);
 hipError_t launch_lowrank_query(const AttnArgs& a, int D, int BQ, hipStream_t stream);
 hipError_t launch_rola_fused(const AttnArgs& a, int D, int BQ, hipStream_t stream);
@@ -133,8 +176,12 @@ hipError_t launch_lowrank_kv(const LowrankKvArgs& a, int D, hipStream_t stream);
 struct RankRows {
   int8_t row[32];
 };
-hipError_t launch_lowrank_finalize(const float* partial, int BH, int n_chunks, int rank, int D, const RankRows& rows,
-                                   float* C_out, uint16_t* Ct_hi, uint16_t* Ct_lo, hipStream_t stream);
+// C of autoregressive chunk c = the sum, in run order, of the partial states
+// of chunks max(0, c - window + 1) .. c (window 0: 0 .. c); outputs per
+// (batch, head, chunk): C_out [rank][D] f32 (optional), Ct_hi/lo [D][32].
+hipError_t launch_lowrank_finalize(const float* partial, int BH, const RunGeo& runs, int n_ar, int window, int rank,
+                                   int D, const RankRows& rows, float* C_out, uint16_t* Ct_hi, uint16_t* Ct_lo,
+                                   hipStream_t stream);
 hipError_t launch_prepare_stream(const PrepareArgs& a, int D, hipStream_t stream);
 hipError_t launch_gate_fuse(const void* Os, const void* Olr, int in_f32, const float* g, int64_t g_sb, int64_t g_sl,
                             int64_t g_sh, void* O, int B, int L, int H, int D, int64_t so_b, int64_t so_l,

@@ -246,3 +246,27 @@ def test_rola_validation():
     assert call(ws_bytes=need - 1) == sd.SD_ERR_WORKSPACE
     assert call(shape=_shape(grid=(1, 1, 1))) == sd.SD_ERR_INVALID_ARG
     assert lib.sd_rola_workspace_size(ctypes.byref(s), ctypes.byref(p), 0) == 0
+
+
+@host_only
+def test_variant_fields_validation():
+    lib = sd.lib()
+
+    def shp(select=0, chunk=0, window=0, **kw):
+        s = _shape(**kw)
+        s.select, s.chunk_tokens, s.window = select, chunk, window
+        return s
+
+    assert _call_select(shp(select=2)) == sd.SD_ERR_INVALID_ARG
+    assert _call_select(shp(chunk=-1)) == sd.SD_ERR_INVALID_ARG
+    assert _call_select(shp(chunk=256, window=-1)) == sd.SD_ERR_INVALID_ARG
+    assert _call_select(shp(window=2)) == sd.SD_ERR_INVALID_ARG  # a window needs chunks
+    assert _call_select(shp(select=1, grid=(1, 1, 1))) == sd.SD_ERR_INVALID_ARG  # the fixed pattern needs the grid
+    assert _call_select(shp(chunk=1, L=8192, grid=(8, 32, 32))) == sd.SD_ERR_UNSUPPORTED  # > 4096 chunks
+    # a causal window sizes one low-rank state per chunk
+    p, keep = _lr()
+    one = lib.sd_rola_workspace_size(ctypes.byref(shp()), ctypes.byref(p), 4)
+    many = lib.sd_rola_workspace_size(ctypes.byref(shp(chunk=256, window=2)), ctypes.byref(p), 4)
+    assert many > one > 0
+    # chunks longer than the sequence are the bidirectional layer
+    assert lib.sd_rola_workspace_size(ctypes.byref(shp(chunk=5000)), ctypes.byref(p), 4) == one
