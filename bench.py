@@ -9,7 +9,10 @@ blocks, sparsity 0.97 (36 of 1182 key blocks kept per query block), rank 32
 bf16 activation. One step = quantise the activation, then the fused layer
 (block map + low-rank state, then the fused sparse/low-rank/gate kernel). The
 W8A8 QKV projection that consumes the quantised activation (75600 x 15360 x
-5120) is timed on its own after the steps and reported beside them.
+5120) is timed on its own after the steps and reported beside them, as are
+the same layer with the fixed spatio-temporal selector and under a causal
+window (3-frame chunks), and the whole attention block in FP8 deployment
+precision.
 Inputs are seeded synthetic tensors of those shapes, resident in HBM before
 the timed region.
 
@@ -52,7 +55,7 @@ def kept_pair_flops(idx, L, bq, bk, d):
     nq = np.minimum(bq, L - np.arange(idx.shape[2]) * bq).astype(np.float64)
     nkb = -(-L // bk)
     nk = np.minimum(bk, L - np.arange(nkb) * bk).astype(np.float64)
-    keys = nk[idx].sum(axis=-1)  # [B, H, Nq]
+    keys = np.where(idx >= 0, nk[np.clip(idx, 0, None)], 0.0).sum(axis=-1)  # [B, H, Nq]; -1 keeps nothing
     return float(4.0 * d * (keys * nq[None, None, :]).sum())
 
 
@@ -158,6 +161,8 @@ def main():
     ap.add_argument("--no-gemm", action="store_true", help="skip the FP8 projection measurement")
     ap.add_argument("--no-block", action="store_true", help="skip the deployment block measurement")
     ap.add_argument("--block-timesteps", type=int, default=3, help="timesteps of the deployment block")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the fixed-selector and causal-window measurements")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter calibration)")
     ap.add_argument("--trace-summary", metavar="DB", help="print a kernel table of a rocprofv3 trace and exit")
@@ -247,6 +252,39 @@ def main():
     t_prep = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     t_apply = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
     t_layer = float(np.mean([e[1].elapsed_time(e[3]) for e in evs]))
+
+    # The same layer with the other selector and under a causal window
+    # (autoregressive use: chunks of 3 latent frames, a window of 2 chunks and
+    # the whole prefix), each with its own block map and workspace.
+    variants = None
+    if not args.no_variants:
+        variants = {}
+        ct = 3 * cfg.Hg * cfg.Wg
+        for name, var in (("fixed spatio-temporal selector", dict(select="fixed")),
+                          ("causal window, 3-frame chunks, window 2", dict(chunk_tokens=ct, window=2)),
+                          ("causal prefix, 3-frame chunks", dict(chunk_tokens=ct, window=0))):
+            wsv = sd.rola_workspace(Q, lr, k, grid=grid, block_q=cfg.block_q, **var)
+            idv = torch.empty_like(idx)
+            for _ in range(max(1, args.warmup)):
+                sd.sd_rola_prepare(Q, K, V, lr, k, wsv, grid=grid, block_q=cfg.block_q, idx_out=idv, **var)
+                sd.sd_rola_apply(Q, K, V, gd, lr, k, wsv, grid=grid, block_q=cfg.block_q, out=O, idx=idv, **var)
+            torch.cuda.synchronize()
+            n_v = max(3, args.steps // 2)
+            vev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_v)]
+            for e in vev:
+                e[0].record()
+                sd.sd_rola_prepare(Q, K, V, lr, k, wsv, grid=grid, block_q=cfg.block_q, idx_out=idv, **var)
+                e[1].record()
+                sd.sd_rola_apply(Q, K, V, gd, lr, k, wsv, grid=grid, block_q=cfg.block_q, out=O, idx=idv, **var)
+                e[2].record()
+            torch.cuda.synchronize()
+            tp = float(np.mean([e[0].elapsed_time(e[1]) for e in vev]))
+            ta = float(np.mean([e[1].elapsed_time(e[2]) for e in vev]))
+            fl = kept_pair_flops(idv.cpu().numpy(), cfg.L, cfg.block_q, cfg.block_k, cfg.d)
+            variants[name] = {"ms_layer": round(tp + ta, 4), "ms_prepare": round(tp, 4), "ms_apply": round(ta, 4),
+                              "kept_pair_tflops": round(fl / (ta * 1e-3) / 1e12, 1)}
+            log(f"variant {name}: {tp + ta:.3f} ms")
+            del wsv, idv
 
     # W8A8 FP8 QKV projection of the same layer (the step that consumes the
     # quantised activation): weights quantised per output channel once,
@@ -389,6 +427,7 @@ def main():
                      "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
                      "algorithmic_flops_per_launch": flops},
+        "variants_720p": variants,
         "w8a8_qkv_projection": gemm,
         "deployment_block_720p": block,
         "cpu_baseline": cpu,

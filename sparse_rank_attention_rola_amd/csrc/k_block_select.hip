@@ -186,8 +186,8 @@ __global__ __launch_bounds__(256) void topk_rows_kernel(const double* __restrict
   // chunks [ck0, ck1] meet [cq0 - W + 1, cq1], the chunks the queries of qb
   // see (no lower limit for W = 0); without a window every block is allowed.
   const int qb = (int)(row % rule.Nq);
-  int cq0, cq1;
-  chunk_span(qb * rule.bq, min(rule.L, (qb + 1) * rule.bq), rule.ar_tokens, cq0, cq1);
+  int cq0 = 0, cq1 = 0;
+  if (rule.ar_tokens < rule.L) chunk_span(qb * rule.bq, min(rule.L, (qb + 1) * rule.bq), rule.ar_tokens, cq0, cq1);
   const int lo_chunk = rule.ar_window > 0 ? cq0 - rule.ar_window + 1 : -1;
   const double* Srow = S + (row % rule.s_rows) * (int64_t)C;
   uint64_t key[NPL];
@@ -197,7 +197,7 @@ __global__ __launch_bounds__(256) void topk_rows_kernel(const double* __restrict
   for (int j = 0; j < NPL; ++j) {
     const int c = j * 64 + lane;
     bool ok = row_ok && c < C;
-    if (ok) {
+    if (ok && rule.ar_tokens < rule.L) {
       int ck0, ck1;
       chunk_span(c * rule.bk, min(rule.L, (c + 1) * rule.bk), rule.ar_tokens, ck0, ck1);
       ok = ck0 <= cq1 && ck1 >= lo_chunk;
