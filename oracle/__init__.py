@@ -21,7 +21,10 @@ Sources (the page, then the section / equation):
     for the producer steps of the deployment block (block.py);
   * the same write-up, section 2.1 (a fixed spatio-temporal pattern as the
     selector) and section 4 (the causal-window restriction for
-    autoregressive video diffusion), for the variants (variants.py).
+    autoregressive video diffusion), for the variants (variants.py);
+  * README_zh, distillation and operators sections (training the sparse
+    student needs a backward kernel of its sparse + low-rank attention),
+    for the backward (backward.py): the exact derivative of the forward.
 
 Where the pages leave a step open, the reading taken is stated in the
 docstring of the function that takes it.
@@ -74,6 +77,12 @@ from .variants import (  # noqa: F401
     sparse_attention_masked,
     lowrank_states_masked,
     rola_attention_head_variant,
+)
+from .backward import (  # noqa: F401
+    phi_elu1_grad,
+    rope_rotate_back,
+    sparse_attention_backward,
+    rola_backward_head,
 )
 from .gemm import (  # noqa: F401
     quant_weight_per_channel,
