@@ -286,6 +286,34 @@ int sd_rola_apply(const sd_attn_shape* shape, const sd_lowrank_params* lr, const
                   int64_t g_stride_h, int k_keep, float sm_scale, void* O, const int32_t* idx, void* ws,
                   size_t ws_bytes, void* stream);
 
+/* ---- (8) backward of the fused layer -----------------------------------------
+ * SparkDiffusion README_zh, distillation and operators sections: training
+ * the sparse student needs a backward kernel of its sparse + low-rank
+ * attention. The gradients are the exact derivatives of the forward of
+ * sd_rola_attention (robotworld.top write-up, section 2.1, under the causal
+ * window of the shape when it has one) with the block map `idx` held fixed
+ * (the map the forward used, e.g. idx_out of sd_rola_prepare):
+ *   dO: bf16 [B, L, H, d] at the so_* strides, the gradient of O.
+ *   dQ, dK, dV: f32 [B, L, H, d] contiguous (required, fully written).
+ *   dQn, dKn: f32 [B, L, H, d] contiguous, the gradient reaching the
+ *     low-rank branch's separate inputs; give them exactly when Qn / Kn are
+ *     given. With Qn (Kn) NULL the branch reads Q (K) and its gradient is
+ *     added into dQ (dK).
+ *   dPq, dPk: f32 [rank, d] (P_head_stride 0) or [H, rank, d], or NULL to
+ *     skip them.
+ *   dg: f32 at the gate's strides (g_stride_h 0: summed over the heads), or
+ *     NULL to skip it.
+ * The forward quantities it needs (low-rank state, sparse output, RMS,
+ * log-sum-exp) are recomputed inside. All sums run in a fixed order (the
+ * result is bitwise reproducible). Needs (L + 64) * max(H * d, sq_l) * 2
+ * < 2^32. */
+size_t sd_rola_backward_workspace_size(const sd_attn_shape* shape, const sd_lowrank_params* lr, int k_keep);
+int sd_rola_backward(const sd_attn_shape* shape, const sd_lowrank_params* lr, const void* Q, const void* K,
+                     const void* V, const void* Qn, const void* Kn, const float* g, int64_t g_stride_b,
+                     int64_t g_stride_l, int64_t g_stride_h, int k_keep, float sm_scale, const int32_t* idx,
+                     const void* dO, float* dQ, float* dK, float* dV, float* dQn, float* dKn, float* dPq,
+                     float* dPk, float* dg, void* ws, size_t ws_bytes, void* stream);
+
 const char* sd_status_string(int status);
 const char* sd_last_error(void);
 

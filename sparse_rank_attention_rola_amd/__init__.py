@@ -32,7 +32,7 @@ EXPORTED = [
     "sd_keep_count", "sd_rope_default", "sd_block_select_workspace_size", "sd_block_select",
     "sd_sparse_attn", "sd_lowrank_workspace_size", "sd_lowrank_attn", "sd_gate_fuse",
     "sd_quant_fp8_per_token", "sd_quant_fp8_gate", "sd_gemm_fp8_w8a8", "sd_qk_norm_rope", "sd_rola_workspace_size", "sd_rola_attention", "sd_rola_prepare",
-    "sd_rola_apply", "sd_status_string", "sd_last_error",
+    "sd_rola_apply", "sd_rola_backward_workspace_size", "sd_rola_backward", "sd_status_string", "sd_last_error",
 ]
 
 
@@ -87,6 +87,9 @@ def _declare(lib):
         "sd_rola_attention": (i32, [S, LR, P, P, P, P, P, P, i64, i64, i64, i32, f32, P, P, P, sz, P]),
         "sd_rola_prepare": (i32, [S, LR, P, P, P, P, P, i32, P, P, sz, P]),
         "sd_rola_apply": (i32, [S, LR, P, P, P, P, P, i64, i64, i64, i32, f32, P, P, P, sz, P]),
+        "sd_rola_backward_workspace_size": (sz, [S, LR, i32]),
+        "sd_rola_backward": (i32, [S, LR, P, P, P, P, P, P, i64, i64, i64, i32, f32, P, P, P, P, P, P, P, P, P, P,
+                                   P, sz, P]),
         "sd_status_string": (ctypes.c_char_p, [i32]),
         "sd_last_error": (ctypes.c_char_p, []),
     }
@@ -399,4 +402,40 @@ def sd_rola_apply(Q, K, V, g, lr: LowrankParams, k_keep, workspace, *, grid, blo
     _check(lib().sd_rola_apply(ctypes.byref(s), ctypes.byref(lr.p), _ptr(Q), _ptr(K), _ptr(V), _ptr(Qn), _ptr(g), gb,
                                gl, gh, int(k_keep), float(scale), _ptr(out), _ptr(idx), _ptr(workspace),
                                workspace.numel(), _stream_ptr(stream)))
+    return out
+
+
+def sd_rola_backward(Q, K, V, g, lr: LowrankParams, k_keep, idx, dO, *, grid, block_q=128, Qn=None, Kn=None,
+                     sm_scale=None, want_dP=True, want_dg=True, chunk_tokens=0, window=0, workspace=None,
+                     stream=None):
+    """Gradients of the fused layer for the bf16 output gradient dO (block
+    map idx held fixed). Returns a dict of f32 tensors: dQ, dK, dV
+    [B, L, H, d]; dQn, dKn (only with Qn / Kn; otherwise that gradient is
+    in dQ / dK); dPq, dPk ([rank, d], or [H, rank, d] with per-head
+    projections); dg (the shape of g)."""
+    torch = _torch()
+    B, L, H, d = Q.shape
+    s = make_shape(Q, K, V, dO, block_q=block_q, grid=grid, chunk_tokens=chunk_tokens, window=window)
+    f32 = dict(dtype=torch.float32, device=Q.device)
+    out = {n: torch.empty((B, L, H, d), **f32) for n in ("dQ", "dK", "dV")}
+    out["dQn"] = torch.empty((B, L, H, d), **f32) if Qn is not None else None
+    out["dKn"] = torch.empty((B, L, H, d), **f32) if Kn is not None else None
+    rank = lr.p.rank
+    p_shape = (rank, d) if lr.p.P_head_stride == 0 else (H, rank, d)
+    out["dPq"] = torch.empty(p_shape, **f32) if want_dP else None
+    out["dPk"] = torch.empty(p_shape, **f32) if want_dP else None
+    if want_dg:
+        out["dg"] = torch.empty_strided(g.shape, g.stride(), **f32)
+    else:
+        out["dg"] = None
+    if workspace is None:
+        workspace = _workspace(lib().sd_rola_backward_workspace_size(ctypes.byref(s), ctypes.byref(lr.p),
+                                                                     int(k_keep)), Q.device)
+    scale = sm_scale if sm_scale is not None else 1.0 / math.sqrt(d)
+    gb, gl, gh = _gate_strides(g, B, L, H)
+    _check(lib().sd_rola_backward(ctypes.byref(s), ctypes.byref(lr.p), _ptr(Q), _ptr(K), _ptr(V), _ptr(Qn), _ptr(Kn),
+                                  _ptr(g), gb, gl, gh, int(k_keep), float(scale), _ptr(idx), _ptr(dO),
+                                  _ptr(out["dQ"]), _ptr(out["dK"]), _ptr(out["dV"]), _ptr(out["dQn"]),
+                                  _ptr(out["dKn"]), _ptr(out["dPq"]), _ptr(out["dPk"]), _ptr(out["dg"]),
+                                  _ptr(workspace), workspace.numel(), _stream_ptr(stream)))
     return out

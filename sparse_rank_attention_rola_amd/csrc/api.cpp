@@ -660,14 +660,10 @@ int check_apply_extra(const void* O, const float* g_ptr, float sm_scale, int64_t
   return SD_OK;
 }
 
-// Block map and low-rank state: one streaming pass over Q, K (Kn), V for the
-// block means and partial states, then scores, top-k and the state sum.
-int run_prepare(const sd_attn_shape* s, const Geo& g, const sd_lowrank_params* lr, const void* Q, const void* K,
-                const void* V, const void* Kn, int k_keep, int32_t* idx, const RolaWs& w, hipStream_t st) {
-  sd::RopeThetas th{};
-  for (int i = 0; i < lr->n_rope; ++i) th.theta[i] = lr->rope[i].theta;
-  hipError_t e = sd::launch_rope_table(th, lr->n_rope, max_extent(s), w.lr.rope_tab, st);
-  if (e != hipSuccess) return hip_fail(e, "rope table");
+// Arguments of the stream pass (the low-rank state of every run of tiles)
+// and the rank row of each of its slots.
+sd::PrepareArgs prepare_args(const sd_attn_shape* s, const Geo& g, const sd_lowrank_params* lr, const void* Q,
+                             const void* K, const void* V, const void* Kn, const LowrankWs& w, sd::RankRows* rows) {
   sd::PrepareArgs a{};
   a.Q = static_cast<const uint16_t*>(Q);
   a.K = static_cast<const uint16_t*>(K);
@@ -692,16 +688,15 @@ int run_prepare(const sd_attn_shape* s, const Geo& g, const sd_lowrank_params* l
   a.Wg = s->Wg;
   a.rcp_hw = 1.0f / (float)(s->Hg * s->Wg);
   a.rcp_wg = 1.0f / (float)s->Wg;
-  a.runs = w.lr.runs;
+  a.runs = w.runs;
   a.Pk = static_cast<const uint16_t*>(lr->Pk);
   a.P_hs = lr->P_head_stride;
   a.rank = lr->rank;
-  a.rope_tab = w.lr.rope_tab;
+  a.rope_tab = w.rope_tab;
   a.rope = rope_args(lr, s);
   // rank slots: each RoPE pair takes the next two slots, then each rank
   // outside every pair one slot; the rest stay empty
-  sd::RankRows rows{};
-  for (int r = 0; r < 32; ++r) rows.row[r] = -1;
+  for (int r = 0; r < 32; ++r) rows->row[r] = -1;
   for (int i = 0; i < 32; ++i) a.slot_rank[i] = -1;
   for (int p = 0; p < 16; ++p) a.slot_pair[p] = -1;
   int nslot = 0;
@@ -709,19 +704,40 @@ int run_prepare(const sd_attn_shape* s, const Geo& g, const sd_lowrank_params* l
     a.slot_pair[nslot / 2] = (int8_t)m;
     for (int k = 0; k < 2; ++k) {
       a.slot_rank[nslot] = (int8_t)(lr->rope[m].dim + k);
-      rows.row[lr->rope[m].dim + k] = (int8_t)nslot;
+      rows->row[lr->rope[m].dim + k] = (int8_t)nslot;
       ++nslot;
     }
   }
   for (int r = 0; r < lr->rank; ++r)
-    if (rows.row[r] < 0) {
+    if (rows->row[r] < 0) {
       a.slot_rank[nslot] = (int8_t)r;
-      rows.row[r] = (int8_t)nslot;
+      rows->row[r] = (int8_t)nslot;
       ++nslot;
     }
   a.slot_mask = 0;
   for (int i = 0; i < 32; ++i)
     if (a.slot_rank[i] >= 0) a.slot_mask |= 1u << i;
+  a.kmean = nullptr;
+  a.partial = w.partial;
+  return a;
+}
+
+int run_rope_table(const sd_attn_shape* s, const sd_lowrank_params* lr, float2* tab, hipStream_t st) {
+  sd::RopeThetas th{};
+  for (int i = 0; i < lr->n_rope; ++i) th.theta[i] = lr->rope[i].theta;
+  const hipError_t e = sd::launch_rope_table(th, lr->n_rope, max_extent(s), tab, st);
+  if (e != hipSuccess) return hip_fail(e, "rope table");
+  return SD_OK;
+}
+
+// Block map and low-rank state: one streaming pass over Q, K (Kn), V for the
+// block means and partial states, then scores, top-k and the state sum.
+int run_prepare(const sd_attn_shape* s, const Geo& g, const sd_lowrank_params* lr, const void* Q, const void* K,
+                const void* V, const void* Kn, int k_keep, int32_t* idx, const RolaWs& w, hipStream_t st) {
+  int rc = run_rope_table(s, lr, w.lr.rope_tab, st);
+  if (rc) return rc;
+  sd::RankRows rows;
+  sd::PrepareArgs a = prepare_args(s, g, lr, Q, K, V, Kn, w.lr, &rows);
   // The scored selector needs the block means: those of K come from the
   // stream pass when it reads K itself and its runs are whole key blocks
   // (no causal window), else from the pooling kernel. The fixed pattern
@@ -729,7 +745,7 @@ int run_prepare(const sd_attn_shape* s, const Geo& g, const sd_lowrank_params* l
   const bool scored = g.select == SD_SELECT_TOPK;
   const bool k_in_stream = scored && a.Kn == a.K && g.n_ar == 1;
   a.kmean = k_in_stream ? w.sel.kmean : nullptr;
-  a.partial = w.lr.partial;
+  hipError_t e;
   if (scored) {
     e = sd::launch_pool_blocks(a.Q, s->sq_b, s->sq_l, s->sq_h, g.B, g.L, g.H, g.D, g.bq, w.sel.qmean, st);
     if (e != hipSuccess) return hip_fail(e, "pool Q");
@@ -740,7 +756,7 @@ int run_prepare(const sd_attn_shape* s, const Geo& g, const sd_lowrank_params* l
   }
   e = sd::launch_prepare_stream(a, g.D, st);
   if (e != hipSuccess) return hip_fail(e, "prepare pass");
-  int rc = run_scores_topk(s, g, k_keep, idx, w.sel, st);
+  rc = run_scores_topk(s, g, k_keep, idx, w.sel, st);
   if (rc) return rc;
   e = sd::launch_lowrank_finalize(w.lr.partial, g.B * g.H, w.lr.runs, g.n_ar, g.win, lr->rank, g.D, rows, nullptr,
                                   w.lr.ct_hi, w.lr.ct_lo, st);
@@ -819,6 +835,244 @@ int sd_rola_attention(const sd_attn_shape* shape, const sd_lowrank_params* lr, c
   if ((rc = run_apply(shape, g, lr, Q, K, V, Qn, g_ptr, g_stride_b, g_stride_l, g_stride_h, k_keep, sm_scale, O, idx,
                       w, st)))
     return rc;
+  return ok();
+}
+
+}  // extern "C"
+
+namespace {
+
+// Workspace of the backward (sizes only when ws is NULL).
+struct BwdWs {
+  LowrankWs lr;
+  float* C;  // [B*H, n_ar, rank, D]
+  float *Os, *rms, *lse, *Dd, *dg_head, *qt, *dy, *da, *db, *dQn_tmp;
+  uint16_t* dOs;
+  float* dC_part;
+  sd::RunGeo dC_runs;
+  float* dC;
+  uint16_t *dCt_hi, *dCt_lo;
+  float* dP_part;
+  sd::RunGeo dP_runs;
+  int32_t *tlist, *toff;
+  size_t bytes;
+};
+
+BwdWs carve_bwd(void* ws, const Geo& g, const sd_attn_shape* shape, const sd_lowrank_params* lr, int k_keep) {
+  Carve c(ws);
+  BwdWs w;
+  const size_t BH = (size_t)g.B * g.H, rows = BH * g.L;
+  w.lr = carve_lowrank(c, g, shape, prepare_runs(g));
+  w.C = static_cast<float*>(c.take(sizeof(float) * BH * g.n_ar * 32 * g.D));
+  w.Os = static_cast<float*>(c.take(sizeof(float) * rows * g.D));
+  w.rms = static_cast<float*>(c.take(sizeof(float) * rows));
+  w.lse = static_cast<float*>(c.take(sizeof(float) * rows));
+  w.Dd = static_cast<float*>(c.take(sizeof(float) * rows));
+  w.dg_head = static_cast<float*>(c.take(sizeof(float) * rows));
+  w.qt = static_cast<float*>(c.take(sizeof(float) * rows * 32));
+  w.dy = static_cast<float*>(c.take(sizeof(float) * rows * g.D));
+  w.da = static_cast<float*>(c.take(sizeof(float) * rows * 32));
+  w.db = static_cast<float*>(c.take(sizeof(float) * rows * 32));
+  w.dQn_tmp = static_cast<float*>(c.take(sizeof(float) * rows * g.D));
+  w.dOs = static_cast<uint16_t*>(c.take(sizeof(uint16_t) * rows * g.D));
+  w.dC_runs = make_runs(g, 2048, 1);
+  w.dC_part = static_cast<float*>(c.take(sizeof(float) * BH * w.dC_runs.n_runs * 32 * g.D));
+  w.dC = static_cast<float*>(c.take(sizeof(float) * BH * g.n_ar * 32 * g.D));
+  w.dCt_hi = static_cast<uint16_t*>(c.take(sizeof(uint16_t) * BH * g.n_ar * g.D * 32));
+  w.dCt_lo = static_cast<uint16_t*>(c.take(sizeof(uint16_t) * BH * g.n_ar * g.D * 32));
+  Geo whole = g;  // one run set over the whole sequence for the projection gradients
+  whole.n_ar = 1;
+  whole.ar = g.L;
+  w.dP_runs = make_runs(whole, 2048, 1);
+  w.dP_part = static_cast<float*>(c.take(sizeof(float) * BH * w.dP_runs.n_runs * 32 * g.D));
+  w.tlist = static_cast<int32_t*>(c.take(sizeof(int32_t) * BH * g.Nq * (size_t)k_keep));
+  w.toff = static_cast<int32_t*>(c.take(sizeof(int32_t) * BH * (g.Nk + 1)));
+  (void)lr;
+  w.bytes = align_up(c.off);
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sd_rola_backward_workspace_size(const sd_attn_shape* shape, const sd_lowrank_params* lr, int k_keep) {
+  Geo g;
+  if (check_shape(shape, &g, true)) return 0;
+  if (k_keep < 1 || k_keep > g.Nk) return 0;
+  return carve_bwd(nullptr, g, shape, lr, k_keep).bytes;
+}
+
+int sd_rola_backward(const sd_attn_shape* shape, const sd_lowrank_params* lr, const void* Q, const void* K,
+                     const void* V, const void* Qn, const void* Kn, const float* g_ptr, int64_t g_stride_b,
+                     int64_t g_stride_l, int64_t g_stride_h, int k_keep, float sm_scale, const int32_t* idx,
+                     const void* dO, float* dQ, float* dK, float* dV, float* dQn, float* dKn, float* dPq, float* dPk,
+                     float* dg, void* ws, size_t ws_bytes, void* stream) {
+  Geo g;
+  int rc;
+  if ((rc = check_shape(shape, &g, true))) return rc;
+  if ((rc = check_lowrank(lr, g))) return rc;
+  if ((rc = check_dev_ptr(Q, "Q")) || (rc = check_dev_ptr(K, "K")) || (rc = check_dev_ptr(V, "V")) ||
+      (rc = check_dev_ptr(idx, "idx", 4)) || (rc = check_dev_ptr(dO, "dO")) || (rc = check_dev_ptr(dQ, "dQ")) ||
+      (rc = check_dev_ptr(dK, "dK")) || (rc = check_dev_ptr(dV, "dV")))
+    return rc;
+  if ((rc = check_apply_extra(dO, g_ptr, sm_scale, g_stride_b, g_stride_l, g_stride_h))) return rc;
+  if (Qn && (rc = check_dev_ptr(Qn, "Qn"))) return rc;
+  if (Kn && (rc = check_dev_ptr(Kn, "Kn"))) return rc;
+  if ((Qn != nullptr) != (dQn != nullptr)) return fail(SD_ERR_INVALID_ARG, "dQn must be given exactly when Qn is");
+  if ((Kn != nullptr) != (dKn != nullptr)) return fail(SD_ERR_INVALID_ARG, "dKn must be given exactly when Kn is");
+  if ((dQn && !aligned(dQn, 16)) || (dKn && !aligned(dKn, 16))) return fail(SD_ERR_ALIGN, "dQn / dKn misaligned");
+  if ((dPq && !aligned(dPq, 4)) || (dPk && !aligned(dPk, 4)) || (dg && !aligned(dg, 4)))
+    return fail(SD_ERR_ALIGN, "dPq / dPk / dg misaligned");
+  if (k_keep < 1 || k_keep > g.Nk) return fail(SD_ERR_INVALID_ARG, "k_keep = %d not in [1, %d]", k_keep, g.Nk);
+  // the staged dO_s tiles are read through 32-bit buffer offsets
+  if ((int64_t)(g.L + 64) * std::max<int64_t>((int64_t)g.H * g.D, shape->sq_l) * 2 >= ((int64_t)1 << 32))
+    return fail(SD_ERR_UNSUPPORTED, "L * H * d (or Q's token stride) too large for the backward");
+  const size_t need = sd_rola_backward_workspace_size(shape, lr, k_keep);
+  if (!ws || ws_bytes < need) return fail(SD_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  if (!aligned(ws, kAlign)) return fail(SD_ERR_ALIGN, "workspace must be 256-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const BwdWs w = carve_bwd(ws, g, shape, lr, k_keep);
+  const int BH = g.B * g.H;
+  const int64_t rows = (int64_t)BH * g.L;
+
+  // forward recomputation: the low-rank state (rows and transposed hi / lo)
+  if ((rc = run_rope_table(shape, lr, w.lr.rope_tab, st))) return rc;
+  sd::RankRows rrows;
+  const sd::PrepareArgs pa = prepare_args(shape, g, lr, Q, K, V, Kn, w.lr, &rrows);
+  hipError_t e = sd::launch_prepare_stream(pa, g.D, st);
+  if (e != hipSuccess) return hip_fail(e, "state pass");
+  e = sd::launch_lowrank_finalize(w.lr.partial, BH, w.lr.runs, g.n_ar, g.win, lr->rank, g.D, rrows, w.C, w.lr.ct_hi,
+                                  w.lr.ct_lo, st);
+  if (e != hipSuccess) return hip_fail(e, "state finalize");
+  // the sparse branch output O_s (f32), its RMS and log-sum-exp
+  {
+    sd::AttnArgs a{};
+    fill_attn_common(a, shape, g);
+    a.so_b = (int64_t)g.L * g.H * g.D;
+    a.so_l = (int64_t)g.H * g.D;
+    a.so_h = g.D;
+    a.Q = static_cast<const uint16_t*>(Q);
+    a.K = static_cast<const uint16_t*>(K);
+    a.V = static_cast<const uint16_t*>(V);
+    a.Qn = a.Q;
+    a.kkeep = k_keep;
+    a.idx = idx;
+    a.scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
+    a.out = w.Os;
+    a.out_f32 = 1;
+    a.rms = w.rms;
+    a.lse = w.lse;
+    e = sd::launch_sparse_attn(a, g.D, g.bq, st);
+    if (e != hipSuccess) return hip_fail(e, "sparse forward");
+  }
+  sd::BwdArgs b{};
+  b.B = g.B;
+  b.H = g.H;
+  b.L = g.L;
+  b.Nq = g.Nq;
+  b.Nk = g.Nk;
+  b.kkeep = k_keep;
+  b.Hg = shape->Hg;
+  b.Wg = shape->Wg;
+  b.block_q = g.bq;
+  b.ar_tokens = g.ar;
+  b.ar_window = g.win;
+  b.sq_b = shape->sq_b;
+  b.sq_l = shape->sq_l;
+  b.sq_h = shape->sq_h;
+  b.sk_b = shape->sk_b;
+  b.sk_l = shape->sk_l;
+  b.sk_h = shape->sk_h;
+  b.sv_b = shape->sv_b;
+  b.sv_l = shape->sv_l;
+  b.sv_h = shape->sv_h;
+  b.so_b = shape->so_b;
+  b.so_l = shape->so_l;
+  b.so_h = shape->so_h;
+  b.Q = static_cast<const uint16_t*>(Q);
+  b.K = static_cast<const uint16_t*>(K);
+  b.V = static_cast<const uint16_t*>(V);
+  b.Qn = static_cast<const uint16_t*>(Qn ? Qn : Q);
+  b.Kn = static_cast<const uint16_t*>(Kn ? Kn : K);
+  b.idx = idx;
+  b.scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
+  b.sm_scale = sm_scale;
+  b.Pq = static_cast<const uint16_t*>(lr->Pq);
+  b.Pk = static_cast<const uint16_t*>(lr->Pk);
+  b.P_hs = lr->P_head_stride;
+  b.rank = lr->rank;
+  b.rope_tab = w.lr.rope_tab;
+  b.rope = rope_args(lr, shape);
+  b.Ct_hi = w.lr.ct_hi;
+  b.Ct_lo = w.lr.ct_lo;
+  b.C = w.C;
+  b.eps = lr->rms_eps;
+  b.rmsw = static_cast<const uint16_t*>(lr->rms_weight);
+  b.g = g_ptr;
+  b.g_sb = g_stride_b;
+  b.g_sl = g_stride_l;
+  b.g_sh = g_stride_h;
+  b.dO = static_cast<const uint16_t*>(dO);
+  b.Os = w.Os;
+  b.rms = w.rms;
+  b.lse = w.lse;
+  b.dOs = w.dOs;
+  b.Dd = w.Dd;
+  b.dg_head = w.dg_head;
+  b.qt = w.qt;
+  b.dy = w.dy;
+  b.da = w.da;
+  b.db = w.db;
+  b.dC = w.dC;
+  b.dCt_hi = w.dCt_hi;
+  b.dCt_lo = w.dCt_lo;
+  b.tlist = w.tlist;
+  b.toff = w.toff;
+  b.dQ = dQ;
+  b.dK = dK;
+  b.dV = dV;
+  b.dQn = dQn ? dQn : w.dQn_tmp;
+  b.dKn = dKn;
+  b.dQn_into_dQ = dQn == nullptr;
+  b.dKn_into_dK = dKn == nullptr;
+  // query side: dO_s, D, dg shares, q~, dy, da, the query-side dQn
+  if ((e = sd::launch_bwd_query(b, g.D, st)) != hipSuccess) return hip_fail(e, "backward, query side");
+  // dC per chunk, then for each chunk the sum over the chunks that see it
+  if ((e = sd::launch_token_outer(w.qt, w.dy, nullptr, 0, 0, 0, g.B, g.H, g.L, g.D, w.dC_runs, w.dC_part, st)) !=
+      hipSuccess)
+    return hip_fail(e, "dC sums");
+  if ((e = sd::launch_dstate_finalize(w.dC_part, BH, w.dC_runs, g.n_ar, g.win, g.D, w.dC, w.dCt_hi, w.dCt_lo, st)) !=
+      hipSuccess)
+    return hip_fail(e, "dC finalize");
+  const bool per_head = lr->P_head_stride != 0;
+  if (dPq) {
+    if ((e = sd::launch_token_outer(w.da, nullptr, b.Qn, shape->sq_b, shape->sq_l, shape->sq_h, g.B, g.H, g.L, g.D,
+                                    w.dP_runs, w.dP_part, st)) != hipSuccess)
+      return hip_fail(e, "dPq sums");
+    if ((e = sd::launch_dproj_finalize(w.dP_part, g.B, g.H, w.dP_runs.n_runs, lr->rank, g.D, per_head, dPq, st)) !=
+        hipSuccess)
+      return hip_fail(e, "dPq finalize");
+  }
+  // softmax branch
+  if ((e = sd::launch_transpose_map(idx, BH, g.Nq, g.Nk, k_keep, w.tlist, w.toff, st)) != hipSuccess)
+    return hip_fail(e, "map transpose");
+  if ((e = sd::launch_bwd_dq(b, g.D, st)) != hipSuccess) return hip_fail(e, "backward dQ");
+  if ((e = sd::launch_bwd_dkdv(b, g.D, st)) != hipSuccess) return hip_fail(e, "backward dK, dV");
+  // key side of the low-rank branch (adds into dV, and into dK without Kn)
+  if ((e = sd::launch_bwd_key(b, g.D, st)) != hipSuccess) return hip_fail(e, "backward, key side");
+  if (dPk) {
+    if ((e = sd::launch_token_outer(w.db, nullptr, b.Kn, shape->sk_b, shape->sk_l, shape->sk_h, g.B, g.H, g.L, g.D,
+                                    w.dP_runs, w.dP_part, st)) != hipSuccess)
+      return hip_fail(e, "dPk sums");
+    if ((e = sd::launch_dproj_finalize(w.dP_part, g.B, g.H, w.dP_runs.n_runs, lr->rank, g.D, per_head, dPk, st)) !=
+        hipSuccess)
+      return hip_fail(e, "dPk finalize");
+  }
+  if (dg && (e = sd::launch_dgate(w.dg_head, g.B, g.L, g.H, g_stride_b, g_stride_l, g_stride_h, dg, st)) !=
+                hipSuccess)
+    return hip_fail(e, "dg");
+  (void)rows;
   return ok();
 }
 

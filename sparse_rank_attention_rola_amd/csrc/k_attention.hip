@@ -201,7 +201,7 @@ __global__ __launch_bounds__(BQ * 2, BQ == 128 ? SD_ATTN_WAVES : 1) void attenti
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
-  float ltot = 1.f;
+  float ltot = 1.f, m_fin = 0.f;
 
   if constexpr (kLoop) {
     const int32_t* irow = a.idx + wi * a.kkeep;
@@ -323,6 +323,7 @@ __global__ __launch_bounds__(BQ * 2, BQ == 128 ? SD_ATTN_WAVES : 1) void attenti
       __syncthreads();
     }
     ltot = lsum + __shfl_xor(lsum, 32);
+    m_fin = m;
   }
 
   const int64_t obase = (int64_t)b * a.so_b + (int64_t)q_tok * a.so_l + (int64_t)h * a.so_h;
@@ -340,6 +341,9 @@ __global__ __launch_bounds__(BQ * 2, BQ == 128 ? SD_ATTN_WAVES : 1) void attenti
     if (q_ok) {
       store_row<D>(a.out, a.out_f32, obase, oacc, hf);
       if (a.rms && hf == 0) a.rms[((int64_t)b * a.L + q_tok) * a.H + h] = sqrtf(ss * (1.0f / D));
+      // log2-domain log-sum-exp of the query's scaled scores, for the
+      // backward's recomputation of P (+inf where the query saw no key)
+      if (a.lse && hf == 0) a.lse[((int64_t)b * a.L + q_tok) * a.H + h] = ltot > 0.f ? m_fin + log2f(ltot) : INFINITY;
     }
   } else {
     float* Fw = reinterpret_cast<float*>(smem0) + wv * (32 * 33);

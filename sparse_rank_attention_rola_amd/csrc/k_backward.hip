@@ -1,0 +1,1086 @@
+// Backward of the RoLA attention layer (block map held fixed).
+//
+// SparkDiffusion README_zh (distillation and operators sections): training
+// the sparse student needs a backward kernel of its sparse + low-rank
+// attention, whose forward is the robotworld.top write-up, section 2.1:
+//   O_i = O_s,i + g_i r_i O_lr,i,  O_lr,i = w * y_i / rho_i,  y_i = C^T q~_i,
+//   C = sum_j k~_j v_j^T,  q~ = R phi(P_q qn),  k~ = R phi(P_k kn).
+// The gradients are the exact derivatives of that forward (chain rule):
+//   dg_i = r_i (dO_i . O_lr,i),  dO_s,i = dO_i + g_i (dO_i . O_lr,i) O_s,i / (d r_i),
+//   dy_i = u_i / rho_i - y_i (u_i . y_i) / (d rho_i^3),  u_i = w * g_i r_i dO_i,
+//   dq~_i = C dy_i,  dC = sum_i q~_i dy_i^T,  dk~_j = dC v_j,  dv_j += dC^T k~_j,
+//   then back through R (rotation by the negative angle), phi' and the
+//   projections; and the softmax branch as in attention backward:
+//   D_i = dO_s,i . O_s,i, dS = P * (dO_s V^T - D), dQ = scale dS K,
+//   dK = scale dS^T Q, dV += P^T dO_s.
+// Under a causal window every chunk has its own state: the query side uses
+// the state of its chunk, and a key receives the sum of dC over the chunks
+// that see it.
+//
+// Kernels:
+//   bwd_query_kernel    per 32 queries (one wave): recompute q~ and y, the
+//                       gate / RMS / RMSNorm derivatives, dq~ = C dy on
+//                       MFMA, back through RoPE and phi, dQn = P_q^T da;
+//                       writes dO_s (bf16), D, q~, dy, da and dg per head.
+//   token_outer_kernel  sum over a run of tokens of X^T Y (X: 32 columns)
+//                       on MFMA with hi/lo bf16 operands: the partial dC
+//                       (q~, dy) and dP_q / dP_k (da / db, qn / kn).
+//   dstate_finalize / dproj_finalize: fixed-order sums of the partials.
+//   bwd_key_kernel      per 32 keys: recompute k~, dk~ = dC v, dv += dC^T k~,
+//                       back through RoPE and phi, dKn = P_k^T db.
+//   transpose_map_kernel  per (batch, head): the query blocks that keep
+//                       each key block, ascending (a counting sort).
+//   bwd_dq_kernel       per query block, like the forward loop: S^T, P^T
+//                       from the saved log-sum-exp, dP^T = V dO_s^T, dS^T,
+//                       dQ^T += K^T dS^T (K^T by transposing LDS reads).
+//   bwd_dkdv_kernel     per key block, over the query blocks that keep it:
+//                       S = Q K^T, dP = dO_s V^T with K, V in registers,
+//                       dV^T += dO_s^T P and dK^T += Q^T dS (transposing
+//                       reads of the staged Q and dO_s tiles).
+// Every sum runs in a fixed order: the results are bitwise reproducible.
+#include "sd_device.h"
+#include "sd_launch.h"
+#include "sd_tiles.h"
+
+namespace sd {
+
+__device__ __forceinline__ float phi_b(float x) { return x > 0.f ? x + 1.f : __expf(x); }
+__device__ __forceinline__ float dphi_b(float x) { return x > 0.f ? 1.f : __expf(x); }
+
+// Channel of accumulator register r of an O^T tile dt (lane half hf).
+__device__ __forceinline__ int och(int dt, int r, int hf) { return 32 * dt + 8 * (r >> 2) + 4 * hf + (r & 3); }
+
+// The 8 channels 16 s + 8 hf .. +7 of the lane's token (the MFMA B-operand
+// slice) from values held in the O^T accumulator layout: each lane holds 4
+// of every 8 channels; one lane-pair exchange per value completes the slice.
+template <int D>
+__device__ __forceinline__ void otile_slice(const f32x16 (&v)[D / 32], int s, int hf, float out[8]) {
+  const int g0 = 2 * s, g1 = 2 * s + 1;
+  float own0[4], own1[4], y[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    own0[e] = v[g0 >> 2][4 * (g0 & 3) + e];
+    own1[e] = v[g1 >> 2][4 * (g1 & 3) + e];
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) y[e] = partner32(hf ? own0[e] : own1[e], hf);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    out[e] = hf ? y[e] : own0[e];
+    out[4 + e] = hf ? own1[e] : y[e];
+  }
+}
+
+__device__ __forceinline__ void load8_split(const float* p, bool ok, bf16x8& hi, bf16x8& lo) {
+  float f[8];
+  if (ok) {
+    const f32x4 u = *reinterpret_cast<const f32x4*>(p);
+    const f32x4 w = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f[e] = u[e];
+      f[4 + e] = w[e];
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = 0.f;
+  }
+  split_bf16x8(f, hi, lo);
+}
+
+// Rotates the RoPE pairs of a wave's 32 x 33 patch (lane l32 = token tok0 +
+// l32, the two lane halves take alternate pairs) by +angle (dir = 1) or by
+// -angle (dir = -1, the transpose).
+__device__ __forceinline__ void rope_patch(float* F, const float2* tab, const RopeArgs& rope, int Hg, int Wg,
+                                           int tok0, int lane, int dir) {
+  const int hf = lane >> 5, l32 = lane & 31;
+  const int tok = tok0 + l32;
+  const int hw = Hg * Wg;
+  const int pos[3] = {min(tok / hw, rope.max_ext - 1), (tok / Wg) % Hg, tok % Wg};
+  for (int m0 = 0; m0 < rope.n; m0 += 2) {
+    const int m = m0 + hf;
+    if (m < rope.n) {
+      const int axis = hf ? rope.axis[m0 + 1] : rope.axis[m0];
+      const int dim = hf ? rope.dim[m0 + 1] : rope.dim[m0];
+      const float2 cs = tab[m * rope.max_ext + (axis == 0 ? pos[0] : axis == 1 ? pos[1] : pos[2])];
+      const float sn = dir > 0 ? cs.y : -cs.y;
+      float* f = F + l32 * 33 + dim;
+      const float u = f[0], v = f[1];
+      f[0] = u * cs.x - v * sn;
+      f[1] = u * sn + v * cs.x;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Query side of the low-rank branch, gate and RMS coupling.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
+  __shared__ float Fw[4][32 * 33];
+  __shared__ float Fa[4][32 * 33];
+  int64_t bh;
+  int blk;
+  if (!xcd_group_item(blockIdx.x, (a.L + 127) / 128, (int64_t)a.B * a.H, bh, blk)) return;
+  const int h = (int)(bh % a.H), b = (int)(bh / a.H);
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int hf = lane >> 5, l32 = lane & 31;
+  const int tok0 = blk * 128 + 32 * wv;
+  const int q_tok = tok0 + l32;
+  const bool q_ok = q_tok < a.L;
+  const int q_cl = min(q_tok, a.L - 1);
+  const int q_chunk = q_cl / a.ar_tokens;
+  const int n_ar = (a.L + a.ar_tokens - 1) / a.ar_tokens;
+  const int c_first = __builtin_amdgcn_readfirstlane(q_chunk);
+  const int c_last = __builtin_amdgcn_readlane(q_chunk, 31);
+  float* fw = Fw[wv];
+  float* fa = Fa[wv];
+  const int64_t row = ((int64_t)b * a.L + q_cl) * a.H + h;
+
+  // 1. a = P_q qn (pre-phi in Fa), q~ = R phi(a) (in Fw)
+  {
+    u32x4 qreg[D / 16];
+    const uint16_t* qp = a.Qn + (int64_t)b * a.sq_b + (int64_t)q_cl * a.sq_l + (int64_t)h * a.sq_h;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s)
+      qreg[s] = q_ok ? *reinterpret_cast<const u32x4*>(qp + 16 * s + 8 * hf) : u32x4{0, 0, 0, 0};
+    const uint16_t* Pq = a.Pq + (int64_t)h * a.P_hs;
+    f32x16 acc = {};
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      const u32x4 pa = (l32 < a.rank) ? *reinterpret_cast<const u32x4*>(Pq + l32 * D + 16 * s + 8 * hf)
+                                      : u32x4{0, 0, 0, 0};
+      acc = mfma32(as_bf16x8(pa), as_bf16x8(qreg[s]), acc);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int ri = 8 * (r >> 2) + 4 * hf + (r & 3);
+      fa[l32 * 33 + ri] = ri < a.rank ? acc[r] : 0.f;
+      fw[l32 * 33 + ri] = ri < a.rank ? phi_b(acc[r]) : 0.f;
+    }
+  }
+  __syncthreads();
+  rope_patch(fw, a.rope_tab, a.rope, a.Hg, a.Wg, tok0, lane, 1);
+  __syncthreads();
+  bf16x8 qhi[2], qlo[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    float t8[8];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) t8[p] = fw[l32 * 33 + 16 * s + 8 * hf + p];
+    split_bf16x8(t8, qhi[s], qlo[s]);
+    if (q_ok) {
+      float* dst = a.qt + row * 32 + 16 * s + 8 * hf;
+      *reinterpret_cast<f32x4*>(dst) = f32x4{t8[0], t8[1], t8[2], t8[3]};
+      *reinterpret_cast<f32x4*>(dst + 4) = f32x4{t8[4], t8[5], t8[6], t8[7]};
+    }
+  }
+
+  // 2. y = C^T q~ with the state of the lane's chunk
+  f32x16 yv[D / 32];
+  for (int c = c_first; c <= c_last; ++c) {
+    const int64_t cbase = (bh * n_ar + c) * D * 32;
+    const bool mine = q_chunk == c;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      f32x16 y = {};
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int64_t off = cbase + (int64_t)(32 * dt + l32) * 32 + 16 * s + 8 * hf;
+        const bf16x8 ch = as_bf16x8(*reinterpret_cast<const u32x4*>(a.Ct_hi + off));
+        const bf16x8 cl = as_bf16x8(*reinterpret_cast<const u32x4*>(a.Ct_lo + off));
+        y = mfma32(ch, qhi[s], y);
+        y = mfma32(cl, qhi[s], y);
+        y = mfma32(ch, qlo[s], y);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) yv[dt][r] = (c == c_first || mine) ? y[r] : yv[dt][r];
+    }
+  }
+
+  // 3. RMSNorm, gate and RMS coupling, per query (lane pair)
+  float ss = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ss += yv[dt][r] * yv[dt][r];
+  ss += partner32(ss, hf);
+  const float inv = rsqrtf(ss * (1.0f / D) + a.eps);
+  const uint16_t* dop = a.dO + (int64_t)b * a.so_b + (int64_t)q_cl * a.so_l + (int64_t)h * a.so_h;
+  const float* osp = a.Os + row * D;
+  f32x16 dov[D / 32], osv[D / 32];
+  float t = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const int c0 = och(dt, 4 * rg, hf);
+      const u32x2 d2 = q_ok ? *reinterpret_cast<const u32x2*>(dop + c0) : u32x2{0, 0};
+      const f32x4 o4 = q_ok ? *reinterpret_cast<const f32x4*>(osp + c0) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * rg + e;
+        dov[dt][r] = (e & 1) ? bf16_hi(d2[e >> 1]) : bf16_lo(d2[e >> 1]);
+        osv[dt][r] = o4[e];
+        const float w = a.rmsw ? bf16_bits_to_f32(a.rmsw[c0 + e]) : 1.f;
+        t += dov[dt][r] * w * yv[dt][r] * inv;
+      }
+    }
+  t += partner32(t, hf);
+  const float rr = q_ok ? a.rms[row] : 0.f;
+  const float gv = q_ok ? a.g[(int64_t)b * a.g_sb + (int64_t)q_cl * a.g_sl + (int64_t)h * a.g_sh] : 0.f;
+  if (q_ok && hf == 0) a.dg_head[row] = rr * t;
+  const float coef = rr > 0.f ? gv * t / ((float)D * rr) : 0.f;
+  const float gr = gv * rr;
+  float dsum = 0.f, uy = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const int c0 = och(dt, 4 * rg, hf);
+      float dsv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * rg + e;
+        const float v = fmaf(coef, osv[dt][r], dov[dt][r]);
+        dsv[e] = bf16_bits_to_f32(f32_to_bf16_bits(v));
+        dsum += dsv[e] * osv[dt][r];
+        const float w = a.rmsw ? bf16_bits_to_f32(a.rmsw[c0 + e]) : 1.f;
+        dov[dt][r] = w * gr * dov[dt][r];  // u
+        uy += dov[dt][r] * yv[dt][r];
+      }
+      if (q_ok) {
+        u32x2 o;
+        o[0] = pack_bf16x2(dsv[0], dsv[1]);
+        o[1] = pack_bf16x2(dsv[2], dsv[3]);
+        *reinterpret_cast<u32x2*>(a.dOs + row * D + c0) = o;
+      }
+    }
+  dsum += partner32(dsum, hf);
+  uy += partner32(uy, hf);
+  if (q_ok && hf == 0) a.Dd[row] = dsum;
+  const float k3 = uy * inv * inv * inv * (1.0f / D);
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) yv[dt][r] = dov[dt][r] * inv - yv[dt][r] * k3;  // dy
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg)
+      if (q_ok)
+        *reinterpret_cast<f32x4*>(a.dy + row * D + och(dt, 4 * rg, hf)) =
+            f32x4{yv[dt][4 * rg], yv[dt][4 * rg + 1], yv[dt][4 * rg + 2], yv[dt][4 * rg + 3]};
+  }
+
+  // 4. dq~ = C dy (rank x token), the state of the lane's chunk
+  bf16x8 dyh[D / 16], dyl[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    float f8[8];
+    otile_slice<D>(yv, s, hf, f8);
+    split_bf16x8(f8, dyh[s], dyl[s]);
+  }
+  f32x16 dq = {};
+  for (int c = c_first; c <= c_last; ++c) {
+    const float* Cr = a.C + (bh * n_ar + c) * (int64_t)a.rank * D;
+    const bool mine = q_chunk == c;
+    f32x16 acc = {};
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      bf16x8 chi, clo;
+      load8_split(Cr + (int64_t)l32 * D + 16 * s + 8 * hf, l32 < a.rank, chi, clo);
+      acc = mfma32(chi, dyh[s], acc);
+      acc = mfma32(clo, dyh[s], acc);
+      acc = mfma32(chi, dyl[s], acc);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dq[r] = (c == c_first || mine) ? acc[r] : dq[r];
+  }
+
+  // 5. da = R^T dq~ * phi'(a)
+  __syncthreads();  // every wave is done reading q~ from its patch
+#pragma unroll
+  for (int r = 0; r < 16; ++r) fw[l32 * 33 + 8 * (r >> 2) + 4 * hf + (r & 3)] = dq[r];
+  __syncthreads();
+  rope_patch(fw, a.rope_tab, a.rope, a.Hg, a.Wg, tok0, lane, -1);
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int i = l32 * 33 + 8 * (r >> 2) + 4 * hf + (r & 3);
+    fw[i] *= dphi_b(fa[i]);
+  }
+  __syncthreads();
+  bf16x8 dah[2], dal[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    float t8[8];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) t8[p] = fw[l32 * 33 + 16 * s + 8 * hf + p];
+    split_bf16x8(t8, dah[s], dal[s]);
+    if (q_ok) {
+      float* dst = a.da + row * 32 + 16 * s + 8 * hf;
+      *reinterpret_cast<f32x4*>(dst) = f32x4{t8[0], t8[1], t8[2], t8[3]};
+      *reinterpret_cast<f32x4*>(dst + 4) = f32x4{t8[4], t8[5], t8[6], t8[7]};
+    }
+  }
+
+  // 6. dqn = P_q^T da (channel x token)
+  const uint16_t* Pq = a.Pq + (int64_t)h * a.P_hs;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+    f32x16 acc = {};
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      bf16x8 pa;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int rk = 16 * s + 8 * hf + e;
+        pa[e] = __builtin_bit_cast(__bf16, rk < a.rank ? Pq[rk * D + 32 * dt + l32] : (uint16_t)0);
+      }
+      acc = mfma32(pa, dah[s], acc);
+      acc = mfma32(pa, dal[s], acc);
+    }
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg)
+      if (q_ok)
+        *reinterpret_cast<f32x4*>(a.dQn + row * D + och(dt, 4 * rg, hf)) =
+            f32x4{acc[4 * rg], acc[4 * rg + 1], acc[4 * rg + 2], acc[4 * rg + 3]};
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Sums over runs of tokens of X^T Y.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void token_outer_kernel(const float* __restrict__ X, const float* __restrict__ Yf,
+                                                          const uint16_t* __restrict__ Yb, int64_t y_sb, int64_t y_sl,
+                                                          int64_t y_sh, int B, int H, int L, RunGeo runs,
+                                                          float* __restrict__ part) {
+  __shared__ float Xs[64][33];
+  __shared__ float Ys[64][D + 1];
+  const int64_t nbh = (int64_t)B * H;
+  const int64_t bh = blockIdx.x % nbh;
+  const int run = (int)(blockIdx.x / nbh);
+  const int h = (int)(bh % H), b = (int)(bh / H);
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int hf = lane >> 5, l32 = lane & 31;
+  int t_begin, t_end, lo, hi;
+  run_extent(runs, L, run, t_begin, t_end, lo, hi);
+  f32x16 acc = {};
+  for (int tl = t_begin; tl < t_end; ++tl) {
+    const int tok0 = tl * 64;
+    __syncthreads();
+    // X tile: 64 tokens x 32 (8 floats per thread); Y tile: 64 x D
+    {
+      const int t = tid >> 2, c = (tid & 3) * 8;
+      const int tok = tok0 + t;
+      const bool ok = tok >= lo && tok < hi;
+      const float* xp = X + (((int64_t)b * L + tok) * H + h) * 32 + c;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) Xs[t][c + e] = ok ? xp[e] : 0.f;
+    }
+    for (int i = tid; i < 64 * (D / 8); i += 256) {
+      const int t = i / (D / 8), c = (i % (D / 8)) * 8;
+      const int tok = tok0 + t;
+      const bool ok = tok >= lo && tok < hi;
+      if (Yf) {
+        const float* yp = Yf + (((int64_t)b * L + tok) * H + h) * D + c;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) Ys[t][c + e] = ok ? yp[e] : 0.f;
+      } else {
+        const u32x4 v = ok ? *reinterpret_cast<const u32x4*>(Yb + (int64_t)b * y_sb + (int64_t)tok * y_sl +
+                                                              (int64_t)h * y_sh + c)
+                           : u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          Ys[t][c + 2 * e] = bf16_lo(v[e]);
+          Ys[t][c + 2 * e + 1] = bf16_hi(v[e]);
+        }
+      }
+    }
+    __syncthreads();
+    if (wv < D / 32) {
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        float xa[8], yb[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          xa[e] = Xs[16 * st + 8 * hf + e][l32];
+          yb[e] = Ys[16 * st + 8 * hf + e][32 * wv + l32];
+        }
+        bf16x8 xh, xl, yh, yl;
+        split_bf16x8(xa, xh, xl);
+        split_bf16x8(yb, yh, yl);
+        acc = mfma32(xh, yh, acc);
+        acc = mfma32(xl, yh, acc);
+        acc = mfma32(xh, yl, acc);
+      }
+    }
+  }
+  if (wv < D / 32) {
+    float* out = part + ((int64_t)bh * runs.n_runs + run) * 32 * D;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) out[(8 * (r >> 2) + 4 * hf + (r & 3)) * D + 32 * wv + l32] = acc[r];
+  }
+}
+
+// dC seen by chunk c: runs of chunks c .. last, in run order.
+__global__ void dstate_finalize_kernel(const float* __restrict__ part, int64_t BH, RunGeo runs, int n_ar, int window,
+                                       int D, float* __restrict__ dC, uint16_t* __restrict__ dCt_hi,
+                                       uint16_t* __restrict__ dCt_lo) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= BH * n_ar * 32 * D) return;
+  const int d = (int)(i % D);
+  const int r = (int)((i / D) % 32);
+  const int64_t bc = i / (32 * D);
+  const int c = (int)(bc % n_ar);
+  const int64_t bh = bc / n_ar;
+  const int last = window > 0 ? min(n_ar - 1, c + window - 1) : n_ar - 1;
+  const float* p = part + (bh * runs.n_runs * 32 + r) * D + d;
+  float s = 0.f;
+  for (int u = c * runs.runs_per_ar; u < (last + 1) * runs.runs_per_ar; ++u) s += p[(int64_t)u * 32 * D];
+  dC[(bc * 32 + r) * D + d] = s;
+  const __bf16 hi = (__bf16)s;
+  const __bf16 lo = (__bf16)(s - (float)hi);
+  dCt_hi[(bc * D + d) * 32 + r] = __builtin_bit_cast(uint16_t, hi);
+  dCt_lo[(bc * D + d) * 32 + r] = __builtin_bit_cast(uint16_t, lo);
+}
+
+__global__ void dproj_finalize_kernel(const float* __restrict__ part, int B, int H, int n_runs, int rank, int D,
+                                      int per_head, float* __restrict__ dP) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int n_out = per_head ? H : 1;
+  if (i >= (int64_t)n_out * rank * D) return;
+  const int d = (int)(i % D);
+  const int r = (int)((i / D) % rank);
+  const int o = (int)(i / ((int64_t)rank * D));
+  float s = 0.f;
+  for (int b = 0; b < B; ++b)
+    for (int h = per_head ? o : 0; h < (per_head ? o + 1 : H); ++h) {
+      const float* p = part + (((int64_t)b * H + h) * n_runs * 32 + r) * D + d;
+      for (int u = 0; u < n_runs; ++u) s += p[(int64_t)u * 32 * D];
+    }
+  dP[i] = s;
+}
+
+__global__ void dgate_kernel(const float* __restrict__ dg_head, int B, int L, int H, int64_t g_sb, int64_t g_sl,
+                             int64_t g_sh, float* __restrict__ dg) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (g_sh == 0) {
+    if (i >= (int64_t)B * L) return;
+    const int l = (int)(i % L), b = (int)(i / L);
+    float s = 0.f;
+    for (int h = 0; h < H; ++h) s += dg_head[i * H + h];
+    dg[(int64_t)b * g_sb + (int64_t)l * g_sl] = s;
+  } else {
+    if (i >= (int64_t)B * L * H) return;
+    const int h = (int)(i % H);
+    const int64_t bl = i / H;
+    const int l = (int)(bl % L), b = (int)(bl / L);
+    dg[(int64_t)b * g_sb + (int64_t)l * g_sl + (int64_t)h * g_sh] = dg_head[i];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Key side of the low-rank branch.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
+  __shared__ float Fw[4][32 * 33];
+  __shared__ float Fa[4][32 * 33];
+  int64_t bh;
+  int blk;
+  if (!xcd_group_item(blockIdx.x, (a.L + 127) / 128, (int64_t)a.B * a.H, bh, blk)) return;
+  const int h = (int)(bh % a.H), b = (int)(bh / a.H);
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int hf = lane >> 5, l32 = lane & 31;
+  const int tok0 = blk * 128 + 32 * wv;
+  const int k_tok = tok0 + l32;
+  const bool k_ok = k_tok < a.L;
+  const int k_cl = min(k_tok, a.L - 1);
+  const int k_chunk = k_cl / a.ar_tokens;
+  const int n_ar = (a.L + a.ar_tokens - 1) / a.ar_tokens;
+  const int c_first = __builtin_amdgcn_readfirstlane(k_chunk);
+  const int c_last = __builtin_amdgcn_readlane(k_chunk, 31);
+  float* fw = Fw[wv];
+  float* fa = Fa[wv];
+  const int64_t row = ((int64_t)b * a.L + k_cl) * a.H + h;
+
+  // 1. b = P_k kn (pre-phi in Fa), k~ = R phi(b) (in Fw)
+  {
+    u32x4 kreg[D / 16];
+    const uint16_t* kp = a.Kn + (int64_t)b * a.sk_b + (int64_t)k_cl * a.sk_l + (int64_t)h * a.sk_h;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s)
+      kreg[s] = k_ok ? *reinterpret_cast<const u32x4*>(kp + 16 * s + 8 * hf) : u32x4{0, 0, 0, 0};
+    const uint16_t* Pk = a.Pk + (int64_t)h * a.P_hs;
+    f32x16 acc = {};
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      const u32x4 pa = (l32 < a.rank) ? *reinterpret_cast<const u32x4*>(Pk + l32 * D + 16 * s + 8 * hf)
+                                      : u32x4{0, 0, 0, 0};
+      acc = mfma32(as_bf16x8(pa), as_bf16x8(kreg[s]), acc);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int ri = 8 * (r >> 2) + 4 * hf + (r & 3);
+      fa[l32 * 33 + ri] = ri < a.rank ? acc[r] : 0.f;
+      fw[l32 * 33 + ri] = ri < a.rank ? phi_b(acc[r]) : 0.f;
+    }
+  }
+  __syncthreads();
+  rope_patch(fw, a.rope_tab, a.rope, a.Hg, a.Wg, tok0, lane, 1);
+  __syncthreads();
+  bf16x8 khi[2], klo[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    float t8[8];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) t8[p] = fw[l32 * 33 + 16 * s + 8 * hf + p];
+    split_bf16x8(t8, khi[s], klo[s]);
+  }
+  u32x4 vreg[D / 16];
+  {
+    const uint16_t* vp = a.V + (int64_t)b * a.sv_b + (int64_t)k_cl * a.sv_l + (int64_t)h * a.sv_h;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s)
+      vreg[s] = k_ok ? *reinterpret_cast<const u32x4*>(vp + 16 * s + 8 * hf) : u32x4{0, 0, 0, 0};
+  }
+
+  // 2. dk~ = dC v (rank x key) and dv = dC^T k~ (channel x key), with the
+  // state gradient seen by the lane's chunk
+  f32x16 dk = {};
+  f32x16 dv[D / 32];
+  for (int c = c_first; c <= c_last; ++c) {
+    const int64_t bc = bh * n_ar + c;
+    const bool mine = k_chunk == c;
+    const bool take = c == c_first || mine;
+    f32x16 acc = {};
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      bf16x8 chi, clo;
+      load8_split(a.dC + (bc * 32 + l32) * D + 16 * s + 8 * hf, true, chi, clo);
+      acc = mfma32(chi, as_bf16x8(vreg[s]), acc);
+      acc = mfma32(clo, as_bf16x8(vreg[s]), acc);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dk[r] = take ? acc[r] : dk[r];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      f32x16 y = {};
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int64_t off = (bc * D + 32 * dt + l32) * 32 + 16 * s + 8 * hf;
+        const bf16x8 ch = as_bf16x8(*reinterpret_cast<const u32x4*>(a.dCt_hi + off));
+        const bf16x8 cl = as_bf16x8(*reinterpret_cast<const u32x4*>(a.dCt_lo + off));
+        y = mfma32(ch, khi[s], y);
+        y = mfma32(cl, khi[s], y);
+        y = mfma32(ch, klo[s], y);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dv[dt][r] = take ? y[r] : dv[dt][r];
+    }
+  }
+  if (k_ok) {
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        float* p = a.dV + row * D + och(dt, 4 * rg, hf);
+        f32x4 v = *reinterpret_cast<f32x4*>(p);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] += dv[dt][4 * rg + e];
+        *reinterpret_cast<f32x4*>(p) = v;
+      }
+  }
+
+  // 3. db = R^T dk~ * phi'(b)
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 16; ++r) fw[l32 * 33 + 8 * (r >> 2) + 4 * hf + (r & 3)] = dk[r];
+  __syncthreads();
+  rope_patch(fw, a.rope_tab, a.rope, a.Hg, a.Wg, tok0, lane, -1);
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int i = l32 * 33 + 8 * (r >> 2) + 4 * hf + (r & 3);
+    fw[i] *= dphi_b(fa[i]);
+  }
+  __syncthreads();
+  bf16x8 dbh[2], dbl[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    float t8[8];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) t8[p] = fw[l32 * 33 + 16 * s + 8 * hf + p];
+    split_bf16x8(t8, dbh[s], dbl[s]);
+    if (k_ok) {
+      float* dst = a.db + row * 32 + 16 * s + 8 * hf;
+      *reinterpret_cast<f32x4*>(dst) = f32x4{t8[0], t8[1], t8[2], t8[3]};
+      *reinterpret_cast<f32x4*>(dst + 4) = f32x4{t8[4], t8[5], t8[6], t8[7]};
+    }
+  }
+
+  // 4. dkn = P_k^T db, into dKn or added into dK
+  const uint16_t* Pk = a.Pk + (int64_t)h * a.P_hs;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+    f32x16 acc = {};
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      bf16x8 pa;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int rk = 16 * s + 8 * hf + e;
+        pa[e] = __builtin_bit_cast(__bf16, rk < a.rank ? Pk[rk * D + 32 * dt + l32] : (uint16_t)0);
+      }
+      acc = mfma32(pa, dbh[s], acc);
+      acc = mfma32(pa, dbl[s], acc);
+    }
+    if (k_ok) {
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        float* p = (a.dKn_into_dK ? a.dK : a.dKn) + row * D + och(dt, 4 * rg, hf);
+        f32x4 v = a.dKn_into_dK ? *reinterpret_cast<f32x4*>(p) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] += acc[4 * rg + e];
+        *reinterpret_cast<f32x4*>(p) = v;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Key block -> the query blocks that keep it (ascending), per (batch, head).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void transpose_map_kernel(const int32_t* __restrict__ idx, int Nq, int Nk, int k,
+                                                            int32_t* __restrict__ tlist, int32_t* __restrict__ toff) {
+  __shared__ int cnt[kMaxKeep + 1];
+  const int64_t bh = blockIdx.x;
+  const int32_t* row0 = idx + bh * (int64_t)Nq * k;
+  const int tid = threadIdx.x;
+  for (int c = tid; c <= Nk; c += 256) cnt[c] = 0;
+  __syncthreads();
+  for (int64_t i = tid; i < (int64_t)Nq * k; i += 256) {
+    const int c = row0[i];
+    if ((unsigned)c < (unsigned)Nk) atomicAdd(&cnt[c], 1);
+  }
+  __syncthreads();
+  if (tid == 0) {  // exclusive prefix sum, in place
+    int run = 0;
+    for (int c = 0; c < Nk; ++c) {
+      const int v = cnt[c];
+      cnt[c] = run;
+      run += v;
+    }
+    cnt[Nk] = run;
+  }
+  __syncthreads();
+  for (int c = tid; c <= Nk; c += 256) toff[bh * (Nk + 1) + c] = cnt[c];
+  __syncthreads();
+  // fill in query-block order, one row per step of the first wave
+  int32_t* out = tlist + bh * (int64_t)Nq * k;
+  if (tid < 64) {
+    for (int qb = 0; qb < Nq; ++qb) {
+      for (int j = tid; j < k; j += 64) {
+        const int c = row0[(int64_t)qb * k + j];
+        if ((unsigned)c < (unsigned)Nk) out[atomicAdd(&cnt[c], 1)] = qb;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Softmax branch: dQ per query block.
+// ---------------------------------------------------------------------------
+// 8 bf16 of row t of a V-swizzled tile, channels 8c .. 8c+7.
+template <int D>
+__device__ __forceinline__ bf16x8 lds_row_vswz(const uint16_t* Ts, int t, int c) {
+  return as_bf16x8(*reinterpret_cast<const u32x4*>(Ts + t * D + ((c ^ v_swz<D>(t)) * 8)));
+}
+
+// Transposed A operand (32 channels x 16 rows) of a K-swizzled tile, rows
+// row_base .. +15 in the order of lds_v_operand.
+template <int D>
+__device__ __forceinline__ bf16x8 lds_kt_operand(const uint16_t* Ks, int lane, int dt, int row_base) {
+  const int G = lane >> 4, j = lane & 15;
+  const int r = j >> 2, q = j & 3;
+  const int row = row_base + 4 * (G >> 1) + r;
+  const int c8 = 8 * dt + 4 * (G & 1) + q;
+  const int off0 = ((c8 >> 1) ^ k_swz<D>(row)) * 8 + (c8 & 1) * 4;
+  const int off1 = ((c8 >> 1) ^ k_swz<D>(row + 8)) * 8 + (c8 & 1) * 4;
+  const u32x2 lo = lds_read_tr16(Ks + row * D + off0);
+  const u32x2 hi = lds_read_tr16(Ks + (row + 8) * D + off1);
+  return cat_bf16x8(lo, hi);
+}
+
+template <int D, int BQ>
+__global__ __launch_bounds__(BQ * 2) void bwd_dq_kernel(BwdArgs a) {
+  constexpr int NW = BQ / 32;
+  constexpr int NT = NW * 64;
+  __shared__ __attribute__((aligned(16))) uint16_t smem0[TileSmem<D>::kElems];
+  __shared__ __attribute__((aligned(16))) uint16_t smem1[TileSmem<D>::kElems];
+  __shared__ int sidx[kMaxKeep];
+  int64_t bh;
+  int qb;
+  if (!xcd_group_item(blockIdx.x, a.Nq, (int64_t)a.B * a.H, bh, qb)) return;
+  const int h = (int)(bh % a.H), b = (int)(bh / a.H);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hf = lane >> 5, l32 = lane & 31;
+  const int tok0 = qb * BQ + wv * 32;
+  const int q_tok = tok0 + l32;
+  const bool q_ok = q_tok < a.L;
+  const int q_cl = min(q_tok, a.L - 1);
+  const int q_chunk = q_cl / a.ar_tokens;
+  const int key_hi = min(a.L, (q_chunk + 1) * a.ar_tokens);
+  const int key_lo = a.ar_window > 0 ? max(0, (q_chunk - a.ar_window + 1) * a.ar_tokens) : 0;
+  const int64_t row = ((int64_t)b * a.L + q_cl) * a.H + h;
+
+  u32x4 qreg[D / 16], dreg[D / 16];
+  {
+    const uint16_t* qp = a.Q + (int64_t)b * a.sq_b + (int64_t)q_cl * a.sq_l + (int64_t)h * a.sq_h;
+    const uint16_t* dp = a.dOs + row * D;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      qreg[s] = q_ok ? *reinterpret_cast<const u32x4*>(qp + 16 * s + 8 * hf) : u32x4{0, 0, 0, 0};
+      dreg[s] = q_ok ? *reinterpret_cast<const u32x4*>(dp + 16 * s + 8 * hf) : u32x4{0, 0, 0, 0};
+    }
+  }
+  const float lse = q_ok ? a.lse[row] : INFINITY;
+  const float Di = q_ok ? a.Dd[row] : 0.f;
+  f32x16 dqa[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) dqa[i] = f32x16{};
+
+  const int32_t* irow = a.idx + (bh * a.Nq + qb) * a.kkeep;
+  const uint16_t* Kb = a.K + (int64_t)b * a.sk_b + (int64_t)h * a.sk_h;
+  const uint16_t* Vb = a.V + (int64_t)b * a.sv_b + (int64_t)h * a.sv_h;
+  DirectTileLoader<D, NW> ld;
+  ld.init(Kb, a.sk_l, Vb, a.sv_l, a.L, lane, wv);
+  for (int i = tid; i < a.kkeep; i += NT) sidx[i] = irow[i];
+  __syncthreads();
+  auto block_tok0 = [&](int i) {
+    const int c = __builtin_amdgcn_readfirstlane(sidx[i]);
+    return (unsigned)c < (unsigned)a.Nk ? c * 64 : a.L;
+  };
+  const int wave_hi = __builtin_amdgcn_readfirstlane(key_hi);
+  const int wave_lo = __builtin_amdgcn_readlane(key_lo, 31);
+  auto mask_half = [&](f32x16& sacc, int key0, int kt) {
+    const int base = key0 + 32 * kt + 4 * hf;
+    const int lim_hi = key_hi - base, lim_lo = key_lo - base;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int o = 8 * (r >> 2) + (r & 3);
+      if (o >= lim_hi || o < lim_lo) sacc[r] = -INFINITY;
+    }
+  };
+  auto compute = [&](const uint16_t* tile, int key0) {
+    const uint16_t* Ks = tile;
+    const uint16_t* Vs = tile + 64 * D;
+    f32x16 s0 = {}, s1 = {}, p0 = {}, p1 = {};
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      s0 = mfma32(lds_k_chunk<D>(Ks, l32, 2 * s + hf), as_bf16x8(qreg[s]), s0);
+      s1 = mfma32(lds_k_chunk<D>(Ks, 32 + l32, 2 * s + hf), as_bf16x8(qreg[s]), s1);
+      p0 = mfma32(lds_row_vswz<D>(Vs, l32, 2 * s + hf), as_bf16x8(dreg[s]), p0);
+      p1 = mfma32(lds_row_vswz<D>(Vs, 32 + l32, 2 * s + hf), as_bf16x8(dreg[s]), p1);
+    }
+    if (key0 + 64 > wave_hi || key0 < wave_lo) {
+      mask_half(s0, key0, 0);
+      mask_half(s1, key0, 1);
+    }
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const f32x16& sv = kt ? s1 : s0;
+      const f32x16& pv = kt ? p1 : p0;
+      float ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(sv[r], a.scale_log2, -lse));
+        ds[r] = p * (pv[r] - Di);
+      }
+      const bf16x8 dsa = to_bf16x8(ds), dsb = to_bf16x8(ds + 8);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) dqa[dt] = mfma32(lds_kt_operand<D>(Ks, lane, dt, 32 * kt), dsa, dqa[dt]);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+        dqa[dt] = mfma32(lds_kt_operand<D>(Ks, lane, dt, 32 * kt + 16), dsb, dqa[dt]);
+    }
+  };
+  ld.issue(smem0, block_tok0(0), lane, wv);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  int it = 0;
+  for (; it + 1 < a.kkeep; it += 2) {
+    ld.issue(smem1, block_tok0(it + 1), lane, wv);
+    compute(smem0, block_tok0(it));
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (it + 2 < a.kkeep) ld.issue(smem0, block_tok0(it + 2), lane, wv);
+    compute(smem1, block_tok0(it + 1));
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+  if (it < a.kkeep) compute(smem0, block_tok0(it));
+
+  if (q_ok) {
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int c0 = och(dt, 4 * rg, hf);
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = a.sm_scale * dqa[dt][4 * rg + e];
+        if (a.dQn_into_dQ) {
+          const f32x4 x = *reinterpret_cast<const f32x4*>(a.dQn + row * D + c0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] += x[e];
+        }
+        *reinterpret_cast<f32x4*>(a.dQ + row * D + c0) = v;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Softmax branch: dK and dV per key block.
+// ---------------------------------------------------------------------------
+// Workgroup = 4 waves on one 64-key block: wave w holds keys 32 (w & 1) ..
+// +31 (K and V rows in registers, B-operand layout) and takes the 32-query
+// sub-tiles s = (w >> 1), (w >> 1) + 2, ... of each staged query block; the
+// two waves of a key half add their dK^T, dV^T through LDS at the end.
+template <int D, int BQ>
+__global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
+  constexpr int NSUB = BQ / 32;
+  __shared__ __attribute__((aligned(16))) uint16_t tiles[2 * BQ * D];
+  __shared__ float lse_s[BQ], dd_s[BQ];
+  uint16_t* Qs = tiles;
+  uint16_t* Ds = tiles + BQ * D;
+  int64_t bh;
+  int kb;
+  if (!xcd_group_item(blockIdx.x, a.Nk, (int64_t)a.B * a.H, bh, kb)) return;
+  const int h = (int)(bh % a.H), b = (int)(bh / a.H);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hf = lane >> 5, l32 = lane & 31;
+  const int kh = wv & 1, qp = wv >> 1;
+  const int k_tok = kb * 64 + 32 * kh + l32;
+  const bool k_ok = k_tok < a.L;
+  const int k_cl = min(k_tok, a.L - 1);
+  // queries that see this key: [q_lo, q_hi)
+  const int k_chunk = k_cl / a.ar_tokens;
+  const int q_lo = k_chunk * a.ar_tokens;
+  const int q_hi = a.ar_window > 0 ? min(a.L, (k_chunk + a.ar_window) * a.ar_tokens) : a.L;
+  const int64_t krow = ((int64_t)b * a.L + k_cl) * a.H + h;
+
+  u32x4 kreg[D / 16], vreg[D / 16];
+  {
+    const uint16_t* kp = a.K + (int64_t)b * a.sk_b + (int64_t)k_cl * a.sk_l + (int64_t)h * a.sk_h;
+    const uint16_t* vp = a.V + (int64_t)b * a.sv_b + (int64_t)k_cl * a.sv_l + (int64_t)h * a.sv_h;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      kreg[s] = k_ok ? *reinterpret_cast<const u32x4*>(kp + 16 * s + 8 * hf) : u32x4{0, 0, 0, 0};
+      vreg[s] = k_ok ? *reinterpret_cast<const u32x4*>(vp + 16 * s + 8 * hf) : u32x4{0, 0, 0, 0};
+    }
+  }
+  f32x16 dka[D / 32], dva[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) {
+    dka[i] = f32x16{};
+    dva[i] = f32x16{};
+  }
+  // staging: Q rows K-swizzled, dO_s rows V-swizzled (range-checked buffers,
+  // rows past L read as zeros)
+  DirectTileLoader<D, 4> ld;
+  ld.init(a.Q + (int64_t)b * a.sq_b + (int64_t)h * a.sq_h, a.sq_l, a.dOs + (int64_t)b * a.L * a.H * D + (int64_t)h * D,
+          (int64_t)a.H * D, a.L, lane, wv);
+  const int32_t* list = a.tlist + bh * (int64_t)a.Nq * a.kkeep;
+  const int e0 = a.toff[bh * (a.Nk + 1) + kb], e1 = a.toff[bh * (a.Nk + 1) + kb + 1];
+  for (int e = e0; e < e1; ++e) {
+    const int qb = __builtin_amdgcn_readfirstlane(list[e]);
+    const int qt0 = qb * BQ;
+    __syncthreads();  // the previous block's readers are done
+#pragma unroll
+    for (int half = 0; half < BQ / 64; ++half) {
+      ld.issue_k(Qs + half * 64 * D, qt0 + 64 * half, lane, wv);
+      ld.issue_v(Ds + half * 64 * D, qt0 + 64 * half, wv);
+    }
+    for (int i = tid; i < BQ; i += 256) {
+      const int q = qt0 + i;
+      const int64_t r = ((int64_t)b * a.L + min(q, a.L - 1)) * a.H + h;
+      lse_s[i] = q < a.L ? a.lse[r] : INFINITY;
+      dd_s[i] = q < a.L ? a.Dd[r] : 0.f;
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    for (int sub = qp; sub < NSUB; sub += 2) {
+      const int qr0 = 32 * sub;  // first row of the sub-tile in the staged block
+      f32x16 sa = {}, pa = {};
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        sa = mfma32(lds_k_chunk<D>(Qs, qr0 + l32, 2 * s + hf), as_bf16x8(kreg[s]), sa);
+        pa = mfma32(lds_row_vswz<D>(Ds, qr0 + l32, 2 * s + hf), as_bf16x8(vreg[s]), pa);
+      }
+      // register r holds query row qr0 + 8 (r / 4) + 4 hf + r % 4 of key l32
+      float pr[16], dsr[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qi = qr0 + 8 * (r >> 2) + 4 * hf + (r & 3);
+        const int q = qt0 + qi;
+        float p = __builtin_amdgcn_exp2f(fmaf(sa[r], a.scale_log2, -lse_s[qi]));
+        p = (q >= q_lo && q < q_hi) ? p : 0.f;
+        pr[r] = p;
+        dsr[r] = p * (pa[r] - dd_s[qi]);
+      }
+      const bf16x8 pa0 = to_bf16x8(pr), pa1 = to_bf16x8(pr + 8);
+      const bf16x8 ds0 = to_bf16x8(dsr), ds1 = to_bf16x8(dsr + 8);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        dva[dt] = mfma32(lds_v_operand<D>(Ds, lane, dt, qr0), pa0, dva[dt]);
+        dva[dt] = mfma32(lds_v_operand<D>(Ds, lane, dt, qr0 + 16), pa1, dva[dt]);
+        dka[dt] = mfma32(lds_kt_operand<D>(Qs, lane, dt, qr0), ds0, dka[dt]);
+        dka[dt] = mfma32(lds_kt_operand<D>(Qs, lane, dt, qr0 + 16), ds1, dka[dt]);
+      }
+    }
+  }
+  // the two waves of each key half add their sums: waves 2, 3 hand theirs
+  // over through the tile memory, dK^T first, then dV^T
+  float* red = reinterpret_cast<float*>(tiles);
+  static_assert(2 * 64 * (D / 2) * 4 <= 2 * BQ * D * 2, "reduction buffer exceeds the staged tiles");
+  const int ridx = (kh * 64 + lane) * (D / 2);
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    __syncthreads();
+    if (qp == 1) {
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) red[ridx + 16 * dt + r] = pass ? dva[dt][r] : dka[dt][r];
+    }
+    __syncthreads();
+    if (qp == 0 && k_ok) {
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          f32x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * rg + e;
+            const float sum = (pass ? dva[dt][r] : dka[dt][r]) + red[ridx + 16 * dt + r];
+            v[e] = pass ? sum : a.sm_scale * sum;
+          }
+          *reinterpret_cast<f32x4*>((pass ? a.dV : a.dK) + krow * D + och(dt, 4 * rg, hf)) = v;
+        }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers.
+// ---------------------------------------------------------------------------
+static int64_t group_grid(int items, int64_t groups) {
+  return (int64_t)kNumXcd * ((items + kNumXcd - 1) / kNumXcd) * groups;
+}
+
+hipError_t launch_bwd_query(const BwdArgs& a, int D, hipStream_t stream) {
+  const dim3 grid((unsigned)group_grid((a.L + 127) / 128, (int64_t)a.B * a.H));
+  if (D == 128)
+    hipLaunchKernelGGL(bwd_query_kernel<128>, grid, dim3(256), 0, stream, a);
+  else if (D == 64)
+    hipLaunchKernelGGL(bwd_query_kernel<64>, grid, dim3(256), 0, stream, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_key(const BwdArgs& a, int D, hipStream_t stream) {
+  const dim3 grid((unsigned)group_grid((a.L + 127) / 128, (int64_t)a.B * a.H));
+  if (D == 128)
+    hipLaunchKernelGGL(bwd_key_kernel<128>, grid, dim3(256), 0, stream, a);
+  else if (D == 64)
+    hipLaunchKernelGGL(bwd_key_kernel<64>, grid, dim3(256), 0, stream, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq(const BwdArgs& a, int D, hipStream_t stream) {
+  const dim3 grid((unsigned)group_grid(a.Nq, (int64_t)a.B * a.H));
+  if (D == 128 && a.block_q == 128)
+    hipLaunchKernelGGL((bwd_dq_kernel<128, 128>), grid, dim3(256), 0, stream, a);
+  else if (D == 128 && a.block_q == 64)
+    hipLaunchKernelGGL((bwd_dq_kernel<128, 64>), grid, dim3(128), 0, stream, a);
+  else if (D == 64 && a.block_q == 128)
+    hipLaunchKernelGGL((bwd_dq_kernel<64, 128>), grid, dim3(256), 0, stream, a);
+  else if (D == 64 && a.block_q == 64)
+    hipLaunchKernelGGL((bwd_dq_kernel<64, 64>), grid, dim3(128), 0, stream, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkdv(const BwdArgs& a, int D, hipStream_t stream) {
+  const dim3 grid((unsigned)group_grid(a.Nk, (int64_t)a.B * a.H));
+  if (D == 128 && a.block_q == 128)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<128, 128>), grid, dim3(256), 0, stream, a);
+  else if (D == 128 && a.block_q == 64)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<128, 64>), grid, dim3(256), 0, stream, a);
+  else if (D == 64 && a.block_q == 128)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<64, 128>), grid, dim3(256), 0, stream, a);
+  else if (D == 64 && a.block_q == 64)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<64, 64>), grid, dim3(256), 0, stream, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_map(const int32_t* idx, int BH, int Nq, int Nk, int k, int32_t* tlist, int32_t* toff,
+                                hipStream_t stream) {
+  hipLaunchKernelGGL(transpose_map_kernel, dim3(BH), dim3(256), 0, stream, idx, Nq, Nk, k, tlist, toff);
+  return hipGetLastError();
+}
+
+hipError_t launch_token_outer(const float* X, const float* Yf, const uint16_t* Yb, int64_t y_sb, int64_t y_sl,
+                              int64_t y_sh, int B, int H, int L, int D, const RunGeo& runs, float* part,
+                              hipStream_t stream) {
+  const dim3 grid((unsigned)((int64_t)runs.n_runs * B * H));
+  if (D == 128)
+    hipLaunchKernelGGL(token_outer_kernel<128>, grid, dim3(256), 0, stream, X, Yf, Yb, y_sb, y_sl, y_sh, B, H, L,
+                       runs, part);
+  else if (D == 64)
+    hipLaunchKernelGGL(token_outer_kernel<64>, grid, dim3(256), 0, stream, X, Yf, Yb, y_sb, y_sl, y_sh, B, H, L,
+                       runs, part);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_dstate_finalize(const float* part, int BH, const RunGeo& runs, int n_ar, int window, int D,
+                                  float* dC, uint16_t* dCt_hi, uint16_t* dCt_lo, hipStream_t stream) {
+  const int64_t total = (int64_t)BH * n_ar * 32 * D;
+  hipLaunchKernelGGL(dstate_finalize_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, part,
+                     (int64_t)BH, runs, n_ar, window, D, dC, dCt_hi, dCt_lo);
+  return hipGetLastError();
+}
+
+hipError_t launch_dproj_finalize(const float* part, int B, int H, int n_runs, int rank, int D, bool per_head,
+                                 float* dP, hipStream_t stream) {
+  const int64_t total = (int64_t)(per_head ? H : 1) * rank * D;
+  hipLaunchKernelGGL(dproj_finalize_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, part, B, H,
+                     n_runs, rank, D, per_head ? 1 : 0, dP);
+  return hipGetLastError();
+}
+
+hipError_t launch_dgate(const float* dg_head, int B, int L, int H, int64_t g_sb, int64_t g_sl, int64_t g_sh,
+                        float* dg, hipStream_t stream) {
+  const int64_t total = g_sh == 0 ? (int64_t)B * L : (int64_t)B * L * H;
+  hipLaunchKernelGGL(dgate_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, dg_head, B, L, H,
+                     g_sb, g_sl, g_sh, dg);
+  return hipGetLastError();
+}
+
+}  // namespace sd

@@ -46,6 +46,7 @@ struct AttnArgs {
   void* out;
   int out_f32;
   float* rms;  // optional [B, L, H]
+  float* lse;  // optional [B, L, H], sparse mode: m + log2(l) of the scaled scores
   // low-rank branch
   const uint16_t* Pq;
   int64_t P_hs;
@@ -183,6 +184,86 @@ hipError_t launch_lowrank_finalize(const float* partial, int BH, const RunGeo& r
                                    int D, const RankRows& rows, float* C_out, uint16_t* Ct_hi, uint16_t* Ct_lo,
                                    hipStream_t stream);
 hipError_t launch_prepare_stream(const PrepareArgs& a, int D, hipStream_t stream);
+
+// Backward of the fused layer (block map fixed). Per-token buffers are
+// contiguous [B, L, H, ...]; Q/Qn share the sq_* strides, K/Kn the sk_*, V
+// the sv_* and dO the so_*.
+struct BwdArgs {
+  int B, H, L, Nq, Nk, kkeep, Hg, Wg, block_q;
+  int ar_tokens, ar_window;
+  int64_t sq_b, sq_l, sq_h, sk_b, sk_l, sk_h, sv_b, sv_l, sv_h, so_b, so_l, so_h;
+  const uint16_t* Q;
+  const uint16_t* K;
+  const uint16_t* V;
+  const uint16_t* Qn;  // may equal Q
+  const uint16_t* Kn;  // may equal K
+  const int32_t* idx;  // [B, H, Nq, kkeep]
+  float scale_log2, sm_scale;
+  // low-rank branch
+  const uint16_t* Pq;
+  const uint16_t* Pk;
+  int64_t P_hs;
+  int rank;
+  const float2* rope_tab;
+  RopeArgs rope;
+  const uint16_t* Ct_hi;  // [B*H, n_ar, D, 32] state transposed, hi / lo
+  const uint16_t* Ct_lo;
+  const float* C;  // [B*H, n_ar, rank, D] state rows
+  float eps;
+  const uint16_t* rmsw;
+  const float* g;
+  int64_t g_sb, g_sl, g_sh;
+  const uint16_t* dO;  // bf16 at so_*
+  // forward intermediates
+  const float* Os;   // [B, L, H, D]
+  const float* rms;  // [B, L, H]
+  const float* lse;  // [B, L, H]
+  // backward intermediates
+  uint16_t* dOs;   // bf16 [B, L, H, D]
+  float* Dd;       // [B, L, H]: dO_s . O_s
+  float* dg_head;  // [B, L, H]
+  float* qt;       // [B, L, H, 32] q~
+  float* dy;       // [B, L, H, D]
+  float* da;       // [B, L, H, 32]
+  float* db;       // [B, L, H, 32]
+  const float* dC;        // [B*H, n_ar, 32, D]: for chunk c, the sum of dC over the chunks that see c
+  const uint16_t* dCt_hi;  // [B*H, n_ar, D, 32] the same transposed, hi / lo
+  const uint16_t* dCt_lo;
+  // key-block -> query-block lists
+  const int32_t* tlist;  // [B*H, Nq*kkeep]
+  const int32_t* toff;   // [B*H, Nk + 1]
+  // outputs, f32 [B, L, H, D]
+  float* dQ;
+  float* dK;
+  float* dV;
+  float* dQn;  // receives the low-rank query-side gradient (may be a workspace buffer)
+  float* dKn;
+  int dQn_into_dQ, dKn_into_dK;  // the branch read Q / K: add into dQ / dK
+};
+hipError_t launch_bwd_query(const BwdArgs& a, int D, hipStream_t stream);
+hipError_t launch_bwd_key(const BwdArgs& a, int D, hipStream_t stream);
+hipError_t launch_bwd_dq(const BwdArgs& a, int D, hipStream_t stream);
+hipError_t launch_bwd_dkdv(const BwdArgs& a, int D, hipStream_t stream);
+hipError_t launch_transpose_map(const int32_t* idx, int BH, int Nq, int Nk, int k, int32_t* tlist, int32_t* toff,
+                                hipStream_t stream);
+// Partial sums over runs of tokens of X^T Y, X [rows][32] f32 (contiguous,
+// row = token*H + head), Y [rows][D] (f32 contiguous when Yf, else bf16 at
+// token stride y_sl and head stride y_sh): part[(bh * runs.n_runs + run)][32][D].
+hipError_t launch_token_outer(const float* X, const float* Yf, const uint16_t* Yb, int64_t y_sb, int64_t y_sl,
+                              int64_t y_sh, int B, int H, int L, int D, const RunGeo& runs, float* part,
+                              hipStream_t stream);
+// Gradient of the state seen by each chunk: for (bh, chunk c) the sum of the
+// run partials of chunks c .. c + window - 1 (window 0: c .. last), written
+// as rows f32 [32][D] and transposed bf16 hi / lo [D][32].
+hipError_t launch_dstate_finalize(const float* part, int BH, const RunGeo& runs, int n_ar, int window, int D,
+                                  float* dC, uint16_t* dCt_hi, uint16_t* dCt_lo, hipStream_t stream);
+// dP [n_out][rank][D] = the sum of the run partials of every (b, h) (n_out = 1)
+// or of every b for each h (n_out = H), in a fixed order.
+hipError_t launch_dproj_finalize(const float* part, int B, int H, int n_runs, int rank, int D, bool per_head,
+                                 float* dP, hipStream_t stream);
+// dg from the per-(token, head) shares: summed over the heads when g_sh == 0.
+hipError_t launch_dgate(const float* dg_head, int B, int L, int H, int64_t g_sb, int64_t g_sl, int64_t g_sh,
+                        float* dg, hipStream_t stream);
 hipError_t launch_gate_fuse(const void* Os, const void* Olr, int in_f32, const float* g, int64_t g_sb, int64_t g_sl,
                             int64_t g_sh, void* O, int B, int L, int H, int D, int64_t so_b, int64_t so_l,
                             int64_t so_h, hipStream_t stream);

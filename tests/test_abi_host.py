@@ -270,3 +270,28 @@ def test_variant_fields_validation():
     assert many > one > 0
     # chunks longer than the sequence are the bidirectional layer
     assert lib.sd_rola_workspace_size(ctypes.byref(shp(chunk=5000)), ctypes.byref(p), 4) == one
+
+
+@host_only
+def test_backward_validation():
+    lib = sd.lib()
+    s = _shape()
+    p, keep = _lr()
+    need = lib.sd_rola_backward_workspace_size(ctypes.byref(s), ctypes.byref(p), 4)
+    assert need > lib.sd_rola_workspace_size(ctypes.byref(s), ctypes.byref(p), 4)
+
+    def call(k=4, ws_bytes=need, Qn=None, dQn=None, idx=FAKE, dO=FAKE, dV=FAKE, g=FAKE, dg=None):
+        return lib.sd_rola_backward(ctypes.byref(s), ctypes.byref(p), FAKE, FAKE, FAKE, Qn, None, g, 0, 1, 0, k,
+                                    0.125, idx, dO, FAKE, FAKE, dV, dQn, None, None, None, dg, FAKE, ws_bytes, None)
+
+    assert call(k=0) == sd.SD_ERR_INVALID_ARG
+    assert call(idx=None) == sd.SD_ERR_INVALID_ARG
+    assert call(dO=None) == sd.SD_ERR_INVALID_ARG
+    assert call(dV=None) == sd.SD_ERR_INVALID_ARG
+    assert call(g=None) == sd.SD_ERR_INVALID_ARG
+    assert call(Qn=FAKE) == sd.SD_ERR_INVALID_ARG  # dQn must come with Qn
+    assert call(dQn=FAKE) == sd.SD_ERR_INVALID_ARG
+    assert call(Qn=FAKE, dQn=FAKE + 4) == sd.SD_ERR_ALIGN
+    assert call(dg=FAKE + 2) == sd.SD_ERR_ALIGN
+    assert call(ws_bytes=need - 1) == sd.SD_ERR_WORKSPACE
+    assert lib.sd_rola_backward_workspace_size(ctypes.byref(s), ctypes.byref(p), 0) == 0

@@ -1,0 +1,136 @@
+"""GPU parity of the backward of the fused layer against the oracle.
+
+The HIP backward (sd_rola_backward, through the C ABI) and the oracle's
+chain-rule backward (oracle/backward.py, pinned by finite differences of
+the forward oracle) run on the same seeded inputs and the same block map
+(the one the GPU forward chose).
+
+Tolerance, from the arithmetic: the softmax branch feeds P, dS and dO_s to
+the matrix cores as bf16 (as attention backward kernels do), each rounded to
+nearest with a relative error of at most 2^-9; every gradient element is a
+sum of products that carry one or two such roundings, so its relative L2
+error is of order 2^-9. The low-rank products use hi/lo bf16 splits (about
+16 bits) and f32 sums. Each of dQ, dK, dV, dQn, dKn is held to a relative
+L2 error of 2^-7 (4 x 2^-9) and a worst element of 2^-6 of its largest
+magnitude; dPq, dPk and dg, whose errors come from the same roundings
+averaged over every token, to a relative L2 error of 2^-9. Measured worst:
+2.5e-3, 3.7e-3 and 4.0e-4.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_rank_attention_rola_amd as sd
+from workloads import synthetic
+from gpu_util import dev_bf16, dev_f32, host, say
+
+pytestmark = pytest.mark.gpu
+
+RAGGED = synthetic.AttnConfig("ragged-330", 1, 3, 128, 3, 10, 11, 128, 64, 0.70, 32)
+RAGGED64 = synthetic.AttnConfig("ragged-d64", 2, 2, 64, 5, 7, 13, 64, 64, 0.60, 16)
+FRAMES = synthetic.AttnConfig("frames-780", 1, 2, 128, 6, 10, 13, 128, 64, 0.70, 32)
+MID = synthetic.AttnConfig("mid-2176", 1, 2, 128, 2, 32, 34, 128, 64, 0.90, 32)
+
+
+def _rel(got, ref, name, rel_l2=2.0 ** -7, max_frac=2.0 ** -6):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert np.isfinite(got).all(), name
+    scale = max(np.abs(ref).max(), 1e-30)
+    ma = np.abs(got - ref).max() / scale
+    rl = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)
+    say(f"  {name}: rel_l2={rl:.2e} max_abs/max|ref|={ma:.2e}")
+    assert rl <= rel_l2 and ma <= max_frac, f"{name}: rel_l2 {rl:.3e}, max {ma:.3e}"
+
+
+def _run(cfg, seed=0, chunk_frames=0, window=0, separate_qk=False, per_head_gate=False):
+    Qb, Kb, Vb = synthetic.gen_qkv(cfg, seed)
+    Pqb, Pkb = synthetic.gen_lowrank_params(cfg)
+    rng = np.random.default_rng(seed + 100)
+    if per_head_gate:
+        g = (1.0 + rng.standard_normal((cfg.B, cfg.L, cfg.H))).astype(np.float32)
+    else:
+        g = synthetic.gen_gate(cfg, amplified=True)
+    dOb = synthetic.f32_to_bf16_bits(rng.standard_normal((cfg.B, cfg.L, cfg.H, cfg.d)).astype(np.float32))
+    Qnb = Knb = None
+    if separate_qk:
+        Qnb, Knb, _ = synthetic.gen_qkv(cfg, seed + 7)
+    ct = chunk_frames * cfg.Hg * cfg.Wg
+    var = dict(chunk_tokens=ct, window=window)
+    grid = (cfg.T, cfg.Hg, cfg.Wg)
+    Q, K, V, dO = dev_bf16(Qb), dev_bf16(Kb), dev_bf16(Vb), dev_bf16(dOb)
+    Qn = dev_bf16(Qnb) if separate_qk else None
+    Kn = dev_bf16(Knb) if separate_qk else None
+    lr = sd.LowrankParams(dev_bf16(Pqb), dev_bf16(Pkb))
+    k = oracle.keep_count(cfg.sparsity, -(-cfg.L // cfg.block_k))
+    nq = -(-cfg.L // cfg.block_q)
+    idx = torch.empty((cfg.B, cfg.H, nq, k), dtype=torch.int32, device="cuda")
+    gd = dev_f32(g)
+    ws = sd.rola_workspace(Q, lr, k, grid=grid, block_q=cfg.block_q, **var)
+    sd.sd_rola_prepare(Q, K, V, lr, k, ws, grid=grid, block_q=cfg.block_q, Qn=Qn, Kn=Kn, idx_out=idx, **var)
+    grads = sd.sd_rola_backward(Q, K, V, gd, lr, k, idx, dO, grid=grid, block_q=cfg.block_q, Qn=Qn, Kn=Kn, **var)
+    torch.cuda.synchronize()
+    got = {n: (host(t) if t is not None else None) for n, t in grads.items()}
+    idx = idx.cpu().numpy()
+    f = oracle.bf16_bits_to_f64
+    Pq, Pk = f(Pqb), f(Pkb)
+    ref = {"dPq": 0.0, "dPk": 0.0, "dg": np.zeros(g.shape)}
+    for b in range(cfg.B):
+        for h in range(cfg.H):
+            X = [f(x[b, :, h]) for x in (Qb, Kb, Vb)]
+            Xn = [f(Qnb[b, :, h]), f(Knb[b, :, h])] if separate_qk else X[:2]
+            gh = (g[b, :, h] if per_head_gate else g[b]).astype(np.float64)
+            res = oracle.rola_backward_head(*X, *Xn, Pq, Pk, gh, idx[b, h], f(dOb[b, :, h]), T=cfg.T, Hg=cfg.Hg,
+                                            Wg=cfg.Wg, bq=cfg.block_q, bk=cfg.block_k,
+                                            sm_scale=1.0 / math.sqrt(cfg.d), chunk_tokens=ct, window=window)
+            dQ, dK = res["dQ"], res["dK"]
+            if separate_qk:
+                _rel(got["dQn"][b, :, h], res["dQn"], f"dQn b{b} h{h}")
+                _rel(got["dKn"][b, :, h], res["dKn"], f"dKn b{b} h{h}")
+            else:
+                dQ, dK = dQ + res["dQn"], dK + res["dKn"]
+            _rel(got["dQ"][b, :, h], dQ, f"dQ b{b} h{h}")
+            _rel(got["dK"][b, :, h], dK, f"dK b{b} h{h}")
+            _rel(got["dV"][b, :, h], res["dV"], f"dV b{b} h{h}")
+            ref["dPq"] = ref["dPq"] + res["dPq"]
+            ref["dPk"] = ref["dPk"] + res["dPk"]
+            if per_head_gate:
+                ref["dg"][b, :, h] = res["dg"]
+            else:
+                ref["dg"][b] += res["dg"]
+    _rel(got["dPq"], ref["dPq"][: cfg.rank], "dPq", rel_l2=2.0 ** -9)
+    _rel(got["dPk"], ref["dPk"][: cfg.rank], "dPk", rel_l2=2.0 ** -9)
+    _rel(got["dg"], ref["dg"], "dg", rel_l2=2.0 ** -9)
+    return grads
+
+
+@pytest.mark.parametrize("cfg", [RAGGED, RAGGED64, MID], ids=lambda c: c.name)
+def test_backward_bidirectional(cfg):
+    say(f"backward {cfg.name}")
+    _run(cfg)
+
+
+def test_backward_separate_qk_and_per_head_gate():
+    say("backward ragged, separate Qn/Kn, per-head gate")
+    _run(RAGGED, seed=3, separate_qk=True, per_head_gate=True)
+
+
+@pytest.mark.parametrize("frames,window", [(1, 0), (1, 2), (2, 1)])
+def test_backward_causal_window(frames, window):
+    say(f"backward frames-780 causal f{frames} w{window}")
+    _run(FRAMES, seed=1, chunk_frames=frames, window=window)
+
+
+def test_backward_d64_causal():
+    say("backward ragged-d64 causal f1 w2")
+    _run(RAGGED64, seed=2, chunk_frames=1, window=2)
+
+
+def test_backward_deterministic():
+    a = _run(RAGGED, seed=5)
+    b = _run(RAGGED, seed=5)
+    for n in ("dQ", "dK", "dV", "dPq", "dPk", "dg"):
+        assert torch.equal(a[n], b[n]), n
