@@ -11,8 +11,8 @@ bf16 activation. One step = quantise the activation, then the fused layer
 W8A8 QKV projection that consumes the quantised activation (75600 x 15360 x
 5120) is timed on its own after the steps and reported beside them, as are
 the same layer with the fixed spatio-temporal selector and under a causal
-window (3-frame chunks), and the whole attention block in FP8 deployment
-precision.
+window (3-frame chunks), the backward of the layer, and the whole
+attention block in FP8 deployment precision.
 Inputs are seeded synthetic tensors of those shapes, resident in HBM before
 the timed region.
 
@@ -163,6 +163,7 @@ def main():
     ap.add_argument("--block-timesteps", type=int, default=3, help="timesteps of the deployment block")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the fixed-selector and causal-window measurements")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward measurement")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter calibration)")
     ap.add_argument("--trace-summary", metavar="DB", help="print a kernel table of a rocprofv3 trace and exit")
@@ -285,6 +286,32 @@ def main():
                               "kept_pair_tflops": round(fl / (ta * 1e-3) / 1e12, 1)}
             log(f"variant {name}: {tp + ta:.3f} ms")
             del wsv, idv
+
+    # Backward of the same layer (the training step of the sparse student):
+    # every gradient for a seeded bf16 output gradient, the block map of the
+    # forward held fixed; it recomputes the forward quantities it needs.
+    backward = None
+    if not args.no_backward:
+        dO = to_dev(synthetic.f32_to_bf16_bits(
+            np.random.default_rng(7).standard_normal((cfg.B, cfg.L, cfg.H, cfg.d)).astype(np.float32)))
+        bws = sd.rola_backward_workspace(Q, lr, k, grid=grid, block_q=cfg.block_q)
+        for _ in range(max(1, args.warmup // 2)):
+            grads = sd.sd_rola_backward(Q, K, V, gd, lr, k, idx, dO, grid=grid, block_q=cfg.block_q, workspace=bws)
+        torch.cuda.synchronize()
+        n_b = max(3, args.steps // 4)
+        bev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        bev[0].record()
+        for _ in range(n_b):
+            grads = sd.sd_rola_backward(Q, K, V, gd, lr, k, idx, dO, grid=grid, block_q=cfg.block_q, workspace=bws)
+        bev[1].record()
+        torch.cuda.synchronize()
+        t_b = bev[0].elapsed_time(bev[1]) / n_b
+        fl_b = 2.5 * kept_pair_flops(idx.cpu().numpy(), cfg.L, cfg.block_q, cfg.block_k, cfg.d)
+        backward = {"ms": round(t_b, 4), "ms_forward_plus_backward": round(t_b + t_layer, 4),
+                    "kept_pair_tflops_softmax_branch": round(fl_b / (t_b * 1e-3) / 1e12, 1),
+                    "note": "recomputes the state, O_s and the log-sum-exp; 2.5x the forward kept-pair FLOPs"}
+        log(f"backward: {t_b:.3f} ms")
+        del grads, bws, dO
 
     # W8A8 FP8 QKV projection of the same layer (the step that consumes the
     # quantised activation): weights quantised per output channel once,
@@ -428,6 +455,7 @@ def main():
                      "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
                      "algorithmic_flops_per_launch": flops},
         "variants_720p": variants,
+        "backward_720p": backward,
         "w8a8_qkv_projection": gemm,
         "deployment_block_720p": block,
         "cpu_baseline": cpu,

@@ -405,6 +405,12 @@ def sd_rola_apply(Q, K, V, g, lr: LowrankParams, k_keep, workspace, *, grid, blo
     return out
 
 
+def rola_backward_workspace(Q, lr: LowrankParams, k_keep, *, grid, block_q=128, chunk_tokens=0, window=0):
+    s = make_shape(Q, Q, Q, block_q=block_q, grid=grid, chunk_tokens=chunk_tokens, window=window)
+    return _workspace(lib().sd_rola_backward_workspace_size(ctypes.byref(s), ctypes.byref(lr.p), int(k_keep)),
+                      Q.device)
+
+
 def sd_rola_backward(Q, K, V, g, lr: LowrankParams, k_keep, idx, dO, *, grid, block_q=128, Qn=None, Kn=None,
                      sm_scale=None, want_dP=True, want_dg=True, chunk_tokens=0, window=0, workspace=None,
                      stream=None):
@@ -429,8 +435,8 @@ def sd_rola_backward(Q, K, V, g, lr: LowrankParams, k_keep, idx, dO, *, grid, bl
     else:
         out["dg"] = None
     if workspace is None:
-        workspace = _workspace(lib().sd_rola_backward_workspace_size(ctypes.byref(s), ctypes.byref(lr.p),
-                                                                     int(k_keep)), Q.device)
+        workspace = rola_backward_workspace(Q, lr, k_keep, grid=grid, block_q=block_q, chunk_tokens=chunk_tokens,
+                                            window=window)
     scale = sm_scale if sm_scale is not None else 1.0 / math.sqrt(d)
     gb, gl, gh = _gate_strides(g, B, L, H)
     _check(lib().sd_rola_backward(ctypes.byref(s), ctypes.byref(lr.p), _ptr(Q), _ptr(K), _ptr(V), _ptr(Qn), _ptr(Kn),

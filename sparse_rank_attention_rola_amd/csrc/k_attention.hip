@@ -343,7 +343,7 @@ __global__ __launch_bounds__(BQ * 2, BQ == 128 ? SD_ATTN_WAVES : 1) void attenti
       if (a.rms && hf == 0) a.rms[((int64_t)b * a.L + q_tok) * a.H + h] = sqrtf(ss * (1.0f / D));
       // log2-domain log-sum-exp of the query's scaled scores, for the
       // backward's recomputation of P (+inf where the query saw no key)
-      if (a.lse && hf == 0) a.lse[((int64_t)b * a.L + q_tok) * a.H + h] = ltot > 0.f ? m_fin + log2f(ltot) : INFINITY;
+      if (a.lse && hf == 0) a.lse[((int64_t)b * a.H + h) * a.L + q_tok] = ltot > 0.f ? m_fin + log2f(ltot) : INFINITY;
     }
   } else {
     float* Fw = reinterpret_cast<float*>(smem0) + wv * (32 * 33);

@@ -33,8 +33,8 @@
 //   bwd_dq_kernel       per query block, like the forward loop: S^T, P^T
 //                       from the saved log-sum-exp, dP^T = V dO_s^T, dS^T,
 //                       dQ^T += K^T dS^T (K^T by transposing LDS reads).
-//   bwd_dkdv_kernel     per key block, over the query blocks that keep it:
-//                       S = Q K^T, dP = dO_s V^T with K, V in registers,
+//   bwd_dkdv_kernel     per key block (K, V staged in LDS once), over the
+//                       query blocks that keep it: S = Q K^T, dP = dO_s V^T,
 //                       dV^T += dO_s^T P and dK^T += Q^T dS (transposing
 //                       reads of the staged Q and dO_s tiles).
 // Every sum runs in a fixed order: the results are bitwise reproducible.
@@ -258,7 +258,7 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
     }
   dsum += partner32(dsum, hf);
   uy += partner32(uy, hf);
-  if (q_ok && hf == 0) a.Dd[row] = dsum;
+  if (q_ok && hf == 0) a.Dd[bh * a.L + q_cl] = dsum;
   const float k3 = uy * inv * inv * inv * (1.0f / D);
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) {
@@ -445,21 +445,35 @@ __global__ void dstate_finalize_kernel(const float* __restrict__ part, int64_t B
   dCt_lo[(bc * D + d) * 32 + r] = __builtin_bit_cast(uint16_t, lo);
 }
 
-__global__ void dproj_finalize_kernel(const float* __restrict__ part, int B, int H, int n_runs, int rank, int D,
-                                      int per_head, float* __restrict__ dP) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+// 64 output elements per workgroup; its 4 waves sum contiguous quarters of
+// the partial list (b, h, run order) with coalesced loads, then the quarters
+// are added in order.
+__global__ __launch_bounds__(256) void dproj_finalize_kernel(const float* __restrict__ part, int B, int H, int n_runs,
+                                                             int rank, int D, int per_head, float* __restrict__ dP) {
+  __shared__ float q4[4][64];
   const int n_out = per_head ? H : 1;
-  if (i >= (int64_t)n_out * rank * D) return;
-  const int d = (int)(i % D);
-  const int r = (int)((i / D) % rank);
-  const int o = (int)(i / ((int64_t)rank * D));
+  const int64_t total = (int64_t)n_out * rank * D;
+  const int64_t i = (int64_t)blockIdx.x * 64 + (threadIdx.x & 63);
+  const int qt = threadIdx.x >> 6;
   float s = 0.f;
-  for (int b = 0; b < B; ++b)
-    for (int h = per_head ? o : 0; h < (per_head ? o + 1 : H); ++h) {
-      const float* p = part + (((int64_t)b * H + h) * n_runs * 32 + r) * D + d;
-      for (int u = 0; u < n_runs; ++u) s += p[(int64_t)u * 32 * D];
+  if (i < total) {
+    const int d = (int)(i % D);
+    const int r = (int)((i / D) % rank);
+    const int o = (int)(i / ((int64_t)rank * D));
+    const int hs = per_head ? 1 : H;  // heads per output
+    const int64_t n = (int64_t)B * hs * n_runs;
+    const int64_t u0 = n * qt / 4, u1 = n * (qt + 1) / 4;
+    for (int64_t u = u0; u < u1; ++u) {
+      const int run = (int)(u % n_runs);
+      const int64_t bh_local = u / n_runs;
+      const int hh = (int)(bh_local % hs), b = (int)(bh_local / hs);
+      const int h = per_head ? o : hh;
+      s += part[((((int64_t)b * H + h) * n_runs + run) * 32 + r) * D + d];
     }
-  dP[i] = s;
+  }
+  q4[qt][threadIdx.x & 63] = s;
+  __syncthreads();
+  if (qt == 0 && i < total) dP[i] = ((q4[0][threadIdx.x] + q4[1][threadIdx.x]) + q4[2][threadIdx.x]) + q4[3][threadIdx.x];
 }
 
 __global__ void dgate_kernel(const float* __restrict__ dg_head, int B, int L, int H, int64_t g_sb, int64_t g_sl,
@@ -749,8 +763,8 @@ __global__ __launch_bounds__(BQ * 2) void bwd_dq_kernel(BwdArgs a) {
       dreg[s] = q_ok ? *reinterpret_cast<const u32x4*>(dp + 16 * s + 8 * hf) : u32x4{0, 0, 0, 0};
     }
   }
-  const float lse = q_ok ? a.lse[row] : INFINITY;
-  const float Di = q_ok ? a.Dd[row] : 0.f;
+  const float lse = q_ok ? a.lse[bh * a.L + q_cl] : INFINITY;
+  const float Di = q_ok ? a.Dd[bh * a.L + q_cl] : 0.f;
   f32x16 dqa[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) dqa[i] = f32x16{};
@@ -848,17 +862,20 @@ __global__ __launch_bounds__(BQ * 2) void bwd_dq_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // Softmax branch: dK and dV per key block.
 // ---------------------------------------------------------------------------
-// Workgroup = 4 waves on one 64-key block: wave w holds keys 32 (w & 1) ..
-// +31 (K and V rows in registers, B-operand layout) and takes the 32-query
-// sub-tiles s = (w >> 1), (w >> 1) + 2, ... of each staged query block; the
-// two waves of a key half add their dK^T, dV^T through LDS at the end.
+// Workgroup = 4 waves on one 64-key block, whose K and V tiles are staged in
+// LDS once: wave w works on keys 32 (w & 1) .. +31 and on query sub-tile
+// (w >> 1) of every 64-query unit; the two waves of a key half add their
+// dK^T, dV^T through LDS at the end. Per unit of the query blocks that keep
+// the key block, the Q rows (K-swizzled), dO_s rows (V-swizzled) and the
+// unit's log-sum-exp and D values are staged with direct-to-LDS loads; the
+// tiles stay small (66 KB) so that two workgroups share a compute unit and
+// one's loads overlap the other's matrix work.
 template <int D, int BQ>
-__global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
-  constexpr int NSUB = BQ / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t tiles[2 * BQ * D];
-  __shared__ float lse_s[BQ], dd_s[BQ];
-  uint16_t* Qs = tiles;
-  uint16_t* Ds = tiles + BQ * D;
+__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
+  constexpr int UPB = BQ / 64;  // 64-query units per query block
+  __shared__ __attribute__((aligned(16))) uint16_t qd[2 * 64 * D];  // Q then dO_s rows of the unit
+  __shared__ __attribute__((aligned(16))) uint16_t kv[2 * 64 * D];  // K then V rows of the key block
+  __shared__ __attribute__((aligned(16))) float rowv[2][256];       // lse, D of the unit (1 KB DMA rows)
   int64_t bh;
   int kb;
   if (!xcd_group_item(blockIdx.x, a.Nk, (int64_t)a.B * a.H, bh, kb)) return;
@@ -867,89 +884,90 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hf = lane >> 5, l32 = lane & 31;
   const int kh = wv & 1, qp = wv >> 1;
-  const int k_tok = kb * 64 + 32 * kh + l32;
+  const int krow0 = 32 * kh;  // the wave's first key row in the key tile
+  const int k_tok = kb * 64 + krow0 + l32;
   const bool k_ok = k_tok < a.L;
   const int k_cl = min(k_tok, a.L - 1);
-  // queries that see this key: [q_lo, q_hi)
+  // queries that see this key: [q_lo, q_hi) (q_hi <= L masks the tail)
   const int k_chunk = k_cl / a.ar_tokens;
   const int q_lo = k_chunk * a.ar_tokens;
   const int q_hi = a.ar_window > 0 ? min(a.L, (k_chunk + a.ar_window) * a.ar_tokens) : a.L;
   const int64_t krow = ((int64_t)b * a.L + k_cl) * a.H + h;
 
-  u32x4 kreg[D / 16], vreg[D / 16];
-  {
-    const uint16_t* kp = a.K + (int64_t)b * a.sk_b + (int64_t)k_cl * a.sk_l + (int64_t)h * a.sk_h;
-    const uint16_t* vp = a.V + (int64_t)b * a.sv_b + (int64_t)k_cl * a.sv_l + (int64_t)h * a.sv_h;
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      kreg[s] = k_ok ? *reinterpret_cast<const u32x4*>(kp + 16 * s + 8 * hf) : u32x4{0, 0, 0, 0};
-      vreg[s] = k_ok ? *reinterpret_cast<const u32x4*>(vp + 16 * s + 8 * hf) : u32x4{0, 0, 0, 0};
-    }
-  }
   f32x16 dka[D / 32], dva[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) {
     dka[i] = f32x16{};
     dva[i] = f32x16{};
   }
-  // staging: Q rows K-swizzled, dO_s rows V-swizzled (range-checked buffers,
-  // rows past L read as zeros)
+  // the key block's K and V tiles (rows past L read as zeros)
+  {
+    DirectTileLoader<D, 4> lkv;
+    lkv.init(a.K + (int64_t)b * a.sk_b + (int64_t)h * a.sk_h, a.sk_l, a.V + (int64_t)b * a.sv_b + (int64_t)h * a.sv_h,
+             a.sv_l, a.L, lane, wv);
+    lkv.issue(kv, kb * 64, lane, wv);
+  }
   DirectTileLoader<D, 4> ld;
   ld.init(a.Q + (int64_t)b * a.sq_b + (int64_t)h * a.sq_h, a.sq_l, a.dOs + (int64_t)b * a.L * a.H * D + (int64_t)h * D,
           (int64_t)a.H * D, a.L, lane, wv);
+  // head-major rows of lse and D: 16 bytes per lane, one wave each
+  const __amdgpu_buffer_rsrc_t lrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.lse + bh * a.L), 0, a.L * 4, 0x00020000);
+  const __amdgpu_buffer_rsrc_t drs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.Dd + bh * a.L), 0, a.L * 4, 0x00020000);
   const int32_t* list = a.tlist + bh * (int64_t)a.Nq * a.kkeep;
   const int e0 = a.toff[bh * (a.Nk + 1) + kb], e1 = a.toff[bh * (a.Nk + 1) + kb + 1];
-  for (int e = e0; e < e1; ++e) {
-    const int qb = __builtin_amdgcn_readfirstlane(list[e]);
-    const int qt0 = qb * BQ;
-    __syncthreads();  // the previous block's readers are done
-#pragma unroll
-    for (int half = 0; half < BQ / 64; ++half) {
-      ld.issue_k(Qs + half * 64 * D, qt0 + 64 * half, lane, wv);
-      ld.issue_v(Ds + half * 64 * D, qt0 + 64 * half, wv);
-    }
-    for (int i = tid; i < BQ; i += 256) {
-      const int q = qt0 + i;
-      const int64_t r = ((int64_t)b * a.L + min(q, a.L - 1)) * a.H + h;
-      lse_s[i] = q < a.L ? a.lse[r] : INFINITY;
-      dd_s[i] = q < a.L ? a.Dd[r] : 0.f;
-    }
+  const uint16_t* Ks = kv;
+  const uint16_t* Vs = kv + 64 * D;
+  const uint16_t* Qs = qd;
+  const uint16_t* Ds = qd + 64 * D;
+  const int n_units = (e1 - e0) * UPB;
+  for (int u = 0; u < n_units; ++u) {
+    const int q0 = __builtin_amdgcn_readfirstlane(list[e0 + u / UPB]) * BQ + 64 * (u % UPB);
+    __syncthreads();  // the previous unit's readers are done
+    ld.issue_k(qd, q0, lane, wv);
+    ld.issue_v(qd + 64 * D, q0, wv);
+    if (wv < 2)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          wv ? drs : lrs, (__attribute__((address_space(3))) void*)((__attribute__((address_space(3))) float*)rowv[wv]),
+          16, 16 * lane, (unsigned)q0 * 4, 0, 0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    for (int sub = qp; sub < NSUB; sub += 2) {
-      const int qr0 = 32 * sub;  // first row of the sub-tile in the staged block
-      f32x16 sa = {}, pa = {};
+    const int qr0 = 32 * qp;  // first row of the wave's sub-tile in the unit
+    f32x16 sa = {}, pa = {};
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-        sa = mfma32(lds_k_chunk<D>(Qs, qr0 + l32, 2 * s + hf), as_bf16x8(kreg[s]), sa);
-        pa = mfma32(lds_row_vswz<D>(Ds, qr0 + l32, 2 * s + hf), as_bf16x8(vreg[s]), pa);
-      }
-      // register r holds query row qr0 + 8 (r / 4) + 4 hf + r % 4 of key l32
-      float pr[16], dsr[16];
+    for (int s = 0; s < D / 16; ++s) {
+      const bf16x8 qa = lds_k_chunk<D>(Qs, qr0 + l32, 2 * s + hf);
+      const bf16x8 da = lds_row_vswz<D>(Ds, qr0 + l32, 2 * s + hf);
+      sa = mfma32(qa, lds_k_chunk<D>(Ks, krow0 + l32, 2 * s + hf), sa);
+      pa = mfma32(da, lds_row_vswz<D>(Vs, krow0 + l32, 2 * s + hf), pa);
+    }
+    // register r holds query row qr0 + 8 (r / 4) + 4 hf + r % 4 of key l32
+    float pr[16], dsr[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qi = qr0 + 8 * (r >> 2) + 4 * hf + (r & 3);
-        const int q = qt0 + qi;
-        float p = __builtin_amdgcn_exp2f(fmaf(sa[r], a.scale_log2, -lse_s[qi]));
-        p = (q >= q_lo && q < q_hi) ? p : 0.f;
-        pr[r] = p;
-        dsr[r] = p * (pa[r] - dd_s[qi]);
-      }
-      const bf16x8 pa0 = to_bf16x8(pr), pa1 = to_bf16x8(pr + 8);
-      const bf16x8 ds0 = to_bf16x8(dsr), ds1 = to_bf16x8(dsr + 8);
+    for (int r = 0; r < 16; ++r) {
+      const int qi = qr0 + 8 * (r >> 2) + 4 * hf + (r & 3);
+      const int q = q0 + qi;
+      float p = __builtin_amdgcn_exp2f(fmaf(sa[r], a.scale_log2, -rowv[0][qi]));
+      p = (q >= q_lo && q < q_hi) ? p : 0.f;
+      pr[r] = p;
+      dsr[r] = p * (pa[r] - rowv[1][qi]);
+    }
+    const bf16x8 p0 = to_bf16x8(pr), p1 = to_bf16x8(pr + 8);
+    const bf16x8 s0 = to_bf16x8(dsr), s1 = to_bf16x8(dsr + 8);
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-        dva[dt] = mfma32(lds_v_operand<D>(Ds, lane, dt, qr0), pa0, dva[dt]);
-        dva[dt] = mfma32(lds_v_operand<D>(Ds, lane, dt, qr0 + 16), pa1, dva[dt]);
-        dka[dt] = mfma32(lds_kt_operand<D>(Qs, lane, dt, qr0), ds0, dka[dt]);
-        dka[dt] = mfma32(lds_kt_operand<D>(Qs, lane, dt, qr0 + 16), ds1, dka[dt]);
-      }
+    for (int dt = 0; dt < D / 32; ++dt) {
+      dva[dt] = mfma32(lds_v_operand<D>(Ds, lane, dt, qr0), p0, dva[dt]);
+      dka[dt] = mfma32(lds_kt_operand<D>(Qs, lane, dt, qr0), s0, dka[dt]);
+      dva[dt] = mfma32(lds_v_operand<D>(Ds, lane, dt, qr0 + 16), p1, dva[dt]);
+      dka[dt] = mfma32(lds_kt_operand<D>(Qs, lane, dt, qr0 + 16), s1, dka[dt]);
     }
   }
+  if (n_units == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the K/V tile loads
   // the two waves of each key half add their sums: waves 2, 3 hand theirs
-  // over through the tile memory, dK^T first, then dV^T
-  float* red = reinterpret_cast<float*>(tiles);
-  static_assert(2 * 64 * (D / 2) * 4 <= 2 * BQ * D * 2, "reduction buffer exceeds the staged tiles");
+  // over through the unit's tile memory, dK^T first, then dV^T
+  float* red = reinterpret_cast<float*>(qd);
+  static_assert(2 * 64 * (D / 2) * 4 <= 2 * 64 * D * 2, "reduction buffer exceeds the staged tiles");
   const int ridx = (kh * 64 + lane) * (D / 2);
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
@@ -1070,7 +1088,7 @@ hipError_t launch_dstate_finalize(const float* part, int BH, const RunGeo& runs,
 hipError_t launch_dproj_finalize(const float* part, int B, int H, int n_runs, int rank, int D, bool per_head,
                                  float* dP, hipStream_t stream) {
   const int64_t total = (int64_t)(per_head ? H : 1) * rank * D;
-  hipLaunchKernelGGL(dproj_finalize_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, part, B, H,
+  hipLaunchKernelGGL(dproj_finalize_kernel, dim3((unsigned)((total + 63) / 64)), dim3(256), 0, stream, part, B, H,
                      n_runs, rank, D, per_head ? 1 : 0, dP);
   return hipGetLastError();
 }

@@ -46,7 +46,7 @@ struct AttnArgs {
   void* out;
   int out_f32;
   float* rms;  // optional [B, L, H]
-  float* lse;  // optional [B, L, H], sparse mode: m + log2(l) of the scaled scores
+  float* lse;  // optional [B, H, L] (head-major), sparse mode: m + log2(l) of the scaled scores
   // low-rank branch
   const uint16_t* Pq;
   int64_t P_hs;
@@ -217,10 +217,10 @@ struct BwdArgs {
   // forward intermediates
   const float* Os;   // [B, L, H, D]
   const float* rms;  // [B, L, H]
-  const float* lse;  // [B, L, H]
+  const float* lse;  // [B, H, L] (head-major)
   // backward intermediates
   uint16_t* dOs;   // bf16 [B, L, H, D]
-  float* Dd;       // [B, L, H]: dO_s . O_s
+  float* Dd;       // [B, H, L] (head-major): dO_s . O_s
   float* dg_head;  // [B, L, H]
   float* qt;       // [B, L, H, 32] q~
   float* dy;       // [B, L, H, D]
