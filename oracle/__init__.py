@@ -82,6 +82,9 @@ from .backward import (  # noqa: F401
     phi_elu1_grad,
     rope_rotate_back,
     sparse_attention_backward,
+    output_backward,
+    lowrank_query_backward,
+    lowrank_key_backward,
     rola_backward_head,
 )
 from .gemm import (  # noqa: F401

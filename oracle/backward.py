@@ -81,6 +81,50 @@ def sparse_attention_backward(Q, K, V, idx, bq, bk, sm_scale, dOs, M=None):
     return dQ, dK, dV, Os
 
 
+def output_backward(dO, Os, r, Olr, g):
+    """The fusion O = O_s + g r O_lr and r = RMS(O_s) backwards, per token:
+    returns (dOs, dOlr, dg) for one head ([L, d], [L, d], [L])."""
+    d = Os.shape[1]
+    t = np.sum(dO * Olr, axis=1)
+    dg = r * t
+    dr = g * t
+    dOlr = (g * r)[:, None] * dO
+    safe_r = np.where(r > 0, r, 1.0)
+    dOs = dO + np.where(r > 0, dr / (d * safe_r), 0.0)[:, None] * Os
+    return dOs, dOlr, dg
+
+
+def lowrank_query_backward(Qn, Pq, pos, pairs, C_tok, dOlr, eps=1e-6, gamma=None):
+    """O_lr,i = w * y_i / rho_i, y_i = C_i^T q~_i, q~_i = R phi(P_q qn_i) backwards.
+
+    C_tok: [L, r, d], the state each query uses. Returns (q~, dy, dq~, da,
+    dqn): everything the state and projection gradients are built from.
+    """
+    d = Qn.shape[1]
+    w = np.ones(d) if gamma is None else np.asarray(gamma, dtype=np.float64)
+    a = Qn @ Pq.T
+    qt = rope_rotate(phi_elu1(a), pos, pairs)
+    y = np.einsum("ir,ird->id", qt, C_tok)
+    rho = np.sqrt(np.mean(y * y, axis=1) + eps)
+    u = w[None, :] * dOlr
+    dy = u / rho[:, None] - y * (np.sum(u * y, axis=1) / (d * rho ** 3))[:, None]
+    dqt = np.einsum("ird,id->ir", C_tok, dy)
+    da = rope_rotate_back(dqt, pos, pairs) * phi_elu1_grad(a)
+    return qt, dy, dqt, da, da @ Pq
+
+
+def lowrank_key_backward(Kn, V, Pk, pos, pairs, dC_tok):
+    """C = sum_j k~_j v_j^T, k~_j = R phi(P_k kn_j) backwards, given for each
+    key the sum dC_tok [L, r, d] of the state gradients of the chunks that
+    see it. Returns (dkn, dv, db) with dv the low-rank share of dV."""
+    bpre = Kn @ Pk.T
+    kt = rope_rotate(phi_elu1(bpre), pos, pairs)
+    dkt = np.einsum("jrd,jd->jr", dC_tok, V)
+    dv = np.einsum("jrd,jr->jd", dC_tok, kt)
+    db = rope_rotate_back(dkt, pos, pairs) * phi_elu1_grad(bpre)
+    return db @ Pk, dv, db
+
+
 def rola_backward_head(Q, K, V, Qn, Kn, Pq, Pk, g, idx, dO, *, T, Hg, Wg, bq, bk, sm_scale,
                        chunk_tokens=0, window=0, eps=1e-6, gamma=None, pairs=None):
     """Forward intermediates and all gradients of one (batch, head).
@@ -123,18 +167,9 @@ def rola_backward_head(Q, K, V, Qn, Kn, Pq, Pk, g, idx, dO, *, T, Hg, Wg, bq, bk
     O = Os + (g * r)[:, None] * Olr
 
     # backward
-    t = np.sum(dO * Olr, axis=1)
-    dg = r * t
-    dr = g * t
-    dOlr = (g * r)[:, None] * dO
-    safe_r = np.where(r > 0, r, 1.0)
-    dOs = dO + np.where(r > 0, dr / (d * safe_r), 0.0)[:, None] * Os
-    u = w[None, :] * dOlr
-    dy = u / rho[:, None] - y * (np.sum(u * y, axis=1) / (d * rho ** 3))[:, None]
-    dqt = np.einsum("ird,id->ir", C[c], dy)
+    dOs, dOlr, dg = output_backward(dO, Os, r, Olr, g)
+    _, dy, _, da, dQn = lowrank_query_backward(Qn, Pq, pos, pairs, C[c], dOlr, eps, gamma)
     dC = np.stack([qt[c == ch].T @ dy[c == ch] for ch in range(n_ch)])
-    da = rope_rotate_back(dqt, pos, pairs) * phi_elu1_grad(a)
-    dQn = da @ Pq
     dPq = da.T @ Qn
     # key side: key j of chunk c' is seen by the queries of chunks c' .. c'+W-1
     # (every later chunk without a window)
@@ -142,10 +177,7 @@ def rola_backward_head(Q, K, V, Qn, Kn, Pq, Pk, g, idx, dO, *, T, Hg, Wg, bq, bk
     for ch in range(n_ch):
         last = n_ch - 1 if (chunk_tokens == 0 or window == 0) else min(n_ch - 1, ch + window - 1)
         dC_seen[ch] = dC[ch:last + 1].sum(axis=0)
-    dkt = np.einsum("jrd,jd->jr", dC_seen[c], V)
-    dV_lr = np.einsum("jrd,jr->jd", dC_seen[c], kt)
-    db = rope_rotate_back(dkt, pos, pairs) * phi_elu1_grad(bpre)
-    dKn = db @ Pk
+    dKn, dV_lr, db = lowrank_key_backward(Kn, V, Pk, pos, pairs, dC_seen[c])
     dPk = db.T @ Kn
     dQ, dK, dV_s, _ = sparse_attention_backward(Q, K, V, idx, bq, bk, sm_scale, dOs, M)
     return dict(O=O, Os=Os, r=r, Olr=Olr, C=C, dC=dC, dOs=dOs, dQ=dQ, dK=dK, dV=dV_s + dV_lr, dQn=dQn, dKn=dKn,

@@ -134,3 +134,70 @@ def test_backward_deterministic():
     b = _run(RAGGED, seed=5)
     for n in ("dQ", "dK", "dV", "dPq", "dPk", "dg"):
         assert torch.equal(a[n], b[n]), n
+
+
+def test_backward_720p_sampled():
+    # the 720P layer as the benchmark runs it; the oracle composes its
+    # backward pieces for one head: every query's forward and low-rank
+    # quantities (the state gradient sums over all of them), then the sparse
+    # branch's dQ of sampled query blocks and dK / dV of sampled key blocks
+    # from exactly the query blocks that keep them
+    cfg = synthetic.WAN14B_720P
+    say("backward 720p: generating inputs")
+    Qb, Kb, Vb = synthetic.gen_qkv(cfg, 0)
+    Pqb, Pkb = synthetic.gen_lowrank_params(cfg)
+    g = synthetic.gen_gate(cfg, amplified=True)
+    dOb = synthetic.f32_to_bf16_bits(
+        np.random.default_rng(9).standard_normal((cfg.B, cfg.L, cfg.H, cfg.d)).astype(np.float32))
+    grid = (cfg.T, cfg.Hg, cfg.Wg)
+    Q, K, V, dO = dev_bf16(Qb), dev_bf16(Kb), dev_bf16(Vb), dev_bf16(dOb)
+    lr = sd.LowrankParams(dev_bf16(Pqb), dev_bf16(Pkb))
+    k = oracle.keep_count(cfg.sparsity, -(-cfg.L // cfg.block_k))
+    nq, nk = -(-cfg.L // cfg.block_q), -(-cfg.L // cfg.block_k)
+    idx = torch.empty((1, cfg.H, nq, k), dtype=torch.int32, device="cuda")
+    ws = sd.rola_workspace(Q, lr, k, grid=grid)
+    sd.sd_rola_prepare(Q, K, V, lr, k, ws, grid=grid, idx_out=idx)
+    say("  running sd_rola_backward")
+    grads = sd.sd_rola_backward(Q, K, V, dev_f32(g), lr, k, idx, dO, grid=grid)
+    torch.cuda.synchronize()
+    heads = (23,)
+    got = {n: grads[n][0, :, list(heads)].cpu().numpy().astype(np.float64) for n in ("dQ", "dK", "dV")}
+    idx = idx.cpu().numpy()
+    del grads, ws, Q, K, V, dO
+    f = oracle.bf16_bits_to_f64
+    Pq, Pk = f(Pqb), f(Pkb)
+    pos = oracle.token_positions(cfg.T, cfg.Hg, cfg.Wg)
+    pairs = oracle.rope_pairs(cfg.rank)
+    scale = 1.0 / math.sqrt(cfg.d)
+    rng = np.random.default_rng(2)
+    for hi, h in enumerate(heads):
+        Qh, Kh, Vh, dOh = (f(x[0, :, h]) for x in (Qb, Kb, Vb, dOb))
+        mh = idx[0, h]
+        Os, r = oracle.sparse_attention(Qh, Kh, Vh, mh, cfg.block_q, cfg.block_k, scale)
+        qt = oracle.lowrank_features(Qh, Pq, pos, pairs)
+        kt = oracle.lowrank_features(Kh, Pk, pos, pairs)
+        C = oracle.lowrank_state(kt, Vh)
+        Olr = oracle.lowrank_output(qt, C, 1e-6)
+        dOs, dOlr, _ = oracle.output_backward(dOh, Os, r, Olr, g[0].astype(np.float64))
+        Ct = np.broadcast_to(C, (cfg.L,) + C.shape)
+        qt, dy, _, _, dQn = oracle.lowrank_query_backward(Qh, Pq, pos, pairs, Ct, dOlr)
+        dC = qt.T @ dy
+        dKn, dv_lr, _ = oracle.lowrank_key_backward(Kh, Vh, Pk, pos, pairs, np.broadcast_to(dC, (cfg.L,) + dC.shape))
+        for qb in sorted(set(rng.choice(nq - 1, 4, replace=False).tolist()) | {nq - 1}):
+            s0, e0 = qb * cfg.block_q, min(cfg.L, (qb + 1) * cfg.block_q)
+            dQs, _, _, _ = oracle.sparse_attention_backward(Qh[s0:e0], Kh, Vh, mh[qb:qb + 1], cfg.block_q,
+                                                            cfg.block_k, scale, dOs[s0:e0])
+            _rel(got["dQ"][s0:e0, hi], dQs + dQn[s0:e0], f"dQ head {h} query block {qb}")
+        # key blocks kept by at most 40 query blocks (the oracle walks every
+        # query of every one of them; the partial tail block and the longest
+        # lists are covered by the smaller cases)
+        counts = np.bincount(mh.ravel(), minlength=nk)
+        cands = np.nonzero((counts > 0) & (counts <= 40))[0]
+        for c in sorted(set(rng.choice(cands, 3, replace=False).tolist()) | {int(cands[counts[cands].argmax()])}):
+            keep = [qb for qb in range(nq) if c in mh[qb]]
+            rows = np.concatenate([np.arange(qb * cfg.block_q, min(cfg.L, (qb + 1) * cfg.block_q)) for qb in keep])
+            _, dKs, dVs, _ = oracle.sparse_attention_backward(Qh[rows], Kh, Vh, mh[keep], cfg.block_q, cfg.block_k,
+                                                             scale, dOs[rows])
+            s0, e0 = c * cfg.block_k, min(cfg.L, (c + 1) * cfg.block_k)
+            _rel(got["dK"][s0:e0, hi], dKs[s0:e0] + dKn[s0:e0], f"dK head {h} key block {c} ({len(keep)} q-blocks)")
+            _rel(got["dV"][s0:e0, hi], dVs[s0:e0] + dv_lr[s0:e0], f"dV head {h} key block {c}")
