@@ -122,7 +122,7 @@ def trace_summary(path, cmd, skip):
     return "\n".join(lines)
 
 
-def pmc_traffic(fetch_path, write_path, kernel="attention_kernel", copy_bytes=1 << 30):
+def pmc_traffic(fetch_path, write_path, kernel="attention_kernel<128, 128, 2>", copy_bytes=1 << 30):
     """HBM bytes per launch of `kernel` from a FETCH_SIZE run and a WRITE_SIZE
     run (KiB per dispatch), each scaled by what the counter reads for the
     1 GiB device copies of --calib-copy."""
