@@ -731,7 +731,7 @@ __device__ __forceinline__ bf16x8 lds_kt_operand(const uint16_t* Ks, int lane, i
 }
 
 template <int D, int BQ>
-__global__ __launch_bounds__(BQ * 2) void bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(BQ * 2, BQ == 128 ? 2 : 1) void bwd_dq_kernel(BwdArgs a) {
   constexpr int NW = BQ / 32;
   constexpr int NT = NW * 64;
   __shared__ __attribute__((aligned(16))) uint16_t smem0[TileSmem<D>::kElems];
@@ -791,25 +791,22 @@ __global__ __launch_bounds__(BQ * 2) void bwd_dq_kernel(BwdArgs a) {
       if (o >= lim_hi || o < lim_lo) sacc[r] = -INFINITY;
     }
   };
+  // One kept block as two halves of 32 keys, each: S^T and dP^T (two
+  // independent MFMA chains), dS^T, then dQ^T += K^T dS^T. Working a half at
+  // a time keeps the register count within two waves per SIMD.
   auto compute = [&](const uint16_t* tile, int key0) {
     const uint16_t* Ks = tile;
     const uint16_t* Vs = tile + 64 * D;
-    f32x16 s0 = {}, s1 = {}, p0 = {}, p1 = {};
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      s0 = mfma32(lds_k_chunk<D>(Ks, l32, 2 * s + hf), as_bf16x8(qreg[s]), s0);
-      s1 = mfma32(lds_k_chunk<D>(Ks, 32 + l32, 2 * s + hf), as_bf16x8(qreg[s]), s1);
-      p0 = mfma32(lds_row_vswz<D>(Vs, l32, 2 * s + hf), as_bf16x8(dreg[s]), p0);
-      p1 = mfma32(lds_row_vswz<D>(Vs, 32 + l32, 2 * s + hf), as_bf16x8(dreg[s]), p1);
-    }
-    if (key0 + 64 > wave_hi || key0 < wave_lo) {
-      mask_half(s0, key0, 0);
-      mask_half(s1, key0, 1);
-    }
+    const bool edge = key0 + 64 > wave_hi || key0 < wave_lo;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      const f32x16& sv = kt ? s1 : s0;
-      const f32x16& pv = kt ? p1 : p0;
+      f32x16 sv = {}, pv = {};
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        sv = mfma32(lds_k_chunk<D>(Ks, 32 * kt + l32, 2 * s + hf), as_bf16x8(qreg[s]), sv);
+        pv = mfma32(lds_row_vswz<D>(Vs, 32 * kt + l32, 2 * s + hf), as_bf16x8(dreg[s]), pv);
+      }
+      if (edge) mask_half(sv, key0, kt);
       float ds[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
