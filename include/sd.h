@@ -286,6 +286,28 @@ int sd_rola_apply(const sd_attn_shape* shape, const sd_lowrank_params* lr, const
                   int64_t g_stride_h, int k_keep, float sm_scale, void* O, const int32_t* idx, void* ws,
                   size_t ws_bytes, void* stream);
 
+/* The forward quantities the backward needs, kept by the forward of a
+ * training step (sd_rola_apply_save) so that the backward does not form them
+ * again. All device memory owned by the caller:
+ *   Os:  bf16 [B, L, H, d] contiguous, the sparse branch output O_s (before
+ *        the gated fusion);
+ *   rms: f32 [B, L, H] contiguous, the RMS over d of each O_s row (r_i);
+ *   lse: f32 [B, H, L] contiguous (head-major), the log2-domain log-sum-exp
+ *        of each query's scaled scores over its kept keys, +inf where the
+ *        query saw no key. */
+typedef struct sd_rola_saved {
+  void* Os;
+  float* rms;
+  float* lse;
+} sd_rola_saved;
+
+/* sd_rola_apply that also writes the quantities of an sd_rola_saved, the same
+ * values the backward would form itself, bit for bit. */
+int sd_rola_apply_save(const sd_attn_shape* shape, const sd_lowrank_params* lr, const void* Q, const void* K,
+                       const void* V, const void* Qn, const float* g, int64_t g_stride_b, int64_t g_stride_l,
+                       int64_t g_stride_h, int k_keep, float sm_scale, void* O, const int32_t* idx, void* ws,
+                       size_t ws_bytes, const sd_rola_saved* save, void* stream);
+
 /* ---- (8) backward of the fused layer -----------------------------------------
  * SparkDiffusion README_zh, distillation and operators sections: training
  * the sparse student needs a backward kernel of its sparse + low-rank
@@ -303,16 +325,17 @@ int sd_rola_apply(const sd_attn_shape* shape, const sd_lowrank_params* lr, const
  *     skip them.
  *   dg: f32 at the gate's strides (g_stride_h 0: summed over the heads), or
  *     NULL to skip it.
- * The forward quantities it needs (low-rank state, sparse output, RMS,
- * log-sum-exp) are recomputed inside. All sums run in a fixed order (the
- * result is bitwise reproducible). Needs (L + 64) * max(H * d, sq_l) * 2
- * < 2^32. */
+ *   saved: the forward's O_s, RMS and log-sum-exp (sd_rola_apply_save with
+ *     the same inputs and block map), or NULL to form them here.
+ * The low-rank state is formed again inside. All sums run in a fixed order
+ * (the result is bitwise reproducible, and the same with or without saved).
+ * Needs (L + 64) * max(H * d, sq_l) * 2 < 2^32. */
 size_t sd_rola_backward_workspace_size(const sd_attn_shape* shape, const sd_lowrank_params* lr, int k_keep);
 int sd_rola_backward(const sd_attn_shape* shape, const sd_lowrank_params* lr, const void* Q, const void* K,
                      const void* V, const void* Qn, const void* Kn, const float* g, int64_t g_stride_b,
                      int64_t g_stride_l, int64_t g_stride_h, int k_keep, float sm_scale, const int32_t* idx,
-                     const void* dO, float* dQ, float* dK, float* dV, float* dQn, float* dKn, float* dPq,
-                     float* dPk, float* dg, void* ws, size_t ws_bytes, void* stream);
+                     const sd_rola_saved* saved, const void* dO, float* dQ, float* dK, float* dV, float* dQn,
+                     float* dKn, float* dPq, float* dPk, float* dg, void* ws, size_t ws_bytes, void* stream);
 
 const char* sd_status_string(int status);
 const char* sd_last_error(void);

@@ -32,7 +32,8 @@ EXPORTED = [
     "sd_keep_count", "sd_rope_default", "sd_block_select_workspace_size", "sd_block_select",
     "sd_sparse_attn", "sd_lowrank_workspace_size", "sd_lowrank_attn", "sd_gate_fuse",
     "sd_quant_fp8_per_token", "sd_quant_fp8_gate", "sd_gemm_fp8_w8a8", "sd_qk_norm_rope", "sd_rola_workspace_size", "sd_rola_attention", "sd_rola_prepare",
-    "sd_rola_apply", "sd_rola_backward_workspace_size", "sd_rola_backward", "sd_status_string", "sd_last_error",
+    "sd_rola_apply", "sd_rola_apply_save", "sd_rola_backward_workspace_size", "sd_rola_backward",
+    "sd_status_string", "sd_last_error",
 ]
 
 
@@ -47,6 +48,10 @@ class sd_attn_shape(ctypes.Structure):
                [(n, ctypes.c_int64) for n in ("sq_b", "sq_l", "sq_h", "sk_b", "sk_l", "sk_h",
                                               "sv_b", "sv_l", "sv_h", "so_b", "so_l", "so_h")] + \
                [(n, ctypes.c_int32) for n in ("select", "chunk_tokens", "window")]
+
+
+class sd_rola_saved(ctypes.Structure):
+    _fields_ = [("Os", ctypes.c_void_p), ("rms", ctypes.c_void_p), ("lse", ctypes.c_void_p)]
 
 
 class sd_rope_pair(ctypes.Structure):
@@ -88,8 +93,9 @@ def _declare(lib):
         "sd_rola_prepare": (i32, [S, LR, P, P, P, P, P, i32, P, P, sz, P]),
         "sd_rola_apply": (i32, [S, LR, P, P, P, P, P, i64, i64, i64, i32, f32, P, P, P, sz, P]),
         "sd_rola_backward_workspace_size": (sz, [S, LR, i32]),
+        "sd_rola_apply_save": (i32, [S, LR, P, P, P, P, P, i64, i64, i64, i32, f32, P, P, P, sz, P, P]),
         "sd_rola_backward": (i32, [S, LR, P, P, P, P, P, P, i64, i64, i64, i32, f32, P, P, P, P, P, P, P, P, P, P,
-                                   P, sz, P]),
+                                   P, P, sz, P]),
         "sd_status_string": (ctypes.c_char_p, [i32]),
         "sd_last_error": (ctypes.c_char_p, []),
     }
@@ -389,9 +395,25 @@ def sd_rola_prepare(Q, K, V, lr: LowrankParams, k_keep, workspace, *, grid, bloc
                                  int(k_keep), _ptr(idx_out), _ptr(workspace), workspace.numel(), _stream_ptr(stream)))
 
 
+class SavedForward:
+    """The forward's O_s (bf16 [B, L, H, d]), RMS ([B, L, H]) and log-sum-exp
+    ([B, H, L]) for the backward; allocated for the shape of Q."""
+
+    def __init__(self, Q):
+        torch = _torch()
+        B, L, H, d = Q.shape
+        self.Os = torch.empty((B, L, H, d), dtype=torch.bfloat16, device=Q.device)
+        self.rms = torch.empty((B, L, H), dtype=torch.float32, device=Q.device)
+        self.lse = torch.empty((B, H, L), dtype=torch.float32, device=Q.device)
+        self.s = sd_rola_saved(self.Os.data_ptr(), self.rms.data_ptr(), self.lse.data_ptr())
+
+
 def sd_rola_apply(Q, K, V, g, lr: LowrankParams, k_keep, workspace, *, grid, block_q=128, Qn=None, sm_scale=None,
-                  out=None, idx=None, select="topk", chunk_tokens=0, window=0, stream=None):
-    """Phase 2 of the fused layer: the fused attention kernel; bf16 O."""
+                  out=None, idx=None, select="topk", chunk_tokens=0, window=0, save: SavedForward = None,
+                  stream=None):
+    """Phase 2 of the fused layer: the fused attention kernel; bf16 O. With
+    `save`, also keeps O_s, its RMS and the log-sum-exp for the backward
+    (sd_rola_apply_save)."""
     torch = _torch()
     B, L, H, d = Q.shape
     if out is None:
@@ -399,6 +421,12 @@ def sd_rola_apply(Q, K, V, g, lr: LowrankParams, k_keep, workspace, *, grid, blo
     s = make_shape(Q, K, V, out, block_q=block_q, grid=grid, select=select, chunk_tokens=chunk_tokens, window=window)
     scale = sm_scale if sm_scale is not None else 1.0 / math.sqrt(d)
     gb, gl, gh = _gate_strides(g, B, L, H)
+    if save is not None:
+        _check(lib().sd_rola_apply_save(ctypes.byref(s), ctypes.byref(lr.p), _ptr(Q), _ptr(K), _ptr(V), _ptr(Qn),
+                                        _ptr(g), gb, gl, gh, int(k_keep), float(scale), _ptr(out), _ptr(idx),
+                                        _ptr(workspace), workspace.numel(), ctypes.byref(save.s),
+                                        _stream_ptr(stream)))
+        return out
     _check(lib().sd_rola_apply(ctypes.byref(s), ctypes.byref(lr.p), _ptr(Q), _ptr(K), _ptr(V), _ptr(Qn), _ptr(g), gb,
                                gl, gh, int(k_keep), float(scale), _ptr(out), _ptr(idx), _ptr(workspace),
                                workspace.numel(), _stream_ptr(stream)))
@@ -413,12 +441,13 @@ def rola_backward_workspace(Q, lr: LowrankParams, k_keep, *, grid, block_q=128, 
 
 def sd_rola_backward(Q, K, V, g, lr: LowrankParams, k_keep, idx, dO, *, grid, block_q=128, Qn=None, Kn=None,
                      sm_scale=None, want_dP=True, want_dg=True, chunk_tokens=0, window=0, workspace=None,
-                     stream=None):
+                     saved: SavedForward = None, stream=None):
     """Gradients of the fused layer for the bf16 output gradient dO (block
     map idx held fixed). Returns a dict of f32 tensors: dQ, dK, dV
     [B, L, H, d]; dQn, dKn (only with Qn / Kn; otherwise that gradient is
     in dQ / dK); dPq, dPk ([rank, d], or [H, rank, d] with per-head
-    projections); dg (the shape of g)."""
+    projections); dg (the shape of g). With `saved` (the forward kept by
+    sd_rola_apply(save=...)) the sparse forward is not formed again."""
     torch = _torch()
     B, L, H, d = Q.shape
     s = make_shape(Q, K, V, dO, block_q=block_q, grid=grid, chunk_tokens=chunk_tokens, window=window)
@@ -440,7 +469,8 @@ def sd_rola_backward(Q, K, V, g, lr: LowrankParams, k_keep, idx, dO, *, grid, bl
     scale = sm_scale if sm_scale is not None else 1.0 / math.sqrt(d)
     gb, gl, gh = _gate_strides(g, B, L, H)
     _check(lib().sd_rola_backward(ctypes.byref(s), ctypes.byref(lr.p), _ptr(Q), _ptr(K), _ptr(V), _ptr(Qn), _ptr(Kn),
-                                  _ptr(g), gb, gl, gh, int(k_keep), float(scale), _ptr(idx), _ptr(dO),
+                                  _ptr(g), gb, gl, gh, int(k_keep), float(scale), _ptr(idx),
+                                  ctypes.byref(saved.s) if saved is not None else None, _ptr(dO),
                                   _ptr(out["dQ"]), _ptr(out["dK"]), _ptr(out["dV"]), _ptr(out["dQn"]),
                                   _ptr(out["dKn"]), _ptr(out["dPq"]), _ptr(out["dPk"]), _ptr(out["dg"]),
                                   _ptr(workspace), workspace.numel(), _stream_ptr(stream)))

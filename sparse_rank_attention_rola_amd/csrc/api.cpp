@@ -766,7 +766,8 @@ int run_prepare(const sd_attn_shape* s, const Geo& g, const sd_lowrank_params* l
 
 int run_apply(const sd_attn_shape* shape, const Geo& g, const sd_lowrank_params* lr, const void* Q, const void* K,
               const void* V, const void* Qn, const float* g_ptr, int64_t gb, int64_t gl, int64_t gh, int k_keep,
-              float sm_scale, void* O, const int32_t* idx, const RolaWs& w, hipStream_t st) {
+              float sm_scale, void* O, const int32_t* idx, const RolaWs& w, hipStream_t st,
+              const sd_rola_saved* save = nullptr) {
   sd::AttnArgs a{};
   fill_attn_common(a, shape, g);
   a.Q = static_cast<const uint16_t*>(Q);
@@ -783,6 +784,11 @@ int run_apply(const sd_attn_shape* shape, const Geo& g, const sd_lowrank_params*
   a.g_sb = gb;
   a.g_sl = gl;
   a.g_sh = gh;
+  if (save) {
+    a.os_save = static_cast<uint16_t*>(save->Os);
+    a.rms = save->rms;
+    a.lse = save->lse;
+  }
   const hipError_t e = sd::launch_rola_fused(a, g.D, g.bq, st);
   if (e != hipSuccess) return hip_fail(e, "fused attention");
   return SD_OK;
@@ -820,6 +826,31 @@ int sd_rola_apply(const sd_attn_shape* shape, const sd_lowrank_params* lr, const
   return ok();
 }
 
+int check_saved(const sd_rola_saved* sv) {
+  if (!sv) return fail(SD_ERR_INVALID_ARG, "saved-forward struct is NULL");
+  int rc;
+  if ((rc = check_dev_ptr(sv->Os, "saved Os", 8)) || (rc = check_dev_ptr(sv->rms, "saved rms", 4)) ||
+      (rc = check_dev_ptr(sv->lse, "saved lse", 4)))
+    return rc;
+  return SD_OK;
+}
+
+int sd_rola_apply_save(const sd_attn_shape* shape, const sd_lowrank_params* lr, const void* Q, const void* K,
+                       const void* V, const void* Qn, const float* g_ptr, int64_t g_stride_b, int64_t g_stride_l,
+                       int64_t g_stride_h, int k_keep, float sm_scale, void* O, const int32_t* idx, void* ws,
+                       size_t ws_bytes, const sd_rola_saved* save, void* stream) {
+  Geo g;
+  int rc;
+  if ((rc = check_rola(shape, lr, Q, K, V, Qn, nullptr, k_keep, idx, ws_bytes, ws, &g))) return rc;
+  if ((rc = check_apply_extra(O, g_ptr, sm_scale, g_stride_b, g_stride_l, g_stride_h))) return rc;
+  if ((rc = check_saved(save))) return rc;
+  const RolaWs w = carve_rola(ws, g, shape, k_keep);
+  if ((rc = run_apply(shape, g, lr, Q, K, V, Qn, g_ptr, g_stride_b, g_stride_l, g_stride_h, k_keep, sm_scale, O,
+                      idx ? idx : w.idx, w, static_cast<hipStream_t>(stream), save)))
+    return rc;
+  return ok();
+}
+
 int sd_rola_attention(const sd_attn_shape* shape, const sd_lowrank_params* lr, const void* Q, const void* K,
                       const void* V, const void* Qn, const void* Kn, const float* g_ptr, int64_t g_stride_b,
                       int64_t g_stride_l, int64_t g_stride_h, int k_keep, float sm_scale, void* O, int32_t* idx_out,
@@ -846,8 +877,8 @@ namespace {
 struct BwdWs {
   LowrankWs lr;
   float* C;  // [B*H, n_ar, rank, D]
-  float *Os, *rms, *lse, *Dd, *dg_head, *qt, *dy, *da, *db, *dQn_tmp;
-  uint16_t* dOs;
+  float *rms, *lse, *Dd, *dg_head, *qt, *dy, *da, *db, *dQn_tmp;
+  uint16_t *Os, *dOs;
   float* dC_part;
   sd::RunGeo dC_runs;
   float* dC;
@@ -864,7 +895,7 @@ BwdWs carve_bwd(void* ws, const Geo& g, const sd_attn_shape* shape, const sd_low
   const size_t BH = (size_t)g.B * g.H, rows = BH * g.L;
   w.lr = carve_lowrank(c, g, shape, prepare_runs(g));
   w.C = static_cast<float*>(c.take(sizeof(float) * BH * g.n_ar * 32 * g.D));
-  w.Os = static_cast<float*>(c.take(sizeof(float) * rows * g.D));
+  w.Os = static_cast<uint16_t*>(c.take(sizeof(uint16_t) * rows * g.D));
   w.rms = static_cast<float*>(c.take(sizeof(float) * rows));
   w.lse = static_cast<float*>(c.take(sizeof(float) * rows));
   w.Dd = static_cast<float*>(c.take(sizeof(float) * rows));
@@ -906,8 +937,8 @@ size_t sd_rola_backward_workspace_size(const sd_attn_shape* shape, const sd_lowr
 int sd_rola_backward(const sd_attn_shape* shape, const sd_lowrank_params* lr, const void* Q, const void* K,
                      const void* V, const void* Qn, const void* Kn, const float* g_ptr, int64_t g_stride_b,
                      int64_t g_stride_l, int64_t g_stride_h, int k_keep, float sm_scale, const int32_t* idx,
-                     const void* dO, float* dQ, float* dK, float* dV, float* dQn, float* dKn, float* dPq, float* dPk,
-                     float* dg, void* ws, size_t ws_bytes, void* stream) {
+                     const sd_rola_saved* saved, const void* dO, float* dQ, float* dK, float* dV, float* dQn,
+                     float* dKn, float* dPq, float* dPk, float* dg, void* ws, size_t ws_bytes, void* stream) {
   Geo g;
   int rc;
   if ((rc = check_shape(shape, &g, true))) return rc;
@@ -925,6 +956,7 @@ int sd_rola_backward(const sd_attn_shape* shape, const sd_lowrank_params* lr, co
   if ((dPq && !aligned(dPq, 4)) || (dPk && !aligned(dPk, 4)) || (dg && !aligned(dg, 4)))
     return fail(SD_ERR_ALIGN, "dPq / dPk / dg misaligned");
   if (k_keep < 1 || k_keep > g.Nk) return fail(SD_ERR_INVALID_ARG, "k_keep = %d not in [1, %d]", k_keep, g.Nk);
+  if (saved && (rc = check_saved(saved))) return rc;
   // the staged dO_s tiles are read through 32-bit buffer offsets
   if ((int64_t)(g.L + 64) * std::max<int64_t>((int64_t)g.H * g.D, shape->sq_l) * 2 >= ((int64_t)1 << 32))
     return fail(SD_ERR_UNSUPPORTED, "L * H * d (or Q's token stride) too large for the backward");
@@ -945,8 +977,12 @@ int sd_rola_backward(const sd_attn_shape* shape, const sd_lowrank_params* lr, co
   e = sd::launch_lowrank_finalize(w.lr.partial, BH, w.lr.runs, g.n_ar, g.win, lr->rank, g.D, rrows, w.C, w.lr.ct_hi,
                                   w.lr.ct_lo, st);
   if (e != hipSuccess) return hip_fail(e, "state finalize");
-  // the sparse branch output O_s (f32), its RMS and log-sum-exp
-  {
+  // the sparse branch output O_s (bf16), its RMS and log-sum-exp: kept by
+  // the forward, or formed here by the sparse kernel
+  const uint16_t* Os = saved ? static_cast<const uint16_t*>(saved->Os) : w.Os;
+  const float* rms = saved ? saved->rms : w.rms;
+  const float* lse = saved ? saved->lse : w.lse;
+  if (!saved) {
     sd::AttnArgs a{};
     fill_attn_common(a, shape, g);
     a.so_b = (int64_t)g.L * g.H * g.D;
@@ -960,7 +996,7 @@ int sd_rola_backward(const sd_attn_shape* shape, const sd_lowrank_params* lr, co
     a.idx = idx;
     a.scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
     a.out = w.Os;
-    a.out_f32 = 1;
+    a.out_f32 = 0;
     a.rms = w.rms;
     a.lse = w.lse;
     e = sd::launch_sparse_attn(a, g.D, g.bq, st);
@@ -1014,9 +1050,9 @@ int sd_rola_backward(const sd_attn_shape* shape, const sd_lowrank_params* lr, co
   b.g_sl = g_stride_l;
   b.g_sh = g_stride_h;
   b.dO = static_cast<const uint16_t*>(dO);
-  b.Os = w.Os;
-  b.rms = w.rms;
-  b.lse = w.lse;
+  b.Os = Os;
+  b.rms = rms;
+  b.lse = lse;
   b.dOs = w.dOs;
   b.Dd = w.Dd;
   b.dg_head = w.dg_head;

@@ -371,6 +371,14 @@ __global__ __launch_bounds__(BQ * 2, BQ == 128 ? SD_ATTN_WAVES : 1) void attenti
         }
       ss += __shfl_xor(ss, 32);
       const float rr = sqrtf(ss * (1.0f / D));
+      if (a.os_save && q_ok) {
+        // the sparse branch's output, RMS and log-sum-exp kept for the backward
+        store_row<D>(a.os_save, false, (((int64_t)b * a.L + q_tok) * a.H + h) * D, oacc, hf);
+        if (hf == 0) {
+          a.rms[((int64_t)b * a.L + q_tok) * a.H + h] = rr;
+          a.lse[((int64_t)b * a.H + h) * a.L + q_tok] = ltot > 0.f ? m_fin + log2f(ltot) : INFINITY;
+        }
+      }
       const float gv = q_ok ? a.g[(int64_t)b * a.g_sb + (int64_t)q_tok * a.g_sl + (int64_t)h * a.g_sh] : 0.f;
       const float coef = gv * rr;
 #pragma unroll

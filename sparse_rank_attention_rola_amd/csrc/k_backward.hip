@@ -207,7 +207,7 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
   ss += partner32(ss, hf);
   const float inv = rsqrtf(ss * (1.0f / D) + a.eps);
   const uint16_t* dop = a.dO + (int64_t)b * a.so_b + (int64_t)q_cl * a.so_l + (int64_t)h * a.so_h;
-  const float* osp = a.Os + row * D;
+  const uint16_t* osp = a.Os + row * D;
   f32x16 dov[D / 32], osv[D / 32];
   float t = 0.f;
 #pragma unroll
@@ -216,12 +216,12 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
     for (int rg = 0; rg < 4; ++rg) {
       const int c0 = och(dt, 4 * rg, hf);
       const u32x2 d2 = q_ok ? *reinterpret_cast<const u32x2*>(dop + c0) : u32x2{0, 0};
-      const f32x4 o4 = q_ok ? *reinterpret_cast<const f32x4*>(osp + c0) : f32x4{0.f, 0.f, 0.f, 0.f};
+      const u32x2 o2 = q_ok ? *reinterpret_cast<const u32x2*>(osp + c0) : u32x2{0, 0};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * rg + e;
         dov[dt][r] = (e & 1) ? bf16_hi(d2[e >> 1]) : bf16_lo(d2[e >> 1]);
-        osv[dt][r] = o4[e];
+        osv[dt][r] = (e & 1) ? bf16_hi(o2[e >> 1]) : bf16_lo(o2[e >> 1]);
         const float w = a.rmsw ? bf16_bits_to_f32(a.rmsw[c0 + e]) : 1.f;
         t += dov[dt][r] * w * yv[dt][r] * inv;
       }

@@ -47,6 +47,9 @@ struct AttnArgs {
   int out_f32;
   float* rms;  // optional [B, L, H]
   float* lse;  // optional [B, H, L] (head-major), sparse mode: m + log2(l) of the scaled scores
+  // fused mode, optional: O_s (bf16 [B, L, H, D] contiguous) with rms and lse
+  // as above, kept for the backward
+  uint16_t* os_save;
   // low-rank branch
   const uint16_t* Pq;
   int64_t P_hs;
@@ -215,7 +218,7 @@ struct BwdArgs {
   int64_t g_sb, g_sl, g_sh;
   const uint16_t* dO;  // bf16 at so_*
   // forward intermediates
-  const float* Os;   // [B, L, H, D]
+  const uint16_t* Os;  // bf16 [B, L, H, D] contiguous
   const float* rms;  // [B, L, H]
   const float* lse;  // [B, H, L] (head-major)
   // backward intermediates

@@ -280,9 +280,10 @@ def test_backward_validation():
     need = lib.sd_rola_backward_workspace_size(ctypes.byref(s), ctypes.byref(p), 4)
     assert need > lib.sd_rola_workspace_size(ctypes.byref(s), ctypes.byref(p), 4)
 
-    def call(k=4, ws_bytes=need, Qn=None, dQn=None, idx=FAKE, dO=FAKE, dV=FAKE, g=FAKE, dg=None):
+    def call(k=4, ws_bytes=need, Qn=None, dQn=None, idx=FAKE, dO=FAKE, dV=FAKE, g=FAKE, dg=None, saved=None):
         return lib.sd_rola_backward(ctypes.byref(s), ctypes.byref(p), FAKE, FAKE, FAKE, Qn, None, g, 0, 1, 0, k,
-                                    0.125, idx, dO, FAKE, FAKE, dV, dQn, None, None, None, dg, FAKE, ws_bytes, None)
+                                    0.125, idx, saved, dO, FAKE, FAKE, dV, dQn, None, None, None, dg, FAKE, ws_bytes,
+                                    None)
 
     assert call(k=0) == sd.SD_ERR_INVALID_ARG
     assert call(idx=None) == sd.SD_ERR_INVALID_ARG
@@ -294,4 +295,9 @@ def test_backward_validation():
     assert call(Qn=FAKE, dQn=FAKE + 4) == sd.SD_ERR_ALIGN
     assert call(dg=FAKE + 2) == sd.SD_ERR_ALIGN
     assert call(ws_bytes=need - 1) == sd.SD_ERR_WORKSPACE
+    assert call(saved=ctypes.byref(sd.sd_rola_saved(FAKE, None, FAKE))) == sd.SD_ERR_INVALID_ARG
+    assert call(saved=ctypes.byref(sd.sd_rola_saved(FAKE + 2, FAKE, FAKE))) == sd.SD_ERR_ALIGN
     assert lib.sd_rola_backward_workspace_size(ctypes.byref(s), ctypes.byref(p), 0) == 0
+    # the saving forward checks its struct too
+    assert lib.sd_rola_apply_save(ctypes.byref(s), ctypes.byref(p), FAKE, FAKE, FAKE, None, FAKE, 0, 1, 0, 4, 0.125,
+                                  FAKE, None, FAKE, 1 << 30, None, None) == sd.SD_ERR_INVALID_ARG

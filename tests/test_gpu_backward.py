@@ -201,3 +201,44 @@ def test_backward_720p_sampled():
             s0, e0 = c * cfg.block_k, min(cfg.L, (c + 1) * cfg.block_k)
             _rel(got["dK"][s0:e0, hi], dKs[s0:e0] + dKn[s0:e0], f"dK head {h} key block {c} ({len(keep)} q-blocks)")
             _rel(got["dV"][s0:e0, hi], dVs[s0:e0] + dv_lr[s0:e0], f"dV head {h} key block {c}")
+
+
+@pytest.mark.parametrize("frames,window", [(0, 0), (1, 2)])
+def test_backward_with_saved_forward_is_identical(frames, window):
+    # a training step keeps O_s, its RMS and the log-sum-exp in the forward;
+    # the backward then skips the sparse recomputation and must give the same
+    # bits, and the saving forward the same output
+    cfg = FRAMES
+    Qb, Kb, Vb = synthetic.gen_qkv(cfg, 4)
+    Pqb, Pkb = synthetic.gen_lowrank_params(cfg)
+    g = synthetic.gen_gate(cfg, amplified=True)
+    dOb = synthetic.f32_to_bf16_bits(
+        np.random.default_rng(5).standard_normal((cfg.B, cfg.L, cfg.H, cfg.d)).astype(np.float32))
+    var = dict(chunk_tokens=frames * cfg.Hg * cfg.Wg, window=window)
+    grid = (cfg.T, cfg.Hg, cfg.Wg)
+    Q, K, V, dO, gd = dev_bf16(Qb), dev_bf16(Kb), dev_bf16(Vb), dev_bf16(dOb), dev_f32(g)
+    lr = sd.LowrankParams(dev_bf16(Pqb), dev_bf16(Pkb))
+    k = oracle.keep_count(cfg.sparsity, -(-cfg.L // cfg.block_k))
+    idx = torch.empty((1, cfg.H, -(-cfg.L // cfg.block_q), k), dtype=torch.int32, device="cuda")
+    ws = sd.rola_workspace(Q, lr, k, grid=grid, **var)
+    sd.sd_rola_prepare(Q, K, V, lr, k, ws, grid=grid, idx_out=idx, **var)
+    save = sd.SavedForward(Q)
+    O1 = sd.sd_rola_apply(Q, K, V, gd, lr, k, ws, grid=grid, idx=idx, save=save, **var)
+    O2 = sd.sd_rola_apply(Q, K, V, gd, lr, k, ws, grid=grid, idx=idx, **var)
+    assert torch.equal(O1.view(torch.int16), O2.view(torch.int16))
+    g1 = sd.sd_rola_backward(Q, K, V, gd, lr, k, idx, dO, grid=grid, saved=save, **var)
+    g2 = sd.sd_rola_backward(Q, K, V, gd, lr, k, idx, dO, grid=grid, **var)
+    torch.cuda.synchronize()
+    for n in ("dQ", "dK", "dV", "dPq", "dPk", "dg"):
+        assert torch.equal(g1[n], g2[n]), n
+    # the kept O_s and RMS against the oracle's sparse branch
+    idx_np = idx.cpu().numpy()
+    ct = var["chunk_tokens"] or cfg.L
+    M = oracle.causal_window_mask(cfg.L, ct, window)
+    for h in range(cfg.H):
+        f = oracle.bf16_bits_to_f64
+        Os, r = oracle.sparse_attention_masked(f(Qb[0, :, h]), f(Kb[0, :, h]), f(Vb[0, :, h]), idx_np[0, h],
+                                               cfg.block_q, cfg.block_k, 1.0 / math.sqrt(cfg.d), M)
+        _rel(host(save.Os[0, :, h]), Os, f"saved O_s h{h}")
+        _rel(host(save.rms[0, :, h]), r, f"saved rms h{h}")
+        assert torch.isfinite(save.lse[0, h]).all()
