@@ -32,7 +32,10 @@
 //                       each key block, ascending (a counting sort).
 //   bwd_dq_kernel       per query block, like the forward loop: S^T, P^T
 //                       from the saved log-sum-exp, dP^T = V dO_s^T, dS^T,
-//                       dQ^T += K^T dS^T (K^T by transposing LDS reads).
+//                       dQ^T += K^T dS^T (K^T by transposing LDS reads; the
+//                       K tile is read both ways, so it is kept with the
+//                       u_swz chunk swizzle that serves both without bank
+//                       conflicts).
 //   bwd_dkdv_kernel     per key block (K, V staged in LDS once), over the
 //                       query blocks that keep it: S = Q K^T, dP = dO_s V^T,
 //                       dV^T += dO_s^T P and dK^T += Q^T dS (transposing
@@ -709,27 +712,6 @@ __global__ __launch_bounds__(256) void transpose_map_kernel(const int32_t* __res
 // ---------------------------------------------------------------------------
 // Softmax branch: dQ per query block.
 // ---------------------------------------------------------------------------
-// 8 bf16 of row t of a V-swizzled tile, channels 8c .. 8c+7.
-template <int D>
-__device__ __forceinline__ bf16x8 lds_row_vswz(const uint16_t* Ts, int t, int c) {
-  return as_bf16x8(*reinterpret_cast<const u32x4*>(Ts + t * D + ((c ^ v_swz<D>(t)) * 8)));
-}
-
-// Transposed A operand (32 channels x 16 rows) of a K-swizzled tile, rows
-// row_base .. +15 in the order of lds_v_operand.
-template <int D>
-__device__ __forceinline__ bf16x8 lds_kt_operand(const uint16_t* Ks, int lane, int dt, int row_base) {
-  const int G = lane >> 4, j = lane & 15;
-  const int r = j >> 2, q = j & 3;
-  const int row = row_base + 4 * (G >> 1) + r;
-  const int c8 = 8 * dt + 4 * (G & 1) + q;
-  const int off0 = ((c8 >> 1) ^ k_swz<D>(row)) * 8 + (c8 & 1) * 4;
-  const int off1 = ((c8 >> 1) ^ k_swz<D>(row + 8)) * 8 + (c8 & 1) * 4;
-  const u32x2 lo = lds_read_tr16(Ks + row * D + off0);
-  const u32x2 hi = lds_read_tr16(Ks + (row + 8) * D + off1);
-  return cat_bf16x8(lo, hi);
-}
-
 template <int D, int BQ>
 __global__ __launch_bounds__(BQ * 2, BQ == 128 ? 2 : 1) void bwd_dq_kernel(BwdArgs a) {
   constexpr int NW = BQ / 32;
@@ -803,8 +785,8 @@ __global__ __launch_bounds__(BQ * 2, BQ == 128 ? 2 : 1) void bwd_dq_kernel(BwdAr
       f32x16 sv = {}, pv = {};
 #pragma unroll
       for (int s = 0; s < D / 16; ++s) {
-        sv = mfma32(lds_k_chunk<D>(Ks, 32 * kt + l32, 2 * s + hf), as_bf16x8(qreg[s]), sv);
-        pv = mfma32(lds_row_vswz<D>(Vs, 32 * kt + l32, 2 * s + hf), as_bf16x8(dreg[s]), pv);
+        sv = mfma32(lds_u_row<D>(Ks, 32 * kt + l32, 2 * s + hf), as_bf16x8(qreg[s]), sv);
+        pv = mfma32(lds_k_chunk<D>(Vs, 32 * kt + l32, 2 * s + hf), as_bf16x8(dreg[s]), pv);
       }
       if (edge) mask_half(sv, key0, kt);
       float ds[16];
@@ -815,22 +797,27 @@ __global__ __launch_bounds__(BQ * 2, BQ == 128 ? 2 : 1) void bwd_dq_kernel(BwdAr
       }
       const bf16x8 dsa = to_bf16x8(ds), dsb = to_bf16x8(ds + 8);
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) dqa[dt] = mfma32(lds_kt_operand<D>(Ks, lane, dt, 32 * kt), dsa, dqa[dt]);
+      for (int dt = 0; dt < D / 32; ++dt) dqa[dt] = mfma32(lds_u_t_operand<D>(Ks, lane, dt, 32 * kt), dsa, dqa[dt]);
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
-        dqa[dt] = mfma32(lds_kt_operand<D>(Ks, lane, dt, 32 * kt + 16), dsb, dqa[dt]);
+        dqa[dt] = mfma32(lds_u_t_operand<D>(Ks, lane, dt, 32 * kt + 16), dsb, dqa[dt]);
     }
   };
-  ld.issue(smem0, block_tok0(0), lane, wv);
+  // K rows read both ways (u_swz), V rows by rows only (k_swz)
+  auto issue = [&](uint16_t* tile, int key0) {
+    ld.issue_swz(tile, key0, lane, wv, false, [](int t) { return u_swz<D>(t); });
+    ld.issue_swz(tile + 64 * D, key0, lane, wv, true, [](int t) { return k_swz<D>(t); });
+  };
+  issue(smem0, block_tok0(0));
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   int it = 0;
   for (; it + 1 < a.kkeep; it += 2) {
-    ld.issue(smem1, block_tok0(it + 1), lane, wv);
+    issue(smem1, block_tok0(it + 1));
     compute(smem0, block_tok0(it));
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (it + 2 < a.kkeep) ld.issue(smem0, block_tok0(it + 2), lane, wv);
+    if (it + 2 < a.kkeep) issue(smem0, block_tok0(it + 2));
     compute(smem1, block_tok0(it + 1));
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -863,8 +850,9 @@ __global__ __launch_bounds__(BQ * 2, BQ == 128 ? 2 : 1) void bwd_dq_kernel(BwdAr
 // LDS once: wave w works on keys 32 (w & 1) .. +31 and on query sub-tile
 // (w >> 1) of every 64-query unit; the two waves of a key half add their
 // dK^T, dV^T through LDS at the end. Per unit of the query blocks that keep
-// the key block, the Q rows (K-swizzled), dO_s rows (V-swizzled) and the
-// unit's log-sum-exp and D values are staged with direct-to-LDS loads; the
+// the key block, the Q and dO_s rows (read by rows and transposed, so kept
+// with the u_swz chunk swizzle) and the unit's log-sum-exp and D values are
+// staged with direct-to-LDS loads; the
 // tiles stay small (66 KB) so that two workgroups share a compute unit and
 // one's loads overlap the other's matrix work.
 template <int D, int BQ>
@@ -902,7 +890,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
     DirectTileLoader<D, 4> lkv;
     lkv.init(a.K + (int64_t)b * a.sk_b + (int64_t)h * a.sk_h, a.sk_l, a.V + (int64_t)b * a.sv_b + (int64_t)h * a.sv_h,
              a.sv_l, a.L, lane, wv);
-    lkv.issue(kv, kb * 64, lane, wv);
+    lkv.issue_swz(kv, kb * 64, lane, wv, false, [](int t) { return k_swz<D>(t); });
+    lkv.issue_swz(kv + 64 * D, kb * 64, lane, wv, true, [](int t) { return k_swz<D>(t); });
   }
   DirectTileLoader<D, 4> ld;
   ld.init(a.Q + (int64_t)b * a.sq_b + (int64_t)h * a.sq_h, a.sq_l, a.dOs + (int64_t)b * a.L * a.H * D + (int64_t)h * D,
@@ -922,8 +911,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
   for (int u = 0; u < n_units; ++u) {
     const int q0 = __builtin_amdgcn_readfirstlane(list[e0 + u / UPB]) * BQ + 64 * (u % UPB);
     __syncthreads();  // the previous unit's readers are done
-    ld.issue_k(qd, q0, lane, wv);
-    ld.issue_v(qd + 64 * D, q0, wv);
+    ld.issue_swz(qd, q0, lane, wv, false, [](int t) { return u_swz<D>(t); });
+    ld.issue_swz(qd + 64 * D, q0, lane, wv, true, [](int t) { return u_swz<D>(t); });
     if (wv < 2)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           wv ? drs : lrs, (__attribute__((address_space(3))) void*)((__attribute__((address_space(3))) float*)rowv[wv]),
@@ -934,10 +923,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
     f32x16 sa = {}, pa = {};
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
-      const bf16x8 qa = lds_k_chunk<D>(Qs, qr0 + l32, 2 * s + hf);
-      const bf16x8 da = lds_row_vswz<D>(Ds, qr0 + l32, 2 * s + hf);
+      const bf16x8 qa = lds_u_row<D>(Qs, qr0 + l32, 2 * s + hf);
+      const bf16x8 da = lds_u_row<D>(Ds, qr0 + l32, 2 * s + hf);
       sa = mfma32(qa, lds_k_chunk<D>(Ks, krow0 + l32, 2 * s + hf), sa);
-      pa = mfma32(da, lds_row_vswz<D>(Vs, krow0 + l32, 2 * s + hf), pa);
+      pa = mfma32(da, lds_k_chunk<D>(Vs, krow0 + l32, 2 * s + hf), pa);
     }
     // register r holds query row qr0 + 8 (r / 4) + 4 hf + r % 4 of key l32
     float pr[16], dsr[16];
@@ -954,18 +943,19 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
     const bf16x8 s0 = to_bf16x8(dsr), s1 = to_bf16x8(dsr + 8);
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
-      dva[dt] = mfma32(lds_v_operand<D>(Ds, lane, dt, qr0), p0, dva[dt]);
-      dka[dt] = mfma32(lds_kt_operand<D>(Qs, lane, dt, qr0), s0, dka[dt]);
-      dva[dt] = mfma32(lds_v_operand<D>(Ds, lane, dt, qr0 + 16), p1, dva[dt]);
-      dka[dt] = mfma32(lds_kt_operand<D>(Qs, lane, dt, qr0 + 16), s1, dka[dt]);
+      dva[dt] = mfma32(lds_u_t_operand<D>(Ds, lane, dt, qr0), p0, dva[dt]);
+      dka[dt] = mfma32(lds_u_t_operand<D>(Qs, lane, dt, qr0), s0, dka[dt]);
+      dva[dt] = mfma32(lds_u_t_operand<D>(Ds, lane, dt, qr0 + 16), p1, dva[dt]);
+      dka[dt] = mfma32(lds_u_t_operand<D>(Qs, lane, dt, qr0 + 16), s1, dka[dt]);
     }
   }
   if (n_units == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the K/V tile loads
   // the two waves of each key half add their sums: waves 2, 3 hand theirs
   // over through the unit's tile memory, dK^T first, then dV^T
+  // (lane-minor: the 64 lanes of a wave write 64 consecutive floats)
   float* red = reinterpret_cast<float*>(qd);
   static_assert(2 * 64 * (D / 2) * 4 <= 2 * 64 * D * 2, "reduction buffer exceeds the staged tiles");
-  const int ridx = (kh * 64 + lane) * (D / 2);
+  const int ridx = kh * (D / 2) * 64 + lane;
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
     __syncthreads();
@@ -973,7 +963,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) red[ridx + 16 * dt + r] = pass ? dva[dt][r] : dka[dt][r];
+        for (int r = 0; r < 16; ++r) red[ridx + (16 * dt + r) * 64] = pass ? dva[dt][r] : dka[dt][r];
     }
     __syncthreads();
     if (qp == 0 && k_ok) {
@@ -985,7 +975,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * rg + e;
-            const float sum = (pass ? dva[dt][r] : dka[dt][r]) + red[ridx + 16 * dt + r];
+            const float sum = (pass ? dva[dt][r] : dka[dt][r]) + red[ridx + (16 * dt + r) * 64];
             v[e] = pass ? sum : a.sm_scale * sum;
           }
           *reinterpret_cast<f32x4*>((pass ? a.dV : a.dK) + krow * D + och(dt, 4 * rg, hf)) = v;

@@ -43,6 +43,18 @@ __device__ __forceinline__ int v_swz(int t) {
   return D == 128 ? 4 * (t & 3) : 4 * ((t & 3) >> 1);
 }
 
+// 16-byte-chunk swizzle of a row-major tile read both ways: by rows (16
+// consecutive rows, one chunk column, per 16-lane cycle) and by transposing
+// reads (4 consecutive rows x 64 bytes per 32-lane cycle). For d = 128 the
+// value is the 4 x 4 transpose of t % 16: bijective on 16 rows, and four
+// consecutive rows differ in the chunk group (bits 2, 3). For d = 64 (8
+// chunks, two rows per bank row) the 8 rows of one parity among 16 take
+// distinct values, and rows t, t + 2 differ in bit 2.
+template <int D>
+__device__ __forceinline__ int u_swz(int t) {
+  return D == 128 ? 4 * (t & 3) + ((t >> 2) & 3) : 4 * ((t >> 1) & 1) + ((t >> 2) & 3);
+}
+
 // Global -> registers -> LDS staging of one 64-token tile of K (row-major,
 // swizzled) and V (transposed, swizzled) by NT threads.
 template <int D, int NT>
@@ -212,7 +224,38 @@ struct DirectTileLoader {
     issue_k(tile, tok0, lane, wv);
     issue_v(tile + 64 * D, tok0, wv);
   }
+  // The K (second = false) or V (second = true) tile of the block at tok0
+  // with the chunk swizzle `swz` of the row (a function of the row that
+  // repeats every 16 rows).
+  template <class Swz>
+  __device__ __forceinline__ void issue_swz(uint16_t* Ts, int tok0, int lane, int wv, bool second, Swz swz) const {
+    const __amdgpu_buffer_rsrc_t rs = second ? vrsrc : krsrc;
+    const unsigned stride = second ? vstride : kstride;
+    int row0, p0;  // the lane's row and slot in the wave's first segment
+    seg_row_chunk(wv, lane, row0, p0);
+    const unsigned voff0 = (unsigned)row0 * stride + (unsigned)((p0 ^ swz(row0)) * 16);
+#pragma unroll
+    for (int i = 0; i < kSpw; ++i) {
+      const int sg = wv + NW * i;
+      unsigned voff = voff0;  // swizzles repeat every 16 rows
+      if constexpr (kRowsPerStep % 16 != 0) {
+        int row, p16;
+        seg_row_chunk(sg, lane, row, p16);
+        voff = (unsigned)(row - i * kRowsPerStep) * stride + (unsigned)((p16 ^ swz(row)) * 16);
+      }
+      const unsigned rows = (unsigned)(tok0 + i * kRowsPerStep);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)((__attribute__((address_space(3))) uint16_t*)(Ts + sg * 512)),
+          16, voff, rows * stride, 0, 0);
+    }
+  }
 };
+
+// 8 bf16 of row t of a u_swz tile, channels 8c .. 8c+7.
+template <int D>
+__device__ __forceinline__ bf16x8 lds_u_row(const uint16_t* Ts, int t, int c) {
+  return as_bf16x8(*reinterpret_cast<const u32x4*>(Ts + t * D + ((c ^ u_swz<D>(t)) * 8)));
+}
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
 
@@ -237,6 +280,21 @@ __device__ __forceinline__ bf16x8 lds_v_operand(const uint16_t* Vs, int lane, in
   const int off = ((c8 >> 1) ^ v_swz<D>(r)) * 8 + (c8 & 1) * 4;
   const u32x2 lo = lds_read_tr16(Vs + row * D + off);
   const u32x2 hi = lds_read_tr16(Vs + (row + 8) * D + off);
+  return cat_bf16x8(lo, hi);
+}
+
+// The A operand of lds_v_operand (32 channels x rows row_base .. +15, the
+// same element order) from a u_swz tile.
+template <int D>
+__device__ __forceinline__ bf16x8 lds_u_t_operand(const uint16_t* Ts, int lane, int dt, int row_base) {
+  const int G = lane >> 4, j = lane & 15;
+  const int r = j >> 2, q = j & 3;
+  const int row = row_base + 4 * (G >> 1) + r;
+  const int c8 = 8 * dt + 4 * (G & 1) + q;
+  const int off0 = ((c8 >> 1) ^ u_swz<D>(row)) * 8 + (c8 & 1) * 4;
+  const int off1 = ((c8 >> 1) ^ u_swz<D>(row + 8)) * 8 + (c8 & 1) * 4;
+  const u32x2 lo = lds_read_tr16(Ts + row * D + off0);
+  const u32x2 hi = lds_read_tr16(Ts + (row + 8) * D + off1);
   return cat_bf16x8(lo, hi);
 }
 
