@@ -36,9 +36,7 @@ namespace sd {
 
 enum AttnMode { kModeSparse = 0, kModeLowrank = 1, kModeFused = 2 };
 
-#ifndef SD_ATTN_WAVES
-#define SD_ATTN_WAVES 2  // minimum waves per SIMD the register budget must allow
-#endif
+constexpr int kAttnMinWaves = 2;  // waves per SIMD the register budget must allow (block_q = 128)
 
 __device__ __forceinline__ float phi_elu1(float x) { return x > 0.f ? x + 1.f : __expf(x); }
 
@@ -161,7 +159,7 @@ __device__ __forceinline__ void store_row(void* base, bool f32, int64_t off, con
 }
 
 template <int D, int BQ, int MODE>
-__global__ __launch_bounds__(BQ * 2, BQ == 128 ? SD_ATTN_WAVES : 1) void attention_kernel(AttnArgs a) {
+__global__ __launch_bounds__(BQ * 2, BQ == 128 ? kAttnMinWaves : 1) void attention_kernel(AttnArgs a) {
   constexpr int NW = BQ / 32;
   constexpr int NT = NW * 64;
   constexpr bool kLoop = MODE != kModeLowrank;

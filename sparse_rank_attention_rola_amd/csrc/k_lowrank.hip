@@ -15,7 +15,9 @@
 // per product and f32 accumulation. K and V are read from HBM exactly once.
 // Each workgroup writes its partial C; lowrank_finalize_kernel sums the
 // partials in a fixed order (bitwise reproducible, no atomics) and emits
-// C (f32) and C^T split into bf16 hi/lo for the query side.
+// C (f32) and C^T split into bf16 hi/lo for the query side. Under a causal
+// window (write-up, section 4) the runs stop at chunk boundaries and each
+// chunk's state is the sum of the runs of the chunks it sees.
 #include "sd_device.h"
 #include "sd_launch.h"
 #include "sd_tiles.h"

@@ -6,7 +6,9 @@
 //
 // One workgroup (4 waves) owns a run of 64-token tiles of one (batch, head),
 // aligned to query blocks; about three workgroups per CU, all resident at
-// once. Per tile:
+// once. Under a causal window the runs follow the autoregressive chunks
+// instead (a run counts only the tokens of its chunk, one partial state per
+// chunk run) and the key-block means come from the pooling kernel. Per tile:
 //   * each thread prefetches its share of the next tile's K and V rows into
 //     registers (buffer loads) and writes them into the LDS tile when the
 //     tile's turn comes;
