@@ -9,7 +9,9 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "sd_launch.h"
 
@@ -722,6 +724,38 @@ sd::PrepareArgs prepare_args(const sd_attn_shape* s, const Geo& g, const sd_lowr
   return a;
 }
 
+// A second stream per device for the prepare phase: its HBM-bound stream
+// pass over K and V runs there beside the ALU-bound block selection on the
+// caller's stream. Events fork it from the caller's stream (it starts after
+// everything enqueued there before) and join it back (the caller's later work
+// waits for it), so to the caller the call stays ordered on its own stream,
+// also under graph capture. The streams and events live until the process
+// ends; a mutex serialises the fork/join sequences of host threads.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+
+std::mutex g_side_mu;
+
+int side_stream(SideStream** out) {
+  static std::vector<SideStream> per_dev;
+  int dev = 0, n = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipGetDeviceCount(&n);
+  if (e != hipSuccess) return hip_fail(e, "side stream: device");
+  if ((int)per_dev.size() < n) per_dev.resize(n);
+  SideStream& ss = per_dev[dev];
+  if (!ss.s) {
+    if ((e = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&ss.join, hipEventDisableTiming)) != hipSuccess)
+      return hip_fail(e, "side stream: create");
+  }
+  *out = &ss;
+  return SD_OK;
+}
+
 int run_rope_table(const sd_attn_shape* s, const sd_lowrank_params* lr, float2* tab, hipStream_t st) {
   sd::RopeThetas th{};
   for (int i = 0; i < lr->n_rope; ++i) th.theta[i] = lr->rope[i].theta;
@@ -730,37 +764,59 @@ int run_rope_table(const sd_attn_shape* s, const sd_lowrank_params* lr, float2* 
   return SD_OK;
 }
 
-// Block map and low-rank state: one streaming pass over Q, K (Kn), V for the
-// block means and partial states, then scores, top-k and the state sum.
+// Block map and low-rank state: a stream pass over K (Kn) and V for the
+// partial states and their sum, and the block selection (pooling, score
+// GEMM, top-k, or the fixed pattern).
+// When the stream pass reads K itself and its runs are whole key blocks (no
+// causal window), it also forms the key-block means; everything then runs in
+// order on the caller's stream (the Q pooling beside the stream pass would
+// only share HBM with it). Otherwise the selection, which keeps the vector
+// ALUs busy, runs on the caller's stream beside the HBM-bound stream pass on
+// the side stream.
 int run_prepare(const sd_attn_shape* s, const Geo& g, const sd_lowrank_params* lr, const void* Q, const void* K,
                 const void* V, const void* Kn, int k_keep, int32_t* idx, const RolaWs& w, hipStream_t st) {
   int rc = run_rope_table(s, lr, w.lr.rope_tab, st);
   if (rc) return rc;
   sd::RankRows rows;
   sd::PrepareArgs a = prepare_args(s, g, lr, Q, K, V, Kn, w.lr, &rows);
-  // The scored selector needs the block means: those of K come from the
-  // stream pass when it reads K itself and its runs are whole key blocks
-  // (no causal window), else from the pooling kernel. The fixed pattern
-  // needs none.
   const bool scored = g.select == SD_SELECT_TOPK;
   const bool k_in_stream = scored && a.Kn == a.K && g.n_ar == 1;
   a.kmean = k_in_stream ? w.sel.kmean : nullptr;
   hipError_t e;
-  if (scored) {
+  auto stream_pass = [&](hipStream_t on) -> int {
+    hipError_t e2 = sd::launch_prepare_stream(a, g.D, on);
+    if (e2 != hipSuccess) return hip_fail(e2, "prepare pass");
+    e2 = sd::launch_lowrank_finalize(w.lr.partial, g.B * g.H, w.lr.runs, g.n_ar, g.win, lr->rank, g.D, rows, nullptr,
+                                     w.lr.ct_hi, w.lr.ct_lo, on);
+    if (e2 != hipSuccess) return hip_fail(e2, "low-rank finalize");
+    return SD_OK;
+  };
+  if (k_in_stream) {
     e = sd::launch_pool_blocks(a.Q, s->sq_b, s->sq_l, s->sq_h, g.B, g.L, g.H, g.D, g.bq, w.sel.qmean, st);
     if (e != hipSuccess) return hip_fail(e, "pool Q");
-    if (!k_in_stream) {
-      e = sd::launch_pool_blocks(a.K, s->sk_b, s->sk_l, s->sk_h, g.B, g.L, g.H, g.D, g.bk, w.sel.kmean, st);
-      if (e != hipSuccess) return hip_fail(e, "pool K");
-    }
+    if ((rc = stream_pass(st))) return rc;
+    return run_scores_topk(s, g, k_keep, idx, w.sel, st);
   }
-  e = sd::launch_prepare_stream(a, g.D, st);
-  if (e != hipSuccess) return hip_fail(e, "prepare pass");
-  rc = run_scores_topk(s, g, k_keep, idx, w.sel, st);
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  SideStream* side = nullptr;
+  if ((rc = side_stream(&side))) return rc;
+  e = hipEventRecord(side->fork, st);
+  if (e == hipSuccess) e = hipStreamWaitEvent(side->s, side->fork, 0);
+  if (e != hipSuccess) return hip_fail(e, "prepare: fork");
+  if ((rc = stream_pass(side->s))) return rc;
+  e = hipEventRecord(side->join, side->s);
+  if (e != hipSuccess) return hip_fail(e, "prepare: record join");
+  if (scored) {
+    e = sd::launch_pool_blocks(a.Q, s->sq_b, s->sq_l, s->sq_h, g.B, g.L, g.H, g.D, g.bq, w.sel.qmean, st);
+    if (e == hipSuccess)
+      e = sd::launch_pool_blocks(a.K, s->sk_b, s->sk_l, s->sk_h, g.B, g.L, g.H, g.D, g.bk, w.sel.kmean, st);
+  }
+  rc = e == hipSuccess ? run_scores_topk(s, g, k_keep, idx, w.sel, st) : hip_fail(e, "block pooling");
+  // the join comes after a failed launch too, so that the side stream's work
+  // is ordered before whatever the caller enqueues next
+  e = hipStreamWaitEvent(st, side->join, 0);
   if (rc) return rc;
-  e = sd::launch_lowrank_finalize(w.lr.partial, g.B * g.H, w.lr.runs, g.n_ar, g.win, lr->rank, g.D, rows, nullptr,
-                                  w.lr.ct_hi, w.lr.ct_lo, st);
-  if (e != hipSuccess) return hip_fail(e, "low-rank finalize");
+  if (e != hipSuccess) return hip_fail(e, "prepare: join");
   return SD_OK;
 }
 
