@@ -22,13 +22,18 @@
  *  - Tokens are in raster order of a T x Hg x Wg latent grid:
  *    token i sits at p_i = (t, h, w) with i = (t*Hg + h)*Wg + w.
  *  - `stream` is a hipStream_t (NULL = the null stream). Every call is
- *    asynchronous and stream-ordered; nothing synchronises the host.
+ *    asynchronous and stream-ordered; nothing synchronises the host. The
+ *    prepare phase (sd_rola_prepare, sd_rola_attention) may run part of its
+ *    work on a second stream the library creates once per device and keeps
+ *    until the process ends; events fork it from `stream` and join it back,
+ *    so the call stays ordered on `stream` (also under graph capture).
  *  - Return value: SD_OK (0) or an SD_ERR_* code. Arguments are validated
  *    on the host before anything is launched; on a validation error no
  *    device memory is touched. sd_last_error() gives a thread-local message.
  *    SD_ERR_HIP reports a launch failure seen right after launching.
  *  - Calls are thread-safe: the library keeps no state beyond the
- *    thread-local error text.
+ *    thread-local error text and that second stream, whose use a mutex
+ *    serialises.
  */
 #ifndef SD_H_
 #define SD_H_
