@@ -82,20 +82,24 @@ __global__ __launch_bounds__(256) void pool_blocks_kernel(const uint16_t* __rest
 
 // S[bh][r][c] = sum_d A[bh][r][d] * Bm[bh][c][d]   (A: [R, D], Bm: [C, D]).
 // 128 x 128 output tile per workgroup; thread (tx, ty) of a 16 x 16 grid
-// owns rows ty + 16 i and columns tx + 16 j (i, j < 8): per 16 x 8-byte
-// LDS reads it issues 64 float64 FMAs, and its stores are 128-byte runs.
-// The d-loop goes in steps of 16 through k-major LDS panels.
+// owns 8 rows and 8 columns in adjacent pairs: per 8 x 16-byte LDS reads it
+// issues 64 float64 FMAs, each output summed over d in order. The d-loop
+// goes in steps of 16 through k-major LDS panels.
 __global__ __launch_bounds__(256) void block_scores_kernel(const double* __restrict__ A, const double* __restrict__ Bm,
                                                            int R, int C, int D, double* __restrict__ S) {
   constexpr int TM = 128, TK = 16;
-  __shared__ double As[TK][TM + 1];
-  __shared__ double Bs[TK][TM + 1];
+  constexpr int TP = TM + 2;  // panel row: 16-byte aligned, loader writes 2-way at most
+  typedef double f64x2 __attribute__((ext_vector_type(2)));
+  __shared__ __attribute__((aligned(16))) double As[TK][TP];
+  __shared__ __attribute__((aligned(16))) double Bs[TK][TP];
   const int bh = blockIdx.z;
   const int r0 = blockIdx.y * TM, c0 = blockIdx.x * TM;
   const double* Ab = A + (int64_t)bh * R * D;
   const double* Bb = Bm + (int64_t)bh * C * D;
   const int tid = threadIdx.x;
   const int tx = tid & 15, ty = tid >> 4;
+  // thread (ty, tx) owns rows 2 ty + 32 i + {0, 1} and columns
+  // 2 tx + 32 j + {0, 1} (i, j < 4): each pair is one 16-byte LDS read
   double acc[8][8];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
@@ -127,26 +131,26 @@ __global__ __launch_bounds__(256) void block_scores_kernel(const double* __restr
     if (k0 + TK < D) load_panel(k0 + TK);  // in flight during this panel's FMAs
 #pragma unroll
     for (int kk = 0; kk < TK; ++kk) {
-      double a[8], b[8];
+      f64x2 a2[4], b2[4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        a[i] = As[kk][ty + 16 * i];
-        b[i] = Bs[kk][tx + 16 * i];
+      for (int i = 0; i < 4; ++i) {
+        a2[i] = *reinterpret_cast<const f64x2*>(&As[kk][2 * ty + 32 * i]);
+        b2[i] = *reinterpret_cast<const f64x2*>(&Bs[kk][2 * tx + 32 * i]);
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = fma(a[i], b[j], acc[i][j]);
+        for (int j = 0; j < 8; ++j) acc[i][j] = fma(a2[i >> 1][i & 1], b2[j >> 1][j & 1], acc[i][j]);
     }
   }
   double* Sb = S + (int64_t)bh * R * C;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int r = r0 + ty + 16 * i;
+    const int r = r0 + 2 * ty + 32 * (i >> 1) + (i & 1);
     if (r >= R) continue;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int c = c0 + tx + 16 * j;
+      const int c = c0 + 2 * tx + 32 * (j >> 1) + (j & 1);
       if (c < C) Sb[(int64_t)r * C + c] = acc[i][j];
     }
   }
