@@ -26,7 +26,9 @@
  *    prepare phase (sd_rola_prepare, sd_rola_attention) may run part of its
  *    work on a second stream the library creates once per device and keeps
  *    until the process ends; events fork it from `stream` and join it back,
- *    so the call stays ordered on `stream` (also under graph capture).
+ *    so the call stays ordered on `stream` (also under graph capture). The
+ *    first such call on a device creates that stream, so make it outside
+ *    graph capture.
  *  - Return value: SD_OK (0) or an SD_ERR_* code. Arguments are validated
  *    on the host before anything is launched; on a validation error no
  *    device memory is touched. sd_last_error() gives a thread-local message.
