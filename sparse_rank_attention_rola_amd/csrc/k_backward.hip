@@ -851,16 +851,16 @@ __global__ __launch_bounds__(BQ * 2, BQ == 128 ? 2 : 1) void bwd_dq_kernel(BwdAr
 // (w >> 1) of every 64-query unit; the two waves of a key half add their
 // dK^T, dV^T through LDS at the end. Per unit of the query blocks that keep
 // the key block, the Q and dO_s rows (read by rows and transposed, so kept
-// with the u_swz chunk swizzle) and the unit's log-sum-exp and D values are
-// staged with direct-to-LDS loads; the
-// tiles stay small (66 KB) so that two workgroups share a compute unit and
-// one's loads overlap the other's matrix work.
+// with the u_swz chunk swizzle) and the unit's 64 log-sum-exp and D values
+// (4 bytes a lane) are staged with direct-to-LDS loads; the tiles stay small
+// (64.5 KB) so that two workgroups share a compute unit and one's loads
+// overlap the other's matrix work.
 template <int D, int BQ>
 __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int UPB = BQ / 64;  // 64-query units per query block
   __shared__ __attribute__((aligned(16))) uint16_t qd[2 * 64 * D];  // Q then dO_s rows of the unit
   __shared__ __attribute__((aligned(16))) uint16_t kv[2 * 64 * D];  // K then V rows of the key block
-  __shared__ __attribute__((aligned(16))) float rowv[2][256];       // lse, D of the unit (1 KB DMA rows)
+  __shared__ __attribute__((aligned(16))) float rowv[2][64];        // lse, D of the unit
   int64_t bh;
   int kb;
   if (!xcd_group_item(blockIdx.x, a.Nk, (int64_t)a.B * a.H, bh, kb)) return;
@@ -896,7 +896,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
   DirectTileLoader<D, 4> ld;
   ld.init(a.Q + (int64_t)b * a.sq_b + (int64_t)h * a.sq_h, a.sq_l, a.dOs + (int64_t)b * a.L * a.H * D + (int64_t)h * D,
           (int64_t)a.H * D, a.L, lane, wv);
-  // head-major rows of lse and D: 16 bytes per lane, one wave each
+  // head-major rows of lse and D: 4 bytes per lane, one wave each
   const __amdgpu_buffer_rsrc_t lrs =
       __builtin_amdgcn_make_buffer_rsrc((void*)(a.lse + bh * a.L), 0, a.L * 4, 0x00020000);
   const __amdgpu_buffer_rsrc_t drs =
@@ -916,7 +916,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
     if (wv < 2)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           wv ? drs : lrs, (__attribute__((address_space(3))) void*)((__attribute__((address_space(3))) float*)rowv[wv]),
-          16, 16 * lane, (unsigned)q0 * 4, 0, 0);
+          4, 4 * lane, (unsigned)q0 * 4, 0, 0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     const int qr0 = 32 * qp;  // first row of the wave's sub-tile in the unit
