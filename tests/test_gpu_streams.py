@@ -104,3 +104,39 @@ def test_graph_replays(case):
         torch.cuda.synchronize()
         assert torch.equal(idx, ref_i), f"block map, replay {rep}"
         assert torch.equal(out, ref_o), f"output, replay {rep}"
+
+
+def test_calls_from_two_host_threads():
+    # the side stream is shared by the calls on a device; a mutex orders the
+    # host side of their fork/join, each call stays ordered on its own stream
+    import threading
+
+    say("two host threads, fixed selector")
+    lay = _Layer(CASES[0])
+    ref_o, ref_i = lay.eager()
+    results, errors = {}, []
+
+    def worker(t):
+        try:
+            s = torch.cuda.Stream()
+            ws, out, idx = lay.buffers()
+            got = []
+            with torch.cuda.stream(s):
+                for _ in range(4):
+                    lay.call(lay.K, lay.V, ws, out, idx)
+                    got.append((out.clone(), idx.clone()))
+            s.synchronize()
+            results[t] = got
+        except Exception as e:  # reported by the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(2)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not errors, errors
+    for t in range(2):
+        for n, (o, i) in enumerate(results[t]):
+            assert torch.equal(i, ref_i), f"thread {t} call {n}: block map"
+            assert torch.equal(o, ref_o), f"thread {t} call {n}: output"
