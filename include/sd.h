@@ -211,7 +211,8 @@ int sd_gate_fuse(const sd_attn_shape* shape, const void* Os, const void* Olr, in
  *   q_mk = E4M3FN(fl32(x_mk * fl32(448 / amax))), nearest-even, saturating.
  * scales are the dequantisation multipliers. q: uint8 codes, row stride ldq.
  * Needs K % 8 == 0, ldx % 8 == 0, ldq % 8 == 0, K <= 16384, x 16-byte and
- * q 8-byte aligned. Non-finite inputs give unspecified codes. */
+ * q 8-byte aligned. Non-finite inputs give unspecified codes. M = 0 (no
+ * rows) does nothing and returns SD_OK; the pointers may then be NULL. */
 int sd_quant_fp8_per_token(const void* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
                            int64_t ldq, float* scales, void* stream);
 

@@ -496,6 +496,7 @@ int sd_quant_fp8_per_token(const void* x, int64_t M, int64_t K, int64_t ldx, uin
   if (K > 16384) return fail(SD_ERR_UNSUPPORTED, "K = %lld exceeds 16384", (long long)K);
   if (ldx < K || ldq < K) return fail(SD_ERR_INVALID_ARG, "ldx and ldq must be >= K");
   if (M > ((int64_t)1 << 31) * 4 - 4) return fail(SD_ERR_UNSUPPORTED, "M too large");
+  if (M == 0) return ok();  // nothing to read or write
   int rc;
   if ((rc = check_dev_ptr(x, "x")) || (rc = check_dev_ptr(q, "q", 8)) || (rc = check_dev_ptr(scales, "scales", 4)))
     return rc;
@@ -512,6 +513,7 @@ int sd_quant_fp8_gate(const void* x, int64_t M, int64_t K, int64_t ldx, uint8_t*
   if (K > 16384) return fail(SD_ERR_UNSUPPORTED, "K = %lld exceeds 16384", (long long)K);
   if (ldx < K || ldq < K) return fail(SD_ERR_INVALID_ARG, "ldx and ldq must be >= K");
   if (!std::isfinite(b_gate)) return fail(SD_ERR_INVALID_ARG, "b_gate must be finite");
+  if (M == 0) return ok();  // nothing to read or write
   int rc;
   if ((rc = check_dev_ptr(x, "x")) || (rc = check_dev_ptr(q, "q", 8)) || (rc = check_dev_ptr(scales, "scales", 4)) ||
       (rc = check_dev_ptr(w_gate, "w_gate")) || (rc = check_dev_ptr(g, "g", 4)))

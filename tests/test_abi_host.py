@@ -163,6 +163,10 @@ def test_gate_fuse_and_quant_validation():
     assert q(-1, 128, 128, 128) == sd.SD_ERR_INVALID_ARG
     assert q(10, 128, 128, 128, x=None) == sd.SD_ERR_INVALID_ARG
     assert q(10, 128, 128, 128, qq=FAKE + 4) == sd.SD_ERR_ALIGN
+    # no rows: nothing to do, NULL pointers accepted, nothing launched
+    assert lib.sd_quant_fp8_per_token(None, 0, 128, 128, None, 128, None, None) == sd.SD_OK
+    assert lib.sd_quant_fp8_gate(None, 0, 128, 128, None, 128, None, None, 0.0, None, None) == sd.SD_OK
+    assert q(0, 100, 104, 104) == sd.SD_ERR_ALIGN  # the shape rules still apply
 
 
 @host_only
