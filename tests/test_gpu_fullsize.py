@@ -2,7 +2,11 @@
 benchmark times (the fused entry point), on sampled outputs that the oracle
 computes head by head: the whole block map of the sampled heads, and the
 fused output O of sampled query blocks (including the partial tail block).
+Also the longest sequence the library takes (131072 tokens, 2048 key
+blocks), at 97% sparsity and with every key block kept (the largest keep
+count).
 """
+import dataclasses
 import math
 
 import numpy as np
@@ -67,3 +71,15 @@ def test_fused_720p_s097_sampled():
 
 def test_fused_480p_13b_sampled():
     _check_layer(synthetic.WAN13B_480P, heads=[0, 11], n_blocks=5, amplified=False)
+
+
+MAXL = synthetic.AttnConfig("max-131072", 1, 2, 128, 32, 64, 64, 128, 64, 0.97, 32)
+
+
+def test_fused_max_length_sampled():
+    _check_layer(MAXL, heads=[0, 1], n_blocks=4, amplified=True)
+
+
+def test_fused_max_length_every_block_kept():
+    _check_layer(dataclasses.replace(MAXL, name="max-131072-dense", sparsity=0.0), heads=[1], n_blocks=1,
+                 amplified=True)
