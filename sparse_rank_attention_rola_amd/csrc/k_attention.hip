@@ -51,6 +51,21 @@ template <int D>
 __device__ __forceinline__ void lowrank_query_tile(const u32x4* qreg, const AttnArgs& a, int b, int h, int tok0,
                                                    int q_chunk, float* Fw, int lane, f32x16 (&out)[D / 32]) {
   const int hf = lane >> 5, l32 = lane & 31;
+  // The RoPE factors of the lane's pairs are loaded with the projection's
+  // operands, so that both loads wait on memory together.
+  const int tok = tok0 + l32;
+  const int hw = a.Hg * a.Wg;
+  const int pos[3] = {min(tok / hw, a.rope.max_ext - 1), (tok / a.Wg) % a.Hg, tok % a.Wg};
+  float2 cs_m[kMaxRopePairs / 2];
+#pragma unroll
+  for (int j = 0; j < kMaxRopePairs / 2; ++j) {
+    const int m = 2 * j + hf;
+    cs_m[j] = float2{1.f, 0.f};
+    if (2 * j < a.rope.n && m < a.rope.n) {
+      const int axis = a.rope.axis[m];
+      cs_m[j] = a.rope_tab[m * a.rope.max_ext + (axis == 0 ? pos[0] : axis == 1 ? pos[1] : pos[2])];
+    }
+  }
   const uint16_t* Pq = a.Pq + (int64_t)h * a.P_hs;
   f32x16 acc = {};
 #pragma unroll
@@ -67,21 +82,15 @@ __device__ __forceinline__ void lowrank_query_tile(const u32x4* qreg, const Attn
   }
   __syncthreads();
   // RoPE: lane l32 = token; the two lane halves take the even and odd pairs
-  {
-    const int tok = tok0 + l32;
-    const int hw = a.Hg * a.Wg;
-    const int pos[3] = {min(tok / hw, a.rope.max_ext - 1), (tok / a.Wg) % a.Hg, tok % a.Wg};
-    for (int m0 = 0; m0 < a.rope.n; m0 += 2) {
-      const int m = m0 + hf;
-      if (m < a.rope.n) {
-        const int axis = hf ? a.rope.axis[m0 + 1] : a.rope.axis[m0];
-        const int dim = hf ? a.rope.dim[m0 + 1] : a.rope.dim[m0];
-        const float2 cs = a.rope_tab[m * a.rope.max_ext + (axis == 0 ? pos[0] : axis == 1 ? pos[1] : pos[2])];
-        float* f = Fw + l32 * 33 + dim;
-        const float u = f[0], v = f[1];
-        f[0] = u * cs.x - v * cs.y;
-        f[1] = u * cs.y + v * cs.x;
-      }
+#pragma unroll
+  for (int j = 0; j < kMaxRopePairs / 2; ++j) {
+    const int m = 2 * j + hf;
+    if (2 * j < a.rope.n && m < a.rope.n) {
+      const float2 cs = cs_m[j];
+      float* f = Fw + l32 * 33 + a.rope.dim[m];
+      const float u = f[0], v = f[1];
+      f[0] = u * cs.x - v * cs.y;
+      f[1] = u * cs.y + v * cs.x;
     }
   }
   __syncthreads();
@@ -354,6 +363,10 @@ __global__ __launch_bounds__(BQ * 2, BQ == 128 ? kAttnMinWaves : 1) void attenti
           qreg[s] = q_ok ? *reinterpret_cast<const u32x4*>(qp + 16 * s + 8 * hf) : u32x4{0, 0, 0, 0};
       }
     }
+    // the gate value is loaded before the low-rank tile, its latency hidden there
+    float gv = 0.f;
+    if constexpr (MODE == kModeFused)
+      gv = q_ok ? a.g[(int64_t)b * a.g_sb + (int64_t)q_tok * a.g_sl + (int64_t)h * a.g_sh] : 0.f;
     lowrank_query_tile<D>(qreg, a, b, h, tok0, q_chunk, Fw, lane, olr);
     if constexpr (MODE == kModeLowrank) {
       if (q_ok) store_row<D>(a.out, a.out_f32, obase, olr, hf);
@@ -377,7 +390,6 @@ __global__ __launch_bounds__(BQ * 2, BQ == 128 ? kAttnMinWaves : 1) void attenti
           a.lse[((int64_t)b * a.H + h) * a.L + q_tok] = ltot > 0.f ? m_fin + log2f(ltot) : INFINITY;
         }
       }
-      const float gv = q_ok ? a.g[(int64_t)b * a.g_sb + (int64_t)q_tok * a.g_sl + (int64_t)h * a.g_sh] : 0.f;
       const float coef = gv * rr;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
