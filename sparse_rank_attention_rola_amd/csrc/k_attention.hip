@@ -74,6 +74,24 @@ __device__ __forceinline__ void lowrank_query_tile(const u32x4* qreg, const Attn
                                     : u32x4{0, 0, 0, 0};
     acc = mfma32(as_bf16x8(pa), as_bf16x8(qreg[s]), acc);
   }
+  // The state of the wave's first chunk, first half of the channel tiles:
+  // loaded once the projection's operands are dead, so that the loads are in
+  // flight during the RoPE patch (the fence keeps them from moving up).
+  const int n_ar = (a.L + a.ar_tokens - 1) / a.ar_tokens;
+  const int c_first = __builtin_amdgcn_readfirstlane(q_chunk);
+  const int c_last = __builtin_amdgcn_readlane(q_chunk, 31);
+  auto state_off = [&](int c, int dt, int s) {
+    return (((int64_t)b * a.H + h) * n_ar + c) * D * 32 + (int64_t)(32 * dt + l32) * 32 + 16 * s + 8 * hf;
+  };
+  __builtin_amdgcn_sched_barrier(0);
+  u32x4 cth0[D / 64][2], ctl0[D / 64][2];
+#pragma unroll
+  for (int dt = 0; dt < D / 64; ++dt)
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      cth0[dt][s] = *reinterpret_cast<const u32x4*>(a.Ct_hi + state_off(c_first, dt, s));
+      ctl0[dt][s] = *reinterpret_cast<const u32x4*>(a.Ct_lo + state_off(c_first, dt, s));
+    }
   // acc: column = query l32, row = rank index 8*(r/4) + 4*hf + r%4
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
@@ -105,20 +123,18 @@ __device__ __forceinline__ void lowrank_query_tile(const u32x4* qreg, const Attn
   // The wave's queries may fall in several autoregressive chunks (the
   // chunk index grows with the token): the product is formed once per chunk
   // with that chunk's state and each lane keeps the one of its own chunk.
-  const int n_ar = (a.L + a.ar_tokens - 1) / a.ar_tokens;
-  const int c_first = __builtin_amdgcn_readfirstlane(q_chunk);
-  const int c_last = __builtin_amdgcn_readlane(q_chunk, 31);
   for (int c = c_first; c <= c_last; ++c) {
-    const int64_t cbase = (((int64_t)b * a.H + h) * n_ar + c) * D * 32;
     const bool mine = q_chunk == c;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
       f32x16 y = {};
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const int64_t off = cbase + (int64_t)(32 * dt + l32) * 32 + 16 * s + 8 * hf;
-        const bf16x8 ch = as_bf16x8(*reinterpret_cast<const u32x4*>(a.Ct_hi + off));
-        const bf16x8 cl = as_bf16x8(*reinterpret_cast<const u32x4*>(a.Ct_lo + off));
+        const bool early = c == c_first && dt < D / 64;
+        const bf16x8 ch = as_bf16x8(early ? cth0[dt % (D / 64)][s]
+                                          : *reinterpret_cast<const u32x4*>(a.Ct_hi + state_off(c, dt, s)));
+        const bf16x8 cl = as_bf16x8(early ? ctl0[dt % (D / 64)][s]
+                                          : *reinterpret_cast<const u32x4*>(a.Ct_lo + state_off(c, dt, s)));
         y = mfma32(ch, qhi[s], y);
         y = mfma32(cl, qhi[s], y);
         y = mfma32(ch, qlo[s], y);
