@@ -91,23 +91,42 @@ __device__ __forceinline__ void load8_split(const float* p, bool ok, bf16x8& hi,
   split_bf16x8(f, hi, lo);
 }
 
-// Rotates the RoPE pairs of a wave's 32 x 33 patch (lane l32 = token tok0 +
-// l32, the two lane halves take alternate pairs) by +angle (dir = 1) or by
-// -angle (dir = -1, the transpose).
-__device__ __forceinline__ void rope_patch(float* F, const float2* tab, const RopeArgs& rope, int Hg, int Wg,
-                                           int tok0, int lane, int dir) {
+// The cos/sin of the RoPE pairs a lane rotates in a wave's 32 x 33 patch
+// (lane l32 = token tok0 + l32; the two lane halves take alternate pairs),
+// loaded once at the start of a kernel so that their latency overlaps its
+// other loads; both rotations use them.
+struct RopeLane {
+  float2 cs[kMaxRopePairs / 2];
+};
+
+__device__ __forceinline__ void rope_lane_load(RopeLane& rl, const float2* tab, const RopeArgs& rope, int Hg, int Wg,
+                                               int tok0, int lane) {
   const int hf = lane >> 5, l32 = lane & 31;
   const int tok = tok0 + l32;
   const int hw = Hg * Wg;
   const int pos[3] = {min(tok / hw, rope.max_ext - 1), (tok / Wg) % Hg, tok % Wg};
-  for (int m0 = 0; m0 < rope.n; m0 += 2) {
-    const int m = m0 + hf;
-    if (m < rope.n) {
-      const int axis = hf ? rope.axis[m0 + 1] : rope.axis[m0];
-      const int dim = hf ? rope.dim[m0 + 1] : rope.dim[m0];
-      const float2 cs = tab[m * rope.max_ext + (axis == 0 ? pos[0] : axis == 1 ? pos[1] : pos[2])];
+#pragma unroll
+  for (int j = 0; j < kMaxRopePairs / 2; ++j) {
+    const int m = 2 * j + hf;
+    rl.cs[j] = float2{1.f, 0.f};
+    if (2 * j < rope.n && m < rope.n) {
+      const int axis = rope.axis[m];
+      rl.cs[j] = tab[m * rope.max_ext + (axis == 0 ? pos[0] : axis == 1 ? pos[1] : pos[2])];
+    }
+  }
+}
+
+// Rotates the RoPE pairs of the patch by +angle (dir = 1) or by -angle
+// (dir = -1, the transpose).
+__device__ __forceinline__ void rope_patch(float* F, const RopeLane& rl, const RopeArgs& rope, int lane, int dir) {
+  const int hf = lane >> 5, l32 = lane & 31;
+#pragma unroll
+  for (int j = 0; j < kMaxRopePairs / 2; ++j) {
+    const int m = 2 * j + hf;
+    if (2 * j < rope.n && m < rope.n) {
+      const float2 cs = rl.cs[j];
       const float sn = dir > 0 ? cs.y : -cs.y;
-      float* f = F + l32 * 33 + dim;
+      float* f = F + l32 * 33 + rope.dim[m];
       const float u = f[0], v = f[1];
       f[0] = u * cs.x - v * sn;
       f[1] = u * sn + v * cs.x;
@@ -139,6 +158,8 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
   float* fw = Fw[wv];
   float* fa = Fa[wv];
   const int64_t row = ((int64_t)b * a.L + q_cl) * a.H + h;
+  RopeLane rl;
+  rope_lane_load(rl, a.rope_tab, a.rope, a.Hg, a.Wg, tok0, lane);
 
   // 1. a = P_q qn (pre-phi in Fa), q~ = R phi(a) (in Fw)
   {
@@ -163,7 +184,7 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
     }
   }
   __syncthreads();
-  rope_patch(fw, a.rope_tab, a.rope, a.Hg, a.Wg, tok0, lane, 1);
+  rope_patch(fw, rl, a.rope, lane, 1);
   __syncthreads();
   bf16x8 qhi[2], qlo[2];
 #pragma unroll
@@ -304,7 +325,7 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) fw[l32 * 33 + 8 * (r >> 2) + 4 * hf + (r & 3)] = dq[r];
   __syncthreads();
-  rope_patch(fw, a.rope_tab, a.rope, a.Hg, a.Wg, tok0, lane, -1);
+  rope_patch(fw, rl, a.rope, lane, -1);
   __syncthreads();
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
@@ -521,6 +542,8 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
   float* fw = Fw[wv];
   float* fa = Fa[wv];
   const int64_t row = ((int64_t)b * a.L + k_cl) * a.H + h;
+  RopeLane rl;
+  rope_lane_load(rl, a.rope_tab, a.rope, a.Hg, a.Wg, tok0, lane);
 
   // 1. b = P_k kn (pre-phi in Fa), k~ = R phi(b) (in Fw)
   {
@@ -545,7 +568,7 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
     }
   }
   __syncthreads();
-  rope_patch(fw, a.rope_tab, a.rope, a.Hg, a.Wg, tok0, lane, 1);
+  rope_patch(fw, rl, a.rope, lane, 1);
   __syncthreads();
   bf16x8 khi[2], klo[2];
 #pragma unroll
@@ -615,7 +638,7 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) fw[l32 * 33 + 8 * (r >> 2) + 4 * hf + (r & 3)] = dk[r];
   __syncthreads();
-  rope_patch(fw, a.rope_tab, a.rope, a.Hg, a.Wg, tok0, lane, -1);
+  rope_patch(fw, rl, a.rope, lane, -1);
   __syncthreads();
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
