@@ -160,6 +160,22 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
   const int64_t row = ((int64_t)b * a.L + q_cl) * a.H + h;
   RopeLane rl;
   rope_lane_load(rl, a.rope_tab, a.rope, a.Hg, a.Wg, tok0, lane);
+  // dO, O_s (their 4-channel groups in the accumulator layout), the RMS and
+  // the gate do not depend on the steps before they are used: loaded here,
+  // with the first loads, instead of after two barriers
+  const uint16_t* dop = a.dO + (int64_t)b * a.so_b + (int64_t)q_cl * a.so_l + (int64_t)h * a.so_h;
+  const uint16_t* osp = a.Os + row * D;
+  u32x2 do2[D / 32][4], os2[D / 32][4];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const int c0 = och(dt, 4 * rg, hf);
+      do2[dt][rg] = q_ok ? *reinterpret_cast<const u32x2*>(dop + c0) : u32x2{0, 0};
+      os2[dt][rg] = q_ok ? *reinterpret_cast<const u32x2*>(osp + c0) : u32x2{0, 0};
+    }
+  const float rr = q_ok ? a.rms[row] : 0.f;
+  const float gv = q_ok ? a.g[(int64_t)b * a.g_sb + (int64_t)q_cl * a.g_sl + (int64_t)h * a.g_sh] : 0.f;
 
   // 1. a = P_q qn (pre-phi in Fa), q~ = R phi(a) (in Fw)
   {
@@ -169,13 +185,16 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
     for (int s = 0; s < D / 16; ++s)
       qreg[s] = q_ok ? *reinterpret_cast<const u32x4*>(qp + 16 * s + 8 * hf) : u32x4{0, 0, 0, 0};
     const uint16_t* Pq = a.Pq + (int64_t)h * a.P_hs;
+    // all of P_q's operands are loaded before the products (one wait on
+    // memory, not one per product; the fence keeps them apart)
+    u32x4 pqa[D / 16];
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s)
+      pqa[s] = (l32 < a.rank) ? *reinterpret_cast<const u32x4*>(Pq + l32 * D + 16 * s + 8 * hf) : u32x4{0, 0, 0, 0};
+    __builtin_amdgcn_sched_barrier(0);
     f32x16 acc = {};
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      const u32x4 pa = (l32 < a.rank) ? *reinterpret_cast<const u32x4*>(Pq + l32 * D + 16 * s + 8 * hf)
-                                      : u32x4{0, 0, 0, 0};
-      acc = mfma32(as_bf16x8(pa), as_bf16x8(qreg[s]), acc);
-    }
+    for (int s = 0; s < D / 16; ++s) acc = mfma32(as_bf16x8(pqa[s]), as_bf16x8(qreg[s]), acc);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int ri = 8 * (r >> 2) + 4 * hf + (r & 3);
@@ -200,19 +219,29 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
     }
   }
 
-  // 2. y = C^T q~ with the state of the lane's chunk
+  // 2. y = C^T q~ with the state of the lane's chunk (each chunk's state
+  // loaded whole before its products)
   f32x16 yv[D / 32];
   for (int c = c_first; c <= c_last; ++c) {
     const int64_t cbase = (bh * n_ar + c) * D * 32;
     const bool mine = q_chunk == c;
+    u32x4 cth[D / 32][2], ctl[D / 32][2];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int64_t off = cbase + (int64_t)(32 * dt + l32) * 32 + 16 * s + 8 * hf;
+        cth[dt][s] = *reinterpret_cast<const u32x4*>(a.Ct_hi + off);
+        ctl[dt][s] = *reinterpret_cast<const u32x4*>(a.Ct_lo + off);
+      }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
       f32x16 y = {};
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const int64_t off = cbase + (int64_t)(32 * dt + l32) * 32 + 16 * s + 8 * hf;
-        const bf16x8 ch = as_bf16x8(*reinterpret_cast<const u32x4*>(a.Ct_hi + off));
-        const bf16x8 cl = as_bf16x8(*reinterpret_cast<const u32x4*>(a.Ct_lo + off));
+        const bf16x8 ch = as_bf16x8(cth[dt][s]);
+        const bf16x8 cl = as_bf16x8(ctl[dt][s]);
         y = mfma32(ch, qhi[s], y);
         y = mfma32(cl, qhi[s], y);
         y = mfma32(ch, qlo[s], y);
@@ -230,8 +259,6 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
     for (int r = 0; r < 16; ++r) ss += yv[dt][r] * yv[dt][r];
   ss += partner32(ss, hf);
   const float inv = rsqrtf(ss * (1.0f / D) + a.eps);
-  const uint16_t* dop = a.dO + (int64_t)b * a.so_b + (int64_t)q_cl * a.so_l + (int64_t)h * a.so_h;
-  const uint16_t* osp = a.Os + row * D;
   f32x16 dov[D / 32], osv[D / 32];
   float t = 0.f;
 #pragma unroll
@@ -239,8 +266,8 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
 #pragma unroll
     for (int rg = 0; rg < 4; ++rg) {
       const int c0 = och(dt, 4 * rg, hf);
-      const u32x2 d2 = q_ok ? *reinterpret_cast<const u32x2*>(dop + c0) : u32x2{0, 0};
-      const u32x2 o2 = q_ok ? *reinterpret_cast<const u32x2*>(osp + c0) : u32x2{0, 0};
+      const u32x2 d2 = do2[dt][rg];
+      const u32x2 o2 = os2[dt][rg];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * rg + e;
@@ -251,8 +278,6 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
       }
     }
   t += partner32(t, hf);
-  const float rr = q_ok ? a.rms[row] : 0.f;
-  const float gv = q_ok ? a.g[(int64_t)b * a.g_sb + (int64_t)q_cl * a.g_sl + (int64_t)h * a.g_sh] : 0.f;
   if (q_ok && hf == 0) a.dg_head[row] = rr * t;
   const float coef = rr > 0.f ? gv * t / ((float)D * rr) : 0.f;
   const float gr = gv * rr;
