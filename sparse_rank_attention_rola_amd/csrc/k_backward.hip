@@ -512,12 +512,22 @@ __global__ __launch_bounds__(256) void dproj_finalize_kernel(const float* __rest
     const int hs = per_head ? 1 : H;  // heads per output
     const int64_t n = (int64_t)B * hs * n_runs;
     const int64_t u0 = n * qt / 4, u1 = n * (qt + 1) / 4;
+    // partial u = (b, head hh of the output's heads, run), run fastest;
+    // walked in order with incremented indices (no division per term)
+    int run = (int)(u0 % n_runs);
+    const int64_t bh0 = u0 / n_runs;
+    int hh = (int)(bh0 % hs), b = (int)(bh0 / hs);
+    const float* pr = part + (int64_t)r * D + d;
     for (int64_t u = u0; u < u1; ++u) {
-      const int run = (int)(u % n_runs);
-      const int64_t bh_local = u / n_runs;
-      const int hh = (int)(bh_local % hs), b = (int)(bh_local / hs);
       const int h = per_head ? o : hh;
-      s += part[((((int64_t)b * H + h) * n_runs + run) * 32 + r) * D + d];
+      s += pr[(((int64_t)b * H + h) * n_runs + run) * 32 * D];
+      if (++run == n_runs) {
+        run = 0;
+        if (++hh == hs) {
+          hh = 0;
+          ++b;
+        }
+      }
     }
   }
   q4[qt][threadIdx.x & 63] = s;
