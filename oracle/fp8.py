@@ -12,11 +12,13 @@ Readings where the page is silent:
     largest finite 448, subnormals m * 2^-9;
   * per row m: amax = max_k |x_mk| (floored at 1e-12 so a zero row stays
     finite); the stored scale is the dequantisation multiplier
-    s = fp32(amax / 448); codes are E4M3(fp32(x * fp32(448 / amax))), i.e.
-    multiply by the float32 reciprocal scale, round once to float32, then
-    round to nearest-even E4M3 with saturation to +-448. Because a float
-    decides each integer code, that decision is taken in float32 exactly as
-    described, so the GPU codes can be compared bit for bit.
+    s = fp32(amax / 448) (one correctly rounded float32 division);
+  * the code of x is E4M3(x / s): the quotient of the element by the stored
+    scale, rounded to nearest with ties to the even code, saturating to
+    +-448. The quotient is formed in float64. That rounding never decides a
+    code: x has 8 significant bits and s 24, so a quotient that is not
+    exactly an E4M3 midpoint (5 significant bits) lies at least 2^-29 of its
+    size away from it, far beyond float64's 2^-53.
 """
 from __future__ import annotations
 
@@ -63,13 +65,16 @@ def e4m3_encode(v) -> np.ndarray:
 
 
 def quant_fp8_per_token(x_bits):
-    """x [M, K] bf16 bits -> (codes uint8 [M, K], scales float32 [M])."""
+    """x [M, K] bf16 bits -> (codes uint8 [M, K], scales float32 [M]).
+
+    amax per row (exact), s = fp32(max(amax, 1e-12) / 448), codes =
+    E4M3(x / s) with the quotient in float64.
+    """
     xb = np.asarray(x_bits, dtype=np.uint16)
     x = (xb.astype(np.uint32) << 16).view(np.float32)  # exact widening
     amax = np.max(np.abs(x), axis=1)
     amax = np.maximum(amax, AMAX_FLOOR).astype(np.float32)
-    inv = (np.float32(E4M3_MAX) / amax).astype(np.float32)        # IEEE fp32 division
-    scales = (amax / np.float32(E4M3_MAX)).astype(np.float32)
-    v = (x * inv[:, None]).astype(np.float32)                       # one fp32 rounding
-    codes = e4m3_encode(v.astype(np.float64))
+    scales = (amax / np.float32(E4M3_MAX)).astype(np.float32)     # IEEE fp32 division
+    v = x.astype(np.float64) / scales.astype(np.float64)[:, None]
+    codes = e4m3_encode(v)
     return codes, scales

@@ -2,11 +2,13 @@
 
 Exhaustive over the 256 codes; checked against the OCP spec's table points,
 against PyTorch's float8_e4m3fn conversion (a library routine; it rounds to
-nearest-even but does not saturate, so it is only used inside +-448) and
-against closed-form error bounds.
+nearest-even but does not saturate, so it is only used inside +-448),
+against closed-form error bounds, and the per-row quantiser against the
+exact rational quotient x / s rounded by exhaustive search.
 """
 import json
 import os
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -110,3 +112,72 @@ def test_quant_zero_row_and_sign():
     assert (codes[0] == 0).all() and np.isfinite(scales[0]) and scales[0] > 0
     assert codes[1, 3] == 0xFE
     assert scales[1] == np.float32(1.0) / np.float32(448.0)
+
+
+def _tie_rows(n_cols, seed):
+    """Student-t rows plus rows whose |x|max has a bf16 significand that is a
+    multiple of 7 (140, 168, 196, 210, 252): 448 / amax then has a factor of
+    1/7 and x / s lands exactly on E4M3 rounding midpoints for many x."""
+    x = synthetic.gen_activation(12, n_cols, seed)
+    xf = oracle.bf16_bits_to_f64(x).astype(np.float32)
+    for i, b in enumerate([140, 168, 196, 210, 252, 154, 182]):
+        amax = np.float32(b) * np.float32(2.0 ** -5)
+        row = np.clip(xf[i], -0.99 * amax, 0.99 * amax)
+        row[np.abs(row).argmax()] = -amax if i % 2 else amax
+        xf[i] = row
+    return synthetic.f32_to_bf16_bits(xf)
+
+
+def _nearest_code_exact(x, s):
+    """E4M3 code of the rational x / s by exhaustive search over the 127
+    finite magnitudes, comparing exact fractions: nearest value, ties to the
+    even code, anything above 448 saturating to 448."""
+    t = Fraction(float(x)) / Fraction(float(s))
+    mag = abs(t)
+    vals = [Fraction(float(v)) for v in oracle.e4m3_decode(np.arange(127))]
+    best = None
+    for c, v in enumerate(vals):
+        d = abs(mag - v)
+        if best is None or d < best[1] or (d == best[1] and c % 2 == 0):
+            best = (c, d)
+    code = best[0]
+    if mag >= vals[126]:
+        code = 126
+    return code | (0x80 if x < 0 or (x == 0 and np.signbit(x)) else 0)
+
+
+def test_quant_codes_are_exact_nearest_of_quotient():
+    # The definition written out independently: the scale from exact amax,
+    # then each sampled code from the exact rational x / s.
+    x = _tie_rows(384, 11)
+    codes, scales = oracle.quant_fp8_per_token(x)
+    xf = oracle.bf16_bits_to_f64(x)
+    rng = np.random.default_rng(2)
+    vals = oracle.e4m3_decode(np.arange(127))
+    mids = {Fraction(float(a)) / 2 + Fraction(float(b)) / 2 for a, b in zip(vals[:-1], vals[1:])}
+    ties = 0
+    for r in range(x.shape[0]):
+        amax = max(float(np.abs(xf[r]).max()), float(np.float32(1e-12)))
+        assert scales[r] == np.float32(np.float32(amax) / np.float32(448.0))
+        cols = rng.choice(x.shape[1], 96, replace=False)
+        for c in cols:
+            assert codes[r, c] == _nearest_code_exact(xf[r, c], scales[r]), (r, c, xf[r, c])
+        ties += sum(1 for c in cols if abs(Fraction(float(xf[r, c])) / Fraction(float(scales[r]))) in mids)
+    assert ties > 0, "the sample holds no exact rounding tie"
+
+
+def test_quant_definition_is_not_the_reciprocal_product():
+    # E4M3(x / s) and E4M3(fp32(x * fp32(448 / amax))) differ by one step on
+    # some elements of these rows; the oracle must follow the former.
+    x = _tie_rows(2048, 12)
+    codes, scales = oracle.quant_fp8_per_token(x)
+    xf = oracle.bf16_bits_to_f64(x).astype(np.float32)
+    amax = np.maximum(np.abs(xf).max(axis=1), np.float32(1e-12)).astype(np.float32)
+    inv = (np.float32(448.0) / amax).astype(np.float32)
+    recip = oracle.e4m3_encode((xf * inv[:, None]).astype(np.float32).astype(np.float64))
+    diff = np.argwhere(recip != codes)
+    assert len(diff) > 0
+    for r, c in diff[:40]:
+        assert codes[r, c] == _nearest_code_exact(float(xf[r, c]), scales[r])
+        step = abs(int(codes[r, c] & 0x7F) - int(recip[r, c] & 0x7F))
+        assert step == 1 and (codes[r, c] & 0x80) == (recip[r, c] & 0x80)
