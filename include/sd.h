@@ -26,9 +26,11 @@
  *    prepare phase (sd_rola_prepare, sd_rola_attention) may run part of its
  *    work on a second stream the library creates once per device and keeps
  *    until the process ends; events fork it from `stream` and join it back,
- *    so the call stays ordered on `stream` (also under graph capture). The
- *    first such call on a device creates that stream, so make it outside
- *    graph capture.
+ *    so the call stays ordered on `stream`, also when a launch fails. A call
+ *    on a stream that is being captured into a graph runs all of its work
+ *    on that stream: the second stream is shared by every host thread, and
+ *    forking it into one thread's capture would record another thread's
+ *    eager work into that graph.
  *  - Return value: SD_OK (0) or an SD_ERR_* code. Arguments are validated
  *    on the host before anything is launched; on a validation error no
  *    device memory is touched. sd_last_error() gives a thread-local message.
@@ -331,8 +333,11 @@ int sd_rola_apply_save(const sd_attn_shape* shape, const sd_lowrank_params* lr, 
  *     added into dQ (dK).
  *   dPq, dPk: f32 [rank, d] (P_head_stride 0) or [H, rank, d], or NULL to
  *     skip them.
- *   dg: f32 at the gate's strides (g_stride_h 0: summed over the heads), or
- *     NULL to skip it.
+ *   dg: f32 at the gate's strides, or NULL to skip it. A stride of 0 is a
+ *     broadcast and dg sums over that dimension (g_stride_h 0: over the
+ *     heads; g_stride_b 0: over the batch; g_stride_l 0: over the tokens), in
+ *     a fixed order. The non-zero strides must not overlap (SD_ERR_UNSUPPORTED
+ *     otherwise: elements of dg would be written by several (b, l, h)).
  *   saved: the forward's O_s, RMS and log-sum-exp (sd_rola_apply_save with
  *     the same inputs and block map), or NULL to form them here.
  * The low-rank state is formed again inside. All sums run in a fixed order

@@ -772,9 +772,9 @@ int run_rope_table(const sd_attn_shape* s, const sd_lowrank_params* lr, float2* 
 // When the stream pass reads K itself and its runs are whole key blocks (no
 // causal window), it also forms the key-block means; everything then runs in
 // order on the caller's stream (the Q pooling beside the stream pass would
-// only share HBM with it). Otherwise the selection, which keeps the vector
-// ALUs busy, runs on the caller's stream beside the HBM-bound stream pass on
-// the side stream.
+// only share HBM with it), as it does on a stream being captured into a
+// graph. Otherwise the selection, which keeps the vector ALUs busy, runs on
+// the caller's stream beside the HBM-bound stream pass on the side stream.
 int run_prepare(const sd_attn_shape* s, const Geo& g, const sd_lowrank_params* lr, const void* Q, const void* K,
                 const void* V, const void* Kn, int k_keep, int32_t* idx, const RolaWs& w, hipStream_t st) {
   int rc = run_rope_table(s, lr, w.lr.rope_tab, st);
@@ -793,9 +793,18 @@ int run_prepare(const sd_attn_shape* s, const Geo& g, const sd_lowrank_params* l
     if (e2 != hipSuccess) return hip_fail(e2, "low-rank finalize");
     return SD_OK;
   };
-  if (k_in_stream) {
-    e = sd::launch_pool_blocks(a.Q, s->sq_b, s->sq_l, s->sq_h, g.B, g.L, g.H, g.D, g.bq, w.sel.qmean, st);
-    if (e != hipSuccess) return hip_fail(e, "pool Q");
+  // A stream being captured into a graph keeps everything on itself: the
+  // side stream is shared by the host threads, and forking it into one
+  // thread's capture would pull another thread's eager work into that graph.
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if ((e = hipStreamIsCapturing(st, &cap)) != hipSuccess) return hip_fail(e, "prepare: capture status");
+  if (k_in_stream || cap != hipStreamCaptureStatusNone) {
+    if (scored) {
+      e = sd::launch_pool_blocks(a.Q, s->sq_b, s->sq_l, s->sq_h, g.B, g.L, g.H, g.D, g.bq, w.sel.qmean, st);
+      if (e == hipSuccess && !k_in_stream)
+        e = sd::launch_pool_blocks(a.K, s->sk_b, s->sk_l, s->sk_h, g.B, g.L, g.H, g.D, g.bk, w.sel.kmean, st);
+      if (e != hipSuccess) return hip_fail(e, "block pooling");
+    }
     if ((rc = stream_pass(st))) return rc;
     return run_scores_topk(s, g, k_keep, idx, w.sel, st);
   }
@@ -805,17 +814,22 @@ int run_prepare(const sd_attn_shape* s, const Geo& g, const sd_lowrank_params* l
   e = hipEventRecord(side->fork, st);
   if (e == hipSuccess) e = hipStreamWaitEvent(side->s, side->fork, 0);
   if (e != hipSuccess) return hip_fail(e, "prepare: fork");
-  if ((rc = stream_pass(side->s))) return rc;
+  rc = stream_pass(side->s);
   e = hipEventRecord(side->join, side->s);
-  if (e != hipSuccess) return hip_fail(e, "prepare: record join");
+  if (rc || e != hipSuccess) {
+    // a failed launch still joins, so that no fork is left open and the side
+    // stream's work is ordered before whatever the caller enqueues next
+    if (e == hipSuccess) e = hipStreamWaitEvent(st, side->join, 0);
+    if (rc) return rc;
+    return hip_fail(e, "prepare: join");
+  }
   if (scored) {
     e = sd::launch_pool_blocks(a.Q, s->sq_b, s->sq_l, s->sq_h, g.B, g.L, g.H, g.D, g.bq, w.sel.qmean, st);
     if (e == hipSuccess)
       e = sd::launch_pool_blocks(a.K, s->sk_b, s->sk_l, s->sk_h, g.B, g.L, g.H, g.D, g.bk, w.sel.kmean, st);
   }
   rc = e == hipSuccess ? run_scores_topk(s, g, k_keep, idx, w.sel, st) : hip_fail(e, "block pooling");
-  // the join comes after a failed launch too, so that the side stream's work
-  // is ordered before whatever the caller enqueues next
+  // the join comes after a failed launch too
   e = hipStreamWaitEvent(st, side->join, 0);
   if (rc) return rc;
   if (e != hipSuccess) return hip_fail(e, "prepare: join");
@@ -882,6 +896,24 @@ int sd_rola_apply(const sd_attn_shape* shape, const sd_lowrank_params* lr, const
                       idx ? idx : w.idx, w, static_cast<hipStream_t>(stream))))
     return rc;
   return ok();
+}
+
+// The gate's (b, l, h) strides address every stored element from one index
+// of its non-broadcast dimensions: sorted by stride, each dimension of
+// extent > 1 and stride > 0 steps past the whole span of the smaller ones.
+// (A stride of 0 is a broadcast; the gradient then sums over it.)
+static bool gate_strides_disjoint(const Geo& g, int64_t sb, int64_t sl, int64_t sh) {
+  std::vector<std::pair<int64_t, int64_t>> dims;  // (stride, extent)
+  if (sb > 0 && g.B > 1) dims.push_back({sb, g.B});
+  if (sl > 0 && g.L > 1) dims.push_back({sl, g.L});
+  if (sh > 0 && g.H > 1) dims.push_back({sh, g.H});
+  std::sort(dims.begin(), dims.end());
+  int64_t span = 1;
+  for (const auto& d : dims) {
+    if (d.first < span) return false;
+    span = d.first * d.second;
+  }
+  return true;
 }
 
 int check_saved(const sd_rola_saved* sv) {
@@ -1013,6 +1045,8 @@ int sd_rola_backward(const sd_attn_shape* shape, const sd_lowrank_params* lr, co
   if ((dQn && !aligned(dQn, 16)) || (dKn && !aligned(dKn, 16))) return fail(SD_ERR_ALIGN, "dQn / dKn misaligned");
   if ((dPq && !aligned(dPq, 4)) || (dPk && !aligned(dPk, 4)) || (dg && !aligned(dg, 4)))
     return fail(SD_ERR_ALIGN, "dPq / dPk / dg misaligned");
+  if (dg && !gate_strides_disjoint(g, g_stride_b, g_stride_l, g_stride_h))
+    return fail(SD_ERR_UNSUPPORTED, "gate strides overlap: dg elements would be written by several (b, l, h)");
   if (k_keep < 1 || k_keep > g.Nk) return fail(SD_ERR_INVALID_ARG, "k_keep = %d not in [1, %d]", k_keep, g.Nk);
   if (saved && (rc = check_saved(saved))) return rc;
   // the staged dO_s tiles are read through 32-bit buffer offsets

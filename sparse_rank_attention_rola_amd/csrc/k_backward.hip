@@ -535,22 +535,27 @@ __global__ __launch_bounds__(256) void dproj_finalize_kernel(const float* __rest
   if (qt == 0 && i < total) dP[i] = ((q4[0][threadIdx.x] + q4[1][threadIdx.x]) + q4[2][threadIdx.x]) + q4[3][threadIdx.x];
 }
 
+// The gate gradient at the gate's own strides. A stride of 0 means the gate
+// is broadcast over that dimension (one gate per token for every head, a
+// gate shared by the batch, ...): the stored element then receives the sum
+// over every (b, l, h) that reads it. One thread per stored element, summing
+// in a fixed order (b, then l, then h), so the result is deterministic.
 __global__ void dgate_kernel(const float* __restrict__ dg_head, int B, int L, int H, int64_t g_sb, int64_t g_sl,
                              int64_t g_sh, float* __restrict__ dg) {
+  const int Bo = g_sb ? B : 1, Lo = g_sl ? L : 1, Ho = g_sh ? H : 1;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (g_sh == 0) {
-    if (i >= (int64_t)B * L) return;
-    const int l = (int)(i % L), b = (int)(i / L);
-    float s = 0.f;
-    for (int h = 0; h < H; ++h) s += dg_head[i * H + h];
-    dg[(int64_t)b * g_sb + (int64_t)l * g_sl] = s;
-  } else {
-    if (i >= (int64_t)B * L * H) return;
-    const int h = (int)(i % H);
-    const int64_t bl = i / H;
-    const int l = (int)(bl % L), b = (int)(bl / L);
-    dg[(int64_t)b * g_sb + (int64_t)l * g_sl + (int64_t)h * g_sh] = dg_head[i];
-  }
+  if (i >= (int64_t)Bo * Lo * Ho) return;
+  const int ho = (int)(i % Ho);
+  const int64_t r = i / Ho;
+  const int lo = (int)(r % Lo), bo = (int)(r / Lo);
+  const int b0 = Bo == 1 ? 0 : bo, b1 = Bo == 1 ? B : bo + 1;
+  const int l0 = Lo == 1 ? 0 : lo, l1 = Lo == 1 ? L : lo + 1;
+  const int h0 = Ho == 1 ? 0 : ho, h1 = Ho == 1 ? H : ho + 1;
+  float s = 0.f;
+  for (int b = b0; b < b1; ++b)
+    for (int l = l0; l < l1; ++l)
+      for (int h = h0; h < h1; ++h) s += dg_head[((int64_t)b * L + l) * H + h];
+  dg[(int64_t)bo * g_sb + (int64_t)lo * g_sl + (int64_t)ho * g_sh] = s;
 }
 
 // ---------------------------------------------------------------------------
@@ -1140,7 +1145,7 @@ hipError_t launch_dproj_finalize(const float* part, int B, int H, int n_runs, in
 
 hipError_t launch_dgate(const float* dg_head, int B, int L, int H, int64_t g_sb, int64_t g_sl, int64_t g_sh,
                         float* dg, hipStream_t stream) {
-  const int64_t total = g_sh == 0 ? (int64_t)B * L : (int64_t)B * L * H;
+  const int64_t total = (int64_t)(g_sb ? B : 1) * (g_sl ? L : 1) * (g_sh ? H : 1);
   hipLaunchKernelGGL(dgate_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, dg_head, B, L, H,
                      g_sb, g_sl, g_sh, dg);
   return hipGetLastError();

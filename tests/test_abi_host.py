@@ -284,8 +284,9 @@ def test_backward_validation():
     need = lib.sd_rola_backward_workspace_size(ctypes.byref(s), ctypes.byref(p), 4)
     assert need > lib.sd_rola_workspace_size(ctypes.byref(s), ctypes.byref(p), 4)
 
-    def call(k=4, ws_bytes=need, Qn=None, dQn=None, idx=FAKE, dO=FAKE, dV=FAKE, g=FAKE, dg=None, saved=None):
-        return lib.sd_rola_backward(ctypes.byref(s), ctypes.byref(p), FAKE, FAKE, FAKE, Qn, None, g, 0, 1, 0, k,
+    def call(k=4, ws_bytes=need, Qn=None, dQn=None, idx=FAKE, dO=FAKE, dV=FAKE, g=FAKE, dg=None, saved=None,
+             gs=(0, 1, 0)):
+        return lib.sd_rola_backward(ctypes.byref(s), ctypes.byref(p), FAKE, FAKE, FAKE, Qn, None, g, *gs, k,
                                     0.125, idx, saved, dO, FAKE, FAKE, dV, dQn, None, None, None, dg, FAKE, ws_bytes,
                                     None)
 
@@ -298,6 +299,12 @@ def test_backward_validation():
     assert call(dQn=FAKE) == sd.SD_ERR_INVALID_ARG
     assert call(Qn=FAKE, dQn=FAKE + 4) == sd.SD_ERR_ALIGN
     assert call(dg=FAKE + 2) == sd.SD_ERR_ALIGN
+    # gate strides whose tokens and heads overlap: dg elements would race
+    assert s.H > 1 and s.L > 1
+    assert call(dg=FAKE, gs=(0, 1, 1)) == sd.SD_ERR_UNSUPPORTED
+    assert call(dg=FAKE, gs=(0, 2, 3)) == sd.SD_ERR_UNSUPPORTED
+    # without dg the same gate is only read; broadcasts are fine with dg
+    assert lib.sd_rola_backward_workspace_size(ctypes.byref(s), ctypes.byref(p), 4) == need
     assert call(ws_bytes=need - 1) == sd.SD_ERR_WORKSPACE
     assert call(saved=ctypes.byref(sd.sd_rola_saved(FAKE, None, FAKE))) == sd.SD_ERR_INVALID_ARG
     assert call(saved=ctypes.byref(sd.sd_rola_saved(FAKE + 2, FAKE, FAKE))) == sd.SD_ERR_ALIGN

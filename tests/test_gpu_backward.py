@@ -46,7 +46,7 @@ def _rel(got, ref, name, rel_l2=2.0 ** -7, max_frac=2.0 ** -6):
     assert rl <= rel_l2 and ma <= max_frac, f"{name}: rel_l2 {rl:.3e}, max {ma:.3e}"
 
 
-def _run(cfg, seed=0, chunk_frames=0, window=0, separate_qk=False, per_head_gate=False):
+def _run(cfg, seed=0, chunk_frames=0, window=0, separate_qk=False, per_head_gate=False, batch_shared_gate=False):
     Qb, Kb, Vb = synthetic.gen_qkv(cfg, seed)
     Pqb, Pkb = synthetic.gen_lowrank_params(cfg)
     rng = np.random.default_rng(seed + 100)
@@ -54,6 +54,8 @@ def _run(cfg, seed=0, chunk_frames=0, window=0, separate_qk=False, per_head_gate
         g = (1.0 + rng.standard_normal((cfg.B, cfg.L, cfg.H))).astype(np.float32)
     else:
         g = synthetic.gen_gate(cfg, amplified=True)
+    if batch_shared_gate:  # one gate row read by every batch element
+        g = np.broadcast_to(g[:1], g.shape).copy()
     dOb = synthetic.f32_to_bf16_bits(rng.standard_normal((cfg.B, cfg.L, cfg.H, cfg.d)).astype(np.float32))
     Qnb = Knb = None
     if separate_qk:
@@ -68,7 +70,7 @@ def _run(cfg, seed=0, chunk_frames=0, window=0, separate_qk=False, per_head_gate
     k = oracle.keep_count(cfg.sparsity, -(-cfg.L // cfg.block_k))
     nq = -(-cfg.L // cfg.block_q)
     idx = torch.empty((cfg.B, cfg.H, nq, k), dtype=torch.int32, device="cuda")
-    gd = dev_f32(g)
+    gd = dev_f32(g[:1]).expand(g.shape) if batch_shared_gate else dev_f32(g)
     ws = sd.rola_workspace(Q, lr, k, grid=grid, block_q=cfg.block_q, **var)
     sd.sd_rola_prepare(Q, K, V, lr, k, ws, grid=grid, block_q=cfg.block_q, Qn=Qn, Kn=Kn, idx_out=idx, **var)
     grads = sd.sd_rola_backward(Q, K, V, gd, lr, k, idx, dO, grid=grid, block_q=cfg.block_q, Qn=Qn, Kn=Kn, **var)
@@ -103,6 +105,10 @@ def _run(cfg, seed=0, chunk_frames=0, window=0, separate_qk=False, per_head_gate
                 ref["dg"][b] += res["dg"]
     _rel(got["dPq"], ref["dPq"][: cfg.rank], "dPq", rel_l2=2.0 ** -9)
     _rel(got["dPk"], ref["dPk"][: cfg.rank], "dPk", rel_l2=2.0 ** -9)
+    if batch_shared_gate:  # the gradient of the shared row sums over the batch
+        assert grads["dg"].stride(0) == 0
+        ref["dg"] = ref["dg"].sum(axis=0, keepdims=True)
+        got["dg"] = got["dg"][:1]
     _rel(got["dg"], ref["dg"], "dg", rel_l2=2.0 ** -9)
     return grads
 
@@ -111,6 +117,13 @@ def _run(cfg, seed=0, chunk_frames=0, window=0, separate_qk=False, per_head_gate
 def test_backward_bidirectional(cfg):
     say(f"backward {cfg.name}")
     _run(cfg)
+
+
+def test_backward_gate_shared_by_the_batch():
+    # B = 2 with one gate row broadcast over the batch (stride 0): dg sums the
+    # two batch elements' gradients instead of keeping one of them
+    say("backward ragged-d64, gate broadcast over the batch")
+    _run(RAGGED64, seed=4, batch_shared_gate=True)
 
 
 def test_backward_separate_qk_and_per_head_gate():
