@@ -48,6 +48,70 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
+def stats(ms_list):
+    """Median, min and mean of a list of per-iteration times (ms)."""
+    import numpy as np
+    a = np.asarray(ms_list, dtype=np.float64)
+    return {"median": round(float(np.median(a)), 4), "min": round(float(a.min()), 4),
+            "mean": round(float(a.mean()), 4)}
+
+
+class ClockSampler:
+    """Samples the GPU's graphics clock (amdsmi) from a host thread while a
+    timed region runs; reports median / min / max in MHz, or None where the
+    library is not available."""
+
+    def __init__(self, period_s=0.002):
+        import threading
+        self.period = period_s
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = None
+        self.ok = False
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self._smi = amdsmi
+            self._h = amdsmi.amdsmi_get_processor_handles()[0]
+            self._read()
+            self.ok = True
+        except Exception:  # pragma: no cover - depends on the machine
+            self._smi = None
+
+    def _read(self):
+        info = self._smi.amdsmi_get_clock_info(self._h, self._smi.AmdSmiClkType.GFX)
+        return float(info["clk"])
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                self.samples.append(self._read())
+            except Exception:  # pragma: no cover
+                return
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        import threading
+        if self.ok:
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+        return False
+
+    def summary(self):
+        import numpy as np
+        if not self.samples:
+            return None
+        a = np.asarray(self.samples)
+        return {"median_mhz": float(np.median(a)), "min_mhz": float(a.min()), "max_mhz": float(a.max()),
+                "samples": int(a.size), "source": "amdsmi GFX clock, sampled every 2 ms over the timed steps"}
+
+
 def kept_pair_flops(idx, L, bq, bk, d):
     """Algorithmic FLOPs of the sparse branch: sum over kept (query block,
     key block) pairs of 4 * n_q * n_k * d with valid-token counts n."""
@@ -150,6 +214,65 @@ def pmc_traffic(fetch_path, write_path, kernel="attention_kernel<128, 128, 2>", 
     return res, total
 
 
+def pmc_summary(paths, kernel_filter, cmd, durations_db=None):
+    """Markdown table of the counters of rocprofv3 --pmc databases for the
+    kernels whose name contains `kernel_filter`: per counter the mean over
+    dispatches of the sum over instances (GRBM_*: the largest instance, one
+    XCD's cycle count), and the utilisations derived from them. With a
+    kernel-trace database, the mean duration gives the clock."""
+    import numpy as np
+    per = {}  # (kernel, counter) -> per-dispatch values
+    for path in paths:
+        db = _rocpd(path)
+        rows = db.execute("select dispatch_id, name, counter_name, counter_value from pmc_events").fetchall()
+        acc = {}
+        for did, name, cname, val in rows:
+            if kernel_filter not in name:
+                continue
+            acc.setdefault((name, cname, did), []).append(float(val))
+        for (name, cname, did), vals in acc.items():
+            v = max(vals) if cname.startswith("GRBM_") else sum(vals)
+            per.setdefault((name.split("(")[0].replace("void ", ""), cname), []).append(v)
+    kernels = sorted({k for k, _ in per})
+    dur = {}
+    if durations_db:
+        db = _rocpd(durations_db)
+        for name, d in db.execute("select name, duration from kernels"):
+            short = name.split("(")[0].replace("void ", "")
+            dur.setdefault(short, []).append(d)
+    lines = [f"Command: `{cmd}`", ""]
+    simds = 256 * 4
+    for kname in kernels:
+        c = {cn: float(np.mean(v)) for (k, cn), v in per.items() if k == kname}
+        lines += [f"### `{kname}`", "", "| counter | mean per dispatch |", "|---|---|"]
+        lines += [f"| {cn} | {v:.4g} |" for cn, v in sorted(c.items())]
+        gui = c.get("GRBM_GUI_ACTIVE")
+        derived = []
+        if gui:
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+                derived.append(("MFMA busy (of every SIMD's cycles)", 100 * c["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * simds)))
+            if "SQ_VALU_MFMA_COEXEC_CYCLES" in c and c.get("SQ_VALU_MFMA_BUSY_CYCLES"):
+                derived.append(("VALU co-executing with MFMA (of MFMA-busy cycles)",
+                                100 * c["SQ_VALU_MFMA_COEXEC_CYCLES"] / c["SQ_VALU_MFMA_BUSY_CYCLES"]))
+            if "SQ_LDS_IDX_ACTIVE" in c:
+                derived.append(("LDS active (of every CU's cycles)", 100 * c["SQ_LDS_IDX_ACTIVE"] / (gui * 256)))
+            if "SQ_BUSY_CYCLES" in c:
+                derived.append(("SQ busy (of GUI-active cycles, per SE sum)", 100 * c["SQ_BUSY_CYCLES"] / (gui * 32)))
+            if kname in dur:
+                derived.append(("clock from GRBM_GUI_ACTIVE / mean duration (MHz)",
+                                gui / (float(np.mean(dur[kname])) * 1e-9) / 1e6))
+        if c.get("TCC_HIT_sum") is not None and c.get("TCC_MISS_sum") is not None:
+            derived.append(("L2 hit rate", 100 * c["TCC_HIT_sum"] / max(c["TCC_HIT_sum"] + c["TCC_MISS_sum"], 1)))
+        if "SQ_INSTS_VALU" in c and "SQ_INSTS_MFMA" in c:
+            derived.append(("VALU instructions per MFMA instruction", c["SQ_INSTS_VALU"] / max(c["SQ_INSTS_MFMA"], 1)))
+        if kname in dur:
+            derived.append(("mean duration (us)", float(np.mean(dur[kname])) / 1e3))
+        if derived:
+            lines += ["", "| derived | value |", "|---|---|"] + [f"| {n} | {v:.3f} |" for n, v in derived]
+        lines.append("")
+    return "\n".join(lines)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -164,15 +287,23 @@ def main():
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the fixed-selector and causal-window measurements")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward measurement")
+    ap.add_argument("--no-s090", action="store_true", help="skip the s = 0.90 comparison of the 720P layer")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter calibration)")
     ap.add_argument("--trace-summary", metavar="DB", help="print a kernel table of a rocprofv3 trace and exit")
     ap.add_argument("--pmc-traffic", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                     help="write the fused kernel's HBM bytes per launch from two rocprofv3 --pmc runs "
                          "(FETCH_SIZE, WRITE_SIZE, each with --calib-copy) to the traffic record and exit")
+    ap.add_argument("--pmc-summary", nargs="+", metavar="DB",
+                    help="print a counter table of rocprofv3 --pmc runs for --kernel and exit")
+    ap.add_argument("--kernel", default="attention_kernel<128, 128, 2>", help="kernel name filter of --pmc-summary")
+    ap.add_argument("--durations", metavar="DB", help="kernel-trace database giving --pmc-summary the durations")
     ap.add_argument("--cmd", default="", help="command line recorded with --trace-summary / --pmc-traffic")
     args = ap.parse_args()
 
+    if args.pmc_summary:
+        print(pmc_summary(args.pmc_summary, args.kernel, args.cmd, args.durations))
+        return
     if args.trace_summary:
         print(trace_summary(args.trace_summary, args.cmd, args.warmup))
         return
@@ -226,6 +357,14 @@ def main():
     torch.cuda.synchronize()
     log(f"inputs resident on {torch.cuda.get_device_name(0)}; k_keep={k} of {nk}")
 
+    # The L2 and the last-level cache (MALL, 256 MB) are flushed before every
+    # timed iteration by writing a 512 MiB buffer on the same stream, outside
+    # the events: each step starts with its inputs in HBM only.
+    flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    def flush():
+        flush_buf.fill_(0x5A)
+
     def step(ev=None):
         if ev: ev[0].record()
         sd.sd_quant_fp8_per_token(X, q=codes, scales=scales)
@@ -236,23 +375,68 @@ def main():
         if ev: ev[3].record()
 
     for _ in range(args.warmup):
+        flush()
         step()
     torch.cuda.synchronize()
     log(f"{args.warmup} warmup steps done")
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with ClockSampler() as clock:
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            flush()
+            step(evs[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     log(f"{args.steps} timed steps done")
 
-    t_quant = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    t_prep = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-    t_apply = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
-    t_layer = float(np.mean([e[1].elapsed_time(e[3]) for e in evs]))
+    st_quant = stats([e[0].elapsed_time(e[1]) for e in evs])
+    st_prep = stats([e[1].elapsed_time(e[2]) for e in evs])
+    st_apply = stats([e[2].elapsed_time(e[3]) for e in evs])
+    st_layer = stats([e[1].elapsed_time(e[3]) for e in evs])
+    t_quant, t_prep, t_apply, t_layer = (x["median"] for x in (st_quant, st_prep, st_apply, st_layer))
+
+    def time_layer(kk, n, idx_v, ws_v, **var):
+        """Median / min / mean of prepare, fused kernel and layer over n
+        flushed iterations of the layer keeping kk key blocks per row."""
+        for _ in range(max(1, args.warmup // 2)):
+            flush()
+            sd.sd_rola_prepare(Q, K, V, lr, kk, ws_v, grid=grid, block_q=cfg.block_q, idx_out=idx_v, **var)
+            sd.sd_rola_apply(Q, K, V, gd, lr, kk, ws_v, grid=grid, block_q=cfg.block_q, out=O, idx=idx_v, **var)
+        torch.cuda.synchronize()
+        vev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+        for e in vev:
+            flush()
+            e[0].record()
+            sd.sd_rola_prepare(Q, K, V, lr, kk, ws_v, grid=grid, block_q=cfg.block_q, idx_out=idx_v, **var)
+            e[1].record()
+            sd.sd_rola_apply(Q, K, V, gd, lr, kk, ws_v, grid=grid, block_q=cfg.block_q, out=O, idx=idx_v, **var)
+            e[2].record()
+        torch.cuda.synchronize()
+        return (stats([e[0].elapsed_time(e[1]) for e in vev]), stats([e[1].elapsed_time(e[2]) for e in vev]),
+                stats([e[0].elapsed_time(e[2]) for e in vev]))
+
+    # The comparison the write-up isolates for sparsity (section 1: 90% ->
+    # 97% keeps about 30% of the block-sparse compute): the same layer at
+    # s = 0.90, with its own block map.
+    s090 = None
+    if not args.no_s090 and abs(cfg.sparsity - 0.97) < 1e-12:
+        k90 = sd.sd_keep_count(0.90, nk)
+        ws90 = sd.rola_workspace(Q, lr, k90, grid=grid, block_q=cfg.block_q)
+        idx90 = torch.empty((cfg.B, cfg.H, nq, k90), dtype=torch.int32, device=dev)
+        p90, a90, l90 = time_layer(k90, max(3, args.steps // 2), idx90, ws90)
+        fl90 = kept_pair_flops(idx90.cpu().numpy(), cfg.L, cfg.block_q, cfg.block_k, cfg.d)
+        fl97 = kept_pair_flops(idx.cpu().numpy(), cfg.L, cfg.block_q, cfg.block_k, cfg.d)
+        s090 = {"sparsity": 0.90, "k_keep": k90, "ms_layer": l90, "ms_prepare": p90, "ms_apply": a90,
+                "kept_pair_tflop": round(fl90 / 1e12, 4),
+                "kept_pair_tflops": round(fl90 / (a90["median"] * 1e-3) / 1e12, 1),
+                "mfma_peak_frac": round(fl90 / (a90["median"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                "kept_pair_flop_ratio_s097_to_s090": round(fl97 / fl90, 4),
+                "fused_kernel_time_ratio_s097_to_s090": round(t_apply / a90["median"], 4),
+                "layer_time_ratio_s097_to_s090": round(t_layer / l90["median"], 4)}
+        log(f"s=0.90 leg: layer {l90['median']:.3f} ms, fused {a90['median']:.3f} ms")
+        del ws90, idx90
 
     # The same layer with the other selector and under a causal window
     # (autoregressive use: chunks of 3 latent frames, a window of 2 chunks and
@@ -266,23 +450,10 @@ def main():
                           ("causal prefix, 3-frame chunks", dict(chunk_tokens=ct, window=0))):
             wsv = sd.rola_workspace(Q, lr, k, grid=grid, block_q=cfg.block_q, **var)
             idv = torch.empty_like(idx)
-            for _ in range(max(1, args.warmup)):
-                sd.sd_rola_prepare(Q, K, V, lr, k, wsv, grid=grid, block_q=cfg.block_q, idx_out=idv, **var)
-                sd.sd_rola_apply(Q, K, V, gd, lr, k, wsv, grid=grid, block_q=cfg.block_q, out=O, idx=idv, **var)
-            torch.cuda.synchronize()
-            n_v = max(3, args.steps // 2)
-            vev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_v)]
-            for e in vev:
-                e[0].record()
-                sd.sd_rola_prepare(Q, K, V, lr, k, wsv, grid=grid, block_q=cfg.block_q, idx_out=idv, **var)
-                e[1].record()
-                sd.sd_rola_apply(Q, K, V, gd, lr, k, wsv, grid=grid, block_q=cfg.block_q, out=O, idx=idv, **var)
-                e[2].record()
-            torch.cuda.synchronize()
-            tp = float(np.mean([e[0].elapsed_time(e[1]) for e in vev]))
-            ta = float(np.mean([e[1].elapsed_time(e[2]) for e in vev]))
+            sp, sa, sl = time_layer(k, max(3, args.steps // 2), idv, wsv, **var)
+            tp, ta = sp["median"], sa["median"]
             fl = kept_pair_flops(idv.cpu().numpy(), cfg.L, cfg.block_q, cfg.block_k, cfg.d)
-            variants[name] = {"ms_layer": round(tp + ta, 4), "ms_prepare": round(tp, 4), "ms_apply": round(ta, 4),
+            variants[name] = {"ms_layer": sl, "ms_prepare": sp, "ms_apply": sa,
                               "kept_pair_tflops": round(fl / (ta * 1e-3) / 1e12, 1)}
             log(f"variant {name}: {tp + ta:.3f} ms")
             del wsv, idv
@@ -432,6 +603,16 @@ def main():
     idx_np = idx.cpu().numpy()
     flops = kept_pair_flops(idx_np, cfg.L, cfg.block_q, cfg.block_k, cfg.d)
     achieved = flops / (t_apply * 1e-3) / 1e12
+    # the fused kernel's compulsory HBM bytes: Q once, each K/V row once, the
+    # O write, the block map, the gate and the two bf16 halves of C^T
+    tok = cfg.B * cfg.L * cfg.H * cfg.d * 2
+    alg_bytes = 4 * tok + idx_np.size * 4 + cfg.B * cfg.L * 4 + cfg.B * cfg.H * cfg.rank * cfg.d * 4
+    mfma_frac = achieved / MFMA_BF16_PEAK_TFLOPS
+    hbm_frac_alg = alg_bytes / (t_apply * 1e-3) / 1e9 / HBM_PEAK_GBPS
+    # The roof is the one the algorithm meets first: the kernel's arithmetic
+    # intensity against the ridge point of the two peaks.
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    bound = "mfma" if flops / alg_bytes >= ridge else "hbm"
     quant_bytes = M * Kc * 3 + M * 4
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
@@ -470,10 +651,24 @@ def main():
         "mfma_peak_frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
         "fp8_quant_gbps": round(quant_bytes / (t_quant * 1e-3) / 1e9, 1),
         "fp8_quant_hbm_frac": round(quant_bytes / (t_quant * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-        "roofline": {"kernel": "rola fused attention (sparse tiles + low-rank query + gate)", "bound": "mfma",
-                     "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
-                     "algorithmic_flops_per_launch": flops},
+        "roofline": {"kernel": "rola fused attention (sparse tiles + low-rank query + gate)", "bound": bound,
+                     "achieved": round(achieved, 2) if bound == "mfma" else
+                     round(alg_bytes / (t_apply * 1e-3) / 1e9, 1),
+                     "peak": MFMA_BF16_PEAK_TFLOPS if bound == "mfma" else HBM_PEAK_GBPS,
+                     "unit": "TFLOP/s" if bound == "mfma" else "GB/s",
+                     "frac": round(mfma_frac if bound == "mfma" else hbm_frac_alg, 4), "traffic": traffic,
+                     "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": alg_bytes,
+                     "arithmetic_intensity_flop_per_byte": round(flops / alg_bytes, 1),
+                     "ridge_flop_per_byte": round(ridge, 1),
+                     "mfma_frac": round(mfma_frac, 4), "hbm_frac_algorithmic_bytes": round(hbm_frac_alg, 4),
+                     "hbm_frac_measured_traffic": (round(traffic / (t_apply * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
+                                                   if traffic else None),
+                     "traffic_over_algorithmic_bytes": round(traffic / alg_bytes, 2) if traffic else None},
+        "timing_ms": {"protocol": "L2 and MALL flushed (512 MiB write) before every timed iteration, outside the "
+                                  "events; median / min / mean over the timed steps; value = median layer time",
+                      "layer": st_layer, "fp8_quant": st_quant, "prepare": st_prep, "fused_kernel": st_apply},
+        "sclk": clock.summary(),
+        "s090_720p": s090,
         "variants_720p": variants,
         "backward_720p": backward,
         "w8a8_qkv_projection": gemm,
