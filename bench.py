@@ -33,6 +33,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MFMA_FP8_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 MFMA
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_rola_fused_720p.json")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_rola_fused_720p.json")
 FUSED_KERNEL_SOURCES = ["k_attention.hip", "sd_tiles.h", "sd_device.h", "sd_launch.h"]
 
 
@@ -54,62 +55,6 @@ def stats(ms_list):
     a = np.asarray(ms_list, dtype=np.float64)
     return {"median": round(float(np.median(a)), 4), "min": round(float(a.min()), 4),
             "mean": round(float(a.mean()), 4)}
-
-
-class ClockSampler:
-    """Samples the GPU's graphics clock (amdsmi) from a host thread while a
-    timed region runs; reports median / min / max in MHz, or None where the
-    library is not available."""
-
-    def __init__(self, period_s=0.002):
-        import threading
-        self.period = period_s
-        self.samples = []
-        self._stop = threading.Event()
-        self._thread = None
-        self.ok = False
-        try:
-            import amdsmi
-            amdsmi.amdsmi_init()
-            self._smi = amdsmi
-            self._h = amdsmi.amdsmi_get_processor_handles()[0]
-            self._read()
-            self.ok = True
-        except Exception:  # pragma: no cover - depends on the machine
-            self._smi = None
-
-    def _read(self):
-        info = self._smi.amdsmi_get_clock_info(self._h, self._smi.AmdSmiClkType.GFX)
-        return float(info["clk"])
-
-    def _run(self):
-        while not self._stop.is_set():
-            try:
-                self.samples.append(self._read())
-            except Exception:  # pragma: no cover
-                return
-            self._stop.wait(self.period)
-
-    def __enter__(self):
-        import threading
-        if self.ok:
-            self._thread = threading.Thread(target=self._run, daemon=True)
-            self._thread.start()
-        return self
-
-    def __exit__(self, *exc):
-        if self._thread is not None:
-            self._stop.set()
-            self._thread.join()
-        return False
-
-    def summary(self):
-        import numpy as np
-        if not self.samples:
-            return None
-        a = np.asarray(self.samples)
-        return {"median_mhz": float(np.median(a)), "min_mhz": float(a.min()), "max_mhz": float(a.max()),
-                "samples": int(a.size), "source": "amdsmi GFX clock, sampled every 2 ms over the timed steps"}
 
 
 def kept_pair_flops(idx, L, bq, bk, d):
@@ -242,6 +187,7 @@ def pmc_summary(paths, kernel_filter, cmd, durations_db=None):
             dur.setdefault(short, []).append(d)
     lines = [f"Command: `{cmd}`", ""]
     simds = 256 * 4
+    record = {}
     for kname in kernels:
         c = {cn: float(np.mean(v)) for (k, cn), v in per.items() if k == kname}
         lines += [f"### `{kname}`", "", "| counter | mean per dispatch |", "|---|---|"]
@@ -270,7 +216,8 @@ def pmc_summary(paths, kernel_filter, cmd, durations_db=None):
         if derived:
             lines += ["", "| derived | value |", "|---|---|"] + [f"| {n} | {v:.3f} |" for n, v in derived]
         lines.append("")
-    return "\n".join(lines)
+        record[kname] = {"counters": c, "derived": dict(derived)}
+    return "\n".join(lines), record
 
 
 def main():
@@ -298,11 +245,17 @@ def main():
                     help="print a counter table of rocprofv3 --pmc runs for --kernel and exit")
     ap.add_argument("--kernel", default="attention_kernel<128, 128, 2>", help="kernel name filter of --pmc-summary")
     ap.add_argument("--durations", metavar="DB", help="kernel-trace database giving --pmc-summary the durations")
+    ap.add_argument("--record", metavar="JSON", help="with --pmc-summary: also write the derived values as JSON")
     ap.add_argument("--cmd", default="", help="command line recorded with --trace-summary / --pmc-traffic")
     args = ap.parse_args()
 
     if args.pmc_summary:
-        print(pmc_summary(args.pmc_summary, args.kernel, args.cmd, args.durations))
+        text, record = pmc_summary(args.pmc_summary, args.kernel, args.cmd, args.durations)
+        print(text)
+        if args.record:
+            with open(args.record, "w") as f:
+                json.dump({"kernel_filter": args.kernel, "source_hash": kernel_source_hash(), "command": args.cmd,
+                           "kernels": record}, f, indent=1)
         return
     if args.trace_summary:
         print(trace_summary(args.trace_summary, args.cmd, args.warmup))
@@ -382,13 +335,12 @@ def main():
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
-    with ClockSampler() as clock:
-        t0 = time.perf_counter()
-        for i in range(args.steps):
-            flush()
-            step(evs[i])
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        flush()
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
     log(f"{args.steps} timed steps done")
 
     st_quant = stats([e[0].elapsed_time(e[1]) for e in evs])
@@ -623,6 +575,20 @@ def main():
         except Exception:
             traffic = None
 
+    # clock and pipe utilisation of the fused kernel from the counter record
+    # of the same sources (rocprofv3 --pmc; GRBM_GUI_ACTIVE / kernel duration)
+    counters = None
+    if os.path.exists(COUNTERS_FILE):
+        try:
+            rec = json.load(open(COUNTERS_FILE))
+            if rec.get("source_hash") == kernel_source_hash():
+                (kname, kv), = [(n, v) for n, v in rec["kernels"].items() if "attention_kernel<128, 128, 2>" in n]
+                d = kv["derived"]
+                counters = {"kernel": kname, "source": os.path.relpath(COUNTERS_FILE, ROOT),
+                            **{n: round(v, 3) for n, v in d.items()}}
+        except Exception:
+            counters = None
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
@@ -667,7 +633,8 @@ def main():
         "timing_ms": {"protocol": "L2 and MALL flushed (512 MiB write) before every timed iteration, outside the "
                                   "events; median / min / mean over the timed steps; value = median layer time",
                       "layer": st_layer, "fp8_quant": st_quant, "prepare": st_prep, "fused_kernel": st_apply},
-        "sclk": clock.summary(),
+        "sclk_mhz_under_load": (counters or {}).get("clock from GRBM_GUI_ACTIVE / mean duration (MHz)"),
+        "fused_kernel_counters": counters,
         "s090_720p": s090,
         "variants_720p": variants,
         "backward_720p": backward,

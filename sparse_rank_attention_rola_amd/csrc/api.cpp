@@ -155,13 +155,21 @@ struct SelectWs {
   double* qmean;
   double* kmean;
   double* S;
+  uint16_t* khi;  // the key-block means split into bf16 hi + lo (scored selector)
+  uint16_t* klo;
 };
 
+// The scored selector forms its scores inside the selection kernel; only the
+// fixed pattern keeps a score matrix (one Nq x Nk map for every head).
 SelectWs carve_select(Carve& c, const Geo& g) {
   SelectWs w;
   w.qmean = static_cast<double*>(c.take(sizeof(double) * g.B * g.H * g.Nq * g.D));
   w.kmean = static_cast<double*>(c.take(sizeof(double) * g.B * g.H * g.Nk * g.D));
-  w.S = static_cast<double*>(c.take(sizeof(double) * g.B * g.H * (size_t)g.Nq * g.Nk));
+  const size_t s_rows = g.select == SD_SELECT_FIXED ? (size_t)g.Nq : 0;
+  w.S = static_cast<double*>(c.take(sizeof(double) * s_rows * g.Nk));
+  const size_t split = g.select == SD_SELECT_TOPK ? (size_t)g.B * g.H * g.Nk * g.D : 0;
+  w.khi = static_cast<uint16_t*>(c.take(sizeof(uint16_t) * split));
+  w.klo = static_cast<uint16_t*>(c.take(sizeof(uint16_t) * split));
   return w;
 }
 
@@ -292,9 +300,7 @@ int run_scores_topk(const sd_attn_shape* s, const Geo& g, int k_keep, int32_t* i
     if (e != hipSuccess) return hip_fail(e, "fixed scores");
     e = sd::launch_topk_rows(w.S, g.Nq, g.Nk, k_keep, rule, idx, st);
   } else {
-    e = sd::launch_block_scores(w.qmean, w.kmean, g.B * g.H, g.Nq, g.Nk, g.D, w.S, st);
-    if (e != hipSuccess) return hip_fail(e, "block scores");
-    e = sd::launch_topk_rows(w.S, (int64_t)g.B * g.H * g.Nq, g.Nk, k_keep, rule, idx, st);
+    e = sd::launch_select_topk(w.qmean, w.kmean, g.B * g.H, g.Nk, g.D, k_keep, rule, w.khi, w.klo, idx, st);
   }
   if (e != hipSuccess) return hip_fail(e, "top-k");
   return SD_OK;

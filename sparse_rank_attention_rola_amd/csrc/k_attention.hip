@@ -40,58 +40,58 @@ constexpr int kAttnMinWaves = 2;  // waves per SIMD the register budget must all
 
 __device__ __forceinline__ float phi_elu1(float x) { return x > 0.f ? x + 1.f : __expf(x); }
 
-// Low-rank query output for the 32 queries of one wave.
-//   qreg: the wave's normalised queries in the B-operand layout
-//         (lane l32 = query, channels 16*s + 8*hf .. +7).
-//   Fw:   wave-private LDS patch of 32 x 33 floats.
-//   q_chunk: the autoregressive chunk of the lane's query (0 without a
-//         causal window); the state C of that chunk is used.
-// Returns y / sqrt(mean(y^2) + eps) * w in the O^T accumulator layout.
+// max(a, b, c) in one v_max3_f32 (the compiler's fmaxf would first quiet each
+// MFMA result; scores are never NaN here).
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// Low-rank query branch for the 32 queries of one wave, in three parts so
+// that the features can be formed while the first K/V tile lands:
+//   lowrank_load:     the lane's P_q rows (A operands of the projection) and
+//                     the cos/sin of its RoPE pairs;
+//   lowrank_features: q~ = R(p) phi(P_q qn) through the wave's LDS patch Fw
+//                     (32 x 33 floats), split into bf16 hi + lo B operands
+//                     (lane l32 = query, ranks 16s + 8hf .. +7);
+//   lowrank_output:   y = C^T q~ with the state C of the lane's chunk (0
+//                     without a causal window), y / sqrt(mean(y^2) + eps) * w
+//                     in the O^T accumulator layout.
 template <int D>
-__device__ __forceinline__ void lowrank_query_tile(const u32x4* qreg, const AttnArgs& a, int b, int h, int tok0,
-                                                   int q_chunk, float* Fw, int lane, f32x16 (&out)[D / 32]) {
+struct LowrankLoads {
+  u32x4 pa[D / 16];
+  float2 cs[kMaxRopePairs / 2];
+};
+
+template <int D>
+__device__ __forceinline__ void lowrank_load(const AttnArgs& a, int h, int tok0, int lane, LowrankLoads<D>& ld) {
   const int hf = lane >> 5, l32 = lane & 31;
-  // The RoPE factors of the lane's pairs are loaded with the projection's
-  // operands, so that both loads wait on memory together.
   const int tok = tok0 + l32;
   const int hw = a.Hg * a.Wg;
   const int pos[3] = {min(tok / hw, a.rope.max_ext - 1), (tok / a.Wg) % a.Hg, tok % a.Wg};
-  float2 cs_m[kMaxRopePairs / 2];
 #pragma unroll
   for (int j = 0; j < kMaxRopePairs / 2; ++j) {
     const int m = 2 * j + hf;
-    cs_m[j] = float2{1.f, 0.f};
+    ld.cs[j] = float2{1.f, 0.f};
     if (2 * j < a.rope.n && m < a.rope.n) {
       const int axis = a.rope.axis[m];
-      cs_m[j] = a.rope_tab[m * a.rope.max_ext + (axis == 0 ? pos[0] : axis == 1 ? pos[1] : pos[2])];
+      ld.cs[j] = a.rope_tab[m * a.rope.max_ext + (axis == 0 ? pos[0] : axis == 1 ? pos[1] : pos[2])];
     }
   }
   const uint16_t* Pq = a.Pq + (int64_t)h * a.P_hs;
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s)
+    ld.pa[s] = (l32 < a.rank) ? *reinterpret_cast<const u32x4*>(Pq + l32 * D + 16 * s + 8 * hf) : u32x4{0, 0, 0, 0};
+}
+
+template <int D>
+__device__ __forceinline__ void lowrank_features(const u32x4* qn, const AttnArgs& a, const LowrankLoads<D>& ld,
+                                                 float* Fw, int lane, bf16x8 (&qhi)[2], bf16x8 (&qlo)[2]) {
+  const int hf = lane >> 5, l32 = lane & 31;
   f32x16 acc = {};
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) {
-    const u32x4 pa = (l32 < a.rank) ? *reinterpret_cast<const u32x4*>(Pq + l32 * D + 16 * s + 8 * hf)
-                                    : u32x4{0, 0, 0, 0};
-    acc = mfma32(as_bf16x8(pa), as_bf16x8(qreg[s]), acc);
-  }
-  // The state of the wave's first chunk, first half of the channel tiles:
-  // loaded once the projection's operands are dead, so that the loads are in
-  // flight during the RoPE patch (the fence keeps them from moving up).
-  const int n_ar = (a.L + a.ar_tokens - 1) / a.ar_tokens;
-  const int c_first = __builtin_amdgcn_readfirstlane(q_chunk);
-  const int c_last = __builtin_amdgcn_readlane(q_chunk, 31);
-  auto state_off = [&](int c, int dt, int s) {
-    return (((int64_t)b * a.H + h) * n_ar + c) * D * 32 + (int64_t)(32 * dt + l32) * 32 + 16 * s + 8 * hf;
-  };
-  __builtin_amdgcn_sched_barrier(0);
-  u32x4 cth0[D / 64][2], ctl0[D / 64][2];
-#pragma unroll
-  for (int dt = 0; dt < D / 64; ++dt)
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      cth0[dt][s] = *reinterpret_cast<const u32x4*>(a.Ct_hi + state_off(c_first, dt, s));
-      ctl0[dt][s] = *reinterpret_cast<const u32x4*>(a.Ct_lo + state_off(c_first, dt, s));
-    }
+  for (int s = 0; s < D / 16; ++s) acc = mfma32(as_bf16x8(ld.pa[s]), as_bf16x8(qn[s]), acc);
   // acc: column = query l32, row = rank index 8*(r/4) + 4*hf + r%4
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
@@ -104,7 +104,7 @@ __device__ __forceinline__ void lowrank_query_tile(const u32x4* qreg, const Attn
   for (int j = 0; j < kMaxRopePairs / 2; ++j) {
     const int m = 2 * j + hf;
     if (2 * j < a.rope.n && m < a.rope.n) {
-      const float2 cs = cs_m[j];
+      const float2 cs = ld.cs[j];
       float* f = Fw + l32 * 33 + a.rope.dim[m];
       const float u = f[0], v = f[1];
       f[0] = u * cs.x - v * cs.y;
@@ -112,7 +112,6 @@ __device__ __forceinline__ void lowrank_query_tile(const u32x4* qreg, const Attn
     }
   }
   __syncthreads();
-  bf16x8 qhi[2], qlo[2];
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     float t8[8];
@@ -120,28 +119,60 @@ __device__ __forceinline__ void lowrank_query_tile(const u32x4* qreg, const Attn
     for (int p = 0; p < 8; ++p) t8[p] = Fw[l32 * 33 + 16 * s + 8 * hf + p];
     split_bf16x8(t8, qhi[s], qlo[s]);
   }
+}
+
+// The state C^T (bf16 hi and lo parts) of chunk c as the A operands of the
+// lane: channel 32 dt + l32, ranks 16 s + 8 hf .. + 7.
+template <int D>
+struct LowrankState {
+  u32x4 hi[D / 32][2], lo[D / 32][2];
+};
+
+template <int D>
+__device__ __forceinline__ void lowrank_state_load(const AttnArgs& a, int b, int h, int c, int lane,
+                                                   LowrankState<D>& st) {
+  const int hf = lane >> 5, l32 = lane & 31;
+  const int n_ar = (a.L + a.ar_tokens - 1) / a.ar_tokens;
+  const int64_t base = (((int64_t)b * a.H + h) * n_ar + c) * D * 32 + (int64_t)l32 * 32 + 8 * hf;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      st.hi[dt][s] = *reinterpret_cast<const u32x4*>(a.Ct_hi + base + (int64_t)32 * dt * 32 + 16 * s);
+      st.lo[dt][s] = *reinterpret_cast<const u32x4*>(a.Ct_lo + base + (int64_t)32 * dt * 32 + 16 * s);
+    }
+}
+
+// first: the state of the wave's first chunk, loaded by the caller
+template <int D>
+__device__ __forceinline__ void lowrank_output(const bf16x8 (&qhi)[2], const bf16x8 (&qlo)[2], const AttnArgs& a,
+                                               int b, int h, int q_chunk, int lane, const LowrankState<D>& first,
+                                               f32x16 (&out)[D / 32]) {
+  const int hf = lane >> 5;
+  const int c_first = __builtin_amdgcn_readfirstlane(q_chunk);
+  const int c_last = __builtin_amdgcn_readlane(q_chunk, 31);
   // The wave's queries may fall in several autoregressive chunks (the
   // chunk index grows with the token): the product is formed once per chunk
   // with that chunk's state and each lane keeps the one of its own chunk.
-  for (int c = c_first; c <= c_last; ++c) {
-    const bool mine = q_chunk == c;
+  auto product = [&](const LowrankState<D>& st, bool keep) __attribute__((always_inline)) {
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
       f32x16 y = {};
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const bool early = c == c_first && dt < D / 64;
-        const bf16x8 ch = as_bf16x8(early ? cth0[dt % (D / 64)][s]
-                                          : *reinterpret_cast<const u32x4*>(a.Ct_hi + state_off(c, dt, s)));
-        const bf16x8 cl = as_bf16x8(early ? ctl0[dt % (D / 64)][s]
-                                          : *reinterpret_cast<const u32x4*>(a.Ct_lo + state_off(c, dt, s)));
-        y = mfma32(ch, qhi[s], y);
-        y = mfma32(cl, qhi[s], y);
-        y = mfma32(ch, qlo[s], y);
+        y = mfma32(as_bf16x8(st.hi[dt][s]), qhi[s], y);
+        y = mfma32(as_bf16x8(st.lo[dt][s]), qhi[s], y);
+        y = mfma32(as_bf16x8(st.hi[dt][s]), qlo[s], y);
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) out[dt][r] = (c == c_first || mine) ? y[r] : out[dt][r];
+      for (int r = 0; r < 16; ++r) out[dt][r] = keep ? y[r] : out[dt][r];
     }
+  };
+  product(first, true);
+  for (int c = c_first + 1; c <= c_last; ++c) {
+    LowrankState<D> st;
+    lowrank_state_load<D>(a, b, h, c, lane, st);
+    product(st, q_chunk == c);
   }
   float ss = 0.f;
 #pragma unroll
@@ -221,10 +252,38 @@ __global__ __launch_bounds__(BQ * 2, BQ == 128 ? kAttnMinWaves : 1) void attenti
       qreg[s] = q_ok ? *reinterpret_cast<const u32x4*>(qp + 16 * s + 8 * hf) : u32x4{0, 0, 0, 0};
   }
 
+  // Low-rank branch (fused and low-rank modes): its operands are loaded
+  // before the first K/V tile, and the features are formed while that tile
+  // lands; their LDS patch is the second tile buffer, which the loop first
+  // fills after the tile-0 barrier. The gate value is loaded here too.
+  bf16x8 lqh[2], lql[2];
+  float gv = 0.f;
+  LowrankLoads<D> lld;
+  u32x4 qn_reg[D / 16];
+  const bool sep_qn = MODE == kModeFused && a.Qn != a.Q;
+  if constexpr (MODE != kModeSparse) {
+    lowrank_load<D>(a, h, tok0, lane, lld);
+    if (sep_qn) {
+      const uint16_t* qp = a.Qn + (int64_t)b * a.sq_b + (int64_t)q_tok * a.sq_l + (int64_t)h * a.sq_h;
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s)
+        qn_reg[s] = q_ok ? *reinterpret_cast<const u32x4*>(qp + 16 * s + 8 * hf) : u32x4{0, 0, 0, 0};
+    }
+    if constexpr (MODE == kModeFused)
+      gv = q_ok ? a.g[(int64_t)b * a.g_sb + (int64_t)q_tok * a.g_sl + (int64_t)h * a.g_sh] : 0.f;
+  }
+  auto form_features = [&]() __attribute__((always_inline)) {
+    if constexpr (MODE != kModeSparse) {
+      float* Fw = reinterpret_cast<float*>(smem1) + wv * (32 * 33);
+      lowrank_features<D>(sep_qn ? qn_reg : qreg, a, lld, Fw, lane, lqh, lql);
+    }
+  };
+
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
   float ltot = 1.f, m_fin = 0.f;
+  if constexpr (!kLoop) form_features();
 
   if constexpr (kLoop) {
     const int32_t* irow = a.idx + wi * a.kkeep;
@@ -234,15 +293,13 @@ __global__ __launch_bounds__(BQ * 2, BQ == 128 ? kAttnMinWaves : 1) void attenti
     ld.init(Kb, a.sk_l, Vb, a.sv_l, a.L, lane, wv);
     float m = -INFINITY, lsum = 0.f;
 
+    // first token of a kept block; an index outside [0, Nk) selects nothing
+    auto tok_of = [&](int c) __attribute__((always_inline)) { return (unsigned)c < (unsigned)a.Nk ? c * 64 : a.L; };
     // The block row goes to LDS once: reading it there (lgkm counter) never
     // waits on the tile prefetches in flight (vm counter, completed in order).
     for (int i = tid; i < a.kkeep; i += NT) sidx[i] = irow[i];
     __syncthreads();
-    // first token of a kept block; an index outside [0, Nk) selects nothing
-    auto block_tok0 = [&](int i) {
-      const int c = __builtin_amdgcn_readfirstlane(sidx[i]);
-      return (unsigned)c < (unsigned)a.Nk ? c * 64 : a.L;
-    };
+    auto block_tok0 = [&](int i) __attribute__((always_inline)) { return tok_of(__builtin_amdgcn_readfirstlane(sidx[i])); };
 
     // One kept block of 64 keys, as two half-tiles of 32 keys. The lane
     // holds 16 of the 32 keys of its query per half-tile.
@@ -259,27 +316,6 @@ __global__ __launch_bounds__(BQ * 2, BQ == 128 ? kAttnMinWaves : 1) void attenti
     };
     const int wave_hi = __builtin_amdgcn_readfirstlane(key_hi);
     const int wave_lo = __builtin_amdgcn_readlane(key_lo, 31);
-    // Online softmax of a half-tile in the log2 domain, without touching O:
-    // returns whether the reference maximum moves (for some lane), the new
-    // maximum and the sum of the bf16 probabilities the PV product consumes.
-    // Lazy rescaling: the maximum only moves when a score exceeds it by more
-    // than 2^8, so P <= 256 and O, l stay well inside f32.
-    auto softmax_half = [&](const f32x16& sacc, bf16x8& p0, bf16x8& p1, float& m_new, float& rs) {
-      float mloc = sacc[0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mloc = fmaxf(mloc, sacc[r]);
-      mloc = fmaxf(mloc, partner32(mloc, hf)) * a.scale_log2;
-      const bool up = mloc > m + 8.f;
-      m_new = up ? mloc : m;
-      const float neg_m = m_new == -INFINITY ? 0.f : -m_new;
-      float p16[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) p16[r] = __builtin_amdgcn_exp2f(fmaf(sacc[r], a.scale_log2, neg_m));
-      p0 = to_bf16x8(p16);
-      p1 = to_bf16x8(p16 + 8);
-      rs = sum_bf16x8(p1, sum_bf16x8(p0, 0.f));
-      return up;
-    };
     auto rescale = [&](bool up, float m_new, float rs) {
       if (__ballot(up)) {
         const float alpha = up ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;
@@ -298,9 +334,38 @@ __global__ __launch_bounds__(BQ * 2, BQ == 128 ? kAttnMinWaves : 1) void attenti
     // alternate in every MFMA sequence (the two halves' S^T chains; the
     // channel tiles of O^T): no MFMA waits on the result of the one issued
     // just before it.
-    auto compute = [&](const uint16_t* tile, int key0) {
-      const uint16_t* Ks = tile;
-      const uint16_t* Vs = tile + 64 * D;
+    // Softmax of one 64-key block in the log2 domain, in two parts: the new
+    // reference maximum (moved lazily: only when a score exceeds it by more
+    // than 2^8, so P <= 256) and whether it moves; then, without touching O,
+    // the probabilities of each 32-key half as the two bf16 B operands of its
+    // PV products (keys 4hf + {0..3}, 8 + 4hf + {0..3} of each 16-key step)
+    // and their sum.
+    auto block_max = [&](const f32x16& s0, const f32x16& s1, float& m_new) __attribute__((always_inline)) {
+      // a v_max3 tree over the 32 scores (depth 4)
+      float t[12];
+#pragma unroll
+      for (int i = 0; i < 5; ++i) t[i] = max3f(s0[3 * i], s0[3 * i + 1], s0[3 * i + 2]);
+#pragma unroll
+      for (int i = 0; i < 5; ++i) t[5 + i] = max3f(s1[3 * i], s1[3 * i + 1], s1[3 * i + 2]);
+      t[10] = s0[15];
+      t[11] = s1[15];
+      const float u0 = max3f(t[0], t[1], t[2]), u1 = max3f(t[3], t[4], t[5]);
+      const float u2 = max3f(t[6], t[7], t[8]), u3 = max3f(t[9], t[10], t[11]);
+      float mloc = max3f(u0, u1, max3f(u2, u3, u3));
+      mloc = fmaxf(mloc, partner32(mloc, hf)) * a.scale_log2;
+      const bool up = mloc > m + 8.f;
+      m_new = up ? mloc : m;
+      return up;
+    };
+    auto half_exp = [&](const f32x16& sh, float neg_m, bf16x8& pa, bf16x8& pb) __attribute__((always_inline)) {
+      float e[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(fmaf(sh[r], a.scale_log2, neg_m));
+      pa = to_bf16x8(e);
+      pb = to_bf16x8(e + 8);
+      return sum_bf16x8(pb, sum_bf16x8(pa, 0.f));
+    };
+    auto compute_kv = [&](const uint16_t* Ks, const uint16_t* Vs, int key0) __attribute__((always_inline)) {
       f32x16 s0 = {}, s1 = {};
 #pragma unroll
       for (int s = 0; s < D / 16; ++s) {
@@ -311,23 +376,35 @@ __global__ __launch_bounds__(BQ * 2, BQ == 128 ? kAttnMinWaves : 1) void attenti
         mask_half(s0, key0, 0);
         mask_half(s1, key0, 1);
       }
+      // one running-maximum update for the block, then each half's
+      // probabilities and products (the second half's exponentials overlap
+      // the first half's MFMAs)
+      float m_new;
+      const bool up = block_max(s0, s1, m_new);
+      rescale(up, m_new, 0.f);
+      const float neg_m = m_new == -INFINITY ? 0.f : -m_new;
+      float rs = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         bf16x8 pa, pb;
-        float mn, rs;
-        const bool up = softmax_half(kt ? s1 : s0, pa, pb, mn, rs);
-        rescale(up, mn, rs);
+        rs += half_exp(kt ? s1 : s0, neg_m, pa, pb);
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = mfma32(lds_v_operand<D>(Vs, lane, dt, 32 * kt), pa, oacc[dt]);
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
           oacc[dt] = mfma32(lds_v_operand<D>(Vs, lane, dt, 32 * kt + 16), pb, oacc[dt]);
       }
+      lsum += rs;
+    };
+    auto compute = [&](const uint16_t* tile, int key0) __attribute__((always_inline)) {
+      compute_kv(tile, tile + 64 * D, key0);
     };
 
     // Double-buffered tiles: block i+1's loads are in flight while block i
-    // computes; one wait + barrier per block.
+    // computes; one wait + barrier per block. The low-rank features are
+    // formed while the first block lands.
     ld.issue(smem0, block_tok0(0), lane, wv);
+    form_features();
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     int it = 0;
@@ -369,21 +446,10 @@ __global__ __launch_bounds__(BQ * 2, BQ == 128 ? kAttnMinWaves : 1) void attenti
       if (a.lse && hf == 0) a.lse[((int64_t)b * a.H + h) * a.L + q_tok] = ltot > 0.f ? m_fin + log2f(ltot) : INFINITY;
     }
   } else {
-    float* Fw = reinterpret_cast<float*>(smem0) + wv * (32 * 33);
+    LowrankState<D> st0;
+    lowrank_state_load<D>(a, b, h, __builtin_amdgcn_readfirstlane(q_chunk), lane, st0);
     f32x16 olr[D / 32];
-    if constexpr (MODE == kModeFused) {
-      if (a.Qn != a.Q) {
-        const uint16_t* qp = a.Qn + (int64_t)b * a.sq_b + (int64_t)q_tok * a.sq_l + (int64_t)h * a.sq_h;
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s)
-          qreg[s] = q_ok ? *reinterpret_cast<const u32x4*>(qp + 16 * s + 8 * hf) : u32x4{0, 0, 0, 0};
-      }
-    }
-    // the gate value is loaded before the low-rank tile, its latency hidden there
-    float gv = 0.f;
-    if constexpr (MODE == kModeFused)
-      gv = q_ok ? a.g[(int64_t)b * a.g_sb + (int64_t)q_tok * a.g_sl + (int64_t)h * a.g_sh] : 0.f;
-    lowrank_query_tile<D>(qreg, a, b, h, tok0, q_chunk, Fw, lane, olr);
+    lowrank_output<D>(lqh, lql, a, b, h, q_chunk, lane, st0, olr);
     if constexpr (MODE == kModeLowrank) {
       if (q_ok) store_row<D>(a.out, a.out_f32, obase, olr, hf);
     } else {

@@ -147,8 +147,6 @@ hipError_t launch_quant_fp8_gate(const uint16_t* x, int64_t M, int64_t K, int64_
                                  float* scales, const uint16_t* wgate, float gate_bias, float* g, hipStream_t stream);
 hipError_t launch_pool_blocks(const uint16_t* X, int64_t sb, int64_t sl, int64_t sh, int B, int L, int H, int D,
                               int bs, double* out, hipStream_t stream);
-hipError_t launch_block_scores(const double* qmean, const double* kmean, int BH, int Nq, int Nk, int D, double* S,
-                               hipStream_t stream);
 // Which key blocks a row of the block map may keep, and where it goes.
 // Row r of the map belongs to query block r % Nq; it is computed from row
 // r % s_rows of S and written to every one of n_rep copies of the map
@@ -161,6 +159,9 @@ struct MapRule {
   int n_rep;
   int64_t rep_stride;
 };
+hipError_t launch_select_topk(const double* qmean, const double* kmean, int BH, int Nk, int D, int k,
+                              const MapRule& rule, uint16_t* khi, uint16_t* klo, int32_t* idx,
+                              hipStream_t stream);
 hipError_t launch_topk_rows(const double* S, int64_t n_rows, int C, int k, const MapRule& rule, int32_t* idx,
                             hipStream_t stream);
 // Fixed spatio-temporal scores: S[b][c] = -|centroid_q(b) - centroid_k(c)|^2
