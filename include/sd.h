@@ -311,6 +311,23 @@ typedef struct sd_rola_saved {
   float* lse;
 } sd_rola_saved;
 
+/* For callers that cannot allocate (code under graph capture, tight serving
+ * loops, harnesses that forbid allocation): sd_rola_attention without a
+ * workspace. Its scratch is a static device array of SD_NOALLOC_SCRATCH_BYTES
+ * (128 MiB: enough for the Wan2.1-14B 720P layer at 90% and 97% sparsity),
+ * held by every GPU the library runs on until the process ends. Shapes whose
+ * sd_rola_workspace_size exceeds it return SD_ERR_UNSUPPORTED. Nothing is
+ * allocated or freed, and no second stream is used: all work is ordered on
+ * `stream`. Every call on one GPU shares that GPU's array (nothing in it has
+ * to start at zero: each call writes what it reads), so calls that overlap on
+ * one GPU, from other streams or threads, race. Other arguments as for
+ * sd_rola_attention; idx_out may be NULL. */
+#define SD_NOALLOC_SCRATCH_BYTES (128u << 20)
+int sd_rola_attention_noalloc(const sd_attn_shape* shape, const sd_lowrank_params* lr, const void* Q,
+                              const void* K, const void* V, const void* Qn, const void* Kn, const float* g,
+                              int64_t g_stride_b, int64_t g_stride_l, int64_t g_stride_h, int k_keep,
+                              float sm_scale, void* O, int32_t* idx_out, void* stream);
+
 /* sd_rola_apply that also writes the quantities of an sd_rola_saved, the same
  * values the backward would form itself, bit for bit. */
 int sd_rola_apply_save(const sd_attn_shape* shape, const sd_lowrank_params* lr, const void* Q, const void* K,

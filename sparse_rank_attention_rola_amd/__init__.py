@@ -21,6 +21,7 @@ SD_ERR_UNSUPPORTED = 2
 SD_ERR_ALIGN = 3
 SD_ERR_WORKSPACE = 4
 SD_ERR_HIP = 5
+SD_NOALLOC_SCRATCH_BYTES = 128 << 20  # the static device scratch of sd_rola_attention_noalloc
 SD_DTYPE_BF16 = 1
 SD_DTYPE_F32 = 2
 SD_PHI_ELU1 = 1
@@ -31,7 +32,7 @@ _SELECT = {"topk": SD_SELECT_TOPK, "fixed": SD_SELECT_FIXED}
 EXPORTED = [
     "sd_keep_count", "sd_rope_default", "sd_block_select_workspace_size", "sd_block_select",
     "sd_sparse_attn", "sd_lowrank_workspace_size", "sd_lowrank_attn", "sd_gate_fuse",
-    "sd_quant_fp8_per_token", "sd_quant_fp8_gate", "sd_gemm_fp8_w8a8", "sd_qk_norm_rope", "sd_rola_workspace_size", "sd_rola_attention", "sd_rola_prepare",
+    "sd_quant_fp8_per_token", "sd_quant_fp8_gate", "sd_gemm_fp8_w8a8", "sd_qk_norm_rope", "sd_rola_workspace_size", "sd_rola_attention", "sd_rola_attention_noalloc", "sd_rola_prepare",
     "sd_rola_apply", "sd_rola_apply_save", "sd_rola_backward_workspace_size", "sd_rola_backward",
     "sd_status_string", "sd_last_error",
 ]
@@ -90,6 +91,7 @@ def _declare(lib):
                                   ctypes.POINTER(sd_rope_pair), i32, P, P, P, P, P]),
         "sd_rola_workspace_size": (sz, [S, LR, i32]),
         "sd_rola_attention": (i32, [S, LR, P, P, P, P, P, P, i64, i64, i64, i32, f32, P, P, P, sz, P]),
+        "sd_rola_attention_noalloc": (i32, [S, LR, P, P, P, P, P, P, i64, i64, i64, i32, f32, P, P, P]),
         "sd_rola_prepare": (i32, [S, LR, P, P, P, P, P, i32, P, P, sz, P]),
         "sd_rola_apply": (i32, [S, LR, P, P, P, P, P, i64, i64, i64, i32, f32, P, P, P, sz, P]),
         "sd_rola_backward_workspace_size": (sz, [S, LR, i32]),
@@ -384,6 +386,24 @@ def sd_rola_attention(Q, K, V, g, lr: LowrankParams, k_keep, *, grid, block_q=12
     _check(lib().sd_rola_attention(ctypes.byref(s), ctypes.byref(lr.p), _ptr(Q), _ptr(K), _ptr(V), _ptr(Qn), _ptr(Kn),
                                    _ptr(g), gb, gl, gh, int(k_keep), float(scale), _ptr(out), _ptr(idx_out), _ptr(ws),
                                    ws.numel(), _stream_ptr(stream)))
+    return out
+
+
+def sd_rola_attention_noalloc(Q, K, V, g, lr: LowrankParams, k_keep, out, *, grid, block_q=128, Qn=None, Kn=None,
+                              sm_scale=None, idx_out=None, select="topk", chunk_tokens=0, window=0, stream=None):
+    """The fused layer on the library's static device scratch: nothing is
+    allocated, here or in the library; `out` (bf16 [B, L, H, d]) is given."""
+    B, L, H, d = Q.shape
+    if Qn is not None and Qn.stride() != Q.stride():
+        raise ValueError("Qn must have the strides of Q")
+    if Kn is not None and Kn.stride() != K.stride():
+        raise ValueError("Kn must have the strides of K")
+    s = make_shape(Q, K, V, out, block_q=block_q, grid=grid, select=select, chunk_tokens=chunk_tokens, window=window)
+    scale = sm_scale if sm_scale is not None else 1.0 / math.sqrt(d)
+    gb, gl, gh = _gate_strides(g, B, L, H)
+    _check(lib().sd_rola_attention_noalloc(ctypes.byref(s), ctypes.byref(lr.p), _ptr(Q), _ptr(K), _ptr(V), _ptr(Qn),
+                                           _ptr(Kn), _ptr(g), gb, gl, gh, int(k_keep), float(scale), _ptr(out),
+                                           _ptr(idx_out), _stream_ptr(stream)))
     return out
 
 

@@ -645,9 +645,9 @@ size_t sd_rola_workspace_size(const sd_attn_shape* shape, const sd_lowrank_param
 namespace {
 
 // Validation shared by the fused entry points.
-int check_rola(const sd_attn_shape* shape, const sd_lowrank_params* lr, const void* Q, const void* K, const void* V,
-               const void* Qn, const void* Kn, int k_keep, const void* idx, size_t ws_bytes, const void* ws,
-               Geo* g) {
+// Everything but the workspace.
+int check_rola_args(const sd_attn_shape* shape, const sd_lowrank_params* lr, const void* Q, const void* K,
+                    const void* V, const void* Qn, const void* Kn, int k_keep, const void* idx, Geo* g) {
   int rc;
   if ((rc = check_shape(shape, g, true))) return rc;
   if ((rc = check_lowrank(lr, *g))) return rc;
@@ -656,6 +656,14 @@ int check_rola(const sd_attn_shape* shape, const sd_lowrank_params* lr, const vo
   if (Kn && (rc = check_dev_ptr(Kn, "Kn"))) return rc;
   if (idx && !aligned(idx, 4)) return fail(SD_ERR_ALIGN, "block map pointer misaligned");
   if (k_keep < 1 || k_keep > g->Nk) return fail(SD_ERR_INVALID_ARG, "k_keep = %d not in [1, %d]", k_keep, g->Nk);
+  return SD_OK;
+}
+
+int check_rola(const sd_attn_shape* shape, const sd_lowrank_params* lr, const void* Q, const void* K, const void* V,
+               const void* Qn, const void* Kn, int k_keep, const void* idx, size_t ws_bytes, const void* ws,
+               Geo* g) {
+  int rc;
+  if ((rc = check_rola_args(shape, lr, Q, K, V, Qn, Kn, k_keep, idx, g))) return rc;
   const size_t need = sd_rola_workspace_size(shape, lr, k_keep);
   if (!ws || ws_bytes < need) return fail(SD_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
   if (!aligned(ws, kAlign)) return fail(SD_ERR_ALIGN, "workspace must be 256-byte aligned");
@@ -779,10 +787,12 @@ int run_rope_table(const sd_attn_shape* s, const sd_lowrank_params* lr, float2* 
 // causal window), it also forms the key-block means; everything then runs in
 // order on the caller's stream (the Q pooling beside the stream pass would
 // only share HBM with it), as it does on a stream being captured into a
-// graph. Otherwise the selection, which keeps the vector ALUs busy, runs on
-// the caller's stream beside the HBM-bound stream pass on the side stream.
+// graph (and when the caller asks for no side stream). Otherwise the
+// selection, which keeps the vector ALUs busy, runs on the caller's stream
+// beside the HBM-bound stream pass on the side stream.
 int run_prepare(const sd_attn_shape* s, const Geo& g, const sd_lowrank_params* lr, const void* Q, const void* K,
-                const void* V, const void* Kn, int k_keep, int32_t* idx, const RolaWs& w, hipStream_t st) {
+                const void* V, const void* Kn, int k_keep, int32_t* idx, const RolaWs& w, hipStream_t st,
+                bool allow_side = true) {
   int rc = run_rope_table(s, lr, w.lr.rope_tab, st);
   if (rc) return rc;
   sd::RankRows rows;
@@ -804,7 +814,7 @@ int run_prepare(const sd_attn_shape* s, const Geo& g, const sd_lowrank_params* l
   // thread's capture would pull another thread's eager work into that graph.
   hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
   if ((e = hipStreamIsCapturing(st, &cap)) != hipSuccess) return hip_fail(e, "prepare: capture status");
-  if (k_in_stream || cap != hipStreamCaptureStatusNone) {
+  if (k_in_stream || cap != hipStreamCaptureStatusNone || !allow_side) {
     if (scored) {
       e = sd::launch_pool_blocks(a.Q, s->sq_b, s->sq_l, s->sq_h, g.B, g.L, g.H, g.D, g.bq, w.sel.qmean, st);
       if (e == hipSuccess && !k_in_stream)
@@ -959,6 +969,69 @@ int sd_rola_attention(const sd_attn_shape* shape, const sd_lowrank_params* lr, c
   const RolaWs w = carve_rola(ws, g, shape, k_keep);
   int32_t* idx = idx_out ? idx_out : w.idx;
   if ((rc = run_prepare(shape, g, lr, Q, K, V, Kn, k_keep, idx, w, st))) return rc;
+  if ((rc = run_apply(shape, g, lr, Q, K, V, Qn, g_ptr, g_stride_b, g_stride_l, g_stride_h, k_keep, sm_scale, O, idx,
+                      w, st)))
+    return rc;
+  return ok();
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// The fused layer without a caller workspace, for callers that cannot
+// allocate: its scratch is a static device array of SD_NOALLOC_SCRATCH_BYTES
+// that every GPU the library runs on holds until the process ends. Host code
+// reaches a device's copy only through the address hipGetSymbolAddress
+// returns for that device (kept per device, taken once with the device
+// current); the array's own name is a host-side stand-in.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[SD_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::mutex g_scratch_mu;
+
+int scratch_address(void** out) {
+  static std::vector<void*> per_dev;
+  int dev = 0, n = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipGetDeviceCount(&n);
+  if (e != hipSuccess) return hip_fail(e, "static scratch: device");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if ((int)per_dev.size() < n) per_dev.resize(n, nullptr);
+  if (!per_dev[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "static scratch: symbol address");
+    per_dev[dev] = ptr;
+  }
+  *out = per_dev[dev];
+  return SD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sd_rola_attention_noalloc(const sd_attn_shape* shape, const sd_lowrank_params* lr, const void* Q, const void* K,
+                              const void* V, const void* Qn, const void* Kn, const float* g_ptr, int64_t g_stride_b,
+                              int64_t g_stride_l, int64_t g_stride_h, int k_keep, float sm_scale, void* O,
+                              int32_t* idx_out, void* stream) {
+  Geo g;
+  int rc;
+  if ((rc = check_rola_args(shape, lr, Q, K, V, Qn, Kn, k_keep, idx_out, &g))) return rc;
+  if ((rc = check_apply_extra(O, g_ptr, sm_scale, g_stride_b, g_stride_l, g_stride_h))) return rc;
+  const size_t need = sd_rola_workspace_size(shape, lr, k_keep);
+  if (need > (size_t)SD_NOALLOC_SCRATCH_BYTES)
+    return fail(SD_ERR_UNSUPPORTED, "this shape needs %zu bytes of scratch; the static buffer holds %zu", need,
+                (size_t)SD_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if ((rc = scratch_address(&ws))) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const RolaWs w = carve_rola(ws, g, shape, k_keep);
+  int32_t* idx = idx_out ? idx_out : w.idx;
+  // no side stream: the prepare phase runs in order on the caller's stream
+  if ((rc = run_prepare(shape, g, lr, Q, K, V, Kn, k_keep, idx, w, st, false))) return rc;
   if ((rc = run_apply(shape, g, lr, Q, K, V, Qn, g_ptr, g_stride_b, g_stride_l, g_stride_h, k_keep, sm_scale, O, idx,
                       w, st)))
     return rc;

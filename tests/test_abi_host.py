@@ -253,6 +253,26 @@ def test_rola_validation():
 
 
 @host_only
+def test_rola_noalloc_validation():
+    # argument errors as for the workspace entry; a shape whose workspace
+    # exceeds the static scratch is refused before any device call
+    lib = sd.lib()
+    p, keep = _lr()
+
+    def call(shape, k=4, g=FAKE):
+        return lib.sd_rola_attention_noalloc(ctypes.byref(shape), ctypes.byref(p), FAKE, FAKE, FAKE, None, None, g,
+                                             0, 1, 0, k, 0.125, FAKE, None, None)
+
+    assert call(_shape(), k=0) == sd.SD_ERR_INVALID_ARG
+    assert call(_shape(), g=None) == sd.SD_ERR_INVALID_ARG
+    assert call(_shape(grid=(1, 1, 1))) == sd.SD_ERR_INVALID_ARG
+    big = _shape(B=2, H=40, L=75600, d=128, grid=(21, 45, 80), bq=128)
+    assert lib.sd_rola_workspace_size(ctypes.byref(big), ctypes.byref(p), 36) > sd.SD_NOALLOC_SCRATCH_BYTES
+    assert call(big, k=36) == sd.SD_ERR_UNSUPPORTED
+    assert "static buffer" in lib.sd_last_error().decode()
+
+
+@host_only
 def test_variant_fields_validation():
     lib = sd.lib()
 
