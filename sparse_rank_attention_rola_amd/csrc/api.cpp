@@ -157,6 +157,7 @@ struct SelectWs {
   double* S;
   uint16_t* khi;  // the key-block means split into bf16 hi + lo (scored selector)
   uint16_t* klo;
+  double* knorm2;  // their squared norms
 };
 
 // The scored selector forms its scores inside the selection kernel; only the
@@ -170,6 +171,7 @@ SelectWs carve_select(Carve& c, const Geo& g) {
   const size_t split = g.select == SD_SELECT_TOPK ? (size_t)g.B * g.H * g.Nk * g.D : 0;
   w.khi = static_cast<uint16_t*>(c.take(sizeof(uint16_t) * split));
   w.klo = static_cast<uint16_t*>(c.take(sizeof(uint16_t) * split));
+  w.knorm2 = static_cast<double*>(c.take(sizeof(double) * (split / g.D)));
   return w;
 }
 
@@ -300,7 +302,8 @@ int run_scores_topk(const sd_attn_shape* s, const Geo& g, int k_keep, int32_t* i
     if (e != hipSuccess) return hip_fail(e, "fixed scores");
     e = sd::launch_topk_rows(w.S, g.Nq, g.Nk, k_keep, rule, idx, st);
   } else {
-    e = sd::launch_select_topk(w.qmean, w.kmean, g.B * g.H, g.Nk, g.D, k_keep, rule, w.khi, w.klo, idx, st);
+    e = sd::launch_select_topk(w.qmean, w.kmean, g.B * g.H, g.Nk, g.D, k_keep, rule, w.khi, w.klo, w.knorm2, idx,
+                               st);
   }
   if (e != hipSuccess) return hip_fail(e, "top-k");
   return SD_OK;

@@ -111,10 +111,9 @@ __device__ __forceinline__ void chunk_span(int t0, int t1, int ar, int& first, i
 // first `remaining` in index order complete them (all of them when the loop
 // stopped early because every candidate left in the chosen bin is kept).
 // With every bit examined, prefix is the exact kk-th largest key.
-template <int NPL, typename Key>
+template <int NPL, typename Key, int kBits = 8 * (int)sizeof(Key)>
 __device__ __forceinline__ void radix_select_desc(const Key (&key)[NPL], uint32_t valid, int kk, uint32_t* hist,
                                                   int lane, Key& prefix, Key& pmask, int& remaining) {
-  constexpr int kBits = 8 * (int)sizeof(Key);
   for (int shift = kBits - 8; shift >= 0 && kk > 0; shift -= 8) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) hist[lane + 64 * i] = 0;
@@ -255,35 +254,34 @@ __global__ __launch_bounds__(256) void topk_rows_kernel(const double* __restrict
 // Scores and exact top-k in one kernel, without the score matrix.
 //
 // kmean_split_kernel first writes each float64 key-block mean as bf16 hi +
-// lo parts (x ~= hi + lo to about 2^-18 of x). A workgroup of 16 waves then
-// takes 16 query-block rows of one (batch, head) (8 for the longest rows)
-// and every key block.
+// lo parts (x ~= hi + lo to about 2^-18 of x) and its squared norm. A
+// workgroup of 16 waves then takes 32 query-block rows of one (batch, head)
+// (16 for the longest rows) and every key block.
 // Phase 1: the approximate scores S' = qbar . kbar on 16x16x32 bf16 MFMAs
-// (three products per pair of split operands, f32 accumulation), kept in
-// LDS as f32. Each product term is exact in f32, so |S - S'| <=
-// (3 * 2^-18 + 3 d 2^-24) sum_d |qbar_d kbar_d|, which the kernel bounds by
-// delta = 2^-12 |qbar_b| max_c |kbar_c| (Cauchy-Schwarz; d <= 128; the
-// largest norm is formed from the split parts in f32 and raised by 2^-10).
-// Phase 2, one wave per row: sigma = the k-th largest S' (radix select on
-// the order-preserving 32-bit images). A block with S' > sigma + 2 delta is
-// kept for certain (fewer than k blocks can reach its score), one with
-// S' < sigma - 2 delta is dropped for certain (k blocks beat it); only the
-// few in between (five per row on average at 720P) get their exact float64
-// score, sixteen lanes each, and a radix select over those exact keys fills
-// the remaining places, equal scores going to the lower block index. The
-// kept set is therefore exactly the top-k of the float64 scores. Rows are
-// written ascending; the causal-window rule and -1 padding are those of
-// topk_rows_kernel.
+// (three products per pair of split operands, f32 accumulation). Each
+// product term is exact in f32, so |S - S'| <= (3 * 2^-18 + 3 d 2^-24)
+// sum_d |qbar_d kbar_d| <= 2^-14.8 |qbar_b| kmax (Cauchy-Schwarz, d <= 128,
+// kmax = the largest key-block norm of the head). They are kept in LDS as
+// 16-bit fixed point of the normalised score S' / (|qbar_b| kmax) (|.| <=
+// 1 + 2^-12), 2^14 steps per unit: rounding adds 2^-15. So every stored
+// value is within Delta = 2^-12 (in normalised units, 4 steps) of the exact
+// normalised score, with room for a coarser MFMA accumulation.
+// Phase 2, one wave per row: sigma = the k-th largest stored value (radix
+// select on two 8-bit digits). A block more than 2 Delta (8 steps) above
+// sigma is kept for certain (fewer than k blocks can reach its score), one
+// more than 2 Delta below is dropped for certain (k blocks beat it); only
+// the few in between (about five per row at 720P) get their exact float64
+// score, sixteen lanes each, and are ranked by it, equal scores going to
+// the lower block index. The kept set is therefore exactly the top-k of the
+// float64 scores. Rows are written ascending; the causal-window rule and -1
+// padding are those of topk_rows_kernel.
 // ---------------------------------------------------------------------------
 constexpr int kSelWaves = 16;
-// query-block rows per workgroup: 16, or 8 for the longest rows, so that the
-// approximate scores fit the LDS
-__host__ __device__ constexpr int sel_rows(int npl) { return npl <= 24 ? 16 : 8; }
-
-__device__ __forceinline__ uint32_t order_key32(float x) {
-  const uint32_t u = __float_as_uint(x);
-  return (u >> 31) ? ~u : (u | 0x80000000u);
-}
+// query-block rows per workgroup: 32, or 16 for the longest rows, so that
+// the approximate scores fit the LDS
+__host__ __device__ constexpr int sel_rows(int npl) { return npl <= 24 ? 32 : 16; }
+constexpr float kSelSteps = 16384.f;  // fixed-point steps per normalised unit
+constexpr int kSelBand = 8;           // 2 Delta in steps
 
 // Split 8 float64 values into bf16 hi + lo MFMA operands (x ~= hi + lo to
 // about 2^-18 of x) and add their squares to ss.
@@ -299,37 +297,45 @@ __device__ __forceinline__ void split_f64x8(const double* v, bf16x8& hi, bf16x8&
 }
 
 // The key-block means as the A operands of the approximate scores: bf16 hi
-// and lo parts of each float64 mean (x ~= hi + lo to about 2^-18 of x).
-// One thread per 8 channels of one key block.
-__global__ __launch_bounds__(256) void kmean_split_kernel(const double* __restrict__ kmean, int64_t n_vec,
-                                                          uint16_t* __restrict__ khi, uint16_t* __restrict__ klo) {
+// and lo parts of each float64 mean (x ~= hi + lo to about 2^-18 of x), and
+// the squared norm of each mean (float64). One thread per 8 channels of one
+// key block; the cpk = d / 8 threads of a block are adjacent lanes of a wave.
+__global__ __launch_bounds__(256) void kmean_split_kernel(const double* __restrict__ kmean, int64_t n_vec, int cpk,
+                                                          uint16_t* __restrict__ khi, uint16_t* __restrict__ klo,
+                                                          double* __restrict__ knorm2) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= n_vec) return;
+  const bool ok = t < n_vec;
   double v[8], ss = 0.0;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = kmean[8 * t + e];
+  for (int e = 0; e < 8; ++e) v[e] = ok ? kmean[8 * t + e] : 0.0;
   bf16x8 hi, lo;
   split_f64x8(v, hi, lo, ss);
+  for (int o = 1; o < cpk; o <<= 1) ss += __shfl_xor(ss, o);
+  if (!ok) return;
   *reinterpret_cast<bf16x8*>(khi + 8 * t) = hi;
   *reinterpret_cast<bf16x8*>(klo + 8 * t) = lo;
+  if ((t & (cpk - 1)) == 0) knorm2[t / cpk] = ss;
 }
 
 template <int D, int NPL>
 __global__ __launch_bounds__(64 * kSelWaves) void select_topk_kernel(const double* __restrict__ qmean,
                                                                      const double* __restrict__ kmean,
                                                                      const uint16_t* __restrict__ khi,
-                                                                     const uint16_t* __restrict__ klo, int k,
+                                                                     const uint16_t* __restrict__ klo,
+                                                                     const double* __restrict__ knorm2, int k,
                                                                      MapRule rule, int Nk,
                                                                      int32_t* __restrict__ idx) {
-  constexpr int R = sel_rows(NPL), NW = kSelWaves;
-  constexpr int NKP = 64 * NPL + 4;  // row pitch of the approximate scores, in floats
-  __shared__ __attribute__((aligned(16))) float Sa[R * NKP];
+  constexpr int R = sel_rows(NPL), RG = R / 16, NW = kSelWaves;
+  constexpr int NKP = 64 * NPL + 8;  // row pitch of the stored scores (int16)
+  __shared__ __attribute__((aligned(16))) int16_t Sa[R * NKP];
   __shared__ uint32_t hist[NW][256];
   __shared__ int lst_c[NW][64];         // undecided blocks of the row, in index order
   __shared__ uint64_t lst_key[NW][64];  // their exact keys
   __shared__ uint32_t chosen[NW][64];   // bit c % 32 of word c / 32: undecided block c is kept
-  __shared__ float kmax2[NW];
-  __shared__ double qn2[R];
+  __shared__ double red[NW];
+  // the query-block means as split B operands: [row group][d step][lane]
+  __shared__ bf16x8 Qs_hi[RG][D / 32][64], Qs_lo[RG][D / 32][64];
+  __shared__ double qn2s[R];
   const int Nq = rule.Nq;
   const int64_t bh = blockIdx.y;
   const int r0 = blockIdx.x * R;
@@ -339,76 +345,110 @@ __global__ __launch_bounds__(64 * kSelWaves) void select_topk_kernel(const doubl
   const double* Qm = qmean + bh * (int64_t)Nq * D;
   const double* Km = kmean + bh * (int64_t)Nk * D;
 
-  // B operands: the query-block means, row l16, d = 32 s + 8 kg .. + 7
-  bf16x8 qh[D / 32], ql[D / 32];
+  // kmax: the largest key-block norm of the head
   {
-    const int row = r0 + l16;
+    double mx = 0.0;
+    for (int c = threadIdx.x; c < Nk; c += 64 * NW) mx = fmax(mx, knorm2[bh * Nk + c]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o));
+    if (lane == 0) red[wv] = mx;
+  }
+  // B operands (wave rg < RG): the query-block means of rows r0 + 16 rg +
+  // l16, d = 32 s + 8 kg .. + 7, split, and each row's squared norm
+  if (wv < RG) {
+    const int row = r0 + 16 * wv + l16;
     double ss = 0.0;
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) {
       double v[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = row < Nq ? Qm[(int64_t)row * D + 32 * s + 8 * kg + e] : 0.0;
-      split_f64x8(v, qh[s], ql[s], ss);
+      bf16x8 hi, lo;
+      split_f64x8(v, hi, lo, ss);
+      Qs_hi[wv][s][lane] = hi;
+      Qs_lo[wv][s][lane] = lo;
     }
     ss += __shfl_xor(ss, 16);
     ss += __shfl_xor(ss, 32);
-    if (wv == 0 && lane < 16) qn2[lane] = ss;
+    if (lane < 16) qn2s[16 * wv + lane] = ss;
   }
-  // S'^T tiles of 16 key blocks x 16 rows: A = the split key means (lane:
-  // key l16, d = 32 s + 8 kg ..), accumulator lane: row l16, keys 4 kg ..
-  // 4 kg + 3
+  __syncthreads();
+  double km2 = 0.0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) km2 = fmax(km2, red[w]);
+  // raised by 2^-30: the float64 norms are within far less of the exact ones
+  const double kmax = sqrt(km2) * (1.0 + 0x1p-30);
+  // the fixed-point scale of each of the lane's rows: 2^14 / (|qbar| kmax)
+  float fscale[RG];
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg) {
+    const double nrm = sqrt(qn2s[16 * rg + l16]) * kmax;
+    fscale[rg] = nrm > 0.0 ? (float)((double)kSelSteps / nrm) : 0.f;
+  }
+
+  // Phase 1. S'^T tiles of 16 key blocks x 16 rows: A = the split key means
+  // (lane: key l16, d = 32 s + 8 kg ..), accumulator lane: row l16, keys
+  // 4 kg .. 4 kg + 3.
   const uint16_t* Kh = khi + bh * (int64_t)Nk * D;
   const uint16_t* Kl = klo + bh * (int64_t)Nk * D;
-  // (also the largest squared norm of the head's key means, from hi + lo in
-  // f32: within 2^-16 of the float64 value)
   const int ntile = (Nk + 15) / 16;
-  float kmx = 0.f;
-  for (int t = wv; t < ntile; t += NW) {
+  auto load_tile = [&](int t, bf16x8 (&kh)[D / 32], bf16x8 (&kl)[D / 32]) __attribute__((always_inline)) {
     const int c = 16 * t + l16;
-    f32x4 acc = {};
-    float ss = 0.f;
+    const bool ok = t < ntile && c < Nk;
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) {
       const int64_t off = (int64_t)c * D + 32 * s + 8 * kg;
-      const bf16x8 kh = c < Nk ? *reinterpret_cast<const bf16x8*>(Kh + off) : bf16x8{};
-      const bf16x8 kl = c < Nk ? *reinterpret_cast<const bf16x8*>(Kl + off) : bf16x8{};
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, qh[s], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, ql[s], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kl, qh[s], acc, 0, 0, 0);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = (float)kh[e] + (float)kl[e];
-        ss = fmaf(x, x, ss);
-      }
+      kh[s] = ok ? *reinterpret_cast<const bf16x8*>(Kh + off) : bf16x8{};
+      kl[s] = ok ? *reinterpret_cast<const bf16x8*>(Kl + off) : bf16x8{};
     }
-    ss += __shfl_xor(ss, 16);
-    ss += __shfl_xor(ss, 32);
-    kmx = fmaxf(kmx, ss);
-    if (l16 < R) *reinterpret_cast<f32x4*>(Sa + l16 * NKP + 16 * t + 4 * kg) = acc;
+  };
+  for (int t = wv; t < ntile; t += NW) {
+    bf16x8 ch[D / 32], cl[D / 32];
+    load_tile(t, ch, cl);
+    f32x4 acc[RG];
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg) acc[rg] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s)
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg) {
+        const bf16x8 bh_ = Qs_hi[rg][s][lane], bl_ = Qs_lo[rg][s][lane];
+        acc[rg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ch[s], bh_, acc[rg], 0, 0, 0);
+        acc[rg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ch[s], bl_, acc[rg], 0, 0, 0);
+        acc[rg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cl[s], bh_, acc[rg], 0, 0, 0);
+      }
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg) {
+      int16_t q4[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x = fminf(fmaxf(acc[rg][e] * fscale[rg], -32767.f), 32767.f);
+        q4[e] = (int16_t)__float2int_rn(x);
+      }
+      *reinterpret_cast<uint64_t*>(Sa + (16 * rg + l16) * NKP + 16 * t + 4 * kg) =
+          __builtin_bit_cast(uint64_t, q4);
+    }
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) kmx = fmaxf(kmx, __shfl_xor(kmx, o));
-  if (lane == 0) kmax2[wv] = kmx;
   __syncthreads();
-  float km2 = 0.f;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) km2 = fmaxf(km2, kmax2[w]);
-  const double kmax = sqrt((double)km2) * (1.0 + 0x1p-10);
 
+  // Phase 2, one wave per row.
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma nounroll
   for (int rr = wv; rr < R; rr += NW) {
     const int qb = r0 + rr;
     if (qb >= Nq) break;
     int cq0 = 0, cq1 = 0;
     if (rule.ar_tokens < rule.L) chunk_span(qb * rule.bq, min(rule.L, (qb + 1) * rule.bq), rule.ar_tokens, cq0, cq1);
     const int lo_chunk = rule.ar_window > 0 ? cq0 - rule.ar_window + 1 : -1;
-    uint32_t akey[NPL];  // order-preserving images of the approximate scores
+    uint32_t akey[NPL];  // order-preserving 16-bit images of the stored scores
     uint32_t valid = 0;
     int n_ok = 0;
 #pragma unroll
     for (int j = 0; j < NPL; ++j) {
-      const int c = j * 64 + lane;
+      int c = j * 64 + lane;
+      // (kept opaque: recomputing the window test per row is cheaper than
+      // holding all NPL of its results in registers across the rows)
+      asm volatile("" : "+v"(c));
       bool ok = c < Nk;
       if (ok && rule.ar_tokens < rule.L) {
         int ck0, ck1;
@@ -416,35 +456,32 @@ __global__ __launch_bounds__(64 * kSelWaves) void select_topk_kernel(const doubl
         ok = ck0 <= cq1 && ck1 >= lo_chunk;
       }
       valid |= (ok ? 1u : 0u) << j;
-      akey[j] = ok ? order_key32(Sa[rr * NKP + c]) : 0u;
+      akey[j] = ok ? (uint32_t)((int)Sa[rr * NKP + c] + 32768) : 0u;
       n_ok += __popcll(__ballot(ok));
     }
     const int kk = min(k, n_ok);
     int32_t* out = idx + (bh * Nq + qb) * (int64_t)k;
     uint32_t take_i = 0;  // bit j: block j * 64 + lane is kept
     if (kk > 0) {
-      // sigma: the kk-th largest approximate score
+      // sigma: the kk-th largest stored value
       uint32_t pre = 0, pm = 0;
       int rem = kk;
-      radix_select_desc<NPL>(akey, valid, kk, hist[wv], lane, pre, pm, rem);
+      radix_select_desc<NPL, uint32_t, 16>(akey, valid, kk, hist[wv], lane, pre, pm, rem);
       uint32_t smin = 0xFFFFFFFFu;
 #pragma unroll
       for (int j = 0; j < NPL; ++j)
         if (((valid >> j) & 1u) && (akey[j] & pm) == pre) smin = min(smin, akey[j]);
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) smin = min(smin, (uint32_t)__shfl_xor((int)smin, o));
-      auto score_of = [](uint32_t k32) { return __uint_as_float((k32 >> 31) ? (k32 & 0x7FFFFFFFu) : ~k32); };
-      const double sigma = (double)score_of(smin);
-      const double delta = 0x1p-12 * sqrt(qn2[rr]) * kmax;
-      const double hi_b = sigma + 2.0 * delta, lo_b = sigma - 2.0 * delta;
+      const int sig = (int)smin;
       uint32_t in_m = 0;  // bit j: undecided
       int n_i = 0, n_m = 0;
 #pragma unroll
       for (int j = 0; j < NPL; ++j) {
-        const double sj = (double)score_of(akey[j]);
+        const int v = (int)akey[j];
         const bool vj = (valid >> j) & 1u;
-        const bool ti = vj && sj > hi_b;
-        const bool mi = vj && !ti && sj >= lo_b;
+        const bool ti = vj && v > sig + kSelBand;
+        const bool mi = vj && !ti && v >= sig - kSelBand;
         take_i |= (ti ? 1u : 0u) << j;
         in_m |= (mi ? 1u : 0u) << j;
         n_i += __popcll(__ballot(ti));
@@ -453,16 +490,19 @@ __global__ __launch_bounds__(64 * kSelWaves) void select_topk_kernel(const doubl
       const int need = kk - n_i;
       const double* qrow = Qm + (int64_t)qb * D;
       if (n_m <= 64) {
-        // Fast path. The undecided blocks, listed in index order, get their
-        // exact scores sixteen lanes each (lane part p sums d in
-        // [p D/16, (p+1) D/16) in order, then a fixed tree over the sixteen
-        // parts); one key per lane, and the best `need` of them are marked.
+        // The undecided blocks, listed in index order, get their exact
+        // scores sixteen lanes each (lane part p sums d in [p D/16,
+        // (p+1) D/16) in order, then a fixed tree over the sixteen parts);
+        // then each is ranked against the others (higher score first, the
+        // lower index first among equal scores) and the best `need` kept.
         int base = 0;
 #pragma unroll
         for (int j = 0; j < NPL; ++j) {
           const bool mj = (in_m >> j) & 1u;
           const uint64_t mm = __ballot(mj);
-          if (mj) lst_c[wv][base + __popcll(mm & lt_mask)] = j * 64 + lane;
+          int c = j * 64 + lane;
+          asm volatile("" : "+v"(c));
+          if (mj) lst_c[wv][base + __popcll(mm & lt_mask)] = c;
           base += __popcll(mm);
         }
         chosen[wv][lane] = 0u;
@@ -490,22 +530,21 @@ __global__ __launch_bounds__(64 * kSelWaves) void select_topk_kernel(const doubl
           if (part == 0 && e < n_m) lst_key[wv][e] = order_key(acc);
         }
         wave_lds_sync();
-        uint64_t ek[1] = {lane < n_m ? lst_key[wv][lane] : 0ull};
-        const uint32_t ev = lane < n_m ? 1u : 0u;
-        uint64_t pre2 = 0, pm2 = 0;
-        int rem2 = need;
-        radix_select_desc<1>(ek, ev, need, hist[wv], lane, pre2, pm2, rem2);
-        const uint64_t km = ek[0] & pm2;
-        const bool eq = ev && km == pre2;
-        const bool pick = (ev && km > pre2) || (eq && __popcll(__ballot(eq) & lt_mask) < rem2);
-        if (pick) {
+        const uint64_t mine = lane < n_m ? lst_key[wv][lane] : 0ull;
+        int rank = 0;
+        for (int i = 0; i < n_m; ++i) {
+          const uint64_t other = lst_key[wv][i];
+          rank += (other > mine || (other == mine && i < lane)) ? 1 : 0;
+        }
+        if (lane < n_m && rank < need) {
           const int c = lst_c[wv][lane];
           atomicOr(&chosen[wv][c >> 5], 1u << (c & 31));
         }
         wave_lds_sync();
 #pragma unroll
         for (int j = 0; j < NPL; ++j) {
-          const int c = j * 64 + lane;
+          int c = j * 64 + lane;
+          asm volatile("" : "+v"(c));
           if (((in_m >> j) & 1u) && ((chosen[wv][c >> 5] >> (c & 31)) & 1u)) take_i |= 1u << j;
         }
       } else {
@@ -621,17 +660,17 @@ hipError_t launch_topk_rows(const double* S, int64_t n_rows, int C, int k, const
 }
 
 hipError_t launch_select_topk(const double* qmean, const double* kmean, int BH, int Nk, int D, int k,
-                              const MapRule& rule, uint16_t* khi, uint16_t* klo, int32_t* idx,
+                              const MapRule& rule, uint16_t* khi, uint16_t* klo, double* knorm2, int32_t* idx,
                               hipStream_t stream) {
   const int64_t n_vec = (int64_t)BH * Nk * (D / 8);
   hipLaunchKernelGGL(kmean_split_kernel, dim3((unsigned)((n_vec + 255) / 256)), dim3(256), 0, stream, kmean, n_vec,
-                     khi, klo);
+                     D / 8, khi, klo, knorm2);
   const int npl = (Nk + 63) / 64;
 #define SD_SEL_CASE(DD, N)                                                                                     \
   if (D == DD && npl <= N) {                                                                                   \
     const dim3 grid((unsigned)((rule.Nq + sel_rows(N) - 1) / sel_rows(N)), (unsigned)BH), block(64 * kSelWaves); \
-    hipLaunchKernelGGL((select_topk_kernel<DD, N>), grid, block, 0, stream, qmean, kmean, khi, klo, k, rule, Nk, \
-                       idx);                                                                                   \
+    hipLaunchKernelGGL((select_topk_kernel<DD, N>), grid, block, 0, stream, qmean, kmean, khi, klo, knorm2, k,  \
+                       rule, Nk, idx);                                                                         \
     return hipGetLastError();                                                                                  \
   }
   SD_SEL_CASE(128, 4)

@@ -160,7 +160,7 @@ struct MapRule {
   int64_t rep_stride;
 };
 hipError_t launch_select_topk(const double* qmean, const double* kmean, int BH, int Nk, int D, int k,
-                              const MapRule& rule, uint16_t* khi, uint16_t* klo, int32_t* idx,
+                              const MapRule& rule, uint16_t* khi, uint16_t* klo, double* knorm2, int32_t* idx,
                               hipStream_t stream);
 hipError_t launch_topk_rows(const double* S, int64_t n_rows, int C, int k, const MapRule& rule, int32_t* idx,
                             hipStream_t stream);
