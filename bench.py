@@ -34,7 +34,10 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MFMA_FP8_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 MFMA
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_rola_fused_720p.json")
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_rola_fused_720p.json")
-FUSED_KERNEL_SOURCES = ["k_attention.hip", "sd_tiles.h", "sd_device.h", "sd_launch.h"]
+# what the fused kernel is built from: its source, the shared device headers
+# and its argument struct (AttnArgs in sd_launch.h; the rest of that header
+# declares other kernels' launchers)
+FUSED_KERNEL_SOURCES = ["k_attention.hip", "sd_tiles.h", "sd_device.h", "sd_launch.h:AttnArgs"]
 
 
 def log(msg):
@@ -44,8 +47,13 @@ def log(msg):
 def kernel_source_hash():
     h = hashlib.sha256()
     for name in FUSED_KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "sparse_rank_attention_rola_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        fname, _, struct = name.partition(":")
+        with open(os.path.join(ROOT, "sparse_rank_attention_rola_amd", "csrc", fname), "rb") as f:
+            text = f.read()
+        if struct:
+            start = text.index(b"struct " + struct.encode() + b" {")
+            text = text[start:text.index(b"\n};", start) + 4]
+        h.update(text)
     return h.hexdigest()[:16]
 
 
