@@ -71,6 +71,47 @@ def test_block_select_constructed_ties():
         assert (idx == np.arange(k)[None, None, None, :]).all()
 
 
+# 140 key blocks: more than 64 blocks can be undecided after the
+# approximate scores, which sends a row through the exact in-place path
+WIDE = synthetic.AttnConfig("wide-8960", 1, 2, 128, 5, 28, 64, 128, 64, 0.90, 32)
+
+
+def test_block_select_wide_rows_all_tied():
+    # identical key blocks: every score of a row is equal (all 140 blocks
+    # undecided), so the map is the k lowest block indices
+    cfg = WIDE
+    rng = np.random.default_rng(3)
+    base = synthetic.f32_to_bf16_bits(rng.standard_normal((1, 64, cfg.H, cfg.d)).astype(np.float32))
+    Kb = np.tile(base, (1, cfg.L // 64, 1, 1))
+    Qb, _, _ = synthetic.gen_qkv(cfg, 2)
+    for k in (1, 10, 70, 140):
+        say(f"wide all-tied k={k}")
+        idx = sd.sd_block_select(dev_bf16(Qb), dev_bf16(Kb), k, block_q=cfg.block_q, block_k=64).cpu().numpy()
+        assert (idx == np.arange(k)[None, None, None, :]).all()
+
+
+def test_block_select_zero_query_block_and_dominant_key_block():
+    # query block 3 is all zeros (its scores are all 0: the k lowest
+    # indices); key block 5 is scaled by 2^8, so the largest key-block norm
+    # is far above the others and their scores sit near the bottom of the
+    # fixed-point range of the approximate scores
+    cfg = WIDE
+    Qb, Kb, _ = synthetic.gen_qkv(cfg, 4)
+    Qb = Qb.copy()
+    Kb = Kb.copy()
+    Qb[:, 3 * 128:4 * 128] = 0
+    kf = oracle.bf16_bits_to_f64(Kb[:, 5 * 64:6 * 64]) * 256.0
+    Kb[:, 5 * 64:6 * 64] = synthetic.f32_to_bf16_bits(kf.astype(np.float32))
+    k = _kkeep(cfg)
+    idx = sd.sd_block_select(dev_bf16(Qb), dev_bf16(Kb), k, block_q=cfg.block_q, block_k=64).cpu().numpy()
+    for h in range(cfg.H):
+        assert (idx[0, h, 3] == np.arange(k)).all()
+        S = oracle.block_scores(_f(Qb, 0, h), _f(Kb, 0, h), cfg.block_q, 64)
+        mism, ties, _ = block_map_diff(idx[0, h], S, k)
+        say(f"  head {h}: {mism} blocks differ, {ties} ties")
+        assert mism == 0
+
+
 @pytest.mark.parametrize("cfg", CASES, ids=lambda c: c.name)
 @pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
 def test_sparse_attn(cfg, out_dtype):
