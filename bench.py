@@ -509,6 +509,9 @@ def main():
         y = torch.empty((M, 3 * C), dtype=torch.bfloat16, device=dev)
         gts = torch.empty((M,), dtype=torch.float32, device=dev)
         qkn = [torch.empty((1, cfg.L, cfg.H, cfg.d), dtype=torch.bfloat16, device=dev) for _ in range(4)]
+        # the producer's block means of Q and K, read by the prepare phase
+        means5 = tuple(torch.empty((1, cfg.H, -(-cfg.L // bs), cfg.d), dtype=torch.float64, device=dev)
+                       for bs in (cfg.block_q, cfg.block_k))
         V5 = y[:, 2 * C:].unflatten(1, (cfg.H, cfg.d)).unsqueeze(0)
         Ob = torch.empty((1, cfg.L, cfg.H, cfg.d), dtype=torch.bfloat16, device=dev)
         ocodes = torch.empty((M, C), dtype=torch.uint8, device=dev)
@@ -521,10 +524,12 @@ def main():
             if ev: ev[1].record()
             sd.sd_gemm_fp8_w8a8(codes, scales, wq, sw, out=y)
             if ev: ev[2].record()
-            Q5, K5, Qn5, Kn5 = sd.sd_qk_norm_rope(y[:, :C], y[:, C:2 * C], heads=cfg.H, grid=grid, gamma_q=gam_q,
-                                                  gamma_k=gam_k, out=qkn)
+            Q5, K5, Qn5, Kn5, _, _ = sd.sd_qk_norm_rope(y[:, :C], y[:, C:2 * C], heads=cfg.H, grid=grid,
+                                                        gamma_q=gam_q, gamma_k=gam_k, out=qkn, means_out=means5,
+                                                        block_q=cfg.block_q, block_k=cfg.block_k)
             if ev: ev[3].record()
-            sd.sd_rola_prepare(Q5, K5, V5, lr, k, ws, grid=grid, block_q=cfg.block_q, Qn=Qn5, Kn=Kn5, idx_out=idx)
+            sd.sd_rola_prepare(Q5, K5, V5, lr, k, ws, grid=grid, block_q=cfg.block_q, Qn=Qn5, Kn=Kn5, idx_out=idx,
+                               means=means5)
             if ev: ev[4].record()
             sd.sd_rola_apply(Q5, K5, V5, gts.view(1, cfg.L), lr, k, ws, grid=grid, block_q=cfg.block_q, Qn=Qn5,
                              out=Ob, idx=idx)
@@ -540,7 +545,7 @@ def main():
         for i in range(args.block_timesteps):
             block_step(bev[i])
         torch.cuda.synchronize()
-        names = ["fp8 quant + gate", "W8A8 QKV projection", "q/k RMSNorm + 3D RoPE",
+        names = ["fp8 quant + gate", "W8A8 QKV projection", "q/k RMSNorm + 3D RoPE + block means",
                  "rola prepare (block map + low-rank state)", "rola fused attention", "fp8 quant of O",
                  "W8A8 output projection"]
         per = {n: round(float(np.mean([e[j].elapsed_time(e[j + 1]) for e in bev])), 4) for j, n in enumerate(names)}

@@ -259,12 +259,20 @@ int sd_gemm_fp8_w8a8(const uint8_t* xq, int64_t M, int64_t K, int64_t ldx, const
  * [B, L, H, d]. gamma_q / gamma_k: bf16 [H*d], or NULL for ones. rope: host
  * array of n_rope pairs (e.g. sd_rope_default(d, 10000, ...)); channels in
  * no pair are copied unrotated.
+ * Optionally (qmean / kmean non-NULL) it also writes the block means of the
+ * rotated Q and K, the q-bar / k-bar of the block scores (section 2.1):
+ * float64 [B, H, ceil(L / block), d], each the exact float64 sum of the
+ * block's stored bf16 values in token order divided by its token count
+ * (the tail block by its own count); block_q in {64, 128}, block_k = 64.
+ * sd_rola_prepare takes them instead of pooling Q and K itself.
  * Needs d in {64, 128}, H*d <= 8192, T*Hg*Wg == L, every pair's dim even
  * (pairs inside 8-channel groups), ld_in >= H*d and a multiple of 8, all
- * device buffers 16-byte aligned. Errors leave the outputs unwritten. */
+ * bf16 device buffers 16-byte aligned, the means 8-byte aligned. Errors
+ * leave the outputs unwritten. */
 int sd_qk_norm_rope(int B, int L, int H, int d, int T, int Hg, int Wg, const void* q, const void* k,
                     int64_t ld_in, const void* gamma_q, const void* gamma_k, float eps, const sd_rope_pair* rope,
-                    int n_rope, void* Q, void* K, void* Qn, void* Kn, void* stream);
+                    int n_rope, void* Q, void* K, void* Qn, void* Kn, double* qmean, double* kmean, int block_q,
+                    int block_k, void* stream);
 
 /* ---- fused layer -------------------------------------------------------------
  * The whole path of section 2.1 in one call: block map, sparse branch,
@@ -287,10 +295,14 @@ int sd_rola_attention(const sd_attn_shape* shape, const sd_lowrank_params* lr, c
  *                   block map from idx (NULL: the workspace) and C from the
  *                   workspace left by sd_rola_prepare with the same shape,
  *                   parameters, k_keep and workspace, earlier on the stream.
- * Arguments mean what they mean for sd_rola_attention. */
+ * Arguments mean what they mean for sd_rola_attention. qmean / kmean: NULL
+ * (prepare pools Q and K itself) or both the float64 block means of Q and K,
+ * [B, H, Nq, d] and [B, H, Nk, d] contiguous, as sd_qk_norm_rope writes them
+ * (read by the scored selector only; the caller keeps them until the call's
+ * work on the stream is done). */
 int sd_rola_prepare(const sd_attn_shape* shape, const sd_lowrank_params* lr, const void* Q, const void* K,
-                    const void* V, const void* Qn, const void* Kn, int k_keep, int32_t* idx_out, void* ws,
-                    size_t ws_bytes, void* stream);
+                    const void* V, const void* Qn, const void* Kn, const double* qmean, const double* kmean,
+                    int k_keep, int32_t* idx_out, void* ws, size_t ws_bytes, void* stream);
 int sd_rola_apply(const sd_attn_shape* shape, const sd_lowrank_params* lr, const void* Q, const void* K,
                   const void* V, const void* Qn, const float* g, int64_t g_stride_b, int64_t g_stride_l,
                   int64_t g_stride_h, int k_keep, float sm_scale, void* O, const int32_t* idx, void* ws,

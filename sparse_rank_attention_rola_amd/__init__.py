@@ -88,11 +88,11 @@ def _declare(lib):
         "sd_quant_fp8_gate": (i32, [P, i64, i64, i64, P, i64, P, P, f32, P, P]),
         "sd_gemm_fp8_w8a8": (i32, [P, i64, i64, i64, P, P, i64, i64, P, P, i64, P]),
         "sd_qk_norm_rope": (i32, [i32, i32, i32, i32, i32, i32, i32, P, P, i64, P, P, f32,
-                                  ctypes.POINTER(sd_rope_pair), i32, P, P, P, P, P]),
+                                  ctypes.POINTER(sd_rope_pair), i32, P, P, P, P, P, P, i32, i32, P]),
         "sd_rola_workspace_size": (sz, [S, LR, i32]),
         "sd_rola_attention": (i32, [S, LR, P, P, P, P, P, P, i64, i64, i64, i32, f32, P, P, P, sz, P]),
         "sd_rola_attention_noalloc": (i32, [S, LR, P, P, P, P, P, P, i64, i64, i64, i32, f32, P, P, P]),
-        "sd_rola_prepare": (i32, [S, LR, P, P, P, P, P, i32, P, P, sz, P]),
+        "sd_rola_prepare": (i32, [S, LR, P, P, P, P, P, P, P, i32, P, P, sz, P]),
         "sd_rola_apply": (i32, [S, LR, P, P, P, P, P, i64, i64, i64, i32, f32, P, P, P, sz, P]),
         "sd_rola_backward_workspace_size": (sz, [S, LR, i32]),
         "sd_rola_apply_save": (i32, [S, LR, P, P, P, P, P, i64, i64, i64, i32, f32, P, P, P, sz, P, P]),
@@ -328,11 +328,13 @@ def sd_gemm_fp8_w8a8(xq, sx, wq, sw, *, out=None, stream=None):
 
 
 def sd_qk_norm_rope(q, k, *, heads, grid, batch=1, gamma_q=None, gamma_k=None, eps=1e-6, rope=None, out=None,
-                    stream=None):
+                    block_means=False, block_q=128, block_k=64, means_out=None, stream=None):
     """q/k producer: RMSNorm of every token row of q and k (bf16 [B*L, H*d]
     row views, e.g. slices of the QKV projection's output) and the backbone
     3D RoPE per head. Returns (Q, K, Qn, Kn), bf16 [B, L, H, d] contiguous
-    (or the given out tuple); rope defaults to sd_rope_default(d)."""
+    (or the given out tuple); rope defaults to sd_rope_default(d). With
+    block_means (or means_out = (qmean, kmean)) it also returns the float64
+    block means of Q and K, [B, H, ceil(L / block), d], for sd_rola_prepare."""
     torch = _torch()
     rows, C = q.shape
     if k.shape != q.shape or k.stride() != q.stride():
@@ -353,12 +355,20 @@ def sd_qk_norm_rope(q, k, *, heads, grid, batch=1, gamma_q=None, gamma_k=None, e
             raise ValueError("out must be four contiguous bf16 [B, L, H, d] tensors")
     else:
         outs = [torch.empty((batch, L, H, d), dtype=torch.bfloat16, device=q.device) for _ in range(4)]
+    means = None
+    if means_out is not None:
+        means = tuple(means_out)
+    elif block_means:
+        means = tuple(torch.empty((batch, H, -(-L // bs), d), dtype=torch.float64, device=q.device)
+                      for bs in (block_q, block_k))
     _check(lib().sd_qk_norm_rope(batch, L, H, d, T, Hg, Wg, _ptr(q), _ptr(k), q.stride(0),
                                  _ptr(gamma_q) if gamma_q is not None else None,
                                  _ptr(gamma_k) if gamma_k is not None else None, float(eps),
                                  ctypes.cast(rp, ctypes.POINTER(sd_rope_pair)), len(pairs),
-                                 *[_ptr(o) for o in outs], _stream_ptr(stream)))
-    return tuple(outs)
+                                 *[_ptr(o) for o in outs], _ptr(means[0]) if means else None,
+                                 _ptr(means[1]) if means else None, int(block_q), int(block_k),
+                                 _stream_ptr(stream)))
+    return tuple(outs) + (means if means else ())
 
 
 def rola_workspace(Q, lr: LowrankParams, k_keep, *, grid, block_q=128, select="topk", chunk_tokens=0, window=0):
@@ -408,11 +418,14 @@ def sd_rola_attention_noalloc(Q, K, V, g, lr: LowrankParams, k_keep, out, *, gri
 
 
 def sd_rola_prepare(Q, K, V, lr: LowrankParams, k_keep, workspace, *, grid, block_q=128, Qn=None, Kn=None,
-                    idx_out=None, select="topk", chunk_tokens=0, window=0, stream=None):
-    """Phase 1 of the fused layer: block map and low-rank state."""
+                    idx_out=None, select="topk", chunk_tokens=0, window=0, means=None, stream=None):
+    """Phase 1 of the fused layer: block map and low-rank state. means:
+    optional (qmean, kmean), the float64 block means sd_qk_norm_rope wrote."""
     s = make_shape(Q, K, V, block_q=block_q, grid=grid, select=select, chunk_tokens=chunk_tokens, window=window)
+    qm, km = means if means is not None else (None, None)
     _check(lib().sd_rola_prepare(ctypes.byref(s), ctypes.byref(lr.p), _ptr(Q), _ptr(K), _ptr(V), _ptr(Qn), _ptr(Kn),
-                                 int(k_keep), _ptr(idx_out), _ptr(workspace), workspace.numel(), _stream_ptr(stream)))
+                                 _ptr(qm), _ptr(km), int(k_keep), _ptr(idx_out), _ptr(workspace), workspace.numel(),
+                                 _stream_ptr(stream)))
 
 
 class SavedForward:

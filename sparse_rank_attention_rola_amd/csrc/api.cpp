@@ -557,7 +557,8 @@ int sd_gemm_fp8_w8a8(const uint8_t* xq, int64_t M, int64_t K, int64_t ldx, const
 
 int sd_qk_norm_rope(int B, int L, int H, int d, int T, int Hg, int Wg, const void* q, const void* k,
                     int64_t ld_in, const void* gamma_q, const void* gamma_k, float eps, const sd_rope_pair* rope,
-                    int n_rope, void* Q, void* K, void* Qn, void* Kn, void* stream) {
+                    int n_rope, void* Q, void* K, void* Qn, void* Kn, double* qmean, double* kmean, int block_q,
+                    int block_k, void* stream) {
   if (B < 1 || L < 1 || H < 1) return fail(SD_ERR_INVALID_ARG, "B, L, H must be >= 1");
   if (d != 64 && d != 128) return fail(SD_ERR_UNSUPPORTED, "d = %d (supported: 64, 128)", d);
   if ((int64_t)H * d > 8192) return fail(SD_ERR_UNSUPPORTED, "H*d = %d exceeds 8192", H * d);
@@ -587,6 +588,19 @@ int sd_qk_norm_rope(int B, int L, int H, int d, int T, int Hg, int Wg, const voi
     return rc;
   if ((gamma_q && !aligned(gamma_q, 16)) || (gamma_k && !aligned(gamma_k, 16)))
     return fail(SD_ERR_ALIGN, "gamma must be 16-byte aligned");
+  if (qmean || kmean) {
+    if ((block_q != 64 && block_q != 128) || block_k != 64)
+      return fail(SD_ERR_UNSUPPORTED, "block means need block_q in {64, 128} and block_k = 64");
+    if ((qmean && !aligned(qmean, 8)) || (kmean && !aligned(kmean, 8)))
+      return fail(SD_ERR_ALIGN, "block means must be 8-byte aligned");
+  }
+  a.qmean = qmean;
+  a.kmean = kmean;
+  a.block_q = block_q;
+  a.block_k = block_k;
+  a.rcp_block_q = 1.0 / block_q;
+  a.rcp_block_k = 1.0 / block_k;
+  a.seg_rows = 128;  // a multiple of both block sizes
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
   a.ld_in = ld_in;
@@ -793,15 +807,19 @@ int run_rope_table(const sd_attn_shape* s, const sd_lowrank_params* lr, float2* 
 // graph (and when the caller asks for no side stream). Otherwise the
 // selection, which keeps the vector ALUs busy, runs on the caller's stream
 // beside the HBM-bound stream pass on the side stream.
+// sel_given: the selection workspace with the caller's block means of Q and
+// K (the q/k producer wrote them), so nothing pools them here.
 int run_prepare(const sd_attn_shape* s, const Geo& g, const sd_lowrank_params* lr, const void* Q, const void* K,
                 const void* V, const void* Kn, int k_keep, int32_t* idx, const RolaWs& w, hipStream_t st,
-                bool allow_side = true) {
+                bool allow_side = true, const SelectWs* sel_given = nullptr) {
   int rc = run_rope_table(s, lr, w.lr.rope_tab, st);
   if (rc) return rc;
   sd::RankRows rows;
   sd::PrepareArgs a = prepare_args(s, g, lr, Q, K, V, Kn, w.lr, &rows);
   const bool scored = g.select == SD_SELECT_TOPK;
-  const bool k_in_stream = scored && a.Kn == a.K && g.n_ar == 1;
+  const bool pool = scored && !sel_given;
+  const SelectWs& sel = sel_given ? *sel_given : w.sel;
+  const bool k_in_stream = pool && a.Kn == a.K && g.n_ar == 1;
   a.kmean = k_in_stream ? w.sel.kmean : nullptr;
   hipError_t e;
   auto stream_pass = [&](hipStream_t on) -> int {
@@ -818,14 +836,14 @@ int run_prepare(const sd_attn_shape* s, const Geo& g, const sd_lowrank_params* l
   hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
   if ((e = hipStreamIsCapturing(st, &cap)) != hipSuccess) return hip_fail(e, "prepare: capture status");
   if (k_in_stream || cap != hipStreamCaptureStatusNone || !allow_side) {
-    if (scored) {
+    if (pool) {
       e = sd::launch_pool_blocks(a.Q, s->sq_b, s->sq_l, s->sq_h, g.B, g.L, g.H, g.D, g.bq, w.sel.qmean, st);
       if (e == hipSuccess && !k_in_stream)
         e = sd::launch_pool_blocks(a.K, s->sk_b, s->sk_l, s->sk_h, g.B, g.L, g.H, g.D, g.bk, w.sel.kmean, st);
       if (e != hipSuccess) return hip_fail(e, "block pooling");
     }
     if ((rc = stream_pass(st))) return rc;
-    return run_scores_topk(s, g, k_keep, idx, w.sel, st);
+    return run_scores_topk(s, g, k_keep, idx, sel, st);
   }
   std::lock_guard<std::mutex> lock(g_side_mu);
   SideStream* side = nullptr;
@@ -842,12 +860,12 @@ int run_prepare(const sd_attn_shape* s, const Geo& g, const sd_lowrank_params* l
     if (rc) return rc;
     return hip_fail(e, "prepare: join");
   }
-  if (scored) {
+  if (pool) {
     e = sd::launch_pool_blocks(a.Q, s->sq_b, s->sq_l, s->sq_h, g.B, g.L, g.H, g.D, g.bq, w.sel.qmean, st);
     if (e == hipSuccess)
       e = sd::launch_pool_blocks(a.K, s->sk_b, s->sk_l, s->sk_h, g.B, g.L, g.H, g.D, g.bk, w.sel.kmean, st);
   }
-  rc = e == hipSuccess ? run_scores_topk(s, g, k_keep, idx, w.sel, st) : hip_fail(e, "block pooling");
+  rc = e == hipSuccess ? run_scores_topk(s, g, k_keep, idx, sel, st) : hip_fail(e, "block pooling");
   // the join comes after a failed launch too
   e = hipStreamWaitEvent(st, side->join, 0);
   if (rc) return rc;
@@ -890,14 +908,20 @@ int run_apply(const sd_attn_shape* shape, const Geo& g, const sd_lowrank_params*
 extern "C" {
 
 int sd_rola_prepare(const sd_attn_shape* shape, const sd_lowrank_params* lr, const void* Q, const void* K,
-                    const void* V, const void* Qn, const void* Kn, int k_keep, int32_t* idx_out, void* ws,
-                    size_t ws_bytes, void* stream) {
+                    const void* V, const void* Qn, const void* Kn, const double* qmean, const double* kmean,
+                    int k_keep, int32_t* idx_out, void* ws, size_t ws_bytes, void* stream) {
   Geo g;
   int rc;
   if ((rc = check_rola(shape, lr, Q, K, V, Qn, Kn, k_keep, idx_out, ws_bytes, ws, &g))) return rc;
+  if ((qmean == nullptr) != (kmean == nullptr)) return fail(SD_ERR_INVALID_ARG, "give both block means or neither");
+  if ((qmean && !aligned(qmean, 8)) || (kmean && !aligned(kmean, 8)))
+    return fail(SD_ERR_ALIGN, "block means must be 8-byte aligned");
   const RolaWs w = carve_rola(ws, g, shape, k_keep);
+  SelectWs given = w.sel;
+  given.qmean = const_cast<double*>(qmean);
+  given.kmean = const_cast<double*>(kmean);
   if ((rc = run_prepare(shape, g, lr, Q, K, V, Kn, k_keep, idx_out ? idx_out : w.idx, w,
-                        static_cast<hipStream_t>(stream))))
+                        static_cast<hipStream_t>(stream), true, qmean ? &given : nullptr)))
     return rc;
   return ok();
 }

@@ -127,6 +127,12 @@ struct QkNormRopeArgs {
   uint16_t* K;
   uint16_t* Qn;
   uint16_t* Kn;
+  // optional block means of Q and K (f64 [B, H, ceil(L / block), d]); rows
+  // go in segments of seg_rows (<= 128), a multiple of both block sizes
+  double* qmean;
+  double* kmean;
+  int block_q, block_k, seg_rows;
+  double rcp_block_q, rcp_block_k;  // 1 / block (exact: powers of two)
 };
 hipError_t launch_qk_norm_rope(const QkNormRopeArgs& a, hipStream_t stream);
 

@@ -215,9 +215,14 @@ def test_qk_norm_rope_validation():
     rptr = ctypes.cast(rp, ctypes.POINTER(sd.sd_rope_pair))
     odd = (sd.sd_rope_pair * 1)(sd.sd_rope_pair(43, 2, 1.0))
 
-    def c(B=1, L=60, H=4, d=128, T=3, Hg=4, Wg=5, q=FAKE, ld=512, eps=1e-6, rope=rptr, n=64, gq=None, Q=FAKE):
+    def c(B=1, L=60, H=4, d=128, T=3, Hg=4, Wg=5, q=FAKE, ld=512, eps=1e-6, rope=rptr, n=64, gq=None, Q=FAKE,
+          qm=None, bq=128, bk=64):
         return lib.sd_qk_norm_rope(B, L, H, d, T, Hg, Wg, q, FAKE, ld, gq, None, eps, rope, n, Q, FAKE, FAKE, FAKE,
-                                   None)
+                                   qm, None, bq, bk, None)
+
+    assert c(qm=FAKE, bq=32) == sd.SD_ERR_UNSUPPORTED  # block means: block_q in {64, 128}
+    assert c(qm=FAKE, bk=128) == sd.SD_ERR_UNSUPPORTED  # block_k = 64
+    assert c(qm=FAKE + 4) == sd.SD_ERR_ALIGN
 
     assert c(d=96) == sd.SD_ERR_UNSUPPORTED
     assert c(H=80) == sd.SD_ERR_UNSUPPORTED  # H*d > 8192

@@ -82,14 +82,16 @@ def test_deployment_block_tiny_end_to_end():
     codes, scales, gd = sd.sd_quant_fp8_gate(X, dev_bf16(wg), synthetic.GATE_BIAS)
     Wq, Sw = sd.sd_quant_fp8_per_token(dev_bf16(wqkv))
     Y = sd.sd_gemm_fp8_w8a8(codes, scales, Wq, Sw)
-    Q5, K5, Qn5, Kn5 = sd.sd_qk_norm_rope(Y[:, :C], Y[:, C:2 * C], heads=H, grid=(cfg.T, cfg.Hg, cfg.Wg),
-                                          gamma_q=dev_bf16(gq), gamma_k=dev_bf16(gk))
+    Q5, K5, Qn5, Kn5, qm5, km5 = sd.sd_qk_norm_rope(Y[:, :C], Y[:, C:2 * C], heads=H, grid=(cfg.T, cfg.Hg, cfg.Wg),
+                                                    gamma_q=dev_bf16(gq), gamma_k=dev_bf16(gk), block_means=True,
+                                                    block_q=cfg.block_q, block_k=cfg.block_k)
     V5 = Y[:, 2 * C:].unflatten(1, (H, d)).unsqueeze(0)
     lr = sd.LowrankParams(dev_bf16(Pqb), dev_bf16(Pkb))
     grid = (cfg.T, cfg.Hg, cfg.Wg)
     ws = sd.rola_workspace(Q5, lr, k_keep, grid=grid, block_q=cfg.block_q)
     idx = torch.empty((1, H, L // cfg.block_q, k_keep), dtype=torch.int32, device="cuda")
-    sd.sd_rola_prepare(Q5, K5, V5, lr, k_keep, ws, grid=grid, block_q=cfg.block_q, Qn=Qn5, Kn=Kn5, idx_out=idx)
+    sd.sd_rola_prepare(Q5, K5, V5, lr, k_keep, ws, grid=grid, block_q=cfg.block_q, Qn=Qn5, Kn=Kn5, idx_out=idx,
+                       means=(qm5, km5))
     Ob = sd.sd_rola_apply(Q5, K5, V5, gd.view(1, L), lr, k_keep, ws, grid=grid, block_q=cfg.block_q, Qn=Qn5,
                           idx=idx)
     OQ, OS = sd.sd_quant_fp8_per_token(Ob.view(L, C))

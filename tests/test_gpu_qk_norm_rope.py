@@ -42,7 +42,7 @@ def _check(name, got, ref, extra):
     assert np.isfinite(got).all() and worst <= 1.0, name
 
 
-def _run_case(B, T, Hg, Wg, H, d, seed, strided=False, with_gamma=True):
+def _run_case(B, T, Hg, Wg, H, d, seed, strided=False, with_gamma=True, block_q=0):
     L = T * Hg * Wg
     C = H * d
     qb = synthetic.gen_qk_rows(B * L, C, seed)
@@ -56,9 +56,11 @@ def _run_case(B, T, Hg, Wg, H, d, seed, strided=False, with_gamma=True):
         q, k = dbuf[:, :C], dbuf[:, C:2 * C]
     else:
         q, k = dev_bf16(qb), dev_bf16(kb)
-    Q, K, Qn, Kn = sd.sd_qk_norm_rope(q, k, heads=H, grid=(T, Hg, Wg), batch=B,
-                                      gamma_q=dev_bf16(gq) if with_gamma else None,
-                                      gamma_k=dev_bf16(gk) if with_gamma else None)
+    res = sd.sd_qk_norm_rope(q, k, heads=H, grid=(T, Hg, Wg), batch=B,
+                             gamma_q=dev_bf16(gq) if with_gamma else None,
+                             gamma_k=dev_bf16(gk) if with_gamma else None,
+                             block_means=block_q > 0, block_q=block_q or 128, block_k=64)
+    Q, K, Qn, Kn = res[:4]
     torch.cuda.synchronize()
     pos = oracle.token_positions(T, Hg, Wg)
     for name, xb, g, outr, outn in (("q", qb, gq, Q, Qn), ("k", kb, gk, K, Kn)):
@@ -68,6 +70,13 @@ def _run_case(B, T, Hg, Wg, H, d, seed, strided=False, with_gamma=True):
             Xn, Xr = oracle.qk_norm_rope(X, H, d, pos, gam, 1e-6)
             _check(f"{name}n b{b}", _f(outn[b]), Xn, 2.0 ** -20 * np.abs(Xn))
             _check(f"{name} rope b{b}", _f(outr[b]), Xr, 2.0 ** -16 * _pair_mag(Xn))
+    if block_q:
+        # the block means of the stored rotated outputs, exact in float64
+        qm, km = (m.cpu().numpy() for m in res[4:])
+        for b in range(B):
+            for h in range(H):
+                assert np.array_equal(qm[b, h], oracle.pooled_means(_f(Q[b, :, h]), block_q)), (b, h)
+                assert np.array_equal(km[b, h], oracle.pooled_means(_f(K[b, :, h]), 64)), (b, h)
 
 
 @pytest.mark.parametrize("B,T,Hg,Wg,H", [(1, 3, 5, 7, 4), (2, 2, 4, 9, 12), (1, 4, 6, 10, 40)])
@@ -110,3 +119,63 @@ def test_qk_norm_rope_deterministic():
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
     # q and k from the same rows give the same outputs
     assert torch.equal(a[0].view(torch.int16), a[1].view(torch.int16))
+
+
+# --- block means of the rotated outputs --------------------------------------
+# The producer's q-bar / k-bar are float64 sums of the stored bf16 values in
+# token order divided by the block's token count. For these inputs the sums
+# are exact in float64 (a block's values span far fewer than 38 binades), so
+# they must equal the oracle's means of the produced Q / K bit for bit,
+# whatever the summation order.
+
+@pytest.mark.parametrize("B,T,Hg,Wg,H,bq", [(2, 3, 5, 7, 4, 128), (1, 5, 9, 11, 3, 64), (1, 4, 16, 16, 40, 128)])
+def test_qk_norm_rope_block_means(B, T, Hg, Wg, H, bq):
+    # the producer with block means: its outputs against the oracle as
+    # above, its means against the oracle's means of those outputs
+    say(f"block means B={B} grid={T}x{Hg}x{Wg} H={H} block_q={bq}")
+    _run_case(B, T, Hg, Wg, H, 128, seed=B * 10 + H, block_q=bq)
+
+
+def test_prepare_with_producer_means_equals_pooling():
+    # the block map and the fused output from the producer's means equal
+    # those of the prepare phase pooling Q and K itself
+    cfg = synthetic.AttnConfig("producer-means", 1, 4, 128, 4, 16, 16, 128, 64, 0.75, 32)
+    C = cfg.H * cfg.d
+    grid = (cfg.T, cfg.Hg, cfg.Wg)
+    q = dev_bf16(synthetic.gen_qk_rows(cfg.L, C, 21))
+    k = dev_bf16(synthetic.gen_qk_rows(cfg.L, C, 22))
+    v = dev_bf16(synthetic.gen_qk_rows(cfg.L, C, 23)).view(1, cfg.L, cfg.H, cfg.d)
+    Q, K, Qn, Kn, qm, km = sd.sd_qk_norm_rope(q, k, heads=cfg.H, grid=grid, block_means=True)
+    Pqb, Pkb = synthetic.gen_lowrank_params(cfg)
+    lr = sd.LowrankParams(dev_bf16(Pqb), dev_bf16(Pkb))
+    k_keep = oracle.keep_count(cfg.sparsity, cfg.L // 64)
+    g = torch.ones((1, cfg.L), dtype=torch.float32, device="cuda")
+    outs = []
+    for means in (None, (qm, km)):
+        ws = sd.rola_workspace(Q, lr, k_keep, grid=grid)
+        idx = torch.empty((1, cfg.H, cfg.L // 128, k_keep), dtype=torch.int32, device="cuda")
+        sd.sd_rola_prepare(Q, K, v, lr, k_keep, ws, grid=grid, Qn=Qn, Kn=Kn, idx_out=idx, means=means)
+        O = sd.sd_rola_apply(Q, K, v, g, lr, k_keep, ws, grid=grid, Qn=Qn, idx=idx)
+        torch.cuda.synchronize()
+        outs.append((idx.cpu(), O.view(torch.int16).cpu()))
+    assert torch.equal(outs[0][0], outs[1][0])
+    assert torch.equal(outs[0][1], outs[1][1])
+
+
+def test_qk_norm_rope_block_means_720p_sampled_blocks():
+    # full 720P size (75600 tokens, 40 heads): the means of sampled query
+    # and key blocks, including the partial tails, against the oracle's means
+    # of the produced Q / K rows of those blocks
+    T, Hg, Wg, H, d = 21, 45, 80, 40, 128
+    L, C = T * Hg * Wg, H * d
+    q = dev_bf16(synthetic.gen_qk_rows(L, C, 41))
+    k = dev_bf16(synthetic.gen_qk_rows(L, C, 42))
+    Q, K, Qn, Kn, qm, km = sd.sd_qk_norm_rope(q, k, heads=H, grid=(T, Hg, Wg), block_means=True)
+    torch.cuda.synchronize()
+    qm, km = qm.cpu().numpy(), km.cpu().numpy()
+    for X, M, bs, blocks in ((Q, qm, 128, [0, 1, 295, 590]), (K, km, 64, [0, 1, 590, 1181])):
+        for c in blocks:
+            rows = _f(X[0, c * bs:min(L, (c + 1) * bs)])  # [tokens, H, d]
+            ref = rows.sum(axis=0) / rows.shape[0]
+            assert np.array_equal(M[0, :, c], ref), (bs, c)
+    say("720P block means: sampled query and key blocks exact")
