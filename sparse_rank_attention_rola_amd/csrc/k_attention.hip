@@ -53,7 +53,7 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
 //   lowrank_load:     the lane's P_q rows (A operands of the projection) and
 //                     the cos/sin of its RoPE pairs;
 //   lowrank_features: q~ = R(p) phi(P_q qn) through the wave's LDS patch Fw
-//                     (32 x 33 floats), split into bf16 hi + lo B operands
+//                     (32 x 32 floats, feat_at), split into bf16 hi + lo B operands
 //                     (lane l32 = query, ranks 16s + 8hf .. +7);
 //   lowrank_output:   y = C^T q~ with the state C of the lane's chunk (0
 //                     without a causal window), y / sqrt(mean(y^2) + eps) * w
@@ -75,7 +75,9 @@ __device__ __forceinline__ void lowrank_load(const AttnArgs& a, int h, int tok0,
     const int m = 2 * j + hf;
     ld.cs[j] = float2{1.f, 0.f};
     if (2 * j < a.rope.n && m < a.rope.n) {
-      const int axis = a.rope.axis[m];
+      // constant offsets into the arguments: scalar loads (a lane-indexed
+      // read of the argument block would be a vector load and a wait)
+      const int axis = hf ? a.rope.axis[2 * j + 1] : a.rope.axis[2 * j];
       ld.cs[j] = a.rope_tab[m * a.rope.max_ext + (axis == 0 ? pos[0] : axis == 1 ? pos[1] : pos[2])];
     }
   }
@@ -85,6 +87,16 @@ __device__ __forceinline__ void lowrank_load(const AttnArgs& a, int h, int tok0,
     ld.pa[s] = (l32 < a.rank) ? *reinterpret_cast<const u32x4*>(Pq + l32 * D + 16 * s + 8 * hf) : u32x4{0, 0, 0, 0};
 }
 
+// A wave's feature patch: 32 rows (queries) of 32 floats (ranks), 4 KB. The
+// column is XORed with an even value that differs between the 16 rows of
+// each parity, so the lanes' rows fall in distinct banks and each even/odd
+// column pair stays adjacent. The patches of up to 4 waves (16 KB) fit the
+// second tile buffer at every head dimension.
+__device__ __forceinline__ int feat_at(int row, int col) { return row * 32 + (col ^ (2 * ((row >> 1) & 15))); }
+static_assert(4 * 32 * 32 * 4 <= TileSmem<64>::kElems * 2, "feature patches exceed the tile buffer");
+
+// The patch belongs to one wave: its LDS accesses complete in issue order, so
+// the steps below need no barrier between them.
 template <int D>
 __device__ __forceinline__ void lowrank_features(const u32x4* qn, const AttnArgs& a, const LowrankLoads<D>& ld,
                                                  float* Fw, int lane, bf16x8 (&qhi)[2], bf16x8 (&qlo)[2]) {
@@ -96,27 +108,27 @@ __device__ __forceinline__ void lowrank_features(const u32x4* qn, const AttnArgs
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int ri = 8 * (r >> 2) + 4 * hf + (r & 3);
-    Fw[l32 * 33 + ri] = ri < a.rank ? phi_elu1(acc[r]) : 0.f;
+    Fw[feat_at(l32, ri)] = ri < a.rank ? phi_elu1(acc[r]) : 0.f;
   }
-  __syncthreads();
   // RoPE: lane l32 = token; the two lane halves take the even and odd pairs
 #pragma unroll
   for (int j = 0; j < kMaxRopePairs / 2; ++j) {
     const int m = 2 * j + hf;
     if (2 * j < a.rope.n && m < a.rope.n) {
       const float2 cs = ld.cs[j];
-      float* f = Fw + l32 * 33 + a.rope.dim[m];
-      const float u = f[0], v = f[1];
-      f[0] = u * cs.x - v * cs.y;
-      f[1] = u * cs.y + v * cs.x;
+      const int d0 = hf ? a.rope.dim[2 * j + 1] : a.rope.dim[2 * j];  // scalar loads, as above
+      float* f0 = Fw + feat_at(l32, d0);
+      float* f1 = Fw + feat_at(l32, d0 + 1);
+      const float u = *f0, v = *f1;
+      *f0 = u * cs.x - v * cs.y;
+      *f1 = u * cs.y + v * cs.x;
     }
   }
-  __syncthreads();
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     float t8[8];
 #pragma unroll
-    for (int p = 0; p < 8; ++p) t8[p] = Fw[l32 * 33 + 16 * s + 8 * hf + p];
+    for (int p = 0; p < 8; ++p) t8[p] = Fw[feat_at(l32, 16 * s + 8 * hf + p)];
     split_bf16x8(t8, qhi[s], qlo[s]);
   }
 }
@@ -274,7 +286,7 @@ __global__ __launch_bounds__(BQ * 2, BQ == 128 ? kAttnMinWaves : 1) void attenti
   }
   auto form_features = [&]() __attribute__((always_inline)) {
     if constexpr (MODE != kModeSparse) {
-      float* Fw = reinterpret_cast<float*>(smem1) + wv * (32 * 33);
+      float* Fw = reinterpret_cast<float*>(smem1) + wv * (32 * 32);
       lowrank_features<D>(sep_qn ? qn_reg : qreg, a, lld, Fw, lane, lqh, lql);
     }
   };

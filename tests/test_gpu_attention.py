@@ -26,7 +26,10 @@ RAGGED = synthetic.AttnConfig("ragged-330", 1, 3, 128, 3, 10, 11, 128, 64, 0.70,
 RAGGED64 = synthetic.AttnConfig("ragged-d64", 2, 2, 64, 5, 7, 13, 64, 64, 0.60, 16)
 MID = synthetic.AttnConfig("mid-2176", 1, 4, 128, 2, 32, 34, 128, 64, 0.90, 32)
 BQ64 = dataclasses.replace(RAGGED, name="ragged-bq64", block_q=64)
-CASES = [synthetic.TINY, RAGGED, RAGGED64, MID, BQ64]
+# d = 64 with 128-query blocks: four waves' feature patches share the two
+# 8 KB tile buffers, and the rank-16 RoPE split has a pair that starts odd
+D64BQ128 = dataclasses.replace(RAGGED64, name="ragged-d64-bq128", block_q=128)
+CASES = [synthetic.TINY, RAGGED, RAGGED64, MID, BQ64, D64BQ128]
 
 
 def _inputs(cfg, seed=0):
