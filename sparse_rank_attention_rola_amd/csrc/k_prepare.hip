@@ -185,10 +185,12 @@ __global__ __launch_bounds__(256, 3) void prepare_stream_kernel(PrepareArgs a) {
       cs[j] = a.rope_tab[cs_row[j] + (cs_axis[j] == 0 ? pos[0] : cs_axis[j] == 1 ? pos[1] : pos[2])];
   };
 
-  // One 64-token tile (its key-block partial sums are left in kred).
-  auto step = [&](RegTile<D>& rt, int tl, float2(&cs)[4]) __attribute__((always_inline)) {
+  // One 64-token tile (its key-block partial sums are left in kred, read
+  // after the next step's first barrier).
+  auto step = [&](RegTile<D>& rt, int tl, float2(&cs)[4], auto&& after_first_barrier) __attribute__((always_inline)) {
     const int tok0 = tl * 64;
     __syncthreads();  // the previous tile's readers are done with the tile
+    after_first_barrier();
     rt.store(tile, tid);
     // refill the registers with tile tl + 1; past the run the loads go to
     // empty buffers (zeros, no memory access), so every path issues the
@@ -197,25 +199,6 @@ __global__ __launch_bounds__(256, 3) void prepare_stream_kernel(PrepareArgs a) {
     rt.load(more ? kr : kr0, more ? vr : vr0, kstr, vstr, (tl + 1) * 64, tid);
     __syncthreads();
 
-    // exact float64 sums of K rows 16 wv .. 16 wv + 15 (rows past L were
-    // loaded as zeros)
-    double ks[CH];
-#pragma unroll
-    for (int c = 0; c < CH; ++c) ks[c] = 0.0;
-    if constexpr (pool_k) {
-      const uint16_t* rows = tile + 16 * wv * D;
-#pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        if constexpr (CH == 2) {
-          const uint32_t w =
-              *reinterpret_cast<const uint32_t*>(rows + t * D + (((c0 >> 3) ^ k_swz<D>(t)) << 3) + (c0 & 7));
-          ks[0] += (double)bf16_lo(w);
-          ks[1] += (double)bf16_hi(w);
-        } else {
-          ks[0] += (double)bf16_bits_to_f32(rows[t * D + (((c0 >> 3) ^ k_swz<D>(t)) << 3) + (c0 & 7)]);
-        }
-      }
-    }
     {
       // k~ of tokens 16 wv .. +15: phi(P_k k) on 16x16x32 MFMAs (both
       // 16-slot halves), the RoPE pairs rotated in registers (a pair sits in
@@ -267,18 +250,23 @@ __global__ __launch_bounds__(256, 3) void prepare_stream_kernel(PrepareArgs a) {
           Fop[kFop + ix] = fl[4 * rh + e];
         }
     }
-    if constexpr (pool_k) {
-#pragma unroll
-      for (int c = 0; c < CH; ++c) kred[wv * D + c0 + c] = ks[c];
-    }
     __syncthreads();
-    // C^T[d][slot] += sum over the tile's tokens of V[tok][d] k~[tok][slot]
-    if (wv < D / 32) {
-      const uint16_t* Vs = tile + 64 * D;
-      const uint16_t* Fh = Fop;
-      const uint16_t* Fl = Fop + kFop;
+    // C^T[d][slot] += sum over the tile's tokens of V[tok][d] k~[tok][slot],
+    // and (POOL) the exact float64 sums of K rows 16 wv .. 16 wv + 15 (rows
+    // past L were loaded as zeros): a quarter of the rows after each pair of
+    // MFMAs, so that the sums run under them. The tile stays in LDS until the
+    // next step's first barrier, and the partials are read after it.
+    const bool ct_wave = D / 32 >= 4 || wv < D / 32;  // d = 128: every wave
+    const uint16_t* Vs = tile + 64 * D;
+    const uint16_t* Fh = Fop;
+    const uint16_t* Fl = Fop + kFop;
+    const uint16_t* rows = tile + 16 * wv * D;
+    double ks[CH];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
+    for (int c = 0; c < CH; ++c) ks[c] = 0.0;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if (ct_wave) {
         const int off = l32 * 64 + (((2 * s + hf) ^ ((l32 >> 1) & 7)) << 3);
         const bf16x8 fhi = as_bf16x8(*reinterpret_cast<const u32x4*>(Fh + off));
         const bf16x8 flo = as_bf16x8(*reinterpret_cast<const u32x4*>(Fl + off));
@@ -286,6 +274,23 @@ __global__ __launch_bounds__(256, 3) void prepare_stream_kernel(PrepareArgs a) {
         cacc = mfma32(vop, fhi, cacc);
         cacc = mfma32(vop, flo, cacc);
       }
+      if constexpr (pool_k) {
+#pragma unroll
+        for (int t = 4 * s; t < 4 * s + 4; ++t) {
+          if constexpr (CH == 2) {
+            const uint32_t w =
+                *reinterpret_cast<const uint32_t*>(rows + t * D + (((c0 >> 3) ^ k_swz<D>(t)) << 3) + (c0 & 7));
+            ks[0] += (double)bf16_lo(w);
+            ks[1] += (double)bf16_hi(w);
+          } else {
+            ks[0] += (double)bf16_bits_to_f32(rows[t * D + (((c0 >> 3) ^ k_swz<D>(t)) << 3) + (c0 & 7)]);
+          }
+        }
+      }
+    }
+    if constexpr (pool_k) {
+#pragma unroll
+      for (int c = 0; c < CH; ++c) kred[wv * D + c0 + c] = ks[c];
     }
     // the next tile's RoPE factors (kred is rewritten only after the next
     // step's two barriers)
@@ -312,23 +317,31 @@ __global__ __launch_bounds__(256, 3) void prepare_stream_kernel(PrepareArgs a) {
       dst[0] = km[0];
     }
   };
-  for (int tl = t_begin; tl < t_end; ++tl) {
-    step(rt, tl, cs);
-    if constexpr (pool_k) {
-      const int pos = (tl - t_begin) & 3;
-      if (pos == wv) {
-        const int kb_tok = min(64, a.L - tl * 64);
+  // the means of tile tl from the partials in kred (after a barrier that
+  // follows their writes)
+  auto finish_means = [&](int tl) __attribute__((always_inline)) {
+    const int pos = (tl - t_begin) & 3;
+    if (pos == wv) {
+      const int kb_tok = min(64, a.L - tl * 64);
 #pragma unroll
-        for (int c = 0; c < CH; ++c) {
-          const int cc = c0k + c;
-          const double sum = ((kred[cc] + kred[D + cc]) + kred[2 * D + cc]) + kred[3 * D + cc];
-          km[c] = kb_tok == 64 ? sum * 0.015625 : sum / kb_tok;
-        }
+      for (int c = 0; c < CH; ++c) {
+        const int cc = c0k + c;
+        const double sum = ((kred[cc] + kred[D + cc]) + kred[2 * D + cc]) + kred[3 * D + cc];
+        km[c] = kb_tok == 64 ? sum * 0.015625 : sum / kb_tok;
       }
-      if (pos == 3) store_means(tl - 3 + wv);
     }
+    if (pos == 3) store_means(tl - 3 + wv);
+  };
+  for (int tl = t_begin; tl < t_end; ++tl) {
+    step(rt, tl, cs, [&]() __attribute__((always_inline)) {
+      if constexpr (pool_k) {
+        if (tl > t_begin) finish_means(tl - 1);
+      }
+    });
   }
   if constexpr (pool_k) {
+    __syncthreads();
+    if (t_end > t_begin) finish_means(t_end - 1);
     const int rem = (t_end - t_begin) & 3;  // tiles of the last, unfinished group
     if (rem != 0 && wv < rem) store_means(t_end - rem + wv);
   }
