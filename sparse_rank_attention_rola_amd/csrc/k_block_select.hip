@@ -268,8 +268,8 @@ __global__ __launch_bounds__(256) void topk_rows_kernel(const double* __restrict
 // 1 + 2^-12), 2^14 steps per unit: rounding adds 2^-15. So every stored
 // value is within Delta = 2^-12 (in normalised units, 4 steps) of the exact
 // normalised score, with room for a coarser MFMA accumulation.
-// Phase 2, one wave per row: sigma = the k-th largest stored value (radix
-// select on two 8-bit digits). A block more than 2 Delta (8 steps) above
+// Phase 2, one wave per row: sigma = the k-th largest stored value (a
+// bitwise search on ballot counts of the 16-bit keys). A block more than 2 Delta (8 steps) above
 // sigma is kept for certain (fewer than k blocks can reach its score), one
 // more than 2 Delta below is dropped for certain (k blocks beat it); only
 // the few in between (about five per row at 720P) get their exact float64
@@ -333,7 +333,7 @@ __global__ __launch_bounds__(64 * kSelWaves) void select_topk_kernel(const doubl
   __shared__ uint32_t hist[NW][256];
   __shared__ int lst_c[NW][64];         // undecided blocks of the row, in index order
   __shared__ uint64_t lst_key[NW][64];  // their exact keys
-  __shared__ uint32_t chosen[NW][64];   // bit c % 32 of word c / 32: undecided block c is kept
+  __shared__ uint32_t lst_pk[NW][128];  // compacted candidates: key << 16 | block
   __shared__ double red[NW];
   // the query-block means as split B operands: [row group][d step][lane]
   __shared__ bf16x8 Qs_hi[RG][D / 32][64], Qs_lo[RG][D / 32][64];
@@ -463,19 +463,155 @@ __global__ __launch_bounds__(64 * kSelWaves) void select_topk_kernel(const doubl
     }
     const int kk = min(k, n_ok);
     int32_t* out = idx + (bh * Nq + qb) * (int64_t)k;
+    const double* qrow = Qm + (int64_t)qb * D;
+
+    // The undecided blocks listed in lst_c[wv][0, n_m) (n_m <= 64, index
+    // order) get their exact scores sixteen lanes each (lane part p sums d
+    // in [p D/16, (p+1) D/16) in order, then a fixed tree over the sixteen
+    // parts) and are ranked against each other (higher score first, the
+    // lower index first among equal scores). Returns the mask of list
+    // entries among the best `need`.
+    auto exact_pick = [&](int n_m, int need) __attribute__((always_inline)) -> uint64_t {
+      constexpr int DP = D / 16;
+      const int e_in = lane >> 4, part = lane & 15;
+      wave_lds_sync();
+      // the query part is the same for every block; two groups of four
+      // blocks go per pass, their loads issued together
+      double qv[DP];
+#pragma unroll
+      for (int u = 0; u < DP; ++u) qv[u] = qrow[part * DP + u];
+      for (int g0 = 0; g0 < n_m; g0 += 8) {
+        int e[2], c[2];
+        double kv[2][DP];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          e[h] = g0 + 4 * h + e_in;
+          c[h] = e[h] < n_m ? lst_c[wv][e[h]] : 0;
+#pragma unroll
+          for (int u = 0; u < DP; ++u) kv[h][u] = Km[(int64_t)c[h] * D + part * DP + u];
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          double acc = 0.0;
+#pragma unroll
+          for (int u = 0; u < DP; ++u) acc = fma(qv[u], kv[h][u], acc);
+          acc += __shfl_xor(acc, 1);
+          acc += __shfl_xor(acc, 2);
+          acc += __shfl_xor(acc, 4);
+          acc += __shfl_xor(acc, 8);
+          if (part == 0 && e[h] < n_m) lst_key[wv][e[h]] = order_key(acc);
+        }
+      }
+      wave_lds_sync();
+      const uint64_t mine = lane < n_m ? lst_key[wv][lane] : 0ull;
+      const uint32_t mine_lo = (uint32_t)mine, mine_hi = (uint32_t)(mine >> 32);
+      int rank = 0;
+      for (int i = 0; i < n_m; ++i) {
+        const uint64_t other = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)mine_hi, i) << 32) |
+                               (uint32_t)__builtin_amdgcn_readlane((int)mine_lo, i);
+        rank += (other > mine || (other == mine && i < lane)) ? 1 : 0;
+      }
+      return __ballot(lane < n_m && rank < need);
+    };
+
+    // Fast path: a lower bound on sigma is the kk-th largest of the lanes'
+    // maxima (each is a key, so at least kk keys reach it). Every block that
+    // can be kept or undecided scores at least that bound minus the band;
+    // at 720P about 50 blocks a row do. With at most 128 of them they are
+    // compacted (index order) to two per lane, and sigma, the decisions and
+    // the output come from those alone.
+    bool done = false;
+    if (kk > 0 && kk <= 64) {
+      uint32_t lmax = 0;
+#pragma unroll
+      for (int j = 0; j < NPL; ++j) lmax = max(lmax, akey[j]);  // invalid keys are 0
+      uint32_t lb = 0;
+#pragma unroll
+      for (int b = 15; b >= 0; --b) {
+        const uint32_t t = lb | (1u << b);
+        if (__popcll(__ballot(lmax >= t)) >= kk) lb = t;
+      }
+      const uint32_t floor_key = lb > (uint32_t)kSelBand + 1u ? lb - (uint32_t)kSelBand : 1u;
+      int n_c = 0;
+#pragma unroll
+      for (int j = 0; j < NPL; ++j) n_c += __popcll(__ballot(akey[j] >= floor_key));
+      if (n_c <= 128) {
+        int base = 0;
+#pragma unroll
+        for (int j = 0; j < NPL; ++j) {
+          const bool f = akey[j] >= floor_key;
+          const uint64_t fm = __ballot(f);
+          int c = j * 64 + lane;
+          asm volatile("" : "+v"(c));
+          if (f) lst_pk[wv][base + __popcll(fm & lt_mask)] = (akey[j] << 16) | (uint32_t)c;
+          base += __popcll(fm);
+        }
+        wave_lds_sync();
+        uint32_t ck[2], cc[2];  // candidate 64 x + lane: key (0: none), block
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          const uint32_t pk = 64 * x + lane < n_c ? lst_pk[wv][64 * x + lane] : 0u;
+          ck[x] = pk >> 16;
+          cc[x] = pk & 0xFFFFu;
+        }
+        uint32_t sig_u = 0;  // the kk-th largest key (sigma >= lb >= floor_key)
+#pragma unroll
+        for (int b = 15; b >= 0; --b) {
+          const uint32_t t = sig_u | (1u << b);
+          if (__popcll(__ballot(ck[0] >= t)) + __popcll(__ballot(ck[1] >= t)) >= kk) sig_u = t;
+        }
+        const int sig = (int)sig_u;
+        bool ti[2], mi[2];
+        uint64_t tm[2], mm[2];
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          const int v = (int)ck[x];
+          ti[x] = v > 0 && v > sig + kSelBand;
+          mi[x] = v > 0 && !ti[x] && v >= sig - kSelBand;
+          tm[x] = __ballot(ti[x]);
+          mm[x] = __ballot(mi[x]);
+        }
+        const int n_m = __popcll(mm[0]) + __popcll(mm[1]);
+        if (n_m <= 64) {
+          const int need = kk - (__popcll(tm[0]) + __popcll(tm[1]));
+          int me[2];  // the candidate's entry in the undecided list
+          me[0] = __popcll(mm[0] & lt_mask);
+          me[1] = __popcll(mm[0]) + __popcll(mm[1] & lt_mask);
+#pragma unroll
+          for (int x = 0; x < 2; ++x)
+            if (mi[x]) lst_c[wv][me[x]] = (int)cc[x];
+          const uint64_t pick = exact_pick(n_m, need);
+          int taken = 0;
+#pragma unroll
+          for (int x = 0; x < 2; ++x) {
+            const bool keep = ti[x] || (mi[x] && ((pick >> me[x]) & 1ull));
+            const uint64_t km = __ballot(keep);
+            const int pos = taken + __popcll(km & lt_mask);
+            if (keep && pos < kk) out[pos] = (int)cc[x];
+            taken += __popcll(km);
+          }
+          for (int i = kk + lane; i < k; i += 64) out[i] = -1;
+          done = true;
+        }
+      }
+    }
+    if (done) continue;
+
     uint32_t take_i = 0;  // bit j: block j * 64 + lane is kept
     if (kk > 0) {
-      // sigma: the kk-th largest stored value
-      uint32_t pre = 0, pm = 0;
-      int rem = kk;
-      radix_select_desc<NPL, uint32_t, 16>(akey, valid, kk, hist[wv], lane, pre, pm, rem);
-      uint32_t smin = 0xFFFFFFFFu;
+      // sigma: the kk-th largest stored value, the largest t with at least
+      // kk keys >= t, found bit by bit from the top with ballot counts (no
+      // LDS; invalid keys are 0 and valid ones at least 1)
+      uint32_t sig_u = 0;
 #pragma unroll
-      for (int j = 0; j < NPL; ++j)
-        if (((valid >> j) & 1u) && (akey[j] & pm) == pre) smin = min(smin, akey[j]);
+      for (int b = 15; b >= 0; --b) {
+        const uint32_t t = sig_u | (1u << b);
+        int cnt = 0;
 #pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) smin = min(smin, (uint32_t)__shfl_xor((int)smin, o));
-      const int sig = (int)smin;
+        for (int j = 0; j < NPL; ++j) cnt += __popcll(__ballot(akey[j] >= t));
+        if (cnt >= kk) sig_u = t;
+      }
+      const int sig = (int)sig_u;
       uint32_t in_m = 0;  // bit j: undecided
       int n_i = 0, n_m = 0;
 #pragma unroll
@@ -490,13 +626,7 @@ __global__ __launch_bounds__(64 * kSelWaves) void select_topk_kernel(const doubl
         n_m += __popcll(__ballot(mi));
       }
       const int need = kk - n_i;
-      const double* qrow = Qm + (int64_t)qb * D;
       if (n_m <= 64) {
-        // The undecided blocks, listed in index order, get their exact
-        // scores sixteen lanes each (lane part p sums d in [p D/16,
-        // (p+1) D/16) in order, then a fixed tree over the sixteen parts);
-        // then each is ranked against the others (higher score first, the
-        // lower index first among equal scores) and the best `need` kept.
         int base = 0;
 #pragma unroll
         for (int j = 0; j < NPL; ++j) {
@@ -507,47 +637,14 @@ __global__ __launch_bounds__(64 * kSelWaves) void select_topk_kernel(const doubl
           if (mj) lst_c[wv][base + __popcll(mm & lt_mask)] = c;
           base += __popcll(mm);
         }
-        chosen[wv][lane] = 0u;
-        wave_lds_sync();
-        constexpr int DP = D / 16;
-        const int e_in = lane >> 4, part = lane & 15;
-        for (int g0 = 0; g0 < n_m; g0 += 4) {
-          const int e = g0 + e_in;
-          const int c = e < n_m ? lst_c[wv][e] : 0;
-          const double* kp = Km + (int64_t)c * D + part * DP;
-          const double* qp = qrow + part * DP;
-          double kv[DP], qv[DP];
-#pragma unroll
-          for (int u = 0; u < DP; ++u) {
-            kv[u] = kp[u];
-            qv[u] = qp[u];
-          }
-          double acc = 0.0;
-#pragma unroll
-          for (int u = 0; u < DP; ++u) acc = fma(qv[u], kv[u], acc);
-          acc += __shfl_xor(acc, 1);
-          acc += __shfl_xor(acc, 2);
-          acc += __shfl_xor(acc, 4);
-          acc += __shfl_xor(acc, 8);
-          if (part == 0 && e < n_m) lst_key[wv][e] = order_key(acc);
-        }
-        wave_lds_sync();
-        const uint64_t mine = lane < n_m ? lst_key[wv][lane] : 0ull;
-        int rank = 0;
-        for (int i = 0; i < n_m; ++i) {
-          const uint64_t other = lst_key[wv][i];
-          rank += (other > mine || (other == mine && i < lane)) ? 1 : 0;
-        }
-        if (lane < n_m && rank < need) {
-          const int c = lst_c[wv][lane];
-          atomicOr(&chosen[wv][c >> 5], 1u << (c & 31));
-        }
-        wave_lds_sync();
+        const uint64_t pick = exact_pick(n_m, need);
+        base = 0;
 #pragma unroll
         for (int j = 0; j < NPL; ++j) {
-          int c = j * 64 + lane;
-          asm volatile("" : "+v"(c));
-          if (((in_m >> j) & 1u) && ((chosen[wv][c >> 5] >> (c & 31)) & 1u)) take_i |= 1u << j;
+          const bool mj = (in_m >> j) & 1u;
+          const uint64_t mm = __ballot(mj);
+          if (mj && ((pick >> (base + __popcll(mm & lt_mask))) & 1ull)) take_i |= 1u << j;
+          base += __popcll(mm);
         }
       } else {
         // Many undecided blocks (only near-constant inputs): each gets its
