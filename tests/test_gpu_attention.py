@@ -93,6 +93,29 @@ def test_block_select_wide_rows_all_tied():
         assert (idx == np.arange(k)[None, None, None, :]).all()
 
 
+def test_block_select_many_undecided_among_few_candidates():
+    # 100 identical key blocks (20..119) score far above the other 40, so a
+    # row has about 100 candidates near its k-th score, all of them
+    # undecided: more than 64, so the row leaves the compacted path for the
+    # full one, whose exact ranking keeps the lowest indices among the ties
+    cfg = WIDE
+    rng = np.random.default_rng(5)
+    u = rng.standard_normal(cfg.d).astype(np.float32)
+    u /= np.linalg.norm(u)
+    q = rng.standard_normal((1, cfg.L, cfg.H, cfg.d)).astype(np.float32) + 3.0 * u
+    kf = 0.01 * rng.standard_normal((1, cfg.L, cfg.H, cfg.d)).astype(np.float32)
+    kf[:, 20 * 64:120 * 64] = 5.0 * u
+    Qb, Kb = synthetic.f32_to_bf16_bits(q), synthetic.f32_to_bf16_bits(kf)
+    k = 36
+    idx = sd.sd_block_select(dev_bf16(Qb), dev_bf16(Kb), k, block_q=cfg.block_q, block_k=64).cpu().numpy()
+    assert (idx == np.arange(20, 20 + k)[None, None, None, :]).all()
+    for h in range(cfg.H):
+        S = oracle.block_scores(_f(Qb, 0, h), _f(Kb, 0, h), cfg.block_q, 64)
+        mism, ties, _ = block_map_diff(idx[0, h], S, k)
+        say(f"  head {h}: {mism} blocks differ, {ties} ties")
+        assert mism == 0
+
+
 def test_block_select_zero_query_block_and_dominant_key_block():
     # query block 3 is all zeros (its scores are all 0: the k lowest
     # indices); key block 5 is scaled by 2^8, so the largest key-block norm
