@@ -346,12 +346,12 @@ __global__ __launch_bounds__(BQ * 2, BQ == 128 ? kAttnMinWaves : 1) void attenti
     // alternate in every MFMA sequence (the two halves' S^T chains; the
     // channel tiles of O^T): no MFMA waits on the result of the one issued
     // just before it.
-    // Softmax of one 64-key block in the log2 domain, in two parts: the new
-    // reference maximum (moved lazily: only when a score exceeds it by more
-    // than 2^8, so P <= 256) and whether it moves; then, without touching O,
-    // the probabilities of each 32-key half as the two bf16 B operands of its
-    // PV products (keys 4hf + {0..3}, 8 + 4hf + {0..3} of each 16-key step)
-    // and their sum.
+    // Softmax of one 64-key block in the log2 domain, in two parts: the
+    // block's maximum and whether it moves the reference maximum (only when
+    // a score exceeds it by more than 8, i.e. P > 256); then, without
+    // touching O, the probabilities of each 32-key half as the two bf16 B
+    // operands of its PV products (keys 4hf + {0..3}, 8 + 4hf + {0..3} of
+    // each 16-key step) and their sum.
     auto block_max = [&](const f32x16& s0, const f32x16& s1, float& m_new) __attribute__((always_inline)) {
       // a v_max3 tree over the 32 scores (depth 4)
       float t[12];
@@ -388,24 +388,33 @@ __global__ __launch_bounds__(BQ * 2, BQ == 128 ? kAttnMinWaves : 1) void attenti
         mask_half(s0, key0, 0);
         mask_half(s1, key0, 1);
       }
-      // one running-maximum update for the block, then each half's
-      // probabilities and products (the second half's exponentials overlap
-      // the first half's MFMAs)
-      float m_new;
-      const bool up = block_max(s0, s1, m_new);
-      rescale(up, m_new, 0.f);
-      const float neg_m = m_new == -INFINITY ? 0.f : -m_new;
+      // The reference maximum m moves only when needed: the probabilities
+      // are formed against the current m, and only if a lane has no m yet
+      // or a block's row sum shows a score far above m (P up to 2^60 is
+      // harmless in bf16 and in the f32 sums) is the block's maximum taken,
+      // m moved and the probabilities formed again.
+      bf16x8 pa0, pb0, pa1, pb1;
       float rs = 0.f;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        bf16x8 pa, pb;
-        rs += half_exp(kt ? s1 : s0, neg_m, pa, pb);
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = mfma32(lds_v_operand<D>(Vs, lane, dt, 32 * kt), pa, oacc[dt]);
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-          oacc[dt] = mfma32(lds_v_operand<D>(Vs, lane, dt, 32 * kt + 16), pb, oacc[dt]);
+      bool redo = __ballot(m == -INFINITY) != 0;
+      if (!redo) {
+        rs = half_exp(s0, -m, pa0, pb0) + half_exp(s1, -m, pa1, pb1);
+        redo = __ballot(!(rs <= 0x1p60f)) != 0;
       }
+      if (redo) {
+        float m_new;
+        const bool up = block_max(s0, s1, m_new);
+        rescale(up, m_new, 0.f);
+        const float neg_m = m_new == -INFINITY ? 0.f : -m_new;
+        rs = half_exp(s0, neg_m, pa0, pb0) + half_exp(s1, neg_m, pa1, pb1);
+      }
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = mfma32(lds_v_operand<D>(Vs, lane, dt, 0), pa0, oacc[dt]);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = mfma32(lds_v_operand<D>(Vs, lane, dt, 16), pb0, oacc[dt]);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = mfma32(lds_v_operand<D>(Vs, lane, dt, 32), pa1, oacc[dt]);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = mfma32(lds_v_operand<D>(Vs, lane, dt, 48), pb1, oacc[dt]);
       lsum += rs;
     };
     auto compute = [&](const uint16_t* tile, int key0) __attribute__((always_inline)) {
