@@ -125,7 +125,8 @@ typedef struct sd_rope_pair {
  *  rope        HOST array of n_rope pairs (read during the call only); the
  *              pairs must not overlap; dims not in any pair are not rotated.
  *  rms_eps     epsilon of the RMSNorm of O_lr.
- *  rms_weight  device bf16 [d] RMSNorm weight, or NULL for ones. */
+ *  rms_weight  device bf16 [d] RMSNorm weight, 8-byte aligned (else
+ *              SD_ERR_ALIGN), or NULL for ones. */
 typedef struct sd_lowrank_params {
   int32_t rank;
   int32_t phi;

@@ -132,7 +132,7 @@ int check_lowrank(const sd_lowrank_params* lr, const Geo& g) {
     used |= bits;
   }
   if (!(lr->rms_eps >= 0.f) || !std::isfinite(lr->rms_eps)) return fail(SD_ERR_INVALID_ARG, "rms_eps invalid");
-  if (lr->rms_weight && !aligned(lr->rms_weight, 2)) return fail(SD_ERR_ALIGN, "rms_weight misaligned");
+  if (lr->rms_weight && !aligned(lr->rms_weight, 8)) return fail(SD_ERR_ALIGN, "rms_weight not 8-byte aligned");
   (void)g;
   return SD_OK;
 }

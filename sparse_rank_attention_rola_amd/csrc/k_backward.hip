@@ -94,11 +94,15 @@ __device__ __forceinline__ void load8_split(const float* p, bool ok, bf16x8& hi,
 // The cos/sin of the RoPE pairs a lane rotates in a wave's 32 x 33 patch
 // (lane l32 = token tok0 + l32; the two lane halves take alternate pairs),
 // loaded once at the start of a kernel so that their latency overlaps its
-// other loads; both rotations use them.
+// other loads; both rotations use them. With kConst the pair arguments are
+// read at constant indices and picked by lane half (no memory load and wait
+// for a lane-indexed argument read); the query side measured faster that
+// way, the key side slower, so each takes its own.
 struct RopeLane {
   float2 cs[kMaxRopePairs / 2];
 };
 
+template <bool kConst>
 __device__ __forceinline__ void rope_lane_load(RopeLane& rl, const float2* tab, const RopeArgs& rope, int Hg, int Wg,
                                                int tok0, int lane) {
   const int hf = lane >> 5, l32 = lane & 31;
@@ -110,7 +114,7 @@ __device__ __forceinline__ void rope_lane_load(RopeLane& rl, const float2* tab, 
     const int m = 2 * j + hf;
     rl.cs[j] = float2{1.f, 0.f};
     if (2 * j < rope.n && m < rope.n) {
-      const int axis = rope.axis[m];
+      const int axis = kConst ? (hf ? rope.axis[2 * j + 1] : rope.axis[2 * j]) : rope.axis[m];
       rl.cs[j] = tab[m * rope.max_ext + (axis == 0 ? pos[0] : axis == 1 ? pos[1] : pos[2])];
     }
   }
@@ -118,6 +122,7 @@ __device__ __forceinline__ void rope_lane_load(RopeLane& rl, const float2* tab, 
 
 // Rotates the RoPE pairs of the patch by +angle (dir = 1) or by -angle
 // (dir = -1, the transpose).
+template <bool kConst>
 __device__ __forceinline__ void rope_patch(float* F, const RopeLane& rl, const RopeArgs& rope, int lane, int dir) {
   const int hf = lane >> 5, l32 = lane & 31;
 #pragma unroll
@@ -126,7 +131,7 @@ __device__ __forceinline__ void rope_patch(float* F, const RopeLane& rl, const R
     if (2 * j < rope.n && m < rope.n) {
       const float2 cs = rl.cs[j];
       const float sn = dir > 0 ? cs.y : -cs.y;
-      float* f = F + l32 * 33 + rope.dim[m];
+      float* f = F + l32 * 33 + (kConst ? (hf ? rope.dim[2 * j + 1] : rope.dim[2 * j]) : rope.dim[m]);
       const float u = f[0], v = f[1];
       f[0] = u * cs.x - v * sn;
       f[1] = u * sn + v * cs.x;
@@ -138,7 +143,7 @@ __device__ __forceinline__ void rope_patch(float* F, const RopeLane& rl, const R
 // Query side of the low-rank branch, gate and RMS coupling.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, 2) void bwd_query_kernel(BwdArgs a) {
   __shared__ float Fw[4][32 * 33];
   __shared__ float Fa[4][32 * 33];
   int64_t bh;
@@ -159,21 +164,7 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
   float* fa = Fa[wv];
   const int64_t row = ((int64_t)b * a.L + q_cl) * a.H + h;
   RopeLane rl;
-  rope_lane_load(rl, a.rope_tab, a.rope, a.Hg, a.Wg, tok0, lane);
-  // dO, O_s (their 4-channel groups in the accumulator layout), the RMS and
-  // the gate do not depend on the steps before they are used: loaded here,
-  // with the first loads, instead of after two barriers
-  const uint16_t* dop = a.dO + (int64_t)b * a.so_b + (int64_t)q_cl * a.so_l + (int64_t)h * a.so_h;
-  const uint16_t* osp = a.Os + row * D;
-  u32x2 do2[D / 32][4], os2[D / 32][4];
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-      const int c0 = och(dt, 4 * rg, hf);
-      do2[dt][rg] = q_ok ? *reinterpret_cast<const u32x2*>(dop + c0) : u32x2{0, 0};
-      os2[dt][rg] = q_ok ? *reinterpret_cast<const u32x2*>(osp + c0) : u32x2{0, 0};
-    }
+  rope_lane_load<true>(rl, a.rope_tab, a.rope, a.Hg, a.Wg, tok0, lane);
   const float rr = q_ok ? a.rms[row] : 0.f;
   const float gv = q_ok ? a.g[(int64_t)b * a.g_sb + (int64_t)q_cl * a.g_sl + (int64_t)h * a.g_sh] : 0.f;
 
@@ -203,7 +194,7 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
     }
   }
   __syncthreads();
-  rope_patch(fw, rl, a.rope, lane, 1);
+  rope_patch<true>(fw, rl, a.rope, lane, 1);
   __syncthreads();
   bf16x8 qhi[2], qlo[2];
 #pragma unroll
@@ -225,23 +216,26 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
   for (int c = c_first; c <= c_last; ++c) {
     const int64_t cbase = (bh * n_ar + c) * D * 32;
     const bool mine = q_chunk == c;
-    u32x4 cth[D / 32][2], ctl[D / 32][2];
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+    // one channel tile of the state at a time, the next one loading while
+    // the current one is used
+    u32x4 cth[2][2], ctl[2][2];
+    auto load_ct = [&](int dt, u32x4 (&th)[2], u32x4 (&tl)[2]) __attribute__((always_inline)) {
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const int64_t off = cbase + (int64_t)(32 * dt + l32) * 32 + 16 * s + 8 * hf;
-        cth[dt][s] = *reinterpret_cast<const u32x4*>(a.Ct_hi + off);
-        ctl[dt][s] = *reinterpret_cast<const u32x4*>(a.Ct_lo + off);
+        th[s] = *reinterpret_cast<const u32x4*>(a.Ct_hi + off);
+        tl[s] = *reinterpret_cast<const u32x4*>(a.Ct_lo + off);
       }
-    __builtin_amdgcn_sched_barrier(0);
+    };
+    load_ct(0, cth[0], ctl[0]);
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
+      if (dt + 1 < D / 32) load_ct(dt + 1, cth[(dt + 1) & 1], ctl[(dt + 1) & 1]);
       f32x16 y = {};
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const bf16x8 ch = as_bf16x8(cth[dt][s]);
-        const bf16x8 cl = as_bf16x8(ctl[dt][s]);
+        const bf16x8 ch = as_bf16x8(cth[dt & 1][s]);
+        const bf16x8 cl = as_bf16x8(ctl[dt & 1][s]);
         y = mfma32(ch, qhi[s], y);
         y = mfma32(cl, qhi[s], y);
         y = mfma32(ch, qlo[s], y);
@@ -251,7 +245,31 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
     }
   }
 
-  // 3. RMSNorm, gate and RMS coupling, per query (lane pair)
+  // 3. RMSNorm, gate and RMS coupling, per query (lane pair); dO and O_s
+  // (their 4-channel groups in the accumulator layout) are loaded here
+  const uint16_t* dop = a.dO + (int64_t)b * a.so_b + (int64_t)q_cl * a.so_l + (int64_t)h * a.so_h;
+  const uint16_t* osp = a.Os + row * D;
+  u32x2 do2[D / 32][4], os2[D / 32][4], w2[D / 32][4];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const int c0 = och(dt, 4 * rg, hf);
+      do2[dt][rg] = q_ok ? *reinterpret_cast<const u32x2*>(dop + c0) : u32x2{0, 0};
+      os2[dt][rg] = q_ok ? *reinterpret_cast<const u32x2*>(osp + c0) : u32x2{0, 0};
+      w2[dt][rg] = a.rmsw ? *reinterpret_cast<const u32x2*>(a.rmsw + c0) : u32x2{0x3F803F80u, 0x3F803F80u};
+    }
+  // the packed values are opaque to the compiler between the loops below, so
+  // each loop unpacks them again instead of keeping 64 unpacked floats live
+  auto reopen = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        asm volatile("" : "+v"(do2[dt][rg]));
+        asm volatile("" : "+v"(w2[dt][rg]));
+      }
+  };
   float ss = 0.f;
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
@@ -259,22 +277,21 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
     for (int r = 0; r < 16; ++r) ss += yv[dt][r] * yv[dt][r];
   ss += partner32(ss, hf);
   const float inv = rsqrtf(ss * (1.0f / D) + a.eps);
-  f32x16 dov[D / 32], osv[D / 32];
+  // dO and O_s stay packed (bf16 pairs) and are unpacked where used, so
+  // that no f32 copy of them is live beside y
+  auto unpack = [&](const u32x2& v2, int e) __attribute__((always_inline)) {
+    return (e & 1) ? bf16_hi(v2[e >> 1]) : bf16_lo(v2[e >> 1]);
+  };
   float t = 0.f;
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int rg = 0; rg < 4; ++rg) {
       const int c0 = och(dt, 4 * rg, hf);
-      const u32x2 d2 = do2[dt][rg];
-      const u32x2 o2 = os2[dt][rg];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * rg + e;
-        dov[dt][r] = (e & 1) ? bf16_hi(d2[e >> 1]) : bf16_lo(d2[e >> 1]);
-        osv[dt][r] = (e & 1) ? bf16_hi(o2[e >> 1]) : bf16_lo(o2[e >> 1]);
-        const float w = a.rmsw ? bf16_bits_to_f32(a.rmsw[c0 + e]) : 1.f;
-        t += dov[dt][r] * w * yv[dt][r] * inv;
+        t += unpack(do2[dt][rg], e) * unpack(w2[dt][rg], e) * yv[dt][r] * inv;
       }
     }
   t += partner32(t, hf);
@@ -282,6 +299,7 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
   const float coef = rr > 0.f ? gv * t / ((float)D * rr) : 0.f;
   const float gr = gv * rr;
   float dsum = 0.f, uy = 0.f;
+  reopen();
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -291,12 +309,11 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * rg + e;
-        const float v = fmaf(coef, osv[dt][r], dov[dt][r]);
+        const float dov = unpack(do2[dt][rg], e), osv = unpack(os2[dt][rg], e);
+        const float v = fmaf(coef, osv, dov);
         dsv[e] = bf16_bits_to_f32(f32_to_bf16_bits(v));
-        dsum += dsv[e] * osv[dt][r];
-        const float w = a.rmsw ? bf16_bits_to_f32(a.rmsw[c0 + e]) : 1.f;
-        dov[dt][r] = w * gr * dov[dt][r];  // u
-        uy += dov[dt][r] * yv[dt][r];
+        dsum += dsv[e] * osv;
+        uy += unpack(w2[dt][rg], e) * gr * dov * yv[dt][r];  // u y
       }
       if (q_ok) {
         u32x2 o;
@@ -309,10 +326,17 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
   uy += partner32(uy, hf);
   if (q_ok && hf == 0) a.Dd[bh * a.L + q_cl] = dsum;
   const float k3 = uy * inv * inv * inv * (1.0f / D);
+  reopen();
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) yv[dt][r] = dov[dt][r] * inv - yv[dt][r] * k3;  // dy
+    for (int rg = 0; rg < 4; ++rg)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * rg + e;
+        const float u = unpack(w2[dt][rg], e) * gr * unpack(do2[dt][rg], e);
+        yv[dt][r] = u * inv - yv[dt][r] * k3;  // dy
+      }
 #pragma unroll
     for (int rg = 0; rg < 4; ++rg)
       if (q_ok)
@@ -345,12 +369,18 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
     for (int r = 0; r < 16; ++r) dq[r] = (c == c_first || mine) ? acc[r] : dq[r];
   }
 
-  // 5. da = R^T dq~ * phi'(a)
+  // 5. da = R^T dq~ * phi'(a); the rotation is read again here rather than
+  // held in registers through phases 2-4 (from opaque copies of the lane and
+  // grid sizes, so that the compiler does not keep the first call's
+  // divisions and masks instead)
+  int lane5 = lane, hg = a.Hg, wg = a.Wg;
+  asm volatile("" : "+v"(lane5), "+s"(hg), "+s"(wg));
+  rope_lane_load<true>(rl, a.rope_tab, a.rope, hg, wg, tok0, lane5);
   __syncthreads();  // every wave is done reading q~ from its patch
 #pragma unroll
   for (int r = 0; r < 16; ++r) fw[l32 * 33 + 8 * (r >> 2) + 4 * hf + (r & 3)] = dq[r];
   __syncthreads();
-  rope_patch(fw, rl, a.rope, lane, -1);
+  rope_patch<true>(fw, rl, a.rope, lane5, -1);
   __syncthreads();
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
@@ -583,7 +613,7 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
   float* fa = Fa[wv];
   const int64_t row = ((int64_t)b * a.L + k_cl) * a.H + h;
   RopeLane rl;
-  rope_lane_load(rl, a.rope_tab, a.rope, a.Hg, a.Wg, tok0, lane);
+  rope_lane_load<false>(rl, a.rope_tab, a.rope, a.Hg, a.Wg, tok0, lane);
 
   // 1. b = P_k kn (pre-phi in Fa), k~ = R phi(b) (in Fw)
   {
@@ -608,7 +638,7 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
     }
   }
   __syncthreads();
-  rope_patch(fw, rl, a.rope, lane, 1);
+  rope_patch<false>(fw, rl, a.rope, lane, 1);
   __syncthreads();
   bf16x8 khi[2], klo[2];
 #pragma unroll
@@ -678,7 +708,7 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) fw[l32 * 33 + 8 * (r >> 2) + 4 * hf + (r & 3)] = dk[r];
   __syncthreads();
-  rope_patch(fw, rl, a.rope, lane, -1);
+  rope_patch<false>(fw, rl, a.rope, lane, -1);
   __syncthreads();
 #pragma unroll
   for (int r = 0; r < 16; ++r) {

@@ -70,11 +70,11 @@ def _shape(**kw):
     return s
 
 
-def _lr(rank=16, pairs=None, eps=1e-6, phi=1):
+def _lr(rank=16, pairs=None, eps=1e-6, phi=1, rms_weight=None):
     pairs = pairs if pairs is not None else sd.sd_rope_default(rank)
     arr = (sd.sd_rope_pair * max(1, len(pairs)))(*[sd.sd_rope_pair(d, a, t) for d, a, t in pairs])
     p = sd.sd_lowrank_params(rank, phi, FAKE, FAKE, 0, ctypes.cast(arr, ctypes.POINTER(sd.sd_rope_pair)),
-                             len(pairs), eps, None)
+                             len(pairs), eps, rms_weight)
     return p, arr
 
 
@@ -142,6 +142,7 @@ def test_lowrank_validation():
     assert call(lr=_lr(pairs=[(0, 3, 1.0)])) == sd.SD_ERR_INVALID_ARG  # bad axis
     assert call(lr=_lr(pairs=[(0, 0, 1.0), (1, 1, 1.0)])) == sd.SD_ERR_INVALID_ARG  # overlap
     assert call(lr=_lr(eps=-1.0)) == sd.SD_ERR_INVALID_ARG
+    assert call(lr=_lr(rms_weight=FAKE + 2)) == sd.SD_ERR_ALIGN  # the weight is read 4 channels at a time
     assert call(dt=0) == sd.SD_ERR_INVALID_ARG
     need = lib.sd_lowrank_workspace_size(ctypes.byref(s), ctypes.byref(_lr()[0]))
     assert need > 0

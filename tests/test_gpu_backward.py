@@ -46,7 +46,8 @@ def _rel(got, ref, name, rel_l2=2.0 ** -7, max_frac=2.0 ** -6):
     assert rl <= rel_l2 and ma <= max_frac, f"{name}: rel_l2 {rl:.3e}, max {ma:.3e}"
 
 
-def _run(cfg, seed=0, chunk_frames=0, window=0, separate_qk=False, per_head_gate=False, batch_shared_gate=False):
+def _run(cfg, seed=0, chunk_frames=0, window=0, separate_qk=False, per_head_gate=False, batch_shared_gate=False,
+         rms_weight=False):
     Qb, Kb, Vb = synthetic.gen_qkv(cfg, seed)
     Pqb, Pkb = synthetic.gen_lowrank_params(cfg)
     rng = np.random.default_rng(seed + 100)
@@ -66,7 +67,8 @@ def _run(cfg, seed=0, chunk_frames=0, window=0, separate_qk=False, per_head_gate
     Q, K, V, dO = dev_bf16(Qb), dev_bf16(Kb), dev_bf16(Vb), dev_bf16(dOb)
     Qn = dev_bf16(Qnb) if separate_qk else None
     Kn = dev_bf16(Knb) if separate_qk else None
-    lr = sd.LowrankParams(dev_bf16(Pqb), dev_bf16(Pkb))
+    wb = synthetic.gen_norm_weight(cfg.d, seed) if rms_weight else None
+    lr = sd.LowrankParams(dev_bf16(Pqb), dev_bf16(Pkb), rms_weight=dev_bf16(wb) if rms_weight else None)
     k = oracle.keep_count(cfg.sparsity, -(-cfg.L // cfg.block_k))
     nq = -(-cfg.L // cfg.block_q)
     idx = torch.empty((cfg.B, cfg.H, nq, k), dtype=torch.int32, device="cuda")
@@ -87,7 +89,8 @@ def _run(cfg, seed=0, chunk_frames=0, window=0, separate_qk=False, per_head_gate
             gh = (g[b, :, h] if per_head_gate else g[b]).astype(np.float64)
             res = oracle.rola_backward_head(*X, *Xn, Pq, Pk, gh, idx[b, h], f(dOb[b, :, h]), T=cfg.T, Hg=cfg.Hg,
                                             Wg=cfg.Wg, bq=cfg.block_q, bk=cfg.block_k,
-                                            sm_scale=1.0 / math.sqrt(cfg.d), chunk_tokens=ct, window=window)
+                                            sm_scale=1.0 / math.sqrt(cfg.d), chunk_tokens=ct, window=window,
+                                            gamma=f(wb) if rms_weight else None)
             dQ, dK = res["dQ"], res["dK"]
             if separate_qk:
                 _rel(got["dQn"][b, :, h], res["dQn"], f"dQn b{b} h{h}")
@@ -124,6 +127,14 @@ def test_backward_gate_shared_by_the_batch():
     # two batch elements' gradients instead of keeping one of them
     say("backward ragged-d64, gate broadcast over the batch")
     _run(RAGGED64, seed=4, batch_shared_gate=True)
+
+
+@pytest.mark.parametrize("cfg", [RAGGED, RAGGED64], ids=lambda c: c.name)
+def test_backward_rms_weight(cfg):
+    # a non-trivial RMSNorm weight on the low-rank output: it enters dg, dy
+    # and the RMS coupling term of dO_s
+    say(f"backward {cfg.name} with an RMSNorm weight")
+    _run(cfg, seed=6, rms_weight=True)
 
 
 def test_backward_separate_qk_and_per_head_gate():
