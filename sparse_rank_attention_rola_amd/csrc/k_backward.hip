@@ -548,16 +548,28 @@ __global__ __launch_bounds__(256) void dproj_finalize_kernel(const float* __rest
     const int64_t bh0 = u0 / n_runs;
     int hh = (int)(bh0 % hs), b = (int)(bh0 / hs);
     const float* pr = part + (int64_t)r * D + d;
-    for (int64_t u = u0; u < u1; ++u) {
-      const int h = per_head ? o : hh;
-      s += pr[(((int64_t)b * H + h) * n_runs + run) * 32 * D];
-      if (++run == n_runs) {
-        run = 0;
-        if (++hh == hs) {
-          hh = 0;
-          ++b;
+    // 8 terms loaded before they are added (in the same order), so that 8
+    // loads are in flight instead of one
+    for (int64_t u = u0; u < u1; u += 8) {
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        v[j] = 0.f;
+        if (u + j < u1) {
+          const int h = per_head ? o : hh;
+          v[j] = pr[(((int64_t)b * H + h) * n_runs + run) * 32 * D];
+          if (++run == n_runs) {
+            run = 0;
+            if (++hh == hs) {
+              hh = 0;
+              ++b;
+            }
+          }
         }
       }
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (u + j < u1) s += v[j];
     }
   }
   q4[qt][threadIdx.x & 63] = s;
