@@ -44,6 +44,7 @@
 #include "sd_device.h"
 #include "sd_launch.h"
 #include "sd_tiles.h"
+#include "sd_reduce.h"
 
 namespace sd {
 
@@ -515,8 +516,7 @@ __global__ void dstate_finalize_kernel(const float* __restrict__ part, int64_t B
   const int64_t bh = bc / n_ar;
   const int last = window > 0 ? min(n_ar - 1, c + window - 1) : n_ar - 1;
   const float* p = part + (bh * runs.n_runs * 32 + r) * D + d;
-  float s = 0.f;
-  for (int u = c * runs.runs_per_ar; u < (last + 1) * runs.runs_per_ar; ++u) s += p[(int64_t)u * 32 * D];
+  const float s = strided_sum_in_order(p, 32 * D, c * runs.runs_per_ar, (last + 1) * runs.runs_per_ar);
   dC[(bc * 32 + r) * D + d] = s;
   const __bf16 hi = (__bf16)s;
   const __bf16 lo = (__bf16)(s - (float)hi);

@@ -21,6 +21,7 @@
 #include "sd_device.h"
 #include "sd_launch.h"
 #include "sd_tiles.h"
+#include "sd_reduce.h"
 
 namespace sd {
 
@@ -140,7 +141,7 @@ __global__ void lowrank_finalize_kernel(const float* __restrict__ partial, int64
   if (row >= 0) {
     const int c0 = window > 0 ? max(0, c - window + 1) : 0;
     const float* p = partial + (bh * runs.n_runs * 32 + row) * D + d;
-    for (int u = c0 * runs.runs_per_ar; u < (c + 1) * runs.runs_per_ar; ++u) s += p[(int64_t)u * 32 * D];
+    s = strided_sum_in_order(p, 32 * D, c0 * runs.runs_per_ar, (c + 1) * runs.runs_per_ar);
   }
   if (C_out && r < rank) C_out[(bc * rank + r) * D + d] = s;
   const __bf16 hi = (__bf16)s;
