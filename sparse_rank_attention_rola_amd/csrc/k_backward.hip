@@ -773,44 +773,74 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // Key block -> the query blocks that keep it (ascending), per (batch, head).
+// A counting sort in 8 slices of query-block rows, one wave each: per-slice
+// counts, offsets (each key block's list start, plus the counts of the
+// earlier slices), then each wave lists its rows in order. Lists come out
+// ascending, and the result does not depend on timing.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void transpose_map_kernel(const int32_t* __restrict__ idx, int Nq, int Nk, int k,
-                                                            int32_t* __restrict__ tlist, int32_t* __restrict__ toff) {
-  __shared__ int cnt[kMaxKeep + 1];
+constexpr int kTmWaves = 8;
+__global__ __launch_bounds__(64 * kTmWaves) void transpose_map_kernel(const int32_t* __restrict__ idx, int Nq, int Nk,
+                                                                     int k, int32_t* __restrict__ tlist,
+                                                                     int32_t* __restrict__ toff) {
+  __shared__ int cnt[kTmWaves][kMaxKeep + 1];
+  __shared__ int wsum[kTmWaves];
   const int64_t bh = blockIdx.x;
   const int32_t* row0 = idx + bh * (int64_t)Nq * k;
-  const int tid = threadIdx.x;
-  for (int c = tid; c <= Nk; c += 256) cnt[c] = 0;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  constexpr int NT = 64 * kTmWaves;
+  const int r0 = (int)((int64_t)Nq * wv / kTmWaves), r1 = (int)((int64_t)Nq * (wv + 1) / kTmWaves);
+  for (int w = 0; w < kTmWaves; ++w)
+    for (int c = tid; c <= Nk; c += NT) cnt[w][c] = 0;
   __syncthreads();
-  for (int64_t i = tid; i < (int64_t)Nq * k; i += 256) {
-    const int c = row0[i];
-    if ((unsigned)c < (unsigned)Nk) atomicAdd(&cnt[c], 1);
+  // 1. counts of the wave's slice
+  for (int64_t e = (int64_t)r0 * k + lane; e < (int64_t)r1 * k; e += 64) {
+    const int c = row0[e];
+    if ((unsigned)c < (unsigned)Nk) atomicAdd(&cnt[wv][c], 1);
   }
   __syncthreads();
-  if (tid == 0) {  // exclusive prefix sum, in place
-    int run = 0;
-    for (int c = 0; c < Nk; ++c) {
-      const int v = cnt[c];
-      cnt[c] = run;
-      run += v;
+  // 2. offsets: thread t takes the key blocks [t S, (t + 1) S); an exclusive
+  // scan of the segments' totals over the threads gives each segment's start
+  const int S = (Nk + NT - 1) / NT;
+  const int c0 = min(Nk, tid * S), c1 = min(Nk, c0 + S);
+  int seg = 0;
+  for (int c = c0; c < c1; ++c)
+    for (int w = 0; w < kTmWaves; ++w) seg += cnt[w][c];
+  int incl = seg;  // inclusive scan within the wave
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) wsum[wv] = incl;
+  __syncthreads();
+  int run = incl - seg;
+  for (int w = 0; w < wv; ++w) run += wsum[w];
+  for (int c = c0; c < c1; ++c) {
+    toff[bh * (Nk + 1) + c] = run;
+    for (int w = 0; w < kTmWaves; ++w) {
+      const int n = cnt[w][c];
+      cnt[w][c] = run;
+      run += n;
     }
-    cnt[Nk] = run;
+  }
+  if (tid == NT - 1) {
+    int total = 0;
+    for (int w = 0; w < kTmWaves; ++w) total += wsum[w];
+    toff[bh * (Nk + 1) + Nk] = total;
   }
   __syncthreads();
-  for (int c = tid; c <= Nk; c += 256) toff[bh * (Nk + 1) + c] = cnt[c];
-  __syncthreads();
-  // fill in query-block order, one row per step of the first wave
+  // 3. each wave lists its slice's rows in order (a row keeps a key block at
+  // most once, so one row's atomics never meet on one counter)
   int32_t* out = tlist + bh * (int64_t)Nq * k;
-  if (tid < 64) {
-    for (int qb = 0; qb < Nq; ++qb) {
-      for (int j = tid; j < k; j += 64) {
-        const int c = row0[(int64_t)qb * k + j];
-        if ((unsigned)c < (unsigned)Nk) out[atomicAdd(&cnt[c], 1)] = qb;
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  for (int qb = r0; qb < r1; ++qb) {
+    for (int jj = lane; jj < k; jj += 64) {
+      const int c = row0[(int64_t)qb * k + jj];
+      if ((unsigned)c < (unsigned)Nk) out[atomicAdd(&cnt[wv][c], 1)] = qb;
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 }
 
@@ -1150,7 +1180,8 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, int D, hipStream_t stream) {
 
 hipError_t launch_transpose_map(const int32_t* idx, int BH, int Nq, int Nk, int k, int32_t* tlist, int32_t* toff,
                                 hipStream_t stream) {
-  hipLaunchKernelGGL(transpose_map_kernel, dim3(BH), dim3(256), 0, stream, idx, Nq, Nk, k, tlist, toff);
+  if (Nk > kMaxKeep) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(transpose_map_kernel, dim3(BH), dim3(64 * kTmWaves), 0, stream, idx, Nq, Nk, k, tlist, toff);
   return hipGetLastError();
 }
 
