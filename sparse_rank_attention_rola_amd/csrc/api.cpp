@@ -1081,7 +1081,7 @@ struct BwdWs {
   uint16_t *dCt_hi, *dCt_lo;
   float* dP_part;
   sd::RunGeo dP_runs;
-  int32_t *tlist, *toff;
+  int32_t *tlist, *toff, *korder;
   size_t bytes;
 };
 
@@ -1114,6 +1114,7 @@ BwdWs carve_bwd(void* ws, const Geo& g, const sd_attn_shape* shape, const sd_low
   w.dP_part = static_cast<float*>(c.take(sizeof(float) * BH * w.dP_runs.n_runs * 32 * g.D));
   w.tlist = static_cast<int32_t*>(c.take(sizeof(int32_t) * BH * g.Nq * (size_t)k_keep));
   w.toff = static_cast<int32_t*>(c.take(sizeof(int32_t) * BH * (g.Nk + 1)));
+  w.korder = static_cast<int32_t*>(c.take(sizeof(int32_t) * BH * g.Nk));
   (void)lr;
   w.bytes = align_up(c.off);
   return w;
@@ -1263,6 +1264,7 @@ int sd_rola_backward(const sd_attn_shape* shape, const sd_lowrank_params* lr, co
   b.dCt_lo = w.dCt_lo;
   b.tlist = w.tlist;
   b.toff = w.toff;
+  b.korder = w.korder;
   b.dQ = dQ;
   b.dK = dK;
   b.dV = dV;
@@ -1289,7 +1291,7 @@ int sd_rola_backward(const sd_attn_shape* shape, const sd_lowrank_params* lr, co
       return hip_fail(e, "dPq finalize");
   }
   // softmax branch
-  if ((e = sd::launch_transpose_map(idx, BH, g.Nq, g.Nk, k_keep, w.tlist, w.toff, st)) != hipSuccess)
+  if ((e = sd::launch_transpose_map(idx, BH, g.Nq, g.Nk, k_keep, w.tlist, w.toff, w.korder, st)) != hipSuccess)
     return hip_fail(e, "map transpose");
   if ((e = sd::launch_bwd_dq(b, g.D, st)) != hipSuccess) return hip_fail(e, "backward dQ");
   if ((e = sd::launch_bwd_dkdv(b, g.D, st)) != hipSuccess) return hip_fail(e, "backward dK, dV");

@@ -39,7 +39,8 @@
 //   bwd_dkdv_kernel     per key block (K, V staged in LDS once), over the
 //                       query blocks that keep it: S = Q K^T, dP = dO_s V^T,
 //                       dV^T += dO_s^T P and dK^T += Q^T dS (transposing
-//                       reads of the staged Q and dO_s tiles).
+//                       reads of the staged Q and dO_s tiles); each head's
+//                       key blocks launched longest query list first.
 // Every sum runs in a fixed order: the results are bitwise reproducible.
 #include "sd_device.h"
 #include "sd_launch.h"
@@ -777,13 +778,20 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
 // counts, offsets (each key block's list start, plus the counts of the
 // earlier slices), then each wave lists its rows in order. Lists come out
 // ascending, and the result does not depend on timing.
+// Also the head's key blocks ordered by their number of query blocks, the
+// largest first (the dK/dV launch takes them in that order, so the longest
+// lists start first and the short ones fill the end; which order equal
+// counts take only moves work between compute units, not any result).
 // ---------------------------------------------------------------------------
 constexpr int kTmWaves = 8;
 __global__ __launch_bounds__(64 * kTmWaves) void transpose_map_kernel(const int32_t* __restrict__ idx, int Nq, int Nk,
                                                                      int k, int32_t* __restrict__ tlist,
-                                                                     int32_t* __restrict__ toff) {
+                                                                     int32_t* __restrict__ toff,
+                                                                     int32_t* __restrict__ korder) {
   __shared__ int cnt[kTmWaves][kMaxKeep + 1];
   __shared__ int wsum[kTmWaves];
+  __shared__ int kdeg[kMaxKeep];      // query blocks per key block
+  __shared__ int dstart[kMaxKeep + 2];  // per count: the first slot of its key blocks
   const int64_t bh = blockIdx.x;
   const int32_t* row0 = idx + bh * (int64_t)Nq * k;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -818,17 +826,43 @@ __global__ __launch_bounds__(64 * kTmWaves) void transpose_map_kernel(const int3
   for (int w = 0; w < wv; ++w) run += wsum[w];
   for (int c = c0; c < c1; ++c) {
     toff[bh * (Nk + 1) + c] = run;
+    const int first = run;
     for (int w = 0; w < kTmWaves; ++w) {
       const int n = cnt[w][c];
       cnt[w][c] = run;
       run += n;
     }
+    kdeg[c] = run - first;
   }
+  for (int d = tid; d <= Nq + 1; d += NT) dstart[d] = 0;
   if (tid == NT - 1) {
     int total = 0;
     for (int w = 0; w < kTmWaves; ++w) total += wsum[w];
     toff[bh * (Nk + 1) + Nk] = total;
   }
+  __syncthreads();
+  // key blocks by count, the largest first: a bucket per count, the buckets
+  // laid out from the largest count down (Nq fits one pass of 512 lanes
+  // for the bucket starts, summed from the top)
+  for (int c = tid; c < Nk; c += NT) atomicAdd(&dstart[Nq - min(kdeg[c], Nq)], 1);
+  __syncthreads();
+  if (wv == 0) {  // exclusive scan over the buckets (count Nq first)
+    int base = 0;
+    for (int d0 = 0; d0 <= Nq; d0 += 64) {
+      const int d = d0 + lane;
+      const int v = d <= Nq ? dstart[d] : 0;
+      int inc = v;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(inc, o);
+        if (lane >= o) inc += u;
+      }
+      if (d <= Nq) dstart[d] = base + inc - v;
+      base += __shfl(inc, 63);
+    }
+  }
+  __syncthreads();
+  for (int c = tid; c < Nk; c += NT) korder[bh * Nk + atomicAdd(&dstart[Nq - min(kdeg[c], Nq)], 1)] = c;
   __syncthreads();
   // 3. each wave lists its slice's rows in order (a row keeps a key block at
   // most once, so one row's atomics never meet on one counter)
@@ -998,7 +1032,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float rowv[2][64];        // lse, D of the unit
   int64_t bh;
   int kb;
-  if (!xcd_group_item(blockIdx.x, a.Nk, (int64_t)a.B * a.H, bh, kb)) return;
+  // the head's key blocks in the order of korder (the longest query lists
+  // first); consecutive workgroups go to consecutive XCDs
+  {
+    const int64_t n = blockIdx.x;
+    bh = n / a.Nk;
+    kb = a.korder[n];
+  }
   const int h = (int)(bh % a.H), b = (int)(bh / a.H);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1164,7 +1204,7 @@ hipError_t launch_bwd_dq(const BwdArgs& a, int D, hipStream_t stream) {
 }
 
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int D, hipStream_t stream) {
-  const dim3 grid((unsigned)group_grid(a.Nk, (int64_t)a.B * a.H));
+  const dim3 grid((unsigned)((int64_t)a.Nk * a.B * a.H));
   if (D == 128 && a.block_q == 128)
     hipLaunchKernelGGL((bwd_dkdv_kernel<128, 128>), grid, dim3(256), 0, stream, a);
   else if (D == 128 && a.block_q == 64)
@@ -1179,9 +1219,11 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, int D, hipStream_t stream) {
 }
 
 hipError_t launch_transpose_map(const int32_t* idx, int BH, int Nq, int Nk, int k, int32_t* tlist, int32_t* toff,
+                                int32_t* korder,
                                 hipStream_t stream) {
   if (Nk > kMaxKeep) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(transpose_map_kernel, dim3(BH), dim3(64 * kTmWaves), 0, stream, idx, Nq, Nk, k, tlist, toff);
+  hipLaunchKernelGGL(transpose_map_kernel, dim3(BH), dim3(64 * kTmWaves), 0, stream, idx, Nq, Nk, k, tlist, toff,
+                     korder);
   return hipGetLastError();
 }
 

@@ -242,6 +242,7 @@ struct BwdArgs {
   // key-block -> query-block lists
   const int32_t* tlist;  // [B*H, Nq*kkeep]
   const int32_t* toff;   // [B*H, Nk + 1]
+  const int32_t* korder; // [B*H, Nk]: each head's key blocks, the most kept first
   // outputs, f32 [B, L, H, D]
   float* dQ;
   float* dK;
@@ -255,6 +256,7 @@ hipError_t launch_bwd_key(const BwdArgs& a, int D, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, int D, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int D, hipStream_t stream);
 hipError_t launch_transpose_map(const int32_t* idx, int BH, int Nq, int Nk, int k, int32_t* tlist, int32_t* toff,
+                                int32_t* korder,
                                 hipStream_t stream);
 // Partial sums over runs of tokens of X^T Y, X [rows][32] f32 (contiguous,
 // row = token*H + head), Y [rows][D] (f32 contiguous when Yf, else bf16 at
