@@ -1102,7 +1102,7 @@ BwdWs carve_bwd(void* ws, const Geo& g, const sd_attn_shape* shape, const sd_low
   w.db = static_cast<float*>(c.take(sizeof(float) * rows * 32));
   w.dQn_tmp = static_cast<float*>(c.take(sizeof(float) * rows * g.D));
   w.dOs = static_cast<uint16_t*>(c.take(sizeof(uint16_t) * rows * g.D));
-  w.dC_runs = make_runs(g, 2048, 1);
+  w.dC_runs = make_runs(g, kPrepareSlots, 1);
   w.dC_part = static_cast<float*>(c.take(sizeof(float) * BH * w.dC_runs.n_runs * 32 * g.D));
   w.dC = static_cast<float*>(c.take(sizeof(float) * BH * g.n_ar * 32 * g.D));
   w.dCt_hi = static_cast<uint16_t*>(c.take(sizeof(uint16_t) * BH * g.n_ar * g.D * 32));
@@ -1110,7 +1110,7 @@ BwdWs carve_bwd(void* ws, const Geo& g, const sd_attn_shape* shape, const sd_low
   Geo whole = g;  // one run set over the whole sequence for the projection gradients
   whole.n_ar = 1;
   whole.ar = g.L;
-  w.dP_runs = make_runs(whole, 2048, 1);
+  w.dP_runs = make_runs(whole, kPrepareSlots, 1);
   w.dP_part = static_cast<float*>(c.take(sizeof(float) * BH * w.dP_runs.n_runs * 32 * g.D));
   w.tlist = static_cast<int32_t*>(c.take(sizeof(int32_t) * BH * g.Nq * (size_t)k_keep));
   w.toff = static_cast<int32_t*>(c.take(sizeof(int32_t) * BH * (g.Nk + 1)));
