@@ -1083,8 +1083,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
   const uint16_t* Qs = qd;
   const uint16_t* Ds = qd + 64 * D;
   const int n_units = (e1 - e0) * UPB;
+  // the query block of the next unit is read right after this unit's tile
+  // loads are issued, so that it arrives with them instead of holding up the
+  // next unit's loads (the barriers' waits would take it in before them)
+  int qb_next = n_units > 0 ? list[e0] : 0;
   for (int u = 0; u < n_units; ++u) {
-    const int q0 = __builtin_amdgcn_readfirstlane(list[e0 + u / UPB]) * BQ + 64 * (u % UPB);
+    const int q0 = __builtin_amdgcn_readfirstlane(qb_next) * BQ + 64 * (u % UPB);
     __syncthreads();  // the previous unit's readers are done
     ld.issue_swz(qd, q0, lane, wv, false, [](int t) { return u_swz<D>(t); });
     ld.issue_swz(qd + 64 * D, q0, lane, wv, true, [](int t) { return u_swz<D>(t); });
@@ -1092,6 +1096,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           wv ? drs : lrs, (__attribute__((address_space(3))) void*)((__attribute__((address_space(3))) float*)rowv[wv]),
           4, 4 * lane, (unsigned)q0 * 4, 0, 0);
+    if (u + 1 < n_units) qb_next = list[e0 + (u + 1) / UPB];
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     const int qr0 = 32 * qp;  // first row of the wave's sub-tile in the unit
