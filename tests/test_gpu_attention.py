@@ -289,6 +289,34 @@ def test_rola_separate_normalised_qk():
         assert_close(O[b, :, h], v["O"], f"O(Qn,Kn) h{h}")
 
 
+@pytest.mark.parametrize("cfg", [RAGGED, RAGGED64], ids=lambda c: c.name)
+def test_rola_per_head_projections(cfg):
+    # one P_q and P_k per head (P_head_stride = rank * d)
+    say(f"rola fused {cfg.name}, per-head projections")
+    g = synthetic.gen_gate(cfg, amplified=True)
+    (Qb, Kb, Vb), (Q, K, V) = _inputs(cfg, 2)
+    pp = [synthetic.gen_lowrank_params(cfg, seed=11 + h) for h in range(cfg.H)]
+    Pqb, Pkb = np.stack([x[0] for x in pp]), np.stack([x[1] for x in pp])
+    lr = sd.LowrankParams(dev_bf16(Pqb), dev_bf16(Pkb), head_stride=cfg.rank * cfg.d)
+    k = _kkeep(cfg)
+    nq = -(-cfg.L // cfg.block_q)
+    idx = torch.empty((cfg.B, cfg.H, nq, k), dtype=torch.int32, device="cuda")
+    O = sd.sd_rola_attention(Q, K, V, dev_f32(g), lr, k, grid=(cfg.T, cfg.Hg, cfg.Wg), block_q=cfg.block_q,
+                             idx_out=idx)
+    torch.cuda.synchronize()
+    O, idx = host(O), idx.cpu().numpy()
+    f = oracle.bf16_bits_to_f64
+    for b in range(cfg.B):
+        for h in range(cfg.H):
+            X = [f(x[b, :, h]) for x in (Qb, Kb, Vb)]
+            v = oracle.rola_attention_head(*X, X[0], X[1], f(Pqb[h]), f(Pkb[h]), np.asarray(g[b], dtype=np.float64),
+                                           T=cfg.T, Hg=cfg.Hg, Wg=cfg.Wg, bq=cfg.block_q, bk=cfg.block_k, k_keep=k,
+                                           sm_scale=1.0 / math.sqrt(cfg.d))
+            mism, ties, rows = block_map_diff(idx[b, h], v["S"], k)
+            assert mism == 0 and rows == 0
+            assert_close(O[b, :, h], v["O"], f"O b{b} h{h}")
+
+
 def test_rola_deterministic():
     cfg = MID
     g = synthetic.gen_gate(cfg, amplified=True)

@@ -47,9 +47,12 @@ def _rel(got, ref, name, rel_l2=2.0 ** -7, max_frac=2.0 ** -6):
 
 
 def _run(cfg, seed=0, chunk_frames=0, window=0, separate_qk=False, per_head_gate=False, batch_shared_gate=False,
-         rms_weight=False):
+         rms_weight=False, per_head_proj=False):
     Qb, Kb, Vb = synthetic.gen_qkv(cfg, seed)
     Pqb, Pkb = synthetic.gen_lowrank_params(cfg)
+    if per_head_proj:  # one P_q, P_k per head: [H, rank, d]
+        pp = [synthetic.gen_lowrank_params(cfg, seed=11 + hh) for hh in range(cfg.H)]
+        Pqb, Pkb = np.stack([x[0] for x in pp]), np.stack([x[1] for x in pp])
     rng = np.random.default_rng(seed + 100)
     if per_head_gate:
         g = (1.0 + rng.standard_normal((cfg.B, cfg.L, cfg.H))).astype(np.float32)
@@ -68,7 +71,8 @@ def _run(cfg, seed=0, chunk_frames=0, window=0, separate_qk=False, per_head_gate
     Qn = dev_bf16(Qnb) if separate_qk else None
     Kn = dev_bf16(Knb) if separate_qk else None
     wb = synthetic.gen_norm_weight(cfg.d, seed) if rms_weight else None
-    lr = sd.LowrankParams(dev_bf16(Pqb), dev_bf16(Pkb), rms_weight=dev_bf16(wb) if rms_weight else None)
+    lr = sd.LowrankParams(dev_bf16(Pqb), dev_bf16(Pkb), rms_weight=dev_bf16(wb) if rms_weight else None,
+                          head_stride=cfg.rank * cfg.d if per_head_proj else 0)
     k = oracle.keep_count(cfg.sparsity, -(-cfg.L // cfg.block_k))
     nq = -(-cfg.L // cfg.block_q)
     idx = torch.empty((cfg.B, cfg.H, nq, k), dtype=torch.int32, device="cuda")
@@ -80,10 +84,14 @@ def _run(cfg, seed=0, chunk_frames=0, window=0, separate_qk=False, per_head_gate
     got = {n: (host(t) if t is not None else None) for n, t in grads.items()}
     idx = idx.cpu().numpy()
     f = oracle.bf16_bits_to_f64
-    Pq, Pk = f(Pqb), f(Pkb)
+    Pq_all, Pk_all = f(Pqb), f(Pkb)
     ref = {"dPq": 0.0, "dPk": 0.0, "dg": np.zeros(g.shape)}
+    if per_head_proj:
+        ref["dPq"] = np.zeros((cfg.H, cfg.rank, cfg.d))
+        ref["dPk"] = np.zeros((cfg.H, cfg.rank, cfg.d))
     for b in range(cfg.B):
         for h in range(cfg.H):
+            Pq, Pk = (Pq_all[h], Pk_all[h]) if per_head_proj else (Pq_all, Pk_all)
             X = [f(x[b, :, h]) for x in (Qb, Kb, Vb)]
             Xn = [f(Qnb[b, :, h]), f(Knb[b, :, h])] if separate_qk else X[:2]
             gh = (g[b, :, h] if per_head_gate else g[b]).astype(np.float64)
@@ -100,14 +108,23 @@ def _run(cfg, seed=0, chunk_frames=0, window=0, separate_qk=False, per_head_gate
             _rel(got["dQ"][b, :, h], dQ, f"dQ b{b} h{h}")
             _rel(got["dK"][b, :, h], dK, f"dK b{b} h{h}")
             _rel(got["dV"][b, :, h], res["dV"], f"dV b{b} h{h}")
-            ref["dPq"] = ref["dPq"] + res["dPq"]
-            ref["dPk"] = ref["dPk"] + res["dPk"]
+            if per_head_proj:
+                ref["dPq"][h] += res["dPq"][: cfg.rank]
+                ref["dPk"][h] += res["dPk"][: cfg.rank]
+            else:
+                ref["dPq"] = ref["dPq"] + res["dPq"]
+                ref["dPk"] = ref["dPk"] + res["dPk"]
             if per_head_gate:
                 ref["dg"][b, :, h] = res["dg"]
             else:
                 ref["dg"][b] += res["dg"]
-    _rel(got["dPq"], ref["dPq"][: cfg.rank], "dPq", rel_l2=2.0 ** -9)
-    _rel(got["dPk"], ref["dPk"][: cfg.rank], "dPk", rel_l2=2.0 ** -9)
+    if per_head_proj:
+        for h in range(cfg.H):
+            _rel(got["dPq"][h], ref["dPq"][h], f"dPq h{h}", rel_l2=2.0 ** -9)
+            _rel(got["dPk"][h], ref["dPk"][h], f"dPk h{h}", rel_l2=2.0 ** -9)
+    else:
+        _rel(got["dPq"], ref["dPq"][: cfg.rank], "dPq", rel_l2=2.0 ** -9)
+        _rel(got["dPk"], ref["dPk"][: cfg.rank], "dPk", rel_l2=2.0 ** -9)
     if batch_shared_gate:  # the gradient of the shared row sums over the batch
         assert grads["dg"].stride(0) == 0
         ref["dg"] = ref["dg"].sum(axis=0, keepdims=True)
@@ -135,6 +152,14 @@ def test_backward_rms_weight(cfg):
     # and the RMS coupling term of dO_s
     say(f"backward {cfg.name} with an RMSNorm weight")
     _run(cfg, seed=6, rms_weight=True)
+
+
+@pytest.mark.parametrize("cfg", [RAGGED, RAGGED64], ids=lambda c: c.name)
+def test_backward_per_head_projections(cfg):
+    # one P_q and P_k per head (P_head_stride = rank * d): dP_q, dP_k are
+    # then per head, each summed over that head's tokens (and the batch)
+    say(f"backward {cfg.name} with per-head projections")
+    _run(cfg, seed=8, per_head_proj=True)
 
 
 def test_backward_separate_qk_and_per_head_gate():
